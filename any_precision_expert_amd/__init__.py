@@ -1,0 +1,237 @@
+"""MI355X-native fused mixed-precision MoE expert path (PagedWeight hot path).
+
+Thin ctypes binding of libpw.so, the C ABI declared in include/pw.h.  This
+module only marshals arguments (device pointers from torch tensors, stream
+handles, host numpy buffers); every step of the path runs in the library's
+HIP kernels.  Importing it does not need a GPU; calling into a missing
+library raises immediately -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpw.so")
+
+PW_OK, PW_ERR_INVALID, PW_ERR_OOM, PW_ERR_HIP, PW_ERR_STATE = 0, 1, 2, 3, 4
+QMIN, QMAX = 3, 8
+MODULE_GATE_UP, MODULE_DOWN = 0, 1
+EXPERT_SHARED = -1
+MAX_TOKENS = 65536
+LUT_HALVES_PER_ROW = sum(1 << k for k in range(QMIN, QMAX + 1))
+
+# every function declared in include/pw.h
+EXPORTS = (
+    "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
+    "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert",
+    "pw_moe_ffn_bitplane", "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
+    "pw_resident_bytes", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
+    "pw_profile_read",
+)
+
+
+class PwError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("pw status %d: %s" % (status, msg))
+        self.status = status
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("inter_shared", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("keep_host_masters", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpw.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libpw.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.pw_last_error.restype = ctypes.c_char_p
+        L.pw_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ModelDesc)]
+        L.pw_destroy.argtypes = [vp]
+        L.pw_pack_bitplanes.argtypes = [vp, i64, i64, vp]
+        L.pw_plane_words.argtypes = [i64, i64]
+        L.pw_plane_words.restype = i64
+        L.pw_register_block.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int]
+        L.pw_workspace_size.argtypes = [vp, ctypes.c_int]
+        L.pw_workspace_size.restype = sz
+        L.pw_route_topk.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
+        L.pw_permute_by_expert.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
+        L.pw_moe_ffn_bitplane.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pw_set_committed_bits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
+        L.pw_get_committed_bits.argtypes = [vp, i32, ctypes.POINTER(i32)]
+        L.pw_block_id.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.pw_block_id.restype = i32
+        L.pw_resident_bytes.argtypes = [vp]
+        L.pw_resident_bytes.restype = i64
+        L.pw_debug_decode_codes.argtypes = [vp, i32, vp, vp]
+        L.pw_debug_dequant.argtypes = [vp, i32, vp, vp]
+        L.pw_profile_enable.argtypes = [vp, ctypes.c_int]
+        L.pw_profile_read.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(i64)]
+        for name in EXPORTS:
+            if name not in ("pw_last_error", "pw_plane_words", "pw_workspace_size", "pw_block_id",
+                            "pw_resident_bytes"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().pw_last_error().decode()
+
+
+def _check(st: int) -> None:
+    if st != PW_OK:
+        raise PwError(st, last_error())
+
+
+def _ptr(t) -> int:
+    """Device or host address of a torch tensor, numpy array or int (0 = NULL)."""
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        assert t.flags["C_CONTIGUOUS"]
+        return t.ctypes.data
+    assert t.is_contiguous(), "tensor must be contiguous"
+    return t.data_ptr()
+
+
+def _stream(s) -> int:
+    """hipStream_t of a torch stream (None = torch's current stream)."""
+    if isinstance(s, int):
+        return s
+    if s is None:
+        import torch
+        s = torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ---------------------------------------------------------------- host helpers
+
+def plane_words(R: int, K: int) -> int:
+    return int(lib().pw_plane_words(R, K))
+
+
+def pack_bitplanes(code8: np.ndarray) -> np.ndarray:
+    """uint8 [R][K] parent codes -> uint32 [8][plane_words] bit-planes (library packer)."""
+    c = np.ascontiguousarray(code8, dtype=np.uint8)
+    R, K = c.shape
+    out = np.empty((8, plane_words(R, K)), dtype=np.uint32)
+    _check(lib().pw_pack_bitplanes(_ptr(c), R, K, _ptr(out)))
+    return out
+
+
+def concat_luts(luts: Dict[int, np.ndarray]) -> np.ndarray:
+    """LUT_3..LUT_8 (fp16 [R][2^k] each) -> uint16 [R * 504] in the ABI's order."""
+    parts = [np.ascontiguousarray(luts[k], dtype=np.float16).view(np.uint16).reshape(-1)
+             for k in range(QMIN, QMAX + 1)]
+    return np.concatenate(parts)
+
+
+class Context:
+    """Owns a pw_ctx: the weight page table, device slabs and host masters."""
+
+    def __init__(self, device: int, num_layers: int, num_experts: int, hidden: int, inter: int,
+                 top_k: int, inter_shared: int = 0, keep_host_masters: bool = True):
+        self.desc = ModelDesc(num_layers, num_experts, hidden, inter, inter_shared, top_k,
+                              1 if keep_host_masters else 0)
+        h = ctypes.c_void_p()
+        _check(lib().pw_create(ctypes.byref(h), device, ctypes.byref(self.desc)))
+        self.h = h
+
+    def close(self) -> None:
+        if self.h:
+            _check(lib().pw_destroy(self.h))
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # page table ---------------------------------------------------------
+    def block_id(self, layer: int, expert: int, module: int) -> int:
+        return int(lib().pw_block_id(self.h, layer, expert, module))
+
+    def register_block(self, layer: int, expert: int, module: int, planes: np.ndarray,
+                       luts: np.ndarray, q: int) -> None:
+        p = np.ascontiguousarray(planes, dtype=np.uint32)
+        l_ = np.ascontiguousarray(luts, dtype=np.uint16)
+        _check(lib().pw_register_block(self.h, layer, expert, module, _ptr(p), _ptr(l_), int(q)))
+
+    def register_code_block(self, layer: int, expert: int, module: int, code8: np.ndarray,
+                            luts: Dict[int, np.ndarray], q: int) -> None:
+        self.register_block(layer, expert, module, pack_bitplanes(code8), concat_luts(luts), q)
+
+    def committed_bits(self, block_id: int) -> int:
+        q = ctypes.c_int32()
+        _check(lib().pw_get_committed_bits(self.h, block_id, ctypes.byref(q)))
+        return int(q.value)
+
+    def set_committed_bits(self, block_ids: Sequence[int], q_new: Sequence[int],
+                           compute=None, copy=None) -> None:
+        ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+        qs = np.ascontiguousarray(q_new, dtype=np.uint8)
+        assert ids.size == qs.size
+        _check(lib().pw_set_committed_bits(self.h, ids.size, _ptr(ids), _ptr(qs), _stream(compute),
+                                           _stream(copy) if copy is not None else _stream(compute)))
+
+    def resident_bytes(self) -> int:
+        return int(lib().pw_resident_bytes(self.h))
+
+    # hot path -----------------------------------------------------------
+    def workspace_size(self, T: int) -> int:
+        return int(lib().pw_workspace_size(self.h, T))
+
+    def route_topk(self, logits, T: int, topk_idx, topk_w, stream=None) -> None:
+        _check(lib().pw_route_topk(self.h, _ptr(logits), T, _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+
+    def permute_by_expert(self, topk_idx, T: int, offsets, sorted_assign, stream=None) -> None:
+        _check(lib().pw_permute_by_expert(self.h, _ptr(topk_idx), T, _ptr(offsets), _ptr(sorted_assign),
+                                          _stream(stream)))
+
+    def moe_ffn_bitplane(self, layer: int, x, T: int, topk_idx, topk_w, offsets, sorted_assign, y,
+                         workspace, ws_bytes: Optional[int] = None, stream=None) -> None:
+        if ws_bytes is None:
+            ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib().pw_moe_ffn_bitplane(self.h, layer, _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
+                                         _ptr(offsets), _ptr(sorted_assign), _ptr(y), _ptr(workspace),
+                                         ws_bytes, _stream(stream)))
+
+    # test exports and profiling ----------------------------------------
+    def debug_decode_codes(self, block_id: int, out, stream=None) -> None:
+        _check(lib().pw_debug_decode_codes(self.h, block_id, _ptr(out), _stream(stream)))
+
+    def debug_dequant(self, block_id: int, out, stream=None) -> None:
+        _check(lib().pw_debug_dequant(self.h, block_id, _ptr(out), _stream(stream)))
+
+    def profile_enable(self, on: bool = True) -> None:
+        _check(lib().pw_profile_enable(self.h, 1 if on else 0))
+
+    def profile_read(self, kernel: str):
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        _check(lib().pw_profile_read(self.h, kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+        return float(ms.value), int(n.value)

@@ -1,0 +1,44 @@
+"""Build libpw.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpw.so")
+SOURCES = ["pw_kernels.hip", "pw_context.cpp", "pw_pack.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if c and (os.path.sep not in c or os.path.exists(c)):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def command(out: str = LIB):
+    return [hipcc(), "-O3", "--offload-arch=" + ARCH, "-std=c++17", "-fPIC", "-shared",
+            # packed fp32 instructions stay disabled in every kernel
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+            "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    print(LIB)

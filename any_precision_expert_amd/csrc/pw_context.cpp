@@ -1,0 +1,760 @@
+// Host side of the C ABI declared in include/pw.h: argument validation, the
+// weight page table (device array of BlockDesc, host mirror), the device slab
+// pool for planes and LUTs, pinned host masters, committed-width changes with
+// asynchronous host->device plane movement, and kernel launches.
+//
+// PagedWeight pages, "Technical summary: PagedWeight", Core components 1
+// (weight page table tracking each linear block's committed width; pages
+// resident on the GPU, on the CPU or in transfer) and 3 (asynchronous page
+// movement, widths committed only at safe boundaries).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pw.h"
+#include "pw_internal.h"
+
+using namespace pw;
+
+namespace {
+
+thread_local std::string g_err;
+
+pw_status fail(pw_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pw_status fail(pw_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+pw_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(PW_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+pw_status ok()
+{
+    g_err.clear();
+    return PW_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Device slabs for planes and LUTs, recycled by size.  A released slab is only
+// reused after an event recorded behind the last work that may read it.
+class SlabPool {
+public:
+    ~SlabPool() { clear(); }
+
+    hipError_t alloc(size_t bytes, void** out)
+    {
+        bytes = round(bytes);
+        reclaim();
+        auto it = free_.find(bytes);
+        if (it != free_.end() && !it->second.empty()) {
+            *out = it->second.back();
+            it->second.pop_back();
+            resident_ += bytes;
+            return hipSuccess;
+        }
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e;
+        }
+        all_[p] = bytes;
+        resident_ += bytes;
+        *out = p;
+        return hipSuccess;
+    }
+
+    void release_now(void* p, size_t bytes)
+    {
+        if (!p) return;
+        bytes = round(bytes);
+        free_[bytes].push_back(p);
+        resident_ -= bytes;
+    }
+
+    void release_after(void* p, size_t bytes, hipEvent_t ev)
+    {
+        if (!p) return;
+        bytes = round(bytes);
+        pending_.push_back({p, bytes, ev});
+        resident_ -= bytes;
+    }
+
+    void reclaim()
+    {
+        size_t w = 0;
+        for (size_t i = 0; i < pending_.size(); ++i) {
+            if (hipEventQuery(pending_[i].ev) == hipSuccess) {
+                free_[pending_[i].bytes].push_back(pending_[i].p);
+            } else {
+                pending_[w++] = pending_[i];
+            }
+        }
+        pending_.resize(w);
+    }
+
+    int64_t resident() const { return (int64_t)resident_; }
+
+    void clear()
+    {
+        for (auto& kv : all_) (void)hipFree(kv.first);
+        all_.clear();
+        free_.clear();
+        pending_.clear();
+        resident_ = 0;
+    }
+
+private:
+    static size_t round(size_t b) { return (b + 255) & ~size_t(255); }
+    struct Pending {
+        void* p;
+        size_t bytes;
+        hipEvent_t ev;
+    };
+    std::unordered_map<size_t, std::vector<void*>> free_;
+    std::vector<Pending> pending_;
+    std::unordered_map<void*, size_t> all_;
+    size_t resident_ = 0;
+};
+
+struct HostBlock {
+    bool registered = false;
+    int R = 0, K = 0, q = 0;
+    int64_t pw = 0;  // words per plane
+    void* dplanes[8] = {};
+    void* dlut = nullptr;
+    uint32_t* hplanes = nullptr;  // pinned master: 8 planes
+    uint16_t* hluts = nullptr;    // pinned master: LUT_3..LUT_8
+};
+
+size_t lut_bytes(int R, int q) { return (size_t)R * ((size_t)1 << q) * 2; }
+size_t lut_offset_halves(int R, int q) { return (size_t)R * (((size_t)1 << q) - 8); }
+
+struct ProfRec {
+    hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct pw_ctx {
+    int device = 0;
+    pw_model_desc d{};
+    int nblocks = 0;
+    BlockDesc* d_table = nullptr;
+    std::vector<BlockDesc> h_table;
+    std::vector<HostBlock> blocks;
+    SlabPool pool;
+    // pinned staging for page-table updates, recycled after their event
+    struct Staging {
+        BlockDesc* p;
+        size_t n;
+        hipEvent_t ev;
+    };
+    std::vector<Staging> staging;
+    std::vector<hipEvent_t> events;  // owned events (released at destroy)
+    bool profiling = false;
+    std::map<std::string, std::vector<ProfRec>> prof;
+};
+
+namespace {
+
+hipError_t new_event(pw_ctx* c, hipEvent_t* ev)
+{
+    hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (e == hipSuccess) c->events.push_back(*ev);
+    return e;
+}
+
+int block_id(const pw_ctx* c, int layer, int expert, int module)
+{
+    const int E = c->d.num_experts;
+    if (layer < 0 || layer >= c->d.num_layers) return -1;
+    if (module != PW_MODULE_GATE_UP && module != PW_MODULE_DOWN) return -1;
+    int slot;
+    if (expert == PW_EXPERT_SHARED) {
+        if (c->d.inter_shared <= 0) return -1;
+        slot = E;
+    } else if (expert >= 0 && expert < E) {
+        slot = expert;
+    } else {
+        return -1;
+    }
+    return (layer * (E + 1) + slot) * 2 + module;
+}
+
+void block_shape(const pw_ctx* c, int id, int* R, int* K)
+{
+    const int E = c->d.num_experts;
+    const int module = id & 1;
+    const int slot = (id >> 1) % (E + 1);
+    const int I = slot == E ? c->d.inter_shared : c->d.inter;
+    if (module == PW_MODULE_GATE_UP) {
+        *R = 2 * I;
+        *K = c->d.hidden;
+    } else {
+        *R = c->d.hidden;
+        *K = I;
+    }
+}
+
+BlockDesc make_desc(const HostBlock& b)
+{
+    BlockDesc d;
+    std::memset(&d, 0, sizeof d);
+    for (int p = 0; p < 8; ++p) d.planes[p] = p < b.q ? (const uint32_t*)b.dplanes[p] : nullptr;
+    d.lut = (const uint16_t*)b.dlut;
+    d.q = b.q;
+    d.R = b.R;
+    d.K = b.K;
+    d.nchunks = (b.K + kChunkCols - 1) / kChunkCols;
+    d.kwords = b.K / 32;
+    return d;
+}
+
+void free_block_now(pw_ctx* c, HostBlock& b)
+{
+    for (int p = 0; p < 8; ++p) {
+        c->pool.release_now(b.dplanes[p], (size_t)b.pw * 4);
+        b.dplanes[p] = nullptr;
+    }
+    c->pool.release_now(b.dlut, lut_bytes(b.R, b.q));
+    b.dlut = nullptr;
+    if (b.hplanes) (void)hipHostFree(b.hplanes);
+    if (b.hluts) (void)hipHostFree(b.hluts);
+    b.hplanes = nullptr;
+    b.hluts = nullptr;
+    b.registered = false;
+}
+
+struct ProfScope {
+    pw_ctx* c;
+    const char* name;
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    ProfScope(pw_ctx* c_, const char* n, hipStream_t s_) : c(c_), name(n), s(s_)
+    {
+        if (c->profiling && hipEventCreate(&a) == hipSuccess) (void)hipEventRecord(a, s);
+    }
+    ~ProfScope()
+    {
+        if (!a) return;
+        hipEvent_t b;
+        if (hipEventCreate(&b) == hipSuccess) {
+            (void)hipEventRecord(b, s);
+            c->prof[name].push_back({a, b});
+        } else {
+            (void)hipEventDestroy(a);
+        }
+    }
+};
+
+void prof_reset(pw_ctx* c)
+{
+    for (auto& kv : c->prof)
+        for (auto& r : kv.second) {
+            (void)hipEventDestroy(r.a);
+            (void)hipEventDestroy(r.b);
+        }
+    c->prof.clear();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pw_last_error(void) { return g_err.c_str(); }
+
+int64_t pw_plane_words(int64_t R, int64_t K) { return (R > 0 && K > 0) ? plane_words(R, K) : 0; }
+
+pw_status pw_pack_bitplanes(const uint8_t* codes, int64_t R, int64_t K, uint32_t* planes)
+{
+    if (!codes || !planes) return fail(PW_ERR_INVALID, "pw_pack_bitplanes: null pointer");
+    if (R <= 0 || K <= 0 || K % 32 != 0 || R > (1 << 24) || K > (1 << 24))
+        return fail(PW_ERR_INVALID, "pw_pack_bitplanes: need R > 0 and K a positive multiple of 32 (R=%lld K=%lld)",
+                    (long long)R, (long long)K);
+    pack_bitplanes(codes, R, K, planes);
+    return ok();
+}
+
+pw_status pw_create(pw_ctx** out, int hip_device, const pw_model_desc* d)
+{
+    if (!out || !d) return fail(PW_ERR_INVALID, "pw_create: null pointer");
+    *out = nullptr;
+    const bool shape_ok = d->num_layers >= 1 && d->num_layers <= 4096 && d->num_experts >= 1 &&
+                          d->num_experts <= 256 && d->hidden >= 32 && d->hidden <= 65536 &&
+                          d->hidden % 32 == 0 && d->inter >= 32 && d->inter <= 131072 && d->inter % 32 == 0 &&
+                          d->inter_shared >= 0 && d->inter_shared <= 131072 && d->inter_shared % 32 == 0 &&
+                          d->top_k >= 1 && d->top_k <= 8 && d->top_k <= d->num_experts;
+    if (!shape_ok) return fail(PW_ERR_INVALID, "pw_create: model description out of range");
+    int ndev = 0;
+    hipError_t e = hipGetDeviceCount(&ndev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (hip_device < 0 || hip_device >= ndev) return fail(PW_ERR_INVALID, "pw_create: no HIP device %d", hip_device);
+    e = hipSetDevice(hip_device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    pw_ctx* c = new (std::nothrow) pw_ctx();
+    if (!c) return fail(PW_ERR_OOM, "pw_create: host allocation");
+    c->device = hip_device;
+    c->d = *d;
+    c->nblocks = d->num_layers * (d->num_experts + 1) * 2;
+    c->h_table.assign(c->nblocks, BlockDesc{});
+    c->blocks.assign(c->nblocks, HostBlock{});
+    e = hipMalloc(&c->d_table, sizeof(BlockDesc) * c->nblocks);
+    if (e != hipSuccess) {
+        delete c;
+        return fail(PW_ERR_OOM, "pw_create: page table: %s", hipGetErrorString(e));
+    }
+    e = hipMemset(c->d_table, 0, sizeof(BlockDesc) * c->nblocks);
+    if (e != hipSuccess) {
+        (void)hipFree(c->d_table);
+        delete c;
+        return hip_fail(e, "hipMemset(page table)");
+    }
+    *out = c;
+    return ok();
+}
+
+pw_status pw_destroy(pw_ctx* c)
+{
+    if (!c) return ok();
+    (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    prof_reset(c);
+    for (auto& b : c->blocks)
+        if (b.registered) free_block_now(c, b);
+    for (auto& s : c->staging) (void)hipHostFree(s.p);
+    for (auto ev : c->events) (void)hipEventDestroy(ev);
+    c->pool.clear();
+    (void)hipFree(c->d_table);
+    delete c;
+    return ok();
+}
+
+int32_t pw_block_id(const pw_ctx* c, int layer, int expert, int module)
+{
+    return c ? block_id(c, layer, expert, module) : -1;
+}
+
+pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const uint32_t* host_planes,
+                            const uint16_t* host_luts, int q_init)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_register_block: null context");
+    const int id = block_id(c, layer, expert, module);
+    if (id < 0) return fail(PW_ERR_INVALID, "pw_register_block: (layer %d, expert %d, module %d) out of range",
+                            layer, expert, module);
+    if (!host_planes || !host_luts) return fail(PW_ERR_INVALID, "pw_register_block: null pointer");
+    if (q_init < PW_QMIN || q_init > PW_QMAX) return fail(PW_ERR_INVALID, "pw_register_block: q_init %d not in 3..8", q_init);
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    int R, K;
+    block_shape(c, id, &R, &K);
+    HostBlock nb;
+    nb.R = R;
+    nb.K = K;
+    nb.q = q_init;
+    nb.pw = plane_words(R, K);
+    const size_t plane_b = (size_t)nb.pw * 4;
+    const size_t luts_b = (size_t)R * kLutHalvesPerRow * 2;
+    auto undo = [&]() {
+        for (int p = 0; p < 8; ++p) c->pool.release_now(nb.dplanes[p], plane_b);
+        c->pool.release_now(nb.dlut, lut_bytes(R, q_init));
+        if (nb.hplanes) (void)hipHostFree(nb.hplanes);
+        if (nb.hluts) (void)hipHostFree(nb.hluts);
+    };
+    for (int p = 0; p < q_init; ++p) {
+        if ((e = c->pool.alloc(plane_b, &nb.dplanes[p])) != hipSuccess) {
+            undo();
+            return fail(PW_ERR_OOM, "pw_register_block: device plane: %s", hipGetErrorString(e));
+        }
+    }
+    if ((e = c->pool.alloc(lut_bytes(R, q_init), &nb.dlut)) != hipSuccess) {
+        undo();
+        return fail(PW_ERR_OOM, "pw_register_block: device LUT: %s", hipGetErrorString(e));
+    }
+    if (c->d.keep_host_masters) {
+        if (hipHostMalloc((void**)&nb.hplanes, plane_b * 8, hipHostMallocDefault) != hipSuccess ||
+            hipHostMalloc((void**)&nb.hluts, luts_b, hipHostMallocDefault) != hipSuccess) {
+            (void)hipGetLastError();
+            undo();
+            return fail(PW_ERR_OOM, "pw_register_block: pinned host master");
+        }
+        std::memcpy(nb.hplanes, host_planes, plane_b * 8);
+        std::memcpy(nb.hluts, host_luts, luts_b);
+    }
+    for (int p = 0; p < q_init && e == hipSuccess; ++p)
+        e = hipMemcpy(nb.dplanes[p], host_planes + (size_t)p * nb.pw, plane_b, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(nb.dlut, host_luts + lut_offset_halves(R, q_init), lut_bytes(R, q_init), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        undo();
+        return hip_fail(e, "pw_register_block: copy to device");
+    }
+    nb.registered = true;
+    BlockDesc desc = make_desc(nb);
+    e = hipMemcpy(c->d_table + id, &desc, sizeof desc, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        undo();
+        return hip_fail(e, "pw_register_block: page-table entry");
+    }
+    if (c->blocks[id].registered) {
+        (void)hipDeviceSynchronize();
+        free_block_now(c, c->blocks[id]);
+    }
+    c->blocks[id] = nb;
+    c->h_table[id] = desc;
+    return ok();
+}
+
+size_t pw_workspace_size(const pw_ctx* c, int T)
+{
+    if (!c || T <= 0) return 0;
+    return ws_layout(T, c->d.top_k, c->d.hidden, c->d.inter, c->d.inter_shared).total;
+}
+
+pw_status pw_route_topk(pw_ctx* c, const float* logits, int T, int32_t* idx, float* w, pw_stream stream)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_route_topk: null context");
+    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_route_topk: T=%d out of range", T);
+    if (T == 0) return ok();
+    if (!logits || !idx || !w) return fail(PW_ERR_INVALID, "pw_route_topk: null pointer");
+    if (!aligned16(logits) || !aligned16(idx) || !aligned16(w))
+        return fail(PW_ERR_INVALID, "pw_route_topk: device pointers must be 16-byte aligned");
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    ProfScope ps(c, "route", (hipStream_t)stream);
+    e = launch_route_topk(logits, T, c->d.num_experts, c->d.top_k, idx, w, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "route_topk launch");
+}
+
+pw_status pw_permute_by_expert(pw_ctx* c, const int32_t* idx, int T, int32_t* offsets, int32_t* sorted,
+                               pw_stream stream)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null context");
+    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_permute_by_expert: T=%d out of range", T);
+    if (!offsets) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null offsets");
+    if (T > 0 && (!idx || !sorted)) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null pointer");
+    if (!aligned16(offsets) || (T > 0 && (!aligned16(idx) || !aligned16(sorted))))
+        return fail(PW_ERR_INVALID, "pw_permute_by_expert: device pointers must be 16-byte aligned");
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    ProfScope ps(c, "permute", (hipStream_t)stream);
+    e = launch_permute(idx, T, c->d.top_k, c->d.num_experts, offsets, sorted, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
+}
+
+pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, const int32_t* idx,
+                              const float* w, const int32_t* offsets, const int32_t* sorted, uint16_t* y,
+                              void* workspace, size_t ws_bytes, pw_stream stream)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: null context");
+    if (layer < 0 || layer >= c->d.num_layers) return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: layer %d out of range", layer);
+    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: T=%d out of range", T);
+    if (T == 0) return ok();
+    if (!x || !idx || !w || !offsets || !sorted || !y || !workspace)
+        return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: null pointer");
+    if (!aligned16(x) || !aligned16(idx) || !aligned16(w) || !aligned16(offsets) || !aligned16(sorted) ||
+        !aligned16(y) || ((uintptr_t)workspace & 255u))
+        return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: misaligned pointer (16 B; workspace 256 B)");
+    const pw_model_desc& d = c->d;
+    const WsLayout L = ws_layout(T, d.top_k, d.hidden, d.inter, d.inter_shared);
+    if (ws_bytes < L.total)
+        return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: workspace %zu B < %zu B needed", ws_bytes, L.total);
+    const int E = d.num_experts;
+    for (int s = 0; s <= E; ++s) {
+        if (s == E && d.inter_shared == 0) break;
+        for (int m = 0; m < 2; ++m) {
+            const int id = (layer * (E + 1) + s) * 2 + m;
+            if (!c->blocks[id].registered)
+                return fail(PW_ERR_STATE, "pw_moe_ffn_bitplane: block (layer %d, slot %d, module %d) not registered",
+                            layer, s, m);
+        }
+    }
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    char* ws = (char*)workspace;
+    FfnArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.table = c->d_table + (size_t)layer * (E + 1) * 2;
+    a.x = x;
+    a.offsets = offsets;
+    a.sorted = sorted;
+    a.topk_w = w;
+    a.h_hi = (uint16_t*)(ws + L.h_hi);
+    a.h_lo = (uint16_t*)(ws + L.h_lo);
+    a.dout = (float*)(ws + L.dout);
+    a.y = y;
+    a.T = T;
+    a.H = d.hidden;
+    a.I = d.inter;
+    a.Is = d.inter_shared;
+    a.E = E;
+    a.k = d.top_k;
+    a.n_slots = std::min(E, T * d.top_k);
+    a.hstride = std::max(d.inter, d.inter_shared);
+    hipStream_t s = (hipStream_t)stream;
+    {
+        ProfScope ps(c, "gate_up", s);
+        a.tiles_routed = d.inter / 32;
+        a.tiles_shared = d.inter_shared / 32;
+        if ((e = launch_gate_up(a, s)) != hipSuccess) return hip_fail(e, "gate_up launch");
+    }
+    {
+        ProfScope ps(c, "down", s);
+        a.tiles_routed = (d.hidden + 63) / 64;
+        a.tiles_shared = d.inter_shared ? (d.hidden + 63) / 64 : 0;
+        if ((e = launch_down(a, s)) != hipSuccess) return hip_fail(e, "down launch");
+    }
+    {
+        ProfScope ps(c, "combine", s);
+        if ((e = launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
+    }
+    return ok();
+}
+
+pw_status pw_get_committed_bits(const pw_ctx* c, int32_t id, int32_t* q_out)
+{
+    if (!c || !q_out) return fail(PW_ERR_INVALID, "pw_get_committed_bits: null pointer");
+    if (id < 0 || id >= c->nblocks) return fail(PW_ERR_INVALID, "pw_get_committed_bits: block id %d out of range", id);
+    *q_out = c->blocks[id].registered ? c->blocks[id].q : 0;
+    return ok();
+}
+
+int64_t pw_resident_bytes(const pw_ctx* c) { return c ? c->pool.resident() : 0; }
+
+pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint8_t* q_new, pw_stream compute,
+                                pw_stream copy)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_set_committed_bits: null context");
+    if (n < 0) return fail(PW_ERR_INVALID, "pw_set_committed_bits: n < 0");
+    if (n == 0) return ok();
+    if (!ids || !q_new) return fail(PW_ERR_INVALID, "pw_set_committed_bits: null pointer");
+    std::unordered_set<int32_t> seen;
+    for (int i = 0; i < n; ++i) {
+        const int32_t id = ids[i];
+        if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+            return fail(PW_ERR_INVALID, "pw_set_committed_bits: block id %d not registered", id);
+        if (q_new[i] < PW_QMIN || q_new[i] > PW_QMAX)
+            return fail(PW_ERR_INVALID, "pw_set_committed_bits: q %d not in 3..8", (int)q_new[i]);
+        if (!seen.insert(id).second) return fail(PW_ERR_INVALID, "pw_set_committed_bits: duplicate block id %d", id);
+    }
+    std::vector<int> changed;
+    for (int i = 0; i < n; ++i)
+        if (q_new[i] != c->blocks[ids[i]].q) changed.push_back(i);
+    if (changed.empty()) return ok();
+    if (!c->d.keep_host_masters)
+        return fail(PW_ERR_STATE, "pw_set_committed_bits: the context keeps no host masters (keep_host_masters = 0)");
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    hipStream_t cs = (hipStream_t)compute, xs = (hipStream_t)copy;
+
+    // 1. allocate everything first so a failure changes nothing
+    struct Plan {
+        int id;
+        int qo, qn;
+        void* planes[8];
+        void* lut;
+    };
+    std::vector<Plan> plans;
+    plans.reserve(changed.size());
+    auto rollback = [&]() {
+        for (auto& p : plans) {
+            const HostBlock& b = c->blocks[p.id];
+            for (int j = p.qo; j < p.qn; ++j) c->pool.release_now(p.planes[j], (size_t)b.pw * 4);
+            c->pool.release_now(p.lut, lut_bytes(b.R, p.qn));
+        }
+    };
+    for (int i : changed) {
+        Plan p;
+        std::memset(&p, 0, sizeof p);
+        p.id = ids[i];
+        const HostBlock& b = c->blocks[p.id];
+        p.qo = b.q;
+        p.qn = q_new[i];
+        plans.push_back(p);
+        Plan& pr = plans.back();
+        for (int j = pr.qo; j < pr.qn; ++j) {
+            if ((e = c->pool.alloc((size_t)b.pw * 4, &pr.planes[j])) != hipSuccess) {
+                rollback();
+                return fail(PW_ERR_OOM, "pw_set_committed_bits: device plane: %s", hipGetErrorString(e));
+            }
+        }
+        if ((e = c->pool.alloc(lut_bytes(b.R, pr.qn), &pr.lut)) != hipSuccess) {
+            rollback();
+            return fail(PW_ERR_OOM, "pw_set_committed_bits: device LUT: %s", hipGetErrorString(e));
+        }
+    }
+    // pinned staging for the page-table entries
+    pw_ctx::Staging st{nullptr, plans.size(), nullptr};
+    for (size_t i = 0; i < c->staging.size(); ++i) {
+        if (c->staging[i].n >= plans.size() && hipEventQuery(c->staging[i].ev) == hipSuccess) {
+            st = c->staging[i];
+            c->staging.erase(c->staging.begin() + i);
+            break;
+        }
+    }
+    if (!st.p) {
+        if (hipHostMalloc((void**)&st.p, sizeof(BlockDesc) * plans.size(), hipHostMallocDefault) != hipSuccess) {
+            (void)hipGetLastError();
+            rollback();
+            return fail(PW_ERR_OOM, "pw_set_committed_bits: pinned staging");
+        }
+        st.n = plans.size();
+        if ((e = new_event(c, &st.ev)) != hipSuccess) {
+            (void)hipHostFree(st.p);
+            rollback();
+            return hip_fail(e, "hipEventCreate");
+        }
+    }
+    // 2. copies of raised planes and every new LUT on the copy stream
+    for (auto& p : plans) {
+        const HostBlock& b = c->blocks[p.id];
+        for (int j = p.qo; j < p.qn && e == hipSuccess; ++j)
+            e = hipMemcpyAsync(p.planes[j], b.hplanes + (size_t)j * b.pw, (size_t)b.pw * 4, hipMemcpyHostToDevice, xs);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(p.lut, b.hluts + lut_offset_halves(b.R, p.qn), lut_bytes(b.R, p.qn),
+                               hipMemcpyHostToDevice, xs);
+        if (e != hipSuccess) break;
+    }
+    hipEvent_t copied = nullptr;
+    if (e == hipSuccess) e = new_event(c, &copied);
+    if (e == hipSuccess) e = hipEventRecord(copied, xs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, copied, 0);
+    if (e != hipSuccess) {
+        // copies may be in flight into the new slabs: wait before recycling them
+        (void)hipStreamSynchronize(xs);
+        rollback();
+        c->staging.push_back(st);
+        return hip_fail(e, "pw_set_committed_bits: enqueue copies");
+    }
+    // 3. page-table update, stream-ordered on the compute stream
+    std::vector<BlockDesc> newdesc(plans.size());
+    for (size_t i = 0; i < plans.size(); ++i) {
+        HostBlock nb = c->blocks[plans[i].id];
+        for (int j = 0; j < 8; ++j)
+            if (j >= plans[i].qo && j < plans[i].qn) nb.dplanes[j] = plans[i].planes[j];
+        for (int j = plans[i].qn; j < 8; ++j) nb.dplanes[j] = nullptr;
+        nb.q = plans[i].qn;
+        nb.dlut = plans[i].lut;
+        newdesc[i] = make_desc(nb);
+        st.p[i] = newdesc[i];
+    }
+    for (size_t i = 0; i < plans.size() && e == hipSuccess; ++i)
+        e = hipMemcpyAsync(c->d_table + plans[i].id, st.p + i, sizeof(BlockDesc), hipMemcpyHostToDevice, cs);
+    hipEvent_t updated = nullptr;
+    if (e == hipSuccess) e = new_event(c, &updated);
+    if (e == hipSuccess) e = hipEventRecord(updated, cs);
+    if (e == hipSuccess) e = hipEventRecord(st.ev, cs);
+    if (e != hipSuccess) {
+        (void)hipStreamSynchronize(cs);
+        (void)hipStreamSynchronize(xs);
+        // the device table may hold some new entries: restore the old ones
+        for (auto& p : plans) (void)hipMemcpy(c->d_table + p.id, &c->h_table[p.id], sizeof(BlockDesc), hipMemcpyHostToDevice);
+        rollback();
+        c->staging.push_back(st);
+        return hip_fail(e, "pw_set_committed_bits: page-table update");
+    }
+    c->staging.push_back(st);
+    // 4. commit on the host; old slabs are recycled after `updated`
+    for (size_t i = 0; i < plans.size(); ++i) {
+        HostBlock& b = c->blocks[plans[i].id];
+        for (int j = plans[i].qn; j < plans[i].qo; ++j) {
+            c->pool.release_after(b.dplanes[j], (size_t)b.pw * 4, updated);
+            b.dplanes[j] = nullptr;
+        }
+        for (int j = plans[i].qo; j < plans[i].qn; ++j) b.dplanes[j] = plans[i].planes[j];
+        c->pool.release_after(b.dlut, lut_bytes(b.R, b.q), updated);
+        b.dlut = plans[i].lut;
+        b.q = plans[i].qn;
+        c->h_table[plans[i].id] = newdesc[i];
+    }
+    return ok();
+}
+
+pw_status pw_debug_decode_codes(pw_ctx* c, int32_t id, uint8_t* out, pw_stream stream)
+{
+    if (!c || !out) return fail(PW_ERR_INVALID, "pw_debug_decode_codes: null pointer");
+    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+        return fail(PW_ERR_INVALID, "pw_debug_decode_codes: block id %d not registered", id);
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    const HostBlock& b = c->blocks[id];
+    e = launch_debug_decode(c->d_table + id, b.R, b.K, out, nullptr, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "debug decode launch");
+}
+
+pw_status pw_debug_dequant(pw_ctx* c, int32_t id, uint16_t* out, pw_stream stream)
+{
+    if (!c || !out) return fail(PW_ERR_INVALID, "pw_debug_dequant: null pointer");
+    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+        return fail(PW_ERR_INVALID, "pw_debug_dequant: block id %d not registered", id);
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    const HostBlock& b = c->blocks[id];
+    e = launch_debug_decode(c->d_table + id, b.R, b.K, nullptr, out, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "debug dequant launch");
+}
+
+pw_status pw_profile_enable(pw_ctx* c, int on)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_profile_enable: null context");
+    (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    prof_reset(c);
+    c->profiling = on != 0;
+    return ok();
+}
+
+pw_status pw_profile_read(pw_ctx* c, const char* kernel, double* total_ms, int64_t* launches)
+{
+    if (!c || !kernel || !total_ms || !launches) return fail(PW_ERR_INVALID, "pw_profile_read: null pointer");
+    *total_ms = 0.0;
+    *launches = 0;
+    auto it = c->prof.find(kernel);
+    if (it == c->prof.end()) return ok();
+    for (auto& r : it->second) {
+        float ms = 0.0f;
+        hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) return hip_fail(e, "pw_profile_read: hipEventElapsedTime (stream not synchronised?)");
+        *total_ms += ms;
+        *launches += 1;
+    }
+    return ok();
+}
+
+}  // extern "C"
+
+namespace pw {
+
+WsLayout ws_layout(int T, int k, int H, int I, int Is)
+{
+    auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+    const size_t rows = (size_t)T * k + (Is ? (size_t)T : 0);
+    const size_t hs = (size_t)std::max(I, Is);
+    WsLayout L;
+    L.h_hi = 0;
+    L.h_lo = up(L.h_hi + rows * hs * 2);
+    L.dout = up(L.h_lo + rows * hs * 2);
+    L.total = up(L.dout + rows * (size_t)H * 4);
+    return L;
+}
+
+}  // namespace pw

@@ -1,0 +1,68 @@
+// Internal declarations shared by the host ABI layer and the HIP kernels of
+// the PagedWeight fused mixed-precision MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pw {
+
+constexpr int kQMin = 3;
+constexpr int kQMax = 8;
+constexpr int kChunkCols = 128;  // columns per plane chunk (4 words of 32)
+constexpr int kLutHalvesPerRow = 8 + 16 + 32 + 64 + 128 + 256;  // LUT_3..LUT_8
+
+// One entry of the device weight page table: a linear block at its committed
+// width q.  planes[p] is valid for p < q; lut points at LUT_q [R][2^q] fp16.
+struct alignas(128) BlockDesc {
+    const uint32_t* planes[8];
+    const uint16_t* lut;
+    int32_t q;
+    int32_t R;
+    int32_t K;
+    int32_t nchunks;  // ceil(K / 128)
+    int32_t kwords;   // K / 32
+    int32_t pad[9];
+};
+static_assert(sizeof(BlockDesc) == 128, "page-table entry must be 128 bytes");
+
+// Arguments of the FFN kernels (passed by value).
+struct FfnArgs {
+    const BlockDesc* table;   // this layer's entries, [(E + 1) * 2]
+    const uint16_t* x;        // fp16 [T][H]
+    const int32_t* offsets;   // [E + 1]
+    const int32_t* sorted;    // [T * k]
+    const float* topk_w;      // [T * k]
+    uint16_t* h_hi;           // fp16 [T * k + T][hstride]
+    uint16_t* h_lo;           // fp16 [T * k + T][hstride]
+    float* dout;              // fp32 [T * k + T][H]
+    uint16_t* y;              // fp16 [T][H]
+    int32_t T, H, I, Is, E, k;
+    int32_t n_slots;          // routed slots: min(E, T * k)
+    int32_t tiles_routed;     // row tiles per routed block
+    int32_t tiles_shared;     // row tiles of the shared block (0 = none)
+    int32_t hstride;          // max(I, Is)
+};
+
+// Workspace carve-up for T tokens (byte offsets, 256-aligned).
+struct WsLayout {
+    size_t h_hi, h_lo, dout, total;
+};
+WsLayout ws_layout(int T, int k, int H, int I, int Is);
+
+// Launchers (return the launch's hipError_t).
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                             hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted, hipStream_t s);
+hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
+hipError_t launch_debug_decode(const BlockDesc* entry, int R, int K, uint8_t* codes_out,
+                               uint16_t* w_out, hipStream_t s);
+
+// Host packer (pw_pack.cpp).
+void pack_bitplanes(const uint8_t* codes, int64_t R, int64_t K, uint32_t* planes);
+int64_t plane_words(int64_t R, int64_t K);
+
+}  // namespace pw

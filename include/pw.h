@@ -1,0 +1,203 @@
+/*
+ * pw.h -- C ABI of the MI355X (gfx950) fused mixed-precision MoE expert
+ * library: PagedWeight's data-parallel hot path.
+ *
+ * Source of the method: the PagedWeight pages ("Technical summary:
+ * PagedWeight", "Core components" 1 and 3).  Expert weights are handled per
+ * linear block (layer, expert, gate_up | down), held in the Any-Precision
+ * overlaid bit-plane form with per-row look-up tables; a weight page table
+ * records each block's committed width q_i; one fused MoE operation reads the
+ * planes and LUTs directly at each block's own q_i; width changes are
+ * committed only at safe boundaries, with pages moved asynchronously between
+ * host and device memory.
+ *
+ * Conventions for every function:
+ *  - Return a pw_status; nothing is thrown across the ABI.  On any error the
+ *    call enqueues no GPU work and changes no library state, and
+ *    pw_last_error() describes the failure (thread-local, valid until the next
+ *    call on the same thread).
+ *  - "dev" pointers are device memory owned by the caller (for example torch
+ *    tensors); "host" pointers are ordinary host memory owned by the caller.
+ *    Device pointers must be 16-byte aligned.  Nothing the caller passes is
+ *    retained after the call returns, except through work enqueued on the
+ *    given stream.
+ *  - Hot-path calls (pw_route_topk, pw_permute_by_expert, pw_moe_ffn_bitplane)
+ *    are asynchronous on `stream`: no host synchronisation, no allocation.
+ *    Kernel faults surface at the caller's next synchronisation.
+ *  - A context is not thread-safe: drive it from one host thread.
+ *
+ * Data formats (all little-endian):
+ *  - Parent codes are p = 8 bits.  The child code at width q (3..8) is
+ *    code8 >> (8 - q), and the weight is LUT_q[row][child code].
+ *  - Bit-planes: plane p (0..7) holds bit (7 - p) of every parent code, so a
+ *    width-q read uses planes 0..q-1 only.  A block with R rows and K columns
+ *    (K a multiple of 32) has K/32 words per row per plane; word w of row r
+ *    covers columns 32w..32w+31, and column 32w + 8P + 2i + h
+ *    (P, i in 0..3, h in 0..1) sits at bit 8i + 4h + P of that word.  Words
+ *    are stored chunk-major: plane p is an array [ceil(K/128)][R][4] of
+ *    uint32 (4 consecutive words = 128 columns of one row are contiguous,
+ *    rows follow each other inside a 128-column chunk; missing words of a
+ *    last partial chunk are zero).
+ *  - LUTs: fp16, for each child width k = 3..8 an array [R][2^k], the six
+ *    arrays concatenated in k order (R * 504 halves per block).
+ *  - gate_up blocks have R = 2*I rows (rows [0, I) gate, [I, 2I) up) and
+ *    K = H; down blocks have R = H, K = I.  The FFN of one expert is
+ *    h = silu(gate x) * (up x), d = down h; token t's output is
+ *    y_t = sum_j w[t][j] * d_(t, idx[t][j]) (+ shared expert d, weight 1).
+ */
+#ifndef PW_H_
+#define PW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PW_OK = 0,
+    PW_ERR_INVALID = 1, /* bad argument: null/misaligned pointer, size or id out of range */
+    PW_ERR_OOM = 2,     /* device or pinned host allocation failed                     */
+    PW_ERR_HIP = 3,     /* a HIP runtime call failed; pw_last_error() has its message   */
+    PW_ERR_STATE = 4    /* the call does not fit the context's state (e.g. a block not
+                           registered yet)                                             */
+} pw_status;
+
+typedef struct pw_ctx pw_ctx;
+
+/* Opaque HIP stream handle (hipStream_t); NULL is the device's null stream. */
+typedef void *pw_stream;
+
+/* Shape of the MoE model whose expert blocks a context manages. */
+typedef struct {
+    int32_t num_layers;        /* >= 1                                            */
+    int32_t num_experts;       /* routed experts per layer, 1..256                 */
+    int32_t hidden;            /* H, multiple of 32, 32..65536                     */
+    int32_t inter;             /* I of a routed expert, multiple of 32             */
+    int32_t inter_shared;      /* I of the shared expert (multiple of 32), 0 = none */
+    int32_t top_k;             /* experts per token, 1..min(8, num_experts)        */
+    int32_t keep_host_masters; /* 1: keep all 8 planes and all LUTs in pinned host
+                                  memory so pw_set_committed_bits can raise widths;
+                                  0: keep nothing on the host (widths may only be
+                                  lowered)                                        */
+} pw_model_desc;
+
+#define PW_QMIN 3
+#define PW_QMAX 8
+#define PW_MAX_TOKENS 65536
+#define PW_MODULE_GATE_UP 0
+#define PW_MODULE_DOWN 1
+#define PW_EXPERT_SHARED (-1)
+
+/* Message of the last failure on this thread ("" if none). */
+const char *pw_last_error(void);
+
+/* Create a context on HIP device `hip_device` for the model `desc`.
+ * *out receives the context.  Errors: INVALID (desc out of range), HIP, OOM. */
+pw_status pw_create(pw_ctx **out, int hip_device, const pw_model_desc *desc);
+
+/* Release every device slab, pinned master and the page table.  The caller
+ * must have synchronised all streams that used the context. NULL is a no-op. */
+pw_status pw_destroy(pw_ctx *ctx);
+
+/* Host bit-plane packer ("overlaid bit-plane format", Core components 1).
+ * codes: host uint8 [R][K] parent codes; planes: host uint32 output of
+ * 8 * ceil(K/128) * R * 4 words in the plane layout above (plane p at offset
+ * p * ceil(K/128) * R * 4).  K must be a multiple of 32.  Pure host code; needs
+ * no device. */
+pw_status pw_pack_bitplanes(const uint8_t *codes, int64_t R, int64_t K, uint32_t *planes);
+
+/* Number of uint32 words of one plane of an R x K block (ceil(K/128)*R*4). */
+int64_t pw_plane_words(int64_t R, int64_t K);
+
+/* Register one linear block (layer, expert, module) of the weight page table
+ * (Core components 1: the page table tracks each block's committed width).
+ * expert = 0..E-1 or PW_EXPERT_SHARED; module = PW_MODULE_GATE_UP / _DOWN.
+ * host_planes: 8 planes as written by pw_pack_bitplanes; host_luts: LUTs for
+ * k = 3..8 as described above.  The library copies planes 0..q_init-1 and
+ * LUT_{q_init} to device memory (synchronously) and, if keep_host_masters,
+ * keeps a pinned host copy of all planes and LUTs.  Re-registering a block
+ * replaces it.  Call only while no work using this layer is in flight.
+ * Errors: INVALID (ids, q_init outside 3..8, null pointers), OOM, HIP. */
+pw_status pw_register_block(pw_ctx *ctx, int layer, int expert, int module,
+                            const uint32_t *host_planes, const uint16_t *host_luts, int q_init);
+
+/* Bytes of workspace pw_moe_ffn_bitplane needs for T tokens (0 if T <= 0). */
+size_t pw_workspace_size(const pw_ctx *ctx, int T);
+
+/* Top-k routing (Problem statement: each token activates a subset of the
+ * experts).  logits: dev fp32 [T][E]; topk_idx: dev int32 [T][k]; topk_w: dev
+ * fp32 [T][k].  Per token the k largest logits are chosen in the order
+ * (logit descending, expert index ascending); topk_w is the softmax over those
+ * k logits only.  Logits must be finite.  T = 0 enqueues nothing. */
+pw_status pw_route_topk(pw_ctx *ctx, const float *logits, int T, int32_t *topk_idx,
+                        float *topk_w, pw_stream stream);
+
+/* Group the T*k assignments a = t*k + j by expert: a stable counting sort.
+ * expert_offsets: dev int32 [E+1] (offsets[0] = 0, offsets[E] = T*k);
+ * sorted_assign: dev int32 [T*k], the assignments routed to expert e, in
+ * ascending a, at [offsets[e], offsets[e+1]).  topk_idx entries must be in
+ * 0..E-1. */
+pw_status pw_permute_by_expert(pw_ctx *ctx, const int32_t *topk_idx, int T,
+                               int32_t *expert_offsets, int32_t *sorted_assign, pw_stream stream);
+
+/* The fused mixed-precision MoE FFN of one layer (Core components 3: "fused
+ * mixed-precision kernel" reading planes and LUTs directly, a different width
+ * per linear block inside one operation).  Every block is decoded at the width
+ * committed in the device page table when the work runs.
+ * x: dev fp16 [T][H]; topk_idx / topk_w: as written by pw_route_topk;
+ * expert_offsets / sorted_assign: as written by pw_permute_by_expert;
+ * y: dev fp16 [T][H] output (fp32 accumulation, rounded once to fp16);
+ * workspace: dev, >= pw_workspace_size(ctx, T) bytes, 256-byte aligned,
+ * contents undefined on entry and exit.  Every routed block of `layer` (and
+ * the shared expert's, if the model has one) must be registered, else STATE. */
+pw_status pw_moe_ffn_bitplane(pw_ctx *ctx, int layer, const uint16_t *x, int T,
+                              const int32_t *topk_idx, const float *topk_w,
+                              const int32_t *expert_offsets, const int32_t *sorted_assign,
+                              uint16_t *y, void *workspace, size_t ws_bytes, pw_stream stream);
+
+/* Change the committed width of n blocks (Core components 3: asynchronous page
+ * movement; widths committed only at safe boundaries).  block_ids: host, each
+ * = (layer * (E + 1) + slot) * 2 + module with slot = expert or E for the
+ * shared expert (see pw_block_id); q_new: host, 3..8.  Lowering frees planes
+ * q_new..q_old-1 once the work already enqueued on `compute` is done.
+ * Raising copies planes q_old..q_new-1 and LUT_{q_new} from the pinned host
+ * masters with asynchronous copies on `copy`; `compute` waits for those
+ * copies before the page-table update.  The new widths apply to all work
+ * enqueued on `compute` after this call returns and never to earlier work.
+ * Errors: INVALID (ids, q outside 3..8, duplicate ids), STATE (raise without
+ * host masters), OOM, HIP.  On error nothing changes. */
+pw_status pw_set_committed_bits(pw_ctx *ctx, int n, const int32_t *block_ids,
+                                const uint8_t *q_new, pw_stream compute, pw_stream copy);
+
+/* Host view of one block's committed width (0 if not registered). */
+pw_status pw_get_committed_bits(const pw_ctx *ctx, int32_t block_id, int32_t *q_out);
+
+/* Block id of (layer, expert or PW_EXPERT_SHARED, module); -1 if out of range. */
+int32_t pw_block_id(const pw_ctx *ctx, int layer, int expert, int module);
+
+/* Device bytes held for planes and LUTs of committed widths. */
+int64_t pw_resident_bytes(const pw_ctx *ctx);
+
+/* Test export: the child codes (code8 >> (8 - q)) of one block at its
+ * committed width, produced by the same device gather routine the FFN uses.
+ * out: dev uint8 [R][K].  Asynchronous on `stream`. */
+pw_status pw_debug_decode_codes(pw_ctx *ctx, int32_t block_id, uint8_t *out, pw_stream stream);
+
+/* Test export: the decoded fp16 weights LUT_q[r][code] of one block, produced
+ * by the same device gather and LDS look-up the FFN uses.  out: dev fp16
+ * [R][K].  Asynchronous on `stream`. */
+pw_status pw_debug_dequant(pw_ctx *ctx, int32_t block_id, uint16_t *out, pw_stream stream);
+
+/* Optional per-kernel timing with HIP events on the launch stream.  While
+ * enabled, every kernel the context launches is bracketed by events; the
+ * totals are read (after the caller synchronised the stream) with
+ * pw_profile_read.  Names: "route", "permute", "gate_up", "down", "combine". */
+pw_status pw_profile_enable(pw_ctx *ctx, int on);
+pw_status pw_profile_read(pw_ctx *ctx, const char *kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PW_H_ */

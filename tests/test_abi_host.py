@@ -1,0 +1,114 @@
+"""Host-side checks of libpw.so that need no GPU: every function declared in
+include/pw.h is exported, the host bit-plane packer matches an independent
+numpy unpacker written from the header's format description, and argument
+validation returns PW_ERR_INVALID."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import any_precision_expert_amd as pw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pw.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pw_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_what_the_binding_lists():
+    assert _declared() == sorted(pw.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(pw.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _unpack_top(planes, R, K, q):
+    """Child codes from the top q planes, following the layout stated in pw.h:
+    word w of row r at [(w // 4) * R + r] * 4 + w % 4 of each plane; column
+    32w + 8P + 2i + h at bit 8i + 4h + P; plane p = bit (7 - p)."""
+    codes = np.zeros((R, K), dtype=np.int64)
+    j = np.arange(32)
+    bitpos = 8 * ((j >> 1) & 3) + 4 * (j & 1) + (j >> 3)
+    for w in range(K // 32):
+        at = ((w // 4) * R + np.arange(R)) * 4 + (w % 4)
+        for p in range(q):
+            words = planes[p][at].astype(np.int64)
+            bits = (words[:, None] >> bitpos[None, :]) & 1
+            codes[:, 32 * w:32 * w + 32] |= bits << (q - 1 - p)
+    return codes
+
+
+@pytest.mark.parametrize("R,K", [(1, 32), (3, 96), (64, 128), (70, 416), (5, 256)])
+def test_packer_truncation_identity(R, K):
+    rng = np.random.default_rng(R * 1000 + K)
+    code8 = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
+    planes = pw.pack_bitplanes(code8)
+    nchunks = -(-K // 128)
+    assert planes.shape == (8, nchunks * R * 4)
+    for q in range(1, 9):
+        assert np.array_equal(_unpack_top(planes, R, K, q), code8.astype(np.int64) >> (8 - q)), q
+
+
+def test_packer_pads_partial_chunk_with_zero_words():
+    code8 = np.full((4, 160), 255, dtype=np.uint8)  # 5 words: one full chunk + 1 word
+    planes = pw.pack_bitplanes(code8)
+    second = planes[:, 4 * 4:].reshape(8, 4, 4)  # chunk 1: [R][4]
+    assert np.all(second[:, :, 0] == 0xFFFFFFFF)
+    assert np.all(second[:, :, 1:] == 0)
+
+
+def test_packer_every_code_every_position():
+    # each code value at every column position of a word, across rows
+    R, K = 256, 32
+    code8 = ((np.arange(R)[:, None] + np.arange(K)[None, :]) % 256).astype(np.uint8)
+    planes = pw.pack_bitplanes(code8)
+    assert np.array_equal(_unpack_top(planes, R, K, 8), code8.astype(np.int64))
+
+
+def test_packer_rejects_bad_shapes():
+    L = pw.lib()
+    buf = np.zeros(1024, dtype=np.uint32)
+    codes = np.zeros(64, dtype=np.uint8)
+    assert L.pw_pack_bitplanes(codes.ctypes.data, 2, 30, buf.ctypes.data) == pw.PW_ERR_INVALID
+    assert "multiple of 32" in pw.last_error()
+    assert L.pw_pack_bitplanes(None, 2, 32, buf.ctypes.data) == pw.PW_ERR_INVALID
+    assert L.pw_pack_bitplanes(codes.ctypes.data, 0, 32, buf.ctypes.data) == pw.PW_ERR_INVALID
+
+
+def test_plane_words():
+    assert pw.plane_words(10, 128) == 40
+    assert pw.plane_words(10, 160) == 80
+    assert pw.plane_words(0, 128) == 0
+
+
+def test_create_rejects_bad_descriptions():
+    L = pw.lib()
+    h = ctypes.c_void_p()
+    bad = [pw.ModelDesc(1, 4, 250, 512, 0, 2, 1),   # H not a multiple of 32
+           pw.ModelDesc(1, 4, 256, 500, 0, 2, 1),   # I not a multiple of 32
+           pw.ModelDesc(1, 4, 256, 512, 0, 9, 1),   # top_k > 8
+           pw.ModelDesc(1, 2, 256, 512, 0, 3, 1),   # top_k > E
+           pw.ModelDesc(0, 4, 256, 512, 0, 2, 1),   # no layers
+           pw.ModelDesc(1, 300, 256, 512, 0, 2, 1)]  # E > 256
+    for d in bad:
+        assert L.pw_create(ctypes.byref(h), 0, ctypes.byref(d)) == pw.PW_ERR_INVALID
+    assert L.pw_create(None, 0, None) == pw.PW_ERR_INVALID
+
+
+def test_null_context_calls_are_invalid():
+    L = pw.lib()
+    assert L.pw_route_topk(None, None, 1, None, None, None) == pw.PW_ERR_INVALID
+    assert L.pw_permute_by_expert(None, None, 1, None, None, None) == pw.PW_ERR_INVALID
+    assert L.pw_moe_ffn_bitplane(None, 0, None, 1, None, None, None, None, None, None, 0, None) == pw.PW_ERR_INVALID
+    assert L.pw_set_committed_bits(None, 1, None, None, None, None) == pw.PW_ERR_INVALID
+    assert L.pw_destroy(None) == pw.PW_OK
+    assert L.pw_workspace_size(None, 4) == 0
+    assert L.pw_block_id(None, 0, 0, 0) == -1

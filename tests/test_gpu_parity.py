@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bit-exact: routing indices, expert offsets, the permutation, decoded child
+codes and dequantised fp16 weights.  Within tolerance: y (relative L2 <= 1e-3,
+max abs <= 1e-2) and the fp32 gate weights (<= 1e-6 from fp64).
+"""
+import numpy as np
+import pytest
+
+import pw_synth
+from tests.gpu_util import check_layer, compare, make_ctx, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(require_gpu):
+    import any_precision_expert_amd as pw
+    pw.lib()  # loud failure if the library is missing
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
+def test_debug_decode_codes_and_weights_bit_exact(q):
+    import torch
+    import any_precision_expert_amd as pw
+    # down block R = H = 352 (ragged 64-row tile), K = I = 224 (one chunk + 3 words)
+    w, _ = pw_synth.make_small(H=352, I=224, E=2, top_k=1, T=1, seed=100 + q, q_fixed=q)
+    ctx = make_ctx(w.shape)
+    try:
+        for e in range(2):
+            for m, blk in ((pw.MODULE_GATE_UP, w.gate_up[e]), (pw.MODULE_DOWN, w.down[e])):
+                ctx.register_code_block(0, e, m, blk.code8, blk.luts, blk.q)
+                bid = ctx.block_id(0, e, m)
+                out = torch.zeros(blk.code8.shape, dtype=torch.uint8, device="cuda")
+                ctx.debug_decode_codes(bid, out)
+                wout = torch.zeros(blk.code8.shape, dtype=torch.float16, device="cuda")
+                ctx.debug_dequant(bid, wout)
+                torch.cuda.synchronize()
+                expect = blk.code8 >> (8 - q)
+                assert np.array_equal(out.cpu().numpy(), expect)
+                direct = np.take_along_axis(blk.luts[q], expect.astype(np.int64), axis=1)
+                assert np.array_equal(wout.cpu().numpy().view(np.uint16), direct.view(np.uint16))
+    finally:
+        ctx.close()
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 2), (16, 4, 2), (37, 60, 4), (300, 8, 2), (4096, 8, 2),
+                                   (64, 256, 8), (5, 7, 7), (1000, 1, 1)])
+def test_route_and_permute_bit_exact(T, E, k):
+    import torch
+    import oracle
+    rng = np.random.default_rng(T * 31 + E)
+    logits = rng.normal(size=(T, E)).astype(np.float32)
+    logits[::4] = np.round(logits[::4] * 2) / 2  # exact ties
+    H, I = 64, 32
+    ctx = make_ctx(pw_synth.LayerShape(H=H, I=I, E=E, top_k=k))
+    try:
+        lg = torch.from_numpy(logits).cuda()
+        idx = torch.zeros((T, k), dtype=torch.int32, device="cuda")
+        wt = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+        offs = torch.zeros((E + 1,), dtype=torch.int32, device="cuda")
+        srt = torch.zeros((T * k,), dtype=torch.int32, device="cuda")
+        ctx.route_topk(lg, T, idx, wt)
+        ctx.permute_by_expert(idx, T, offs, srt)
+        torch.cuda.synchronize()
+        ridx, rw = oracle.route_topk(logits, k)
+        roff, rsrt = oracle.permute(ridx, E)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        assert np.max(np.abs(wt.cpu().numpy() - rw)) <= 1e-6
+        assert np.array_equal(offs.cpu().numpy(), roff)
+        assert np.array_equal(srt.cpu().numpy(), rsrt)
+    finally:
+        ctx.close()
+
+
+# ------------------------------------------------------------------ FFN, small shapes
+
+@pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
+def test_ffn_each_width(q):
+    w, a = pw_synth.make_small(H=352, I=224, E=6, top_k=3, T=7, I_shared=96, seed=200 + q, q_fixed=q)
+    check_layer(w, a, label="q=%d" % q)
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 9, 33])
+def test_ffn_mixed_widths_ragged(T):
+    w, a = pw_synth.make_small(H=352, I=224, E=5, top_k=2, T=T, seed=300 + T)
+    check_layer(w, a, label="mixed T=%d" % T)
+
+
+def test_ffn_single_expert_all_tokens():
+    w, a = pw_synth.make_small(H=256, I=128, E=1, top_k=1, T=11, seed=401)
+    check_layer(w, a, label="E=1")
+
+
+def test_ffn_all_tokens_to_one_expert():
+    w, a = pw_synth.make_small(H=256, I=128, E=8, top_k=2, T=13, seed=402)
+    a.logits[:, 3] += 100.0
+    check_layer(w, a, label="hot expert")
+
+
+def test_ffn_k_equals_E_and_large_tiles():
+    w, a = pw_synth.make_small(H=1024, I=512, E=4, top_k=4, T=6, I_shared=256, seed=403)
+    check_layer(w, a, label="k=E")
+
+
+def test_zero_tokens_enqueues_nothing():
+    import torch
+    w, a = pw_synth.make_small(H=64, I=32, E=2, top_k=1, T=1, seed=404)
+    from any_precision_expert_amd.layer import register_layer
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        assert ctx.workspace_size(0) == 0
+        y = torch.full((1, 64), 7.0, dtype=torch.float16, device="cuda")
+        ctx.route_topk(0, 0, 0, 0)
+        ctx.moe_ffn_bitplane(0, 0, 0, 0, 0, 0, 0, y, 0, 0)
+        torch.cuda.synchronize()
+        assert torch.all(y == 7.0)
+    finally:
+        ctx.close()
+
+
+# ------------------------------------------------------------------ the workload configurations
+
+def test_config0_toy():
+    w, a = pw_synth.make_config(0)
+    check_layer(w, a, label="cfg0")
+
+
+def test_config1_qwen_decode():
+    w, a = pw_synth.make_config(1)
+    check_layer(w, a, label="cfg1")
+
+
+@pytest.fixture(scope="module")
+def mixtral():
+    import any_precision_expert_amd as pw
+    from any_precision_expert_amd.layer import register_layer
+    spec = pw_synth.CONFIGS[2]
+    w = pw_synth.make_weights(spec.shape, pw_synth.config_seed(2), 0, spec.q_policy, spec.logits)
+    ctx = make_ctx(w.shape)
+    register_layer(ctx, 0, w)
+    yield w, ctx
+    ctx.close()
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
+def test_config2_mixtral_decode(mixtral, T):
+    w, ctx = mixtral
+    spec = pw_synth.CONFIGS[2]
+    a = pw_synth.make_activations(spec.shape, T, pw_synth.config_seed(2), 0, 0, spec.logits)
+    tokens = None if T <= 16 else list(range(0, T, 4))
+    check_layer(w, a, tokens=tokens, label="cfg2 T=%d" % T, ctx=ctx)
+
+
+def test_config3_mixtral_prefill_sampled():
+    w, a = pw_synth.make_config(3)
+    rng = np.random.default_rng(3)
+    tokens = sorted(set(rng.choice(4096, size=8, replace=False).tolist()) | {0, 4095})
+    check_layer(w, a, tokens=tokens, label="cfg3 prefill")
