@@ -173,6 +173,8 @@ struct pw_ctx {
     std::vector<hipEvent_t> events;  // owned events (released at destroy)
     bool profiling = false;
     std::map<std::string, std::vector<ProfRec>> prof;
+    std::vector<hipEvent_t> prof_pool;
+    size_t prof_next = 0;
 };
 
 namespace {
@@ -245,6 +247,10 @@ void free_block_now(pw_ctx* c, HostBlock& b)
     b.registered = false;
 }
 
+// Per-kernel HIP-event timing: events come from a pool created when profiling
+// is enabled, so recording adds no allocation to the launch path.
+constexpr size_t kProfEvents = 1 << 14;
+
 struct ProfScope {
     pw_ctx* c;
     const char* name;
@@ -252,29 +258,31 @@ struct ProfScope {
     hipEvent_t a = nullptr;
     ProfScope(pw_ctx* c_, const char* n, hipStream_t s_) : c(c_), name(n), s(s_)
     {
-        if (c->profiling && hipEventCreate(&a) == hipSuccess) (void)hipEventRecord(a, s);
+        if (c->profiling && c->prof_next + 2 <= c->prof_pool.size()) {
+            a = c->prof_pool[c->prof_next++];
+            (void)hipEventRecord(a, s);
+        }
     }
     ~ProfScope()
     {
         if (!a) return;
-        hipEvent_t b;
-        if (hipEventCreate(&b) == hipSuccess) {
-            (void)hipEventRecord(b, s);
-            c->prof[name].push_back({a, b});
-        } else {
-            (void)hipEventDestroy(a);
-        }
+        hipEvent_t b = c->prof_pool[c->prof_next++];
+        (void)hipEventRecord(b, s);
+        c->prof[name].push_back({a, b});
     }
 };
 
 void prof_reset(pw_ctx* c)
 {
-    for (auto& kv : c->prof)
-        for (auto& r : kv.second) {
-            (void)hipEventDestroy(r.a);
-            (void)hipEventDestroy(r.b);
-        }
     c->prof.clear();
+    c->prof_next = 0;
+}
+
+void prof_release(pw_ctx* c)
+{
+    prof_reset(c);
+    for (auto ev : c->prof_pool) (void)hipEventDestroy(ev);
+    c->prof_pool.clear();
 }
 
 }  // namespace
@@ -300,7 +308,7 @@ pw_status pw_create(pw_ctx** out, int hip_device, const pw_model_desc* d)
     if (!out || !d) return fail(PW_ERR_INVALID, "pw_create: null pointer");
     *out = nullptr;
     const bool shape_ok = d->num_layers >= 1 && d->num_layers <= 4096 && d->num_experts >= 1 &&
-                          d->num_experts <= 256 && d->hidden >= 32 && d->hidden <= 65536 &&
+                          d->num_experts <= 256 && d->hidden >= 32 && d->hidden <= 32768 &&
                           d->hidden % 32 == 0 && d->inter >= 32 && d->inter <= 131072 && d->inter % 32 == 0 &&
                           d->inter_shared >= 0 && d->inter_shared <= 131072 && d->inter_shared % 32 == 0 &&
                           d->top_k >= 1 && d->top_k <= 8 && d->top_k <= d->num_experts;
@@ -338,7 +346,7 @@ pw_status pw_destroy(pw_ctx* c)
     if (!c) return ok();
     (void)hipSetDevice(c->device);
     (void)hipDeviceSynchronize();
-    prof_reset(c);
+    prof_release(c);
     for (auto& b : c->blocks)
         if (b.registered) free_block_now(c, b);
     for (auto& s : c->staging) (void)hipHostFree(s.p);
@@ -510,17 +518,22 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
     a.k = d.top_k;
     a.n_slots = std::min(E, T * d.top_k);
     a.hstride = std::max(d.inter, d.inter_shared);
+    a.drows = T * d.top_k + (d.inter_shared ? T : 0);
     hipStream_t s = (hipStream_t)stream;
     {
         ProfScope ps(c, "gate_up", s);
         a.tiles_routed = d.inter / 32;
         a.tiles_shared = d.inter_shared / 32;
+        a.splits_routed = 1;
+        a.splits_shared = 1;
         if ((e = launch_gate_up(a, s)) != hipSuccess) return hip_fail(e, "gate_up launch");
     }
     {
         ProfScope ps(c, "down", s);
         a.tiles_routed = (d.hidden + 63) / 64;
         a.tiles_shared = d.inter_shared ? (d.hidden + 63) / 64 : 0;
+        a.splits_routed = down_splits(d.inter);
+        a.splits_shared = d.inter_shared ? down_splits(d.inter_shared) : 1;
         if ((e = launch_down(a, s)) != hipSuccess) return hip_fail(e, "down launch");
     }
     {
@@ -716,9 +729,21 @@ pw_status pw_debug_dequant(pw_ctx* c, int32_t id, uint16_t* out, pw_stream strea
 pw_status pw_profile_enable(pw_ctx* c, int on)
 {
     if (!c) return fail(PW_ERR_INVALID, "pw_profile_enable: null context");
-    (void)hipSetDevice(c->device);
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
     (void)hipDeviceSynchronize();
     prof_reset(c);
+    if (on && c->prof_pool.empty()) {
+        c->prof_pool.reserve(kProfEvents);
+        for (size_t i = 0; i < kProfEvents; ++i) {
+            hipEvent_t ev;
+            if ((e = hipEventCreate(&ev)) != hipSuccess) {
+                prof_release(c);
+                return hip_fail(e, "pw_profile_enable: hipEventCreate");
+            }
+            c->prof_pool.push_back(ev);
+        }
+    }
     c->profiling = on != 0;
     return ok();
 }
@@ -749,11 +774,12 @@ WsLayout ws_layout(int T, int k, int H, int I, int Is)
     auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
     const size_t rows = (size_t)T * k + (Is ? (size_t)T : 0);
     const size_t hs = (size_t)std::max(I, Is);
+    const size_t splits = (size_t)std::max(down_splits(I), Is ? down_splits(Is) : 1);
     WsLayout L;
     L.h_hi = 0;
     L.h_lo = up(L.h_hi + rows * hs * 2);
     L.dout = up(L.h_lo + rows * hs * 2);
-    L.total = up(L.dout + rows * (size_t)H * 4);
+    L.total = up(L.dout + splits * rows * (size_t)H * 4);
     return L;
 }
 

@@ -41,10 +41,24 @@ struct FfnArgs {
     int32_t n_slots;          // routed slots: min(E, T * k)
     int32_t tiles_routed;     // row tiles per routed block
     int32_t tiles_shared;     // row tiles of the shared block (0 = none)
+    int32_t splits_routed;    // K splits per routed row tile (down: >= 1; gate_up: 1)
+    int32_t splits_shared;    // K splits per shared row tile
     int32_t hstride;          // max(I, Is)
+    int32_t drows;            // rows of one dout split plane: T * k (+ T with a shared expert)
 };
 
-// Workspace carve-up for T tokens (byte offsets, 256-aligned).
+// K splits of a down-projection row tile: about kChunksPerSplit 128-column
+// chunks per workgroup (two per wave), so long K ranges spread over the chip.
+constexpr int kChunksPerSplit = 16;
+inline int down_splits(int K)
+{
+    const int nchunks = (K + kChunkCols - 1) / kChunkCols;
+    return nchunks <= kChunksPerSplit ? 1 : (nchunks + kChunksPerSplit - 1) / kChunksPerSplit;
+}
+
+// Workspace carve-up for T tokens (byte offsets, 256-aligned): h as fp16 hi
+// and lo [T*k (+T)][max(I, Is)], then the per-split down outputs
+// [splits][T*k (+T)][H] fp32.
 struct WsLayout {
     size_t h_hi, h_lo, dout, total;
 };

@@ -34,7 +34,11 @@ typedef __attribute__((address_space(1))) const u32x4* gu32x4p;    // global (no
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kLutBytes = 65536;  // largest LDS LUT: 256 slots x 64 lanes x 4 B
-constexpr int kGemvLdsWords = kLutBytes / 4 + kWaves * 4 * 64;  // LUT + cross-wave reduction
+constexpr int kStageWords = 16 * 64;  // pair-table staging (single LUT of q <= 4)
+constexpr int kXTileBytes = 90112;     // activation tile of one token pass (88 KB)
+// LUT (reused for the cross-wave reduction) + pair staging + activation tile:
+// 156 KB, one workgroup per CU (the contraction's VGPR budget allows 8 waves).
+constexpr int kGemvLdsWords = kLutBytes / 4 + kStageWords + kXTileBytes / 4;
 constexpr int kDebugLdsWords = kLutBytes / 4 + 16 * 64;        // LUT + pair staging
 
 // ---------------------------------------------------------------- bit gather
@@ -46,7 +50,35 @@ __device__ __forceinline__ uint32_t rotl(uint32_t x, int n)
 __device__ __forceinline__ uint32_t rotr(uint32_t x, int n) { return __builtin_amdgcn_alignbit(x, x, n & 31); }
 
 // 0x01010101 rotated left by n: one bit in each byte, at position n mod 8.
-__host__ __device__ constexpr uint32_t rep_bit(int n) { return 0x01010101u << (((n % 8) + 8) % 8); }
+__host__ __device__ constexpr int rep_index(int n) { return ((n % 8) + 8) % 8; }
+
+// The eight masks 0x01010101 << s live in scalar registers: a VOP3 and-or on
+// gfx9 cannot encode a 32-bit literal, and with the mask in an SGPR every
+// (plane, register) step of the gather is a single v_and_or_b32.
+struct RepMasks {
+    uint32_t m[8];
+};
+
+// acc | (a & m) in one v_bitop3_b32 (truth table 0xEC = (S0 & S2) | S1).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t acc)
+{
+    return (uint32_t)__builtin_amdgcn_bitop3_b32((int)a, (int)acc, (int)m, 0xEC);
+}
+#define PW_SMASK(s) asm("s_mov_b32 %0, %1" : "=s"(r.m[s]) : "n"(0x01010101u << (s)))
+__device__ __forceinline__ RepMasks make_masks()
+{
+    RepMasks r;
+    PW_SMASK(0);
+    PW_SMASK(1);
+    PW_SMASK(2);
+    PW_SMASK(3);
+    PW_SMASK(4);
+    PW_SMASK(5);
+    PW_SMASK(6);
+    PW_SMASK(7);
+    return r;
+}
+#undef PW_SMASK
 
 // Gathered child codes of one 32-column plane word set (W[p] = word of plane p).
 //  single (q >= 5): r[2P + h] byte i = code of column 8P + 2i + h
@@ -63,7 +95,7 @@ struct Gathered {
 // right position of four bytes at once; one final rotate per register aligns
 // the bytes.
 template <int Q>
-__device__ __forceinline__ void gather(const uint32_t (&W)[Q], Gathered<Q>& g)
+__device__ __forceinline__ void gather(const uint32_t (&W)[Q], Gathered<Q>& g, const RepMasks& M)
 {
     uint32_t A[Q];
 #pragma unroll
@@ -77,8 +109,8 @@ __device__ __forceinline__ void gather(const uint32_t (&W)[Q], Gathered<Q>& g)
             uint32_t acc = 0;
 #pragma unroll
             for (int p = 0; p < Q; ++p) {
-                acc |= A[p] & rep_bit(P + Q - 1 - p);
-                acc |= B[p] & rep_bit(P + 2 * Q - 1 - p);
+                acc = and_or(A[p], M.m[rep_index(P + Q - 1 - p)], acc);
+                acc = and_or(B[p], M.m[rep_index(P + 2 * Q - 1 - p)], acc);
             }
             g.r[P] = rotr(acc, P);
         }
@@ -89,7 +121,7 @@ __device__ __forceinline__ void gather(const uint32_t (&W)[Q], Gathered<Q>& g)
             for (int h = 0; h < 2; ++h) {
                 uint32_t acc = 0;
 #pragma unroll
-                for (int p = 0; p < Q; ++p) acc |= A[p] & rep_bit(4 * h + P + Q - 1 - p);
+                for (int p = 0; p < Q; ++p) acc = and_or(A[p], M.m[rep_index(4 * h + P + Q - 1 - p)], acc);
                 g.r[2 * P + h] = rotr(acc, 4 * h + P);
             }
         }
@@ -168,47 +200,75 @@ __device__ __forceinline__ float dot2(h2 a, uint32_t b, float c)
 
 // ---------------------------------------------------------------- routing
 
+// One wave per token: lane l holds the logits of experts l, l+64, l+128,
+// l+192.  Each of the k rounds takes the wave-wide best entry by the key
+// (value descending, expert index ascending) with a butterfly of shuffles and
+// retires it; the softmax runs over the k selected logits.
+__device__ __forceinline__ bool route_better(float av, int ai, float bv, int bi)
+{
+    return av > bv || (av == bv && ai < bi);
+}
+
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T, int E,
                                                          int k, int32_t* __restrict__ idx,
                                                          float* __restrict__ w)
 {
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= T) return;
-    float v[8];
-    int id[8];
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // whole wave
+    const float* l = logits + (size_t)t * E;
+    float v[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        live[i] = e < E;
+        v[i] = live[i] ? l[e] : 0.0f;
+    }
+    float sv[8];
+    int si[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        v[j] = 0.0f;
-        id[j] = -1;
-    }
-    const float* l = logits + (size_t)t * E;
-    for (int e = 0; e < E; ++e) {
-        // insert (l[e], e) by the key (value descending, index ascending); the
-        // displaced entry moves down one slot at a time, branch-free
-        float cv = l[e];
-        int ci = e;
+        sv[j] = 0.0f;
+        si[j] = 0;
+        if (j < k) {
+            float bv = 0.0f;
+            int bi = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool take = j < k && ci >= 0 && (id[j] < 0 || cv > v[j] || (cv == v[j] && ci < id[j]));
-            const float nv = take ? cv : v[j];
-            const int ni = take ? ci : id[j];
-            cv = take ? v[j] : cv;
-            ci = take ? id[j] : ci;
-            v[j] = nv;
-            id[j] = ni;
+            for (int i = 0; i < 4; ++i) {
+                const int e = lane + 64 * i;
+                if (live[i] && (bi == 0x7fffffff || route_better(v[i], e, bv, bi))) {
+                    bv = v[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off, 64);
+                const int oi = __shfl_xor(bi, off, 64);
+                if (oi != 0x7fffffff && (bi == 0x7fffffff || route_better(ov, oi, bv, bi))) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (lane + 64 * i == bi) live[i] = false;
+            sv[j] = bv;
+            si[j] = bi;
         }
     }
-    const float m = v[0];
+    const float m = sv[0];
     float ex[8], s = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        ex[j] = j < k ? expf(v[j] - m) : 0.0f;
+        ex[j] = j < k ? expf(sv[j] - m) : 0.0f;
         s += ex[j];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        if (j < k) {
-            idx[(size_t)t * k + j] = id[j];
+        if (j < k && lane == j) {
+            idx[(size_t)t * k + j] = si[j];
             w[(size_t)t * k + j] = ex[j] / s;
         }
     }
@@ -232,14 +292,31 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-        int s = 0;
-        for (int e = 0; e < E; ++e) {
-            base[e] = s;
-            offsets[e] = s;
-            s += cnt[e];
+    if (wave == 0) {  // exclusive scan of the counts: 4 experts per lane + a shuffle scan
+        int c[4], s = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            c[i] = e < E ? cnt[e] : 0;
+            s += c[i];
         }
-        offsets[E] = s;
+        int incl = s;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int nb = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += nb;
+        }
+        int ex = incl - s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            if (e < E) {
+                base[e] = ex;
+                offsets[e] = ex;
+            }
+            ex += c[i];
+        }
+        if (lane == 63) offsets[E] = incl;
     }
     __syncthreads();
     for (int a0 = 0; a0 < n; a0 += 1024) {
@@ -276,129 +353,244 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
 
 // ---------------------------------------------------------------- FFN GEMV
 
-// MODE 0: gate_up. 64 lanes = 32 gate rows + the 32 matching up rows; input
-//         x (fp16); epilogue h = silu(g) * u stored as fp16 hi + fp16 lo.
-// MODE 1: down. 64 lanes = 64 output rows; input h = hi + lo; epilogue writes
-//         the fp32 expert output of each assignment.
-template <int MODE>
-struct ModeTraits {
-    static constexpr int TT = MODE == 0 ? 4 : 2;  // tokens per pass
-};
+// Contraction of one 64-row tile on the matrix cores (v_mfma_f32_32x32x16_f16).
+//
+// MODE 0: gate_up. Row group 0 = 32 gate rows, row group 1 = the matching 32
+//         up rows; input x (fp16); epilogue h = silu(g) * u stored as fp16 hi
+//         + fp16 lo (hi + lo carries h to about 2^-22 relative).
+// MODE 1: down. Row groups 0 / 1 = 64 consecutive output rows; input h = hi +
+//         lo (two MFMAs per step); the K range may be split over several
+//         workgroups, each writing the fp32 partial expert output of its split
+//         (summed in split order by the combine).
+//
+// Lane l = (rho = l % 32, kh = l / 32) decodes rows rho (group 0) and 32 + rho
+// (group 1).  In a 128-column chunk it owns words 2*kh and 2*kh + 1 of both
+// rows (8-byte loads; 64 lanes read 32 rows x 16 B = 512 B contiguous per row
+// group).  The word pair u pairs word u (kh = 0) with word 2 + u (kh = 1) in
+// one 16-deep MFMA step set: step P takes columns 8P..8P+7 of each word, which
+// is exactly what the gather produces for register P.  The up-to-32 tokens of
+// a pass are the MFMA's N columns (B lanes: token rho, k half kh), so a weight
+// is decoded once per 32 tokens and no VALU multiply-add remains.  The eight
+// waves split K; their fp32 partials are summed in wave order through the
+// LUT's LDS region once the pass no longer needs the LUT.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2* gu32x2p;
+typedef __attribute__((address_space(1))) const u32x4* gcu32x4p;
+
+constexpr int kTokTile = 32;
+
+template <int Q>
+__device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const uint32_t* const (&planes)[Q], int c, int R,
+                                                int row, bool valid, int kh)
+{
+#pragma unroll
+    for (int p = 0; p < Q; ++p) {
+        if (valid)
+            pg[p] = __builtin_nontemporal_load((gu32x2p)(uintptr_t)planes[p] + (((size_t)c * R + row) * 2 + kh));
+        else
+            pg[p] = u32x2{0, 0};
+    }
+}
+
+// MFMA B fragment (8 consecutive fp16 of one staged activation row) from LDS.
+__device__ __forceinline__ half8 lds_frag(const uint16_t* p, bool ok)
+{
+    if (!ok) return half8{0, 0, 0, 0, 0, 0, 0, 0};
+    return __builtin_bit_cast(half8, *(const u32x4*)p);
+}
+
+__device__ __forceinline__ half8 frag_of(const h2 (&w2)[16], int P)
+{
+    half8 r;
+    r[0] = w2[4 * P + 0].x;
+    r[1] = w2[4 * P + 0].y;
+    r[2] = w2[4 * P + 1].x;
+    r[3] = w2[4 * P + 1].y;
+    r[4] = w2[4 * P + 2].x;
+    r[5] = w2[4 * P + 2].y;
+    r[6] = w2[4 * P + 3].x;
+    r[7] = w2[4 * P + 3].y;
+    return r;
+}
 
 template <int MODE, int Q>
-__device__ void gemv_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
-                           int ntok, int tile, uint32_t* lds)
+__device__ void mfma_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0, int ntok,
+                           int tile, int split, int nsplit, uint32_t* lds)
 {
-    constexpr int TT = ModeTraits<MODE>::TT;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps K offsets scalar
+    const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int R = bd->R;
     const int nchunks = bd->nchunks, kwords = bd->kwords;
-    int row;
-    bool valid;
+    int row[2], srow;
+    bool rvalid[2], svalid;
     if (MODE == 0) {
         const int Iblk = R >> 1;
-        const int i = tile * 32 + (lane & 31);
-        valid = i < Iblk;
-        row = lane < 32 ? i : Iblk + i;
+        const int i = tile * 32 + rho;
+        rvalid[0] = rvalid[1] = svalid = i < Iblk;
+        row[0] = i;
+        row[1] = Iblk + i;
+        srow = kh ? row[1] : row[0];  // LDS slot `lane` holds the LUT of this row
     } else {
-        row = tile * 64 + lane;
-        valid = row < R;
+        row[0] = tile * 64 + rho;
+        row[1] = tile * 64 + 32 + rho;
+        rvalid[0] = row[0] < R;
+        rvalid[1] = row[1] < R;
+        srow = tile * 64 + lane;
+        svalid = srow < R;
     }
-    load_lut<Q>(lds, lds + kLutBytes / 4, bd->lut, row, valid, lane, wave, kWaves);
-    __syncthreads();
-
-    const char* lutb = (const char*)lds;
-    float* red = (float*)(lds + kLutBytes / 4);
-    const uint32_t lane_off = (uint32_t)lane * 4u;
     const uint32_t* planes[Q];
 #pragma unroll
     for (int p = 0; p < Q; ++p) planes[p] = bd->planes[p];
+
+    const int cps = (nchunks + nsplit - 1) / nsplit;
+    const int c_begin = split * cps;
+    const int c_end = min(nchunks, c_begin + cps);
+    const int first = c_begin + wave;
+    const int nch = first < c_end ? (c_end - first + kWaves - 1) / kWaves : 0;
+
+    // ring of D chunks in flight per wave (both row groups), deeper for low q
+    constexpr int D = Q <= 4 ? 3 : (Q <= 6 ? 2 : 1);
+    u32x2 pg[D][2][Q];
+    const uint32_t off0 = (uint32_t)rho * 4u, off1 = (uint32_t)(32 + rho) * 4u;
+    const char* lutb = (const char*)lds;
+    const RepMasks masks = make_masks();
     const int TK = a.T * a.k;
 
-    for (int t0 = 0; t0 < ntok; t0 += TT) {
-        const int nt = min(TT, ntok - t0);
-        cu32p in_hi[TT];
-        cu32p in_lo[TT];
+    // activation tile in LDS: the tokens of one pass over this workgroup's
+    // column range [kc0, kc0 + kcols), rows padded by 16 B to spread banks
+    const int kc0 = c_begin * kChunkCols;
+    const int kcols = max(0, min(bd->K, c_end * kChunkCols) - kc0);
+    const int xstride = kcols + 8;  // halves per staged row
+    const int per_tok = (MODE == 0 ? 1 : 2) * xstride * 2;
+    const int ttile = min(kTokTile, kXTileBytes / per_tok);
+    uint16_t* xt = (uint16_t*)(lds + kLutBytes / 4 + kStageWords);
+
+    for (int t0 = 0; t0 < ntok; t0 += ttile) {
+        // the pass's first chunks are in flight while its LUT and activations are staged
 #pragma unroll
-        for (int j = 0; j < TT; ++j) {
-            const int jj = t0 + min(j, nt - 1);
-            if (MODE == 0) {
-                const int tok = __builtin_amdgcn_readfirstlane(shared ? jj : a.sorted[p0 + jj] / a.k);
-                in_hi[j] = (cu32p)(uintptr_t)(a.x + (size_t)tok * a.H);
-                in_lo[j] = in_hi[j];
-            } else {
-                const int hrow = __builtin_amdgcn_readfirstlane(shared ? TK + jj : p0 + jj);
-                in_hi[j] = (cu32p)(uintptr_t)(a.h_hi + (size_t)hrow * a.hstride);
-                in_lo[j] = (cu32p)(uintptr_t)(a.h_lo + (size_t)hrow * a.hstride);
+        for (int d = 0; d < D; ++d) {
+            if (d < nch) {
+                load_pair_words<Q>(pg[d][0], planes, first + d * kWaves, R, row[0], rvalid[0], kh);
+                load_pair_words<Q>(pg[d][1], planes, first + d * kWaves, R, row[1], rvalid[1], kh);
             }
         }
-        float acc[TT];
-#pragma unroll
-        for (int j = 0; j < TT; ++j) acc[j] = 0.0f;
+        const int nt = min(ttile, ntok - t0);
+        {
+            const int v8 = kcols >> 3;  // 16-byte vectors per row
+            const int nvec = (MODE == 0 ? 1 : 2) * nt * v8;
+            for (int i = tid; i < nvec; i += kThreads) {
+                const int part = MODE == 0 ? 0 : i / (nt * v8);
+                const int r = (i - part * nt * v8) / v8, v = i - part * nt * v8 - r * v8;
+                const uint16_t* src;
+                if (MODE == 0) {
+                    const int tok = shared ? t0 + r : a.sorted[p0 + t0 + r] / a.k;
+                    src = a.x + (size_t)tok * a.H;
+                } else {
+                    const int hrow = shared ? TK + t0 + r : p0 + t0 + r;
+                    src = (part ? a.h_lo : a.h_hi) + (size_t)hrow * a.hstride;
+                }
+                const u32x4 val = *(gcu32x4p)(uintptr_t)(src + kc0 + 8 * v);
+                *(u32x4*)(xt + (size_t)(part * nt + r) * xstride + 8 * v) = val;
+            }
+        }
+        load_lut<Q>(lds, lds + kLutBytes / 4, bd->lut, srow, svalid, lane, wave, kWaves);
+        __syncthreads();
+        const bool nvalid = rho < nt;
+        const uint16_t* xs_hi = xt + (size_t)rho * xstride - kc0;
+        const uint16_t* xs_lo = xt + (size_t)(nt + rho) * xstride - kc0;
+        f32x16 C0 = {}, C1 = {};
 
-        for (int c = wave; c < nchunks; c += kWaves) {
-            uint4 pv[Q];
+        for (int ci0 = 0; ci0 < nch; ci0 += D) {
 #pragma unroll
-            for (int p = 0; p < Q; ++p) pv[p] = load_planes_chunk(planes[p], c, R, row, valid);
-            const int nw = min(4, kwords - 4 * c);
+            for (int d = 0; d < D; ++d) {
+                const int ci = ci0 + d;
+                if (ci >= nch) break;
+                const int c = first + ci * kWaves;
+                const int nw = min(4, kwords - 4 * c);
+                const int ulast = nw > 1 ? 1 : 0;
+                const bool more = ci + D < nch;
+                const int cn = first + (ci + D) * kWaves;
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww) {
-                if (ww < nw) {
-                    uint32_t W[Q];
+                for (int u = 0; u < 2; ++u) {
+                    if (u > ulast) break;
+                    const int wd = 2 * kh + u;
+                    const bool bv = nvalid && wd < nw;  // zero B columns beyond K
+                    const int col = c * kChunkCols + 32 * wd;
+                    half8 Bh[4], Bl[4];
 #pragma unroll
-                    for (int p = 0; p < Q; ++p) W[p] = word_of(pv[p], ww);
-                    Gathered<Q> g;
-                    gather<Q>(W, g);
-                    h2 w2[16];
-                    lookup<Q>(g, lane_off, lutb, w2);
-                    const int col2 = c * 64 + ww * 16;
+                    for (int P = 0; P < 4; ++P) {
+                        Bh[P] = lds_frag(xs_hi + col + 8 * P, bv);
+                        if (MODE == 1) Bl[P] = lds_frag(xs_lo + col + 8 * P, bv);
+                    }
 #pragma unroll
-                    for (int j = 0; j < TT; ++j) {
-                        if (j < nt) {
+                    for (int g = 0; g < 2; ++g) {
+                        uint32_t W[Q];
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) acc[j] = dot2(w2[i], in_hi[j][col2 + i], acc[j]);
-                            if (MODE == 1) {
+                        for (int p = 0; p < Q; ++p) W[p] = pg[d][g][p][u];
+                        Gathered<Q> gr;
+                        gather<Q>(W, gr, masks);
+                        h2 w2[16];
+                        lookup<Q>(gr, g == 0 ? off0 : off1, lutb, w2);
+                        f32x16& C = g == 0 ? C0 : C1;
 #pragma unroll
-                                for (int i = 0; i < 16; ++i) acc[j] = dot2(w2[i], in_lo[j][col2 + i], acc[j]);
-                            }
+                        for (int P = 0; P < 4; ++P) {
+                            const half8 A = frag_of(w2, P);
+                            C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh[P], C, 0, 0, 0);
+                            if (MODE == 1) C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl[P], C, 0, 0, 0);
                         }
+                        if (u == ulast && more)  // this buffer's row group is consumed: refill it
+                            load_pair_words<Q>(pg[d][g], planes, cn, R, row[g], rvalid[g], kh);
                     }
                 }
             }
         }
 
-#pragma unroll
-        for (int j = 0; j < TT; ++j) red[(wave * TT + j) * 64 + lane] = acc[j];
+        // cross-wave reduction through the (no longer needed) LUT region
         __syncthreads();
-        if (wave == 0) {
-            for (int j = 0; j < nt; ++j) {
-                if (MODE == 0) {
-                    if (lane < 32) {
-                        float g = 0.0f, u = 0.0f;
+        float* red = (float*)lds;  // [wave][group][row 32][token 32]
+        if (nvalid) {
 #pragma unroll
-                        for (int w = 0; w < kWaves; ++w) {
-                            g += red[(w * TT + j) * 64 + lane];
-                            u += red[(w * TT + j) * 64 + lane + 32];
-                        }
-                        const float h = g / (1.0f + __expf(-g)) * u;
-                        const _Float16 hi = (_Float16)h;
-                        const _Float16 lo = (_Float16)(h - (float)hi);
-                        if (valid) {
-                            const int hrow = shared ? TK + t0 + j : p0 + t0 + j;
-                            const size_t o = (size_t)hrow * a.hstride + tile * 32 + lane;
-                            a.h_hi[o] = __builtin_bit_cast(uint16_t, hi);
-                            a.h_lo[o] = __builtin_bit_cast(uint16_t, lo);
-                        }
-                    }
-                } else {
-                    float d = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                const int r = 8 * (i >> 2) + 4 * kh + (i & 3);
+                red[((wave * 2 + 0) * 32 + r) * 32 + rho] = C0[i];
+                red[((wave * 2 + 1) * 32 + r) * 32 + rho] = C1[i];
+            }
+        }
+        __syncthreads();
+        if (MODE == 0) {
+            const int Iblk = R >> 1;
+            for (int idx = tid; idx < 32 * nt; idx += kThreads) {
+                const int r = idx / nt, n = idx - r * nt;
+                float g = 0.0f, u = 0.0f;
 #pragma unroll
-                    for (int w = 0; w < kWaves; ++w) d += red[(w * TT + j) * 64 + lane];
-                    if (valid) {
-                        const int orow = shared ? TK + t0 + j : a.sorted[p0 + t0 + j];
-                        a.dout[(size_t)orow * a.H + row] = d;
-                    }
+                for (int w = 0; w < kWaves; ++w) {
+                    g += red[((w * 2 + 0) * 32 + r) * 32 + n];
+                    u += red[((w * 2 + 1) * 32 + r) * 32 + n];
+                }
+                const int i = tile * 32 + r;
+                if (i < Iblk) {
+                    const float h = g / (1.0f + __expf(-g)) * u;
+                    const _Float16 hi = (_Float16)h;
+                    const _Float16 lo = (_Float16)(h - (float)hi);
+                    const int hrow = shared ? TK + t0 + n : p0 + t0 + n;
+                    const size_t o = (size_t)hrow * a.hstride + i;
+                    a.h_hi[o] = __builtin_bit_cast(uint16_t, hi);
+                    a.h_lo[o] = __builtin_bit_cast(uint16_t, lo);
+                }
+            }
+        } else {
+            for (int idx = tid; idx < 64 * nt; idx += kThreads) {
+                const int r64 = idx / nt, n = idx - r64 * nt;
+                const int g = r64 >> 5, r = r64 & 31;
+                float d = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) d += red[((w * 2 + g) * 32 + r) * 32 + n];
+                const int orow_r = tile * 64 + r64;
+                if (orow_r < R) {
+                    const int orow = shared ? TK + t0 + n : a.sorted[p0 + t0 + n];
+                    a.dout[((size_t)split * a.drows + orow) * a.H + orow_r] = d;
                 }
             }
         }
@@ -407,17 +599,21 @@ __device__ void gemv_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, b
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(kThreads) ffn_gemv_kernel(FfnArgs a)
+__global__ void __launch_bounds__(kThreads, 2) ffn_gemv_kernel(FfnArgs a)
 {
     __shared__ uint32_t lds[kGemvLdsWords];
     const int wg = blockIdx.x;
-    const int routed_wgs = a.n_slots * a.tiles_routed;
+    const int per_slot = a.tiles_routed * a.splits_routed;
+    const int routed_wgs = a.n_slots * per_slot;
     bool shared;
-    int tile, p0, ntok, slot_expert;
+    int tile, split, nsplit, p0, ntok, slot_expert;
     if (wg < routed_wgs) {
         shared = false;
-        const int slot = wg / a.tiles_routed;
-        tile = wg - slot * a.tiles_routed;
+        const int slot = wg / per_slot;
+        const int rem = wg - slot * per_slot;
+        tile = rem / a.splits_routed;
+        split = rem - tile * a.splits_routed;
+        nsplit = a.splits_routed;
         // the slot-th expert with at least one routed assignment
         int e = -1, cnt = 0;
         for (int ee = 0; ee < a.E; ++ee) {
@@ -435,32 +631,47 @@ __global__ void __launch_bounds__(kThreads) ffn_gemv_kernel(FfnArgs a)
         slot_expert = e;
     } else {
         shared = true;
-        tile = wg - routed_wgs;
+        const int rem = wg - routed_wgs;
+        tile = rem / a.splits_shared;
+        split = rem - tile * a.splits_shared;
+        nsplit = a.splits_shared;
         p0 = 0;
         ntok = a.T;
         slot_expert = a.E;
     }
     const BlockDesc* bd = a.table + (slot_expert * 2 + MODE);
     switch (bd->q) {
-        case 3: gemv_block<MODE, 3>(a, bd, shared, p0, ntok, tile, lds); break;
-        case 4: gemv_block<MODE, 4>(a, bd, shared, p0, ntok, tile, lds); break;
-        case 5: gemv_block<MODE, 5>(a, bd, shared, p0, ntok, tile, lds); break;
-        case 6: gemv_block<MODE, 6>(a, bd, shared, p0, ntok, tile, lds); break;
-        case 7: gemv_block<MODE, 7>(a, bd, shared, p0, ntok, tile, lds); break;
-        case 8: gemv_block<MODE, 8>(a, bd, shared, p0, ntok, tile, lds); break;
+        case 3: mfma_block<MODE, 3>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 4: mfma_block<MODE, 4>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 5: mfma_block<MODE, 5>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 6: mfma_block<MODE, 6>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 7: mfma_block<MODE, 7>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 8: mfma_block<MODE, 8>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
         default: break;
     }
 }
 
+// y[t][o] = sum_j w[t][j] * (sum over splits of d_(t,j)[o]) (+ shared d), rounded once to fp16.
 __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a)
 {
     const size_t n = (size_t)a.T * a.H;
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const int t = (int)(i / a.H), o = (int)(i - (size_t)t * a.H);
+    const size_t plane = (size_t)a.drows * a.H;
     float s = 0.0f;
-    for (int j = 0; j < a.k; ++j) s += a.topk_w[t * a.k + j] * a.dout[((size_t)t * a.k + j) * a.H + o];
-    if (a.tiles_shared) s += a.dout[((size_t)a.T * a.k + t) * a.H + o];
+    for (int j = 0; j < a.k; ++j) {
+        const float* d = a.dout + ((size_t)t * a.k + j) * a.H + o;
+        float dj = 0.0f;
+        for (int sp = 0; sp < a.splits_routed; ++sp) dj += d[sp * plane];
+        s += a.topk_w[t * a.k + j] * dj;
+    }
+    if (a.tiles_shared) {
+        const float* d = a.dout + ((size_t)a.T * a.k + t) * a.H + o;
+        float ds = 0.0f;
+        for (int sp = 0; sp < a.splits_shared; ++sp) ds += d[sp * plane];
+        s += ds;
+    }
     a.y[i] = __builtin_bit_cast(uint16_t, (_Float16)s);
 }
 
@@ -478,6 +689,7 @@ __device__ void debug_block(const BlockDesc* __restrict__ bd, int R, int K, uint
     __syncthreads();
     const char* lutb = (const char*)lds;
     const uint32_t lane_off = (uint32_t)lane * 4u;
+    const RepMasks masks = make_masks();
     for (int c = 0; c < bd->nchunks; ++c) {
         uint4 pv[Q];
 #pragma unroll
@@ -487,7 +699,7 @@ __device__ void debug_block(const BlockDesc* __restrict__ bd, int R, int K, uint
 #pragma unroll
             for (int p = 0; p < Q; ++p) W[p] = word_of(pv[p], ww);
             Gathered<Q> g;
-            gather<Q>(W, g);
+            gather<Q>(W, g, masks);
             h2 w2[16];
             lookup<Q>(g, lane_off, lutb, w2);
             if (!valid) continue;
@@ -541,7 +753,7 @@ __global__ void __launch_bounds__(64) debug_decode_kernel(const BlockDesc* __res
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s)
 {
-    hipLaunchKernelGGL(route_topk_kernel, dim3((T + 255) / 256), dim3(256), 0, s, logits, T, E, k, idx, w);
+    hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
     return hipGetLastError();
 }
 
@@ -554,7 +766,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
 {
-    const int grid = a.n_slots * a.tiles_routed + a.tiles_shared;
+    const int grid = a.n_slots * a.tiles_routed * a.splits_routed + a.tiles_shared * a.splits_shared;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(ffn_gemv_kernel<0>, dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
@@ -562,7 +774,7 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
 
 hipError_t launch_down(const FfnArgs& a, hipStream_t s)
 {
-    const int grid = a.n_slots * a.tiles_routed + a.tiles_shared;
+    const int grid = a.n_slots * a.tiles_routed * a.splits_routed + a.tiles_shared * a.splits_shared;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(ffn_gemv_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();

@@ -73,7 +73,7 @@ typedef void *pw_stream;
 typedef struct {
     int32_t num_layers;        /* >= 1                                            */
     int32_t num_experts;       /* routed experts per layer, 1..256                 */
-    int32_t hidden;            /* H, multiple of 32, 32..65536                     */
+    int32_t hidden;            /* H, multiple of 32, 32..32768                     */
     int32_t inter;             /* I of a routed expert, multiple of 32             */
     int32_t inter_shared;      /* I of the shared expert (multiple of 32), 0 = none */
     int32_t top_k;             /* experts per token, 1..min(8, num_experts)        */
