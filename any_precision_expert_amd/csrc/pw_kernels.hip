@@ -27,6 +27,7 @@
 namespace pw {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const uint32_t* cu32p;  // scalar-loadable
 typedef __attribute__((address_space(1))) const u32x4* gu32x4p;    // global (not flat)
@@ -35,10 +36,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kLutBytes = 65536;  // largest LDS LUT: 256 slots x 64 lanes x 4 B
 constexpr int kStageWords = 16 * 64;  // pair-table staging (single LUT of q <= 4)
-constexpr int kXTileBytes = 90112;     // activation tile of one token pass (88 KB)
-// LUT (reused for the cross-wave reduction) + pair staging + activation tile:
-// 156 KB, one workgroup per CU (the contraction's VGPR budget allows 8 waves).
-constexpr int kGemvLdsWords = kLutBytes / 4 + kStageWords + kXTileBytes / 4;
+// LUT (reused for the cross-wave reduction) + pair staging: 68 KB, two 8-wave
+// workgroups per CU.
+constexpr int kGemvLdsWords = kLutBytes / 4 + kStageWords;
 constexpr int kDebugLdsWords = kLutBytes / 4 + 16 * 64;        // LUT + pair staging
 
 // ---------------------------------------------------------------- bit gather
@@ -153,6 +153,64 @@ __device__ __forceinline__ void lookup(const Gathered<Q>& g, uint32_t lane_off, 
             }
         }
     }
+}
+
+// Step-wise form of gather + lookup used by the contraction: the planes are
+// rotated once (Rot), then each MFMA step P assembles only its own code
+// register(s) and looks up its 8 weights, which keeps few registers live.
+template <int Q>
+struct Rot {
+    uint32_t A[Q];
+    uint32_t B[Q <= 4 ? Q : 1];
+};
+
+template <int Q>
+__device__ __forceinline__ void rotate_planes(const uint32_t (&W)[Q], Rot<Q>& r)
+{
+#pragma unroll
+    for (int p = 0; p < Q; ++p) r.A[p] = rotl(W[p], Q - 1 - p);
+    if constexpr (Q <= 4) {
+#pragma unroll
+        for (int p = 0; p < Q; ++p) r.B[p] = rotl(W[p], 2 * Q - 5 - p);
+    }
+}
+
+// Weights of columns 8P..8P+7 of the word as an MFMA A fragment (8 x fp16).
+template <int Q>
+__device__ __forceinline__ half8_t step_weights(const Rot<Q>& r, int P, const RepMasks& M, uint32_t lane_off,
+                                               const char* lutb)
+{
+    half8_t f;
+    if constexpr (Q <= 4) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int p = 0; p < Q; ++p) {
+            acc = and_or(r.A[p], M.m[rep_index(P + Q - 1 - p)], acc);
+            acc = and_or(r.B[p], M.m[rep_index(P + 2 * Q - 1 - p)], acc);
+        }
+        const uint32_t pr = rotr(acc, P);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h2 v = *(const h2*)(lutb + lut_addr(pr, lane_off, i));
+            f[2 * i] = v.x;
+            f[2 * i + 1] = v.y;
+        }
+    } else {
+        uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+        for (int p = 0; p < Q; ++p) {
+            c0 = and_or(r.A[p], M.m[rep_index(P + Q - 1 - p)], c0);
+            c1 = and_or(r.A[p], M.m[rep_index(4 + P + Q - 1 - p)], c1);
+        }
+        c0 = rotr(c0, P);
+        c1 = rotr(c1, 4 + P);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = *(const _Float16*)(lutb + lut_addr(c0, lane_off, i));
+            f[2 * i + 1] = *(const _Float16*)(lutb + lut_addr(c1, lane_off, i));
+        }
+    }
+    return f;
 }
 
 // LUT_q of this lane's row -> LDS slots [entry][lane] (32-bit each).
@@ -363,16 +421,19 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
 //         workgroups, each writing the fp32 partial expert output of its split
 //         (summed in split order by the combine).
 //
-// Lane l = (rho = l % 32, kh = l / 32) decodes rows rho (group 0) and 32 + rho
-// (group 1).  In a 128-column chunk it owns words 2*kh and 2*kh + 1 of both
-// rows (8-byte loads; 64 lanes read 32 rows x 16 B = 512 B contiguous per row
-// group).  The word pair u pairs word u (kh = 0) with word 2 + u (kh = 1) in
-// one 16-deep MFMA step set: step P takes columns 8P..8P+7 of each word, which
-// is exactly what the gather produces for register P.  The up-to-32 tokens of
-// a pass are the MFMA's N columns (B lanes: token rho, k half kh), so a weight
-// is decoded once per 32 tokens and no VALU multiply-add remains.  The eight
-// waves split K; their fp32 partials are summed in wave order through the
-// LUT's LDS region once the pass no longer needs the LUT.
+// Waves 0-3 own row group 0 and waves 4-7 row group 1; the four waves of a
+// group split K by 128-column chunks.  Lane l = (rho = l % 32, kh = l / 32)
+// decodes row rho of its group and, in each chunk, words 2*kh and 2*kh + 1
+// (8-byte loads: a wave reads 32 rows x 16 B = 512 B contiguous per plane).
+// Word pair u pairs word u (kh = 0) with word 2 + u (kh = 1) in one 16-deep
+// MFMA step set: step P takes columns 8P..8P+7 of each word, which is exactly
+// what the gather produces for register P.  The up-to-32 tokens of a pass are
+// the MFMA's N columns (B lanes: token rho, k half kh, staged in LDS), so a
+// weight is decoded once per 32 tokens and no VALU multiply-add remains.  The
+// kernel is bound by HBM bytes in flight: each wave keeps a ring of D chunks
+// (about 12-16 KB) of plane loads outstanding, spending its VGPR budget (one
+// 8-wave workgroup per CU) on that ring.  The partials of a group's four waves
+// are summed in wave order through the LUT's LDS region after the pass.
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -380,168 +441,151 @@ typedef __attribute__((address_space(1))) const u32x2* gu32x2p;
 typedef __attribute__((address_space(1))) const u32x4* gcu32x4p;
 
 constexpr int kTokTile = 32;
+constexpr int kKWaves = kWaves / 2;  // waves per row group (K split)
 
+// The kernel's FfnArgs viewed in the (constant) kernarg segment: fields are
+// read with scalar loads on demand instead of being copied to scratch.
+typedef __attribute__((address_space(4))) const FfnArgs KArgs;
+__device__ __forceinline__ KArgs& kernel_args()
+{
+    return *(KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// Words 2*kh, 2*kh+1 of chunk c of `row` from each of the q planes.  Plane
+// pointers are read from the page-table entry (scalar loads, K-cache hits).
+// The loads are unconditional (callers pass an in-range row even for lanes
+// whose row is past the block; those lanes' outputs are never stored): a
+// lane-divergent load makes the compiler wait for every outstanding load
+// (vmcnt(0)), which would serialise the prefetch ring.
 template <int Q>
-__device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const uint32_t* const (&planes)[Q], int c, int R,
-                                                int row, bool valid, int kh)
+__device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const BlockDesc* __restrict__ bd, int c, int R,
+                                                int row, int kh)
 {
+    const size_t at = ((size_t)c * R + row) * 2 + kh;
+    const __attribute__((address_space(4))) BlockDesc* cbd = (const __attribute__((address_space(4))) BlockDesc*)(uintptr_t)bd;
 #pragma unroll
-    for (int p = 0; p < Q; ++p) {
-        if (valid)
-            pg[p] = __builtin_nontemporal_load((gu32x2p)(uintptr_t)planes[p] + (((size_t)c * R + row) * 2 + kh));
-        else
-            pg[p] = u32x2{0, 0};
-    }
+    for (int p = 0; p < Q; ++p) pg[p] = __builtin_nontemporal_load((gu32x2p)(uintptr_t)cbd->planes[p] + at);
 }
 
-// MFMA B fragment (8 consecutive fp16 of one staged activation row) from LDS.
-__device__ __forceinline__ half8 lds_frag(const uint16_t* p, bool ok)
+// MFMA B fragment: 8 consecutive fp16 of one activation row (L2-resident).
+__device__ __forceinline__ half8 load_frag(const uint16_t* p)
 {
-    if (!ok) return half8{0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_bit_cast(half8, *(const u32x4*)p);
-}
-
-__device__ __forceinline__ half8 frag_of(const h2 (&w2)[16], int P)
-{
-    half8 r;
-    r[0] = w2[4 * P + 0].x;
-    r[1] = w2[4 * P + 0].y;
-    r[2] = w2[4 * P + 1].x;
-    r[3] = w2[4 * P + 1].y;
-    r[4] = w2[4 * P + 2].x;
-    r[5] = w2[4 * P + 2].y;
-    r[6] = w2[4 * P + 3].x;
-    r[7] = w2[4 * P + 3].y;
-    return r;
+    return __builtin_bit_cast(half8, *(gcu32x4p)(uintptr_t)p);
 }
 
 template <int MODE, int Q>
-__device__ void mfma_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0, int ntok,
+__device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0, int ntok,
                            int tile, int split, int nsplit, uint32_t* lds)
 {
     const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave / kKWaves, kw = wave % kKWaves;
     const int R = bd->R;
     const int nchunks = bd->nchunks, kwords = bd->kwords;
-    int row[2], srow;
-    bool rvalid[2], svalid;
+    int row, srow;
+    bool rvalid, svalid;
     if (MODE == 0) {
         const int Iblk = R >> 1;
         const int i = tile * 32 + rho;
-        rvalid[0] = rvalid[1] = svalid = i < Iblk;
-        row[0] = i;
-        row[1] = Iblk + i;
-        srow = kh ? row[1] : row[0];  // LDS slot `lane` holds the LUT of this row
+        rvalid = svalid = i < Iblk;
+        row = grp ? Iblk + i : i;
+        srow = kh ? Iblk + i : i;  // LDS slot `lane` holds the LUT of this row
     } else {
-        row[0] = tile * 64 + rho;
-        row[1] = tile * 64 + 32 + rho;
-        rvalid[0] = row[0] < R;
-        rvalid[1] = row[1] < R;
+        row = tile * 64 + 32 * grp + rho;
+        rvalid = row < R;
         srow = tile * 64 + lane;
         svalid = srow < R;
     }
-    const uint32_t* planes[Q];
-#pragma unroll
-    for (int p = 0; p < Q; ++p) planes[p] = bd->planes[p];
-
+    const int lrow = rvalid ? row : 0;  // in-range load row
     const int cps = (nchunks + nsplit - 1) / nsplit;
     const int c_begin = split * cps;
     const int c_end = min(nchunks, c_begin + cps);
-    const int first = c_begin + wave;
-    const int nch = first < c_end ? (c_end - first + kWaves - 1) / kWaves : 0;
+    const int first = c_begin + kw;
+    const int nch = first < c_end ? (c_end - first + kKWaves - 1) / kKWaves : 0;
 
-    // ring of D chunks in flight per wave (both row groups), deeper for low q
-    constexpr int D = Q <= 4 ? 3 : (Q <= 6 ? 2 : 1);
-    u32x2 pg[D][2][Q];
-    const uint32_t off0 = (uint32_t)rho * 4u, off1 = (uint32_t)(32 + rho) * 4u;
+    // ring of D chunks in flight per wave
+    constexpr int D = 1;
+    u32x2 pg[D][Q];
+    const uint32_t lane_off = (uint32_t)(32 * grp + rho) * 4u;
     const char* lutb = (const char*)lds;
     const RepMasks masks = make_masks();
     const int TK = a.T * a.k;
 
-    // activation tile in LDS: the tokens of one pass over this workgroup's
-    // column range [kc0, kc0 + kcols), rows padded by 16 B to spread banks
-    const int kc0 = c_begin * kChunkCols;
-    const int kcols = max(0, min(bd->K, c_end * kChunkCols) - kc0);
-    const int xstride = kcols + 8;  // halves per staged row
-    const int per_tok = (MODE == 0 ? 1 : 2) * xstride * 2;
-    const int ttile = min(kTokTile, kXTileBytes / per_tok);
-    uint16_t* xt = (uint16_t*)(lds + kLutBytes / 4 + kStageWords);
-
-    for (int t0 = 0; t0 < ntok; t0 += ttile) {
-        // the pass's first chunks are in flight while its LUT and activations are staged
+    for (int t0 = 0; t0 < ntok; t0 += kTokTile) {
+        // the pass's first chunks are in flight while its LUT is staged
+        if (nch > 0) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            if (d < nch) {
-                load_pair_words<Q>(pg[d][0], planes, first + d * kWaves, R, row[0], rvalid[0], kh);
-                load_pair_words<Q>(pg[d][1], planes, first + d * kWaves, R, row[1], rvalid[1], kh);
-            }
+            for (int d = 0; d < D; ++d)
+                load_pair_words<Q>(pg[d], bd, first + min(d, nch - 1) * kKWaves, R, lrow, kh);
         }
-        const int nt = min(ttile, ntok - t0);
-        {
-            const int v8 = kcols >> 3;  // 16-byte vectors per row
-            const int nvec = (MODE == 0 ? 1 : 2) * nt * v8;
-            for (int i = tid; i < nvec; i += kThreads) {
-                const int part = MODE == 0 ? 0 : i / (nt * v8);
-                const int r = (i - part * nt * v8) / v8, v = i - part * nt * v8 - r * v8;
-                const uint16_t* src;
-                if (MODE == 0) {
-                    const int tok = shared ? t0 + r : a.sorted[p0 + t0 + r] / a.k;
-                    src = a.x + (size_t)tok * a.H;
-                } else {
-                    const int hrow = shared ? TK + t0 + r : p0 + t0 + r;
-                    src = (part ? a.h_lo : a.h_hi) + (size_t)hrow * a.hstride;
-                }
-                const u32x4 val = *(gcu32x4p)(uintptr_t)(src + kc0 + 8 * v);
-                *(u32x4*)(xt + (size_t)(part * nt + r) * xstride + 8 * v) = val;
-            }
-        }
+        const int nt = min(kTokTile, ntok - t0);
         load_lut<Q>(lds, lds + kLutBytes / 4, bd->lut, srow, svalid, lane, wave, kWaves);
         __syncthreads();
+        // B rows: token lanes past the pass read token 0's row (their output
+        // columns are never stored)
+        const int n = rho < nt ? rho : 0;
+        const uint16_t* src_hi;
+        const uint16_t* src_lo = a.x;
+        if (MODE == 0) {
+            const int tok = shared ? t0 + n : a.sorted[p0 + t0 + n] / a.k;
+            src_hi = a.x + (size_t)tok * a.H;
+        } else {
+            const int hrow = shared ? TK + t0 + n : p0 + t0 + n;
+            src_hi = a.h_hi + (size_t)hrow * a.hstride;
+            src_lo = a.h_lo + (size_t)hrow * a.hstride;
+        }
         const bool nvalid = rho < nt;
-        const uint16_t* xs_hi = xt + (size_t)rho * xstride - kc0;
-        const uint16_t* xs_lo = xt + (size_t)(nt + rho) * xstride - kc0;
-        f32x16 C0 = {}, C1 = {};
+        f32x16 C = {};
 
+        // The ring is unrolled by D: buffer d always holds chunk ci0 + d, so no
+        // in-flight register is ever moved.  Every load is unconditional (the
+        // refill past the wave's range re-reads its last chunk, an L2 hit) and
+        // every B fragment read is unconditional (lanes and padding chunks that
+        // need zeros read the zero slot), so the body is straight-line code
+        // and the wait counts follow the ring exactly.
+        const int lastc = first + (nch - 1) * kKWaves;
         for (int ci0 = 0; ci0 < nch; ci0 += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
+                // keep the scheduler from hoisting the next slot's decode (which
+                // would wait on that slot's loads too)
+                __builtin_amdgcn_sched_barrier(0);
                 const int ci = ci0 + d;
-                if (ci >= nch) break;
-                const int c = first + ci * kWaves;
+                const bool live = ci < nch;  // padding chunk: B = 0
+                const int c = min(first + ci * kKWaves, lastc);
                 const int nw = min(4, kwords - 4 * c);
-                const int ulast = nw > 1 ? 1 : 0;
-                const bool more = ci + D < nch;
-                const int cn = first + (ci + D) * kWaves;
+                u32x2 cur[Q];
+#pragma unroll
+                for (int p = 0; p < Q; ++p) cur[p] = pg[d][p];
+                load_pair_words<Q>(pg[d], bd, min(c + D * kKWaves, lastc), R, lrow, kh);
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    if (u > ulast) break;
                     const int wd = 2 * kh + u;
-                    const bool bv = nvalid && wd < nw;  // zero B columns beyond K
-                    const int col = c * kChunkCols + 32 * wd;
+                    const bool bv = live && wd < nw;  // zero B beyond K and in padding chunks
+                    const int col = min(c * kChunkCols + 32 * wd, kwords * 32 - 32);
                     half8 Bh[4], Bl[4];
 #pragma unroll
                     for (int P = 0; P < 4; ++P) {
-                        Bh[P] = lds_frag(xs_hi + col + 8 * P, bv);
-                        if (MODE == 1) Bl[P] = lds_frag(xs_lo + col + 8 * P, bv);
+                        Bh[P] = load_frag(src_hi + col + 8 * P);
+                        if (MODE == 1) Bl[P] = load_frag(src_lo + col + 8 * P);
                     }
-#pragma unroll
-                    for (int g = 0; g < 2; ++g) {
-                        uint32_t W[Q];
-#pragma unroll
-                        for (int p = 0; p < Q; ++p) W[p] = pg[d][g][p][u];
-                        Gathered<Q> gr;
-                        gather<Q>(W, gr, masks);
-                        h2 w2[16];
-                        lookup<Q>(gr, g == 0 ? off0 : off1, lutb, w2);
-                        f32x16& C = g == 0 ? C0 : C1;
+                    if (!(live && nw == 4)) {  // rare: partial last chunk or padding chunk
 #pragma unroll
                         for (int P = 0; P < 4; ++P) {
-                            const half8 A = frag_of(w2, P);
-                            C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh[P], C, 0, 0, 0);
-                            if (MODE == 1) C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl[P], C, 0, 0, 0);
+                            if (!bv) Bh[P] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+                            if (MODE == 1 && !bv) Bl[P] = half8{0, 0, 0, 0, 0, 0, 0, 0};
                         }
-                        if (u == ulast && more)  // this buffer's row group is consumed: refill it
-                            load_pair_words<Q>(pg[d][g], planes, cn, R, row[g], rvalid[g], kh);
+                    }
+                    uint32_t W[Q];
+#pragma unroll
+                    for (int p = 0; p < Q; ++p) W[p] = cur[p][u];
+                    Rot<Q> rt;
+                    rotate_planes<Q>(W, rt);
+#pragma unroll
+                    for (int P = 0; P < 4; ++P) {
+                        const half8 A = step_weights<Q>(rt, P, masks, lane_off, lutb);
+                        C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh[P], C, 0, 0, 0);
+                        if (MODE == 1) C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl[P], C, 0, 0, 0);
                     }
                 }
             }
@@ -549,13 +593,12 @@ __device__ void mfma_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, b
 
         // cross-wave reduction through the (no longer needed) LUT region
         __syncthreads();
-        float* red = (float*)lds;  // [wave][group][row 32][token 32]
+        float* red = (float*)lds;  // [wave][row 32][token 32]
         if (nvalid) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = 8 * (i >> 2) + 4 * kh + (i & 3);
-                red[((wave * 2 + 0) * 32 + r) * 32 + rho] = C0[i];
-                red[((wave * 2 + 1) * 32 + r) * 32 + rho] = C1[i];
+                red[(wave * 32 + r) * 32 + rho] = C[i];
             }
         }
         __syncthreads();
@@ -565,9 +608,9 @@ __device__ void mfma_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, b
                 const int r = idx / nt, n = idx - r * nt;
                 float g = 0.0f, u = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
-                    g += red[((w * 2 + 0) * 32 + r) * 32 + n];
-                    u += red[((w * 2 + 1) * 32 + r) * 32 + n];
+                for (int w = 0; w < kKWaves; ++w) {
+                    g += red[(w * 32 + r) * 32 + n];
+                    u += red[((kKWaves + w) * 32 + r) * 32 + n];
                 }
                 const int i = tile * 32 + r;
                 if (i < Iblk) {
@@ -586,7 +629,7 @@ __device__ void mfma_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, b
                 const int g = r64 >> 5, r = r64 & 31;
                 float d = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) d += red[((w * 2 + g) * 32 + r) * 32 + n];
+                for (int w = 0; w < kKWaves; ++w) d += red[((g * kKWaves + w) * 32 + r) * 32 + n];
                 const int orow_r = tile * 64 + r64;
                 if (orow_r < R) {
                     const int orow = shared ? TK + t0 + n : a.sorted[p0 + t0 + n];
@@ -599,7 +642,7 @@ __device__ void mfma_block(const FfnArgs& a, const BlockDesc* __restrict__ bd, b
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(kThreads, 2) ffn_gemv_kernel(FfnArgs a)
+__global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 {
     __shared__ uint32_t lds[kGemvLdsWords];
     const int wg = blockIdx.x;
@@ -640,13 +683,14 @@ __global__ void __launch_bounds__(kThreads, 2) ffn_gemv_kernel(FfnArgs a)
         slot_expert = a.E;
     }
     const BlockDesc* bd = a.table + (slot_expert * 2 + MODE);
+    KArgs& ka = kernel_args();
     switch (bd->q) {
-        case 3: mfma_block<MODE, 3>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 4: mfma_block<MODE, 4>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 5: mfma_block<MODE, 5>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 6: mfma_block<MODE, 6>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 7: mfma_block<MODE, 7>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 8: mfma_block<MODE, 8>(a, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 3: mfma_block<MODE, 3>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 4: mfma_block<MODE, 4>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 5: mfma_block<MODE, 5>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 6: mfma_block<MODE, 6>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 7: mfma_block<MODE, 7>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 8: mfma_block<MODE, 8>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
         default: break;
     }
 }
