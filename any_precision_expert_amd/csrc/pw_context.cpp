@@ -53,6 +53,7 @@ pw_status ok()
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Device slabs for planes and LUTs, recycled by size.  A released slab is only
 // reused after an event recorded behind the last work that may read it.
@@ -444,8 +445,8 @@ pw_status pw_route_topk(pw_ctx* c, const float* logits, int T, int32_t* idx, flo
     if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_route_topk: T=%d out of range", T);
     if (T == 0) return ok();
     if (!logits || !idx || !w) return fail(PW_ERR_INVALID, "pw_route_topk: null pointer");
-    if (!aligned16(logits) || !aligned16(idx) || !aligned16(w))
-        return fail(PW_ERR_INVALID, "pw_route_topk: device pointers must be 16-byte aligned");
+    if (!aligned4(logits) || !aligned4(idx) || !aligned4(w))
+        return fail(PW_ERR_INVALID, "pw_route_topk: device pointers must be 4-byte aligned");
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
     ProfScope ps(c, "route", (hipStream_t)stream);
@@ -460,8 +461,8 @@ pw_status pw_permute_by_expert(pw_ctx* c, const int32_t* idx, int T, int32_t* of
     if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_permute_by_expert: T=%d out of range", T);
     if (!offsets) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null offsets");
     if (T > 0 && (!idx || !sorted)) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null pointer");
-    if (!aligned16(offsets) || (T > 0 && (!aligned16(idx) || !aligned16(sorted))))
-        return fail(PW_ERR_INVALID, "pw_permute_by_expert: device pointers must be 16-byte aligned");
+    if (!aligned4(offsets) || (T > 0 && (!aligned4(idx) || !aligned4(sorted))))
+        return fail(PW_ERR_INVALID, "pw_permute_by_expert: device pointers must be 4-byte aligned");
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
     ProfScope ps(c, "permute", (hipStream_t)stream);
@@ -479,9 +480,10 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
     if (T == 0) return ok();
     if (!x || !idx || !w || !offsets || !sorted || !y || !workspace)
         return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: null pointer");
-    if (!aligned16(x) || !aligned16(idx) || !aligned16(w) || !aligned16(offsets) || !aligned16(sorted) ||
+    if (!aligned16(x) || !aligned4(idx) || !aligned4(w) || !aligned4(offsets) || !aligned4(sorted) ||
         !aligned16(y) || ((uintptr_t)workspace & 255u))
-        return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: misaligned pointer (16 B; workspace 256 B)");
+        return fail(PW_ERR_INVALID,
+                    "pw_moe_ffn_bitplane: misaligned pointer (x, y 16 B; index arrays 4 B; workspace 256 B)");
     const pw_model_desc& d = c->d;
     const WsLayout L = ws_layout(T, d.top_k, d.hidden, d.inter, d.inter_shared);
     if (ws_bytes < L.total)

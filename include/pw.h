@@ -18,7 +18,8 @@
  *    call on the same thread).
  *  - "dev" pointers are device memory owned by the caller (for example torch
  *    tensors); "host" pointers are ordinary host memory owned by the caller.
- *    Device pointers must be 16-byte aligned.  Nothing the caller passes is
+ *    Activation arrays (x, y) must be 16-byte aligned, the workspace 256-byte
+ *    aligned, every other device array 4-byte aligned.  Nothing the caller passes is
  *    retained after the call returns, except through work enqueued on the
  *    given stream.
  *  - Hot-path calls (pw_route_topk, pw_permute_by_expert, pw_moe_ffn_bitplane)

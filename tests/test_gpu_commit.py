@@ -1,0 +1,165 @@
+"""GPU tests of committed-width changes (pw_set_committed_bits): lowering
+frees planes, raising reloads planes and LUTs from the pinned host masters on
+a copy stream, the new widths apply exactly to work enqueued after the call,
+and bad requests change nothing.  Outputs are checked against the fp64 oracle
+evaluated at the widths committed for that work."""
+import copy
+
+import numpy as np
+import pytest
+
+import pw_synth
+from tests.gpu_util import compare, make_ctx, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(require_gpu):
+    import any_precision_expert_amd as pw
+    pw.lib()
+
+
+def _layer(seed=500, T=6):
+    return pw_synth.make_small(H=256, I=160, E=5, top_k=2, T=T, I_shared=64, seed=seed)
+
+
+def _run(ctx, acts, stream=None):
+    import torch
+    from any_precision_expert_amd.layer import Batch
+    b = Batch(ctx, acts.x.shape[0])
+    b.load(acts.logits, acts.x)
+    b.step(0, stream)
+    return b
+
+
+def _fetch(b):
+    import torch
+    torch.cuda.synchronize()
+    T = b.T
+    return dict(idx=b.idx.cpu().numpy(), w=b.w.cpu().numpy(), offsets=b.offsets.cpu().numpy(),
+                sorted=b.sorted.cpu().numpy()[:T * b.ctx.desc.top_k], y=b.y.cpu().numpy().astype(np.float64))
+
+
+def _with_q(w, qs):
+    w2 = copy.copy(w)
+    w2.gate_up = [copy.copy(b) for b in w.gate_up]
+    w2.down = [copy.copy(b) for b in w.down]
+    for e, (qg, qd) in enumerate(qs):
+        w2.gate_up[e].q, w2.down[e].q = int(qg), int(qd)
+    return w2
+
+
+def test_lower_then_raise_matches_oracle_and_frees_memory():
+    import oracle
+    import torch
+    import any_precision_expert_amd as pw
+    from any_precision_expert_amd.layer import register_layer
+    w, a = _layer()
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        q0 = [(b.q, d.q) for b, d in zip(w.gate_up, w.down)]
+        res0 = ctx.resident_bytes()
+        compare(_fetch(_run(ctx, a)), oracle.moe_layer(w, a), label="initial")
+        ids = [ctx.block_id(0, e, m) for e in range(w.shape.E) for m in (0, 1)]
+        # lower every routed block to 3
+        ctx.set_committed_bits(ids, [3] * len(ids))
+        assert all(ctx.committed_bits(i) == 3 for i in ids)
+        y3 = _fetch(_run(ctx, a))
+        compare(y3, oracle.moe_layer(_with_q(w, [(3, 3)] * w.shape.E), a), label="lowered")
+        assert ctx.resident_bytes() < res0
+        # debug decode sees the new width
+        bid = ctx.block_id(0, 1, pw.MODULE_DOWN)
+        out = torch.zeros(w.down[1].code8.shape, dtype=torch.uint8, device="cuda")
+        ctx.debug_decode_codes(bid, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), w.down[1].code8 >> 5)
+        # raise every routed block to 8 (planes and LUT_8 reloaded from the host masters)
+        copy_stream = torch.cuda.Stream()
+        ctx.set_committed_bits(ids, [8] * len(ids), torch.cuda.current_stream(), copy_stream)
+        y8 = _fetch(_run(ctx, a))
+        compare(y8, oracle.moe_layer(_with_q(w, [(8, 8)] * w.shape.E), a), label="raised")
+        # back to the initial widths
+        ctx.set_committed_bits(ids, [q for e in q0 for q in e])
+        compare(_fetch(_run(ctx, a)), oracle.moe_layer(w, a), label="restored")
+    finally:
+        ctx.close()
+
+
+def test_new_widths_apply_only_to_later_work():
+    """Enqueue a step, change widths, enqueue another step -- no host sync in
+    between: the first sees the old widths, the second the new ones."""
+    import oracle
+    import torch
+    from any_precision_expert_amd.layer import Batch, register_layer
+    w, a = _layer(seed=501)
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        cs = torch.cuda.Stream()
+        b1 = Batch(ctx, a.x.shape[0])
+        b2 = Batch(ctx, a.x.shape[0])
+        b1.load(a.logits, a.x)
+        b2.load(a.logits, a.x)
+        torch.cuda.synchronize()
+        ids = [ctx.block_id(0, e, m) for e in range(w.shape.E) for m in (0, 1)]
+        qa = [5 if i % 2 else 8 for i in range(len(ids))]
+        qb = [4 if i % 3 else 7 for i in range(len(ids))]
+        ctx.set_committed_bits(ids, qa, s, cs)
+        torch.cuda.synchronize()
+        for _ in range(3):  # several rounds without a host sync
+            b1.step(0, s)
+            ctx.set_committed_bits(ids, qb, s, cs)
+            b2.step(0, s)
+            ctx.set_committed_bits(ids, qa, s, cs)
+        r1, r2 = _fetch(b1), _fetch(b2)
+        pa = list(zip(qa[0::2], qa[1::2]))
+        pb = list(zip(qb[0::2], qb[1::2]))
+        compare(r1, oracle.moe_layer(_with_q(w, pa), a), label="before change")
+        compare(r2, oracle.moe_layer(_with_q(w, pb), a), label="after change")
+    finally:
+        ctx.close()
+
+
+def test_bad_requests_change_nothing():
+    import any_precision_expert_amd as pw
+    from any_precision_expert_amd.layer import register_layer
+    w, a = _layer(seed=502)
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        ids = [ctx.block_id(0, 0, 0), ctx.block_id(0, 1, 1)]
+        before = [ctx.committed_bits(i) for i in ids]
+        res = ctx.resident_bytes()
+        for bad_ids, bad_q in (([ids[0], ids[0]], [4, 5]),      # duplicate id
+                               ([ids[0], 10 ** 6], [4, 5]),      # unknown id
+                               ([ids[0], ids[1]], [2, 5]),       # q below 3
+                               ([ids[0], ids[1]], [4, 9])):      # q above 8
+            with pytest.raises(pw.PwError) as ei:
+                ctx.set_committed_bits(bad_ids, bad_q)
+            assert ei.value.status == pw.PW_ERR_INVALID
+            assert [ctx.committed_bits(i) for i in ids] == before
+            assert ctx.resident_bytes() == res
+    finally:
+        ctx.close()
+
+
+def test_no_host_masters_means_no_width_changes():
+    import any_precision_expert_amd as pw
+    from any_precision_expert_amd.layer import register_layer
+    w, a = _layer(seed=503)
+    ctx = make_ctx(w.shape, keep_host_masters=False)
+    try:
+        register_layer(ctx, 0, w)
+        bid = ctx.block_id(0, 2, 0)
+        q = ctx.committed_bits(bid)
+        with pytest.raises(pw.PwError) as ei:
+            ctx.set_committed_bits([bid], [3 if q != 3 else 4])
+        assert ei.value.status == pw.PW_ERR_STATE
+        assert ctx.committed_bits(bid) == q
+        ctx.set_committed_bits([bid], [q])  # unchanged width: a no-op, accepted
+    finally:
+        ctx.close()
