@@ -60,11 +60,114 @@ def step_bytes(shape, wq, offsets, T):
     return dict(gate_up=gate_up, down=down, path=path, weights=gu + dn, active=len(active))
 
 
+KERNEL_SRC = os.path.join(ROOT, "any_precision_expert_amd", "csrc", "pw_kernels.hip")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "gate_up_qwen_decode_traffic.md")
+GATE_UP_NAME = "ffn_gemv_kernel<0>"
+COPY_NAME = "copyBuffer"
+
+
+def kernel_sha() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per gate_up launch from the committed PMC summary, or None if
+    the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_MD) as f:
+            for line in f:
+                if line.startswith("TRAFFIC_JSON:"):
+                    t = json.loads(line.split(":", 1)[1])
+                    return t if t.get("kernel_sha") == kernel_sha() else None
+    except OSError:
+        pass
+    return None
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError("%s under %s" % (suffix, d))
+
+
+def summarize_trace(trace_dir, out, command):
+    """Kernel-trace statistics (rocprofv3 --kernel-trace --stats) -> markdown."""
+    rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
+    lines = ["# Kernel time, Qwen-shaped decode layer (bench.py)", "",
+             "Command: `%s`" % command, "",
+             "| kernel | calls | average us | total ms | share % |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if not name.startswith("void pw::") and not name.startswith("pw::"):
+            continue
+        lines.append("| %s | %s | %.2f | %.2f | %.1f |" % (name.split("(")[0], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                       float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _pmc_mean(d, counter, kname, largest_only=False):
+    """Mean counter value over the dispatches of kernels named like `kname`
+    (largest_only: only those within 2x of the largest, i.e. the calibration
+    copies rather than small staging copies)."""
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(_find(d, "counter_collection.csv"))
+            if r["Counter_Name"] == counter and kname in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError("no %s samples for %s in %s" % (counter, kname, d))
+    if largest_only:
+        top = max(vals)
+        vals = [v for v in vals if v >= 0.5 * top]
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, copy_mib, alg_bytes):
+    """FETCH_SIZE / WRITE_SIZE per gate_up launch, scaled by the same counters
+    on a device copy of known size (copy reads and writes copy_mib MiB)."""
+    gu_f, n_f = _pmc_mean(fetch_dir, "FETCH_SIZE", GATE_UP_NAME)
+    gu_w, n_w = _pmc_mean(write_dir, "WRITE_SIZE", GATE_UP_NAME)
+    cp_f, _ = _pmc_mean(fetch_dir, "FETCH_SIZE", COPY_NAME, largest_only=True)
+    cp_w, _ = _pmc_mean(write_dir, "WRITE_SIZE", COPY_NAME, largest_only=True)
+    known_kib = copy_mib * 1024.0
+    sf, sw = known_kib / cp_f, known_kib / cp_w
+    fetch_b = gu_f * sf * 1024.0
+    write_b = gu_w * sw * 1024.0
+    t = dict(kernel_sha=kernel_sha(), fetch_bytes=fetch_b, write_bytes=write_b,
+             traffic_bytes=fetch_b + write_b, scale_fetch=sf, scale_write=sw,
+             algorithmic_bytes=alg_bytes)
+    lines = ["# HBM traffic of the gate_up kernel, Qwen-shaped decode layer", "",
+             "FETCH_SIZE command: `%s`" % command_fetch, "",
+             "WRITE_SIZE command: `%s`" % command_write, "",
+             "| quantity | value |", "|---|---|",
+             "| gate_up FETCH_SIZE per launch (raw KiB, %d launches) | %.1f |" % (n_f, gu_f),
+             "| gate_up WRITE_SIZE per launch (raw KiB, %d launches) | %.1f |" % (n_w, gu_w),
+             "| copy kernel FETCH_SIZE / WRITE_SIZE (raw KiB, %d MiB copied) | %.1f / %.1f |" % (copy_mib, cp_f, cp_w),
+             "| scale factor fetch / write (known KiB / counted KiB) | %.3f / %.3f |" % (sf, sw),
+             "| gate_up HBM read per launch (scaled, MB) | %.2f |" % (fetch_b / 1e6),
+             "| gate_up HBM write per launch (scaled, MB) | %.2f |" % (write_b / 1e6),
+             "| gate_up algorithmic bytes per launch (MB) | %.2f |" % (alg_bytes / 1e6),
+             "| traffic / algorithmic | %.3f |" % ((fetch_b + write_b) / alg_bytes), "",
+             "TRAFFIC_JSON: " + json.dumps(t)]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(weights, acts_list, budget_s):
     import oracle
     P = oracle.PreparedLayer(weights)
     n_tok, secs, batches = 0, 0.0, 0
-    while secs < budget_s and batches < len(acts_list) * 50:
+    while secs < budget_s:
         a = acts_list[batches % len(acts_list)]
         dt, _ = oracle.timed_layer(P, a)
         secs += dt
@@ -84,7 +187,21 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="distinct weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the bench, copy this many MiB device-to-device (PMC scale reference)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"))
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_MD"))
+    ap.add_argument("--command", default="", help="command line recorded in the summary")
+    ap.add_argument("--command2", default="", help="second command line (WRITE_SIZE pass)")
+    ap.add_argument("--alg-bytes", type=float, default=0.0, help="gate_up algorithmic bytes per launch")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2], args.command,
+                      args.command2, args.copy_calibration_mib, args.alg_bytes)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",
               file=sys.stderr)
@@ -194,6 +311,9 @@ def main():
         cpu = cpu_baseline(w, acts, args.cpu_seconds)
         log("cpu oracle: %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
 
+    tr = stored_traffic()
+    traffic = int(tr["traffic_bytes"]) if tr else None  # HBM bytes per launch (PMC, scaled)
+
     out = {
         "metric": "routed tokens/s per MoE layer at mixed 3-8 bit + achieved HBM GB/s vs peak",
         "value": round(tok_s, 1),
@@ -217,11 +337,19 @@ def main():
         "kernels_us": {k: round(v["mean_us"], 3) for k, v in kern.items()},
         "roofline": {"bound": "hbm", "kernel": "gate_up", "achieved": round(gu_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": int(mean_b["gate_up"]),
+                     "traffic": traffic, "bytes_per_launch": int(mean_b["gate_up"]),
                      "down_achieved": round(dn_gbps, 1)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 x %d MiB device-to-device" % args.copy_calibration_mib)
     ctx.close()
 
 
