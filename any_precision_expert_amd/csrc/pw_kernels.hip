@@ -9,16 +9,18 @@
 // one fused MoE operation.  The parent code has 8 bits; the width-q child
 // code is code >> (8 - q) = the top q planes; the weight is LUT_q[row][code].
 //
-// Decode-sized contraction ("bit-plane-streaming GEMV"): one workgroup owns 64
-// weight rows (one per lane) and splits K across its 8 waves.  Each lane
-// streams its row's q plane words with 16-byte loads ([chunk][row][4] layout:
-// 64 lanes read 1 KB contiguous), assembles child codes with a register-level
-// bit gather, looks weights up in the LDS copy of its row's LUT and
-// accumulates against fp16 activations held in scalar registers with
-// v_dot2_f32_f16 (fp32 accumulation).  The LUT lives in LDS as [code][lane]
-// 32-bit slots so a wave's 64 look-ups hit 32 distinct banks per half-wave;
-// for q <= 4 a pair table [code_a | code_b << q][lane] returns two weights
-// (a packed half2) per look-up.
+// Contraction: one 8-wave workgroup owns a 64-row tile of one block (gate_up
+// pairs 32 gate rows with the matching 32 up rows).  Waves 0-3 take row group
+// 0, waves 4-7 row group 1; the four waves of a group split K by 128-column
+// chunks.  Lane (row, half) of a wave streams two words of each of its row's q
+// planes per chunk ([chunk][row][4] layout: 512 contiguous bytes per wave and
+// plane), assembles child codes with a register-level bit gather, looks the
+// weights up in the LDS copy of the rows' LUTs and feeds them as the A operand
+// of v_mfma_f32_32x32x16_f16, with up to 32 tokens as B (fp32 accumulation).
+// Each weight is decoded once per 32 tokens.  The LUT lives in LDS as
+// [code][64 slots] 32-bit slots so a half-wave's 32 look-ups hit 32 distinct
+// banks; for q <= 4 a pair table [code_a | code_b << q] returns two weights (a
+// packed half2) per look-up.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -249,11 +251,6 @@ __device__ __forceinline__ uint4 load_planes_chunk(const uint32_t* plane, int c,
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int ww)
 {
     return ww == 0 ? v.x : ww == 1 ? v.y : ww == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ float dot2(h2 a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(h2, b), c, false);
 }
 
 // ---------------------------------------------------------------- routing

@@ -80,8 +80,9 @@ typedef struct {
     int32_t top_k;             /* experts per token, 1..min(8, num_experts)        */
     int32_t keep_host_masters; /* 1: keep all 8 planes and all LUTs in pinned host
                                   memory so pw_set_committed_bits can raise widths;
-                                  0: keep nothing on the host (widths may only be
-                                  lowered)                                        */
+                                  0: keep nothing on the host; every width is then
+                                  fixed at its registered value (a change fails
+                                  with PW_ERR_STATE)                              */
 } pw_model_desc;
 
 #define PW_QMIN 3
