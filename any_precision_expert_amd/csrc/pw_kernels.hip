@@ -38,9 +38,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kLutBytes = 65536;  // largest LDS LUT: 256 slots x 64 lanes x 4 B
 constexpr int kStageWords = 16 * 64;  // pair-table staging (single LUT of q <= 4)
-// LUT (reused for the cross-wave reduction) + pair staging: 68 KB, two 8-wave
-// workgroups per CU.
-constexpr int kGemvLdsWords = kLutBytes / 4 + kStageWords;
+// LUT + eight 2 KB per-wave activation slices (which also hold the pair-table
+// staging and the cross-wave reduction): 80 KB, two 8-wave workgroups per CU.
+constexpr int kGemvLdsWords = kLutBytes / 4 + kWaves * 512;
 constexpr int kDebugLdsWords = kLutBytes / 4 + 16 * 64;        // LUT + pair staging
 
 // ---------------------------------------------------------------- bit gather
@@ -219,26 +219,55 @@ __device__ __forceinline__ half8_t step_weights(const Rot<Q>& r, int P, const Re
 // Single (q >= 5): entry = code, low half = LUT[code].  Pair (q <= 4):
 // entry = a | b << q, value = LUT[a] | LUT[b] << 16; the single table is
 // staged first in `stage` (2^q x 64 slots) and the caller's barrier follows.
-template <int Q>
-__device__ __forceinline__ void load_lut(uint32_t* lds, uint32_t* stage, const uint16_t* lut, int row,
-                                         bool valid, int lane, int wave, int nwaves)
-{
-    constexpr int NC = 1 << Q;
-    uint32_t* single = Q <= 4 ? stage : lds;
-    gu32x4p src = (gu32x4p)(uintptr_t)(lut + (size_t)row * NC);
-    for (int c8 = wave; c8 < NC / 8; c8 += nwaves) {
-        u32x4 u = valid ? src[c8] : u32x4{0, 0, 0, 0};
-        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+// The NW waves share the 2^q / 8 16-byte pieces of each row.  Staging is split
+// in two so callers can put other loads between the LUT loads and their first
+// use: issue() starts every load of the wave, commit() writes LDS.  Lanes
+// whose row is past the block load row 0 (their slots are never used).
+template <int Q, int NW>
+struct LutPieces {
+    static constexpr int NC = 1 << Q;
+    static constexpr int NP = NC / 8;               // 16-byte pieces per row
+    static constexpr int PER = (NP + NW - 1) / NW;  // pieces per wave
+    u32x4 u[PER];
+
+    __device__ __forceinline__ void issue(const uint16_t* lut, int row, bool valid, int wave)
+    {
+        gu32x4p src = (gu32x4p)(uintptr_t)(lut + (size_t)(valid ? row : 0) * NC);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) single[((8 * c8 + j) << 6) | lane] = (w4[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        for (int j = 0; j < PER; ++j)
+            if (wave + j * NW < NP) u[j] = src[wave + j * NW];  // wave-uniform condition
     }
-    if constexpr (Q <= 4) {
-        __syncthreads();
-        for (int e = wave; e < NC * NC; e += nwaves) {
-            const int ea = e & (NC - 1), eb = e >> Q;
-            lds[(e << 6) | lane] = single[(ea << 6) | lane] | (single[(eb << 6) | lane] << 16);
+
+    __device__ __forceinline__ void commit(uint32_t* lds, uint32_t* stage, int lane, int wave)
+    {
+        uint32_t* single = Q <= 4 ? stage : lds;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int c8 = wave + j * NW;
+            if (c8 < NP) {
+                const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    single[((8 * c8 + i) << 6) | lane] = (w4[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            }
+        }
+        if constexpr (Q <= 4) {
+            __syncthreads();
+            for (int e = wave; e < NC * NC; e += NW) {
+                const int ea = e & (NC - 1), eb = e >> Q;
+                lds[(e << 6) | lane] = single[(ea << 6) | lane] | (single[(eb << 6) | lane] << 16);
+            }
         }
     }
+};
+
+template <int Q, int NW>
+__device__ __forceinline__ void load_lut(uint32_t* lds, uint32_t* stage, const uint16_t* lut, int row,
+                                         bool valid, int lane, int wave)
+{
+    LutPieces<Q, NW> lp;
+    lp.issue(lut, row, valid, wave);
+    lp.commit(lds, stage, lane, wave);
 }
 
 __device__ __forceinline__ uint4 load_planes_chunk(const uint32_t* plane, int c, int R, int row, bool valid)
@@ -424,21 +453,30 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
 // (8-byte loads: a wave reads 32 rows x 16 B = 512 B contiguous per plane).
 // Word pair u pairs word u (kh = 0) with word 2 + u (kh = 1) in one 16-deep
 // MFMA step set: step P takes columns 8P..8P+7 of each word, which is exactly
-// what the gather produces for register P.  The up-to-32 tokens of a pass are
-// the MFMA's N columns (B lanes: token rho, k half kh, staged in LDS), so a
-// weight is decoded once per 32 tokens and no VALU multiply-add remains.  The
-// kernel is bound by HBM bytes in flight: each wave keeps a ring of D chunks
-// (about 12-16 KB) of plane loads outstanding, spending its VGPR budget (one
-// 8-wave workgroup per CU) on that ring.  The partials of a group's four waves
-// are summed in wave order through the LUT's LDS region after the pass.
+// what the gather produces for register P.  The tokens of a pass (up to
+// kTokPass) are the MFMA's N columns; a weight is decoded once per pass.
+//
+// Memory pipeline.  Each wave keeps D chunks of plane loads in flight (a
+// static ring, so no in-flight register is ever moved) and loads the next
+// chunk's activations one chunk ahead: the 64 lanes fetch the pass's tokens x
+// 128 columns cooperatively (16 bytes each) and store them in the wave's own
+// LDS slice, from which the B fragments are read.  B reads therefore count on
+// lgkmcnt only, and waiting for this chunk's data never waits for the
+// prefetch of later chunks (global loads complete in order on vmcnt).  The
+// partials of a group's four waves are summed in wave order through the slice
+// region after the pass; the LUT stays resident for every pass.
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const u32x2* gu32x2p;
 typedef __attribute__((address_space(1))) const u32x4* gcu32x4p;
+typedef __attribute__((address_space(4))) const int32_t* ci32p;
 
-constexpr int kTokTile = 32;
-constexpr int kKWaves = kWaves / 2;  // waves per row group (K split)
+constexpr int kTokPass = 4;               // tokens per pass
+constexpr int kKWaves = kWaves / 2;       // waves per row group (K split)
+constexpr int kSliceWords = 512;          // per-wave slice: [part 2][token 4][16 units of 16 B]
+static_assert(kWaves * kSliceWords >= kStageWords, "pair staging lives in the slice region");
+static_assert(kWaves * 32 * kTokPass <= kWaves * kSliceWords, "reduction lives in the slice region");
 
 // The kernel's FfnArgs viewed in the (constant) kernarg segment: fields are
 // read with scalar loads on demand instead of being copied to scratch.
@@ -464,21 +502,26 @@ __device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const BlockDesc*
     for (int p = 0; p < Q; ++p) pg[p] = __builtin_nontemporal_load((gu32x2p)(uintptr_t)cbd->planes[p] + at);
 }
 
-// MFMA B fragment: 8 consecutive fp16 of one activation row (L2-resident).
-__device__ __forceinline__ half8 load_frag(const uint16_t* p)
+// 16-byte unit g (8 fp16 columns) of token t, part 0 (x or h hi) or 1 (h lo),
+// in a wave's slice.  The unit index is XOR-swizzled with the token so the B
+// reads of different tokens in one instruction fall in different banks.
+__device__ __forceinline__ int slice_unit(int part, int t, int g)
 {
-    return __builtin_bit_cast(half8, *(gcu32x4p)(uintptr_t)p);
+    return (part * kTokPass + t) * 16 + (g ^ t);
 }
 
 template <int MODE, int Q>
 __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0, int ntok,
                            int tile, int split, int nsplit, uint32_t* lds)
 {
+    constexpr int D = Q <= 4 ? 2 : 1;      // chunks of plane loads in flight
+    constexpr int NPART = MODE == 0 ? 1 : 2;
     const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave / kKWaves, kw = wave % kKWaves;
     const int R = bd->R;
     const int nchunks = bd->nchunks, kwords = bd->kwords;
+    const int K = kwords * 32;
     int row, srow;
     bool rvalid, svalid;
     if (MODE == 0) {
@@ -499,80 +542,102 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
     const int c_end = min(nchunks, c_begin + cps);
     const int first = c_begin + kw;
     const int nch = first < c_end ? (c_end - first + kKWaves - 1) / kKWaves : 0;
+    const int lastc = nch > 0 ? first + (nch - 1) * kKWaves : 0;  // chunk 0 always exists
+    const int TK = a.T * a.k;
 
-    // ring of D chunks in flight per wave
-    constexpr int D = 1;
-    u32x2 pg[D][Q];
+    uint32_t* slice = lds + kLutBytes / 4 + wave * kSliceWords;
+    u32x4* slice4 = (u32x4*)slice;
     const uint32_t lane_off = (uint32_t)(32 * grp + rho) * 4u;
     const char* lutb = (const char*)lds;
     const RepMasks masks = make_masks();
-    const int TK = a.T * a.k;
 
-    for (int t0 = 0; t0 < ntok; t0 += kTokTile) {
-        // the pass's first chunks are in flight while its LUT is staged
-        if (nch > 0) {
-#pragma unroll
-            for (int d = 0; d < D; ++d)
-                load_pair_words<Q>(pg[d], bd, first + min(d, nch - 1) * kKWaves, R, lrow, kh);
-        }
-        const int nt = min(kTokTile, ntok - t0);
-        load_lut<Q>(lds, lds + kLutBytes / 4, bd->lut, srow, svalid, lane, wave, kWaves);
-        __syncthreads();
-        // B rows: token lanes past the pass read token 0's row (their output
-        // columns are never stored)
-        const int n = rho < nt ? rho : 0;
-        const uint16_t* src_hi;
-        const uint16_t* src_lo = a.x;
+    // cooperative activation loads: lane = (token xt, 16-byte unit xg)
+    const int xt = lane >> 4, xg = lane & 15;
+
+    u32x2 pg[D][Q];
+    u32x4 xv[NPART];
+    const uint16_t* xsrc[NPART];
+    int nt = 0;
+
+    // Activation rows of the pass starting at t0 (token xt; tokens past the
+    // pass repeat its first token, whose slots are never read).
+    auto set_sources = [&](int t0) {
+        nt = min(kTokPass, ntok - t0);
+        const int te = min(xt, nt - 1);
         if (MODE == 0) {
-            const int tok = shared ? t0 + n : a.sorted[p0 + t0 + n] / a.k;
-            src_hi = a.x + (size_t)tok * a.H;
+            int tok;
+            if (shared) {
+                tok = t0 + te;
+            } else {
+                // the pass's assignment ids through scalar loads (lgkmcnt)
+                const ci32p srt = (ci32p)(uintptr_t)a.sorted;
+                const int base = p0 + t0;
+                const int s0 = srt[base], s1 = srt[base + min(1, nt - 1)];
+                const int s2 = srt[base + min(2, nt - 1)], s3 = srt[base + min(3, nt - 1)];
+                const int sa = te == 0 ? s0 : te == 1 ? s1 : te == 2 ? s2 : s3;
+                tok = sa / a.k;
+            }
+            xsrc[0] = a.x + (size_t)tok * a.H;
         } else {
-            const int hrow = shared ? TK + t0 + n : p0 + t0 + n;
-            src_hi = a.h_hi + (size_t)hrow * a.hstride;
-            src_lo = a.h_lo + (size_t)hrow * a.hstride;
+            const int hrow = shared ? TK + t0 + te : p0 + t0 + te;
+            xsrc[0] = a.h_hi + (size_t)hrow * a.hstride;
+            xsrc[NPART - 1] = a.h_lo + (size_t)hrow * a.hstride;
         }
+    };
+    // activation unit of chunk c (column clamped into the row; the store zeroes it)
+    auto issue_x = [&](int c) {
+        const int col = min(c * kChunkCols + 8 * xg, K - 8);
+#pragma unroll
+        for (int pp = 0; pp < NPART; ++pp) xv[pp] = *(gcu32x4p)(uintptr_t)(xsrc[pp] + col);
+    };
+    auto issue_ring = [&]() {
+        issue_x(first);
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_pair_words<Q>(pg[d], bd, min(first + d * kKWaves, lastc), R, lrow, kh);
+    };
+
+    // pass 0: LUT loads first, then the ring's first loads, then LUT -> LDS
+    {
+        LutPieces<Q, kWaves> lp;
+        lp.issue(bd->lut, srow, svalid, wave);
+        set_sources(0);
+        if (ntok > 0) issue_ring();
+        lp.commit(lds, lds + kLutBytes / 4, lane, wave);
+        __syncthreads();
+    }
+
+    for (int t0 = 0; t0 < ntok; t0 += kTokPass) {
+        if (t0 > 0) {
+            set_sources(t0);
+            issue_ring();
+        }
+        const int te = rho < nt ? rho : 0;  // B lanes past the pass read token 0
         const bool nvalid = rho < nt;
         f32x16 C = {};
 
-        // The ring is unrolled by D: buffer d always holds chunk ci0 + d, so no
-        // in-flight register is ever moved.  Every load is unconditional (the
-        // refill past the wave's range re-reads its last chunk, an L2 hit) and
-        // every B fragment read is unconditional (lanes and padding chunks that
-        // need zeros read the zero slot), so the body is straight-line code
-        // and the wait counts follow the ring exactly.
-        const int lastc = first + (nch - 1) * kKWaves;
         for (int ci0 = 0; ci0 < nch; ci0 += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                // keep the scheduler from hoisting the next slot's decode (which
+                // keep the scheduler from hoisting the next slot's work (which
                 // would wait on that slot's loads too)
                 __builtin_amdgcn_sched_barrier(0);
                 const int ci = ci0 + d;
-                const bool live = ci < nch;  // padding chunk: B = 0
+                const bool live = ci < nch;  // padding chunk of the ring: B = 0
                 const int c = min(first + ci * kKWaves, lastc);
-                const int nw = min(4, kwords - 4 * c);
+                // this chunk's activations -> the wave's slice (zero past K and
+                // in padding chunks)
+                const bool ok = live && c * kChunkCols + 8 * xg < K;
+#pragma unroll
+                for (int pp = 0; pp < NPART; ++pp)
+                    slice4[slice_unit(pp, xt, xg)] = ok ? xv[pp] : u32x4{0, 0, 0, 0};
+                // prefetch: next chunk's activations, then the planes D chunks on
                 u32x2 cur[Q];
 #pragma unroll
                 for (int p = 0; p < Q; ++p) cur[p] = pg[d][p];
+                issue_x(min(c + kKWaves, lastc));
                 load_pair_words<Q>(pg[d], bd, min(c + D * kKWaves, lastc), R, lrow, kh);
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int wd = 2 * kh + u;
-                    const bool bv = live && wd < nw;  // zero B beyond K and in padding chunks
-                    const int col = min(c * kChunkCols + 32 * wd, kwords * 32 - 32);
-                    half8 Bh[4], Bl[4];
-#pragma unroll
-                    for (int P = 0; P < 4; ++P) {
-                        Bh[P] = load_frag(src_hi + col + 8 * P);
-                        if (MODE == 1) Bl[P] = load_frag(src_lo + col + 8 * P);
-                    }
-                    if (!(live && nw == 4)) {  // rare: partial last chunk or padding chunk
-#pragma unroll
-                        for (int P = 0; P < 4; ++P) {
-                            if (!bv) Bh[P] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-                            if (MODE == 1 && !bv) Bl[P] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-                        }
-                    }
                     uint32_t W[Q];
 #pragma unroll
                     for (int p = 0; p < Q; ++p) W[p] = cur[p][u];
@@ -581,21 +646,26 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
 #pragma unroll
                     for (int P = 0; P < 4; ++P) {
                         const half8 A = step_weights<Q>(rt, P, masks, lane_off, lutb);
-                        C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh[P], C, 0, 0, 0);
-                        if (MODE == 1) C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl[P], C, 0, 0, 0);
+                        const int g = 4 * (2 * kh + u) + P;
+                        const half8 Bh = __builtin_bit_cast(half8, slice4[slice_unit(0, te, g)]);
+                        C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh, C, 0, 0, 0);
+                        if (MODE == 1) {
+                            const half8 Bl = __builtin_bit_cast(half8, slice4[slice_unit(1, te, g)]);
+                            C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl, C, 0, 0, 0);
+                        }
                     }
                 }
             }
         }
 
-        // cross-wave reduction through the (no longer needed) LUT region
+        // cross-wave reduction through the slice region
         __syncthreads();
-        float* red = (float*)lds;  // [wave][row 32][token 32]
+        float* red = (float*)(lds + kLutBytes / 4);  // [wave][row 32][token kTokPass]
         if (nvalid) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = 8 * (i >> 2) + 4 * kh + (i & 3);
-                red[(wave * 32 + r) * 32 + rho] = C[i];
+                red[(wave * 32 + r) * kTokPass + rho] = C[i];
             }
         }
         __syncthreads();
@@ -606,8 +676,8 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
                 float g = 0.0f, u = 0.0f;
 #pragma unroll
                 for (int w = 0; w < kKWaves; ++w) {
-                    g += red[(w * 32 + r) * 32 + n];
-                    u += red[((kKWaves + w) * 32 + r) * 32 + n];
+                    g += red[(w * 32 + r) * kTokPass + n];
+                    u += red[((kKWaves + w) * 32 + r) * kTokPass + n];
                 }
                 const int i = tile * 32 + r;
                 if (i < Iblk) {
@@ -626,7 +696,7 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
                 const int g = r64 >> 5, r = r64 & 31;
                 float d = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kKWaves; ++w) d += red[((g * kKWaves + w) * 32 + r) * 32 + n];
+                for (int w = 0; w < kKWaves; ++w) d += red[((g * kKWaves + w) * 32 + r) * kTokPass + n];
                 const int orow_r = tile * 64 + r64;
                 if (orow_r < R) {
                     const int orow = shared ? TK + t0 + n : a.sorted[p0 + t0 + n];
@@ -638,48 +708,91 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
     }
 }
 
+// The expert of routed slot `slot`: the active experts (at least one routed
+// assignment) ordered by committed width, widest first, then by index, so the
+// largest blocks are dispatched first and the last workgroups of a launch are
+// the cheapest.  Every lane tests up to four experts (offsets and widths are
+// loaded together: one memory round trip), ballots give the bitmap of active
+// experts of each width, and the lane holding the wanted expert is found by its
+// rank; its offsets are read from that lane.  Wave-uniform result, e = -1 if
+// the slot has no expert.
+struct SlotExpert {
+    int e, p0, ntok;
+};
+
+__device__ __forceinline__ SlotExpert slot_expert(const int32_t* __restrict__ offsets,
+                                                  const BlockDesc* __restrict__ table, int module, int E, int slot)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int lo[4], hi[4], q[4];
+    bool act[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int e = 64 * g + lane;
+        const int ec = e < E ? e : 0;  // in-range address for every lane
+        lo[g] = offsets[ec];
+        hi[g] = offsets[ec + 1];
+        q[g] = table[ec * 2 + module].q;
+        act[g] = e < E && hi[g] > lo[g];
+    }
+    int base = 0;
+#pragma unroll
+    for (int qq = kQMax; qq >= kQMin; --qq) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const bool mine = act[g] && q[g] == qq;
+            const uint64_t m = __ballot(mine);
+            const uint64_t hit = __ballot(mine && base + __popcll(m & below) == slot);
+            if (hit) {
+                const int h = __ffsll((long long)hit) - 1;
+                const int p0 = __builtin_amdgcn_readlane(lo[g], h);
+                return SlotExpert{64 * g + h, p0, __builtin_amdgcn_readlane(hi[g], h) - p0};
+            }
+            base += __popcll(m);
+        }
+    }
+    return SlotExpert{-1, 0, 0};
+}
+
+// Workgroup order: the shared expert's tiles first (its work is known to
+// exist and is at the widest width), then the routed tiles slot by slot (slots
+// in decreasing width).  The dispatcher deals consecutive workgroups
+// round-robin to the XCDs, so the workgroups that find work (slots below the
+// active-expert count) form one contiguous run and every XCD gets an equal
+// share of them.
 template <int MODE>
 __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 {
     __shared__ uint32_t lds[kGemvLdsWords];
     const int wg = blockIdx.x;
-    const int per_slot = a.tiles_routed * a.splits_routed;
-    const int routed_wgs = a.n_slots * per_slot;
+    const int shared_wgs = a.tiles_shared * a.splits_shared;
     bool shared;
-    int tile, split, nsplit, p0, ntok, slot_expert;
-    if (wg < routed_wgs) {
+    int tile, split, nsplit, p0, ntok, slot_e;
+    if (wg >= shared_wgs) {
         shared = false;
-        const int slot = wg / per_slot;
-        const int rem = wg - slot * per_slot;
-        tile = rem / a.splits_routed;
-        split = rem - tile * a.splits_routed;
+        const int rem = wg - shared_wgs;
+        const int per_slot = a.tiles_routed * a.splits_routed;
+        const int slot = rem / per_slot;
+        const int ts = rem - slot * per_slot;
+        tile = ts / a.splits_routed;
+        split = ts - tile * a.splits_routed;
         nsplit = a.splits_routed;
-        // the slot-th expert with at least one routed assignment
-        int e = -1, cnt = 0;
-        for (int ee = 0; ee < a.E; ++ee) {
-            if (a.offsets[ee + 1] > a.offsets[ee]) {
-                if (cnt == slot) {
-                    e = ee;
-                    break;
-                }
-                ++cnt;
-            }
-        }
-        if (e < 0) return;
-        p0 = a.offsets[e];
-        ntok = a.offsets[e + 1] - p0;
-        slot_expert = e;
+        const SlotExpert se = slot_expert(a.offsets, a.table, MODE, a.E, slot);
+        if (se.e < 0) return;
+        p0 = se.p0;
+        ntok = se.ntok;
+        slot_e = se.e;
     } else {
         shared = true;
-        const int rem = wg - routed_wgs;
-        tile = rem / a.splits_shared;
-        split = rem - tile * a.splits_shared;
+        tile = wg / a.splits_shared;
+        split = wg - tile * a.splits_shared;
         nsplit = a.splits_shared;
         p0 = 0;
         ntok = a.T;
-        slot_expert = a.E;
+        slot_e = a.E;
     }
-    const BlockDesc* bd = a.table + (slot_expert * 2 + MODE);
+    const BlockDesc* bd = a.table + (slot_e * 2 + MODE);
     KArgs& ka = kernel_args();
     switch (bd->q) {
         case 3: mfma_block<MODE, 3>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
@@ -726,7 +839,7 @@ __device__ void debug_block(const BlockDesc* __restrict__ bd, int R, int K, uint
     const int lane = threadIdx.x;
     const int row = blockIdx.x * 64 + lane;
     const bool valid = row < R;
-    load_lut<Q>(lds, lds + kLutBytes / 4, bd->lut, row, valid, lane, 0, 1);
+    load_lut<Q, 1>(lds, lds + kLutBytes / 4, bd->lut, row, valid, lane, 0);
     __syncthreads();
     const char* lutb = (const char*)lds;
     const uint32_t lane_off = (uint32_t)lane * 4u;
