@@ -524,16 +524,18 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
     hipStream_t s = (hipStream_t)stream;
     {
         ProfScope ps(c, "gate_up", s);
-        a.tiles_routed = d.inter / 32;
-        a.tiles_shared = d.inter_shared / 32;
+        a.rg = kGateUpRowGroups;
+        a.tiles_routed = (d.inter + 16 * a.rg - 1) / (16 * a.rg);
+        a.tiles_shared = (d.inter_shared + 16 * a.rg - 1) / (16 * a.rg);
         a.splits_routed = 1;
         a.splits_shared = 1;
         if ((e = launch_gate_up(a, s)) != hipSuccess) return hip_fail(e, "gate_up launch");
     }
     {
         ProfScope ps(c, "down", s);
-        a.tiles_routed = (d.hidden + 63) / 64;
-        a.tiles_shared = d.inter_shared ? (d.hidden + 63) / 64 : 0;
+        a.rg = kDownRowGroups;
+        a.tiles_routed = (d.hidden + 32 * a.rg - 1) / (32 * a.rg);
+        a.tiles_shared = d.inter_shared ? (d.hidden + 32 * a.rg - 1) / (32 * a.rg) : 0;
         a.splits_routed = down_splits(d.inter);
         a.splits_shared = d.inter_shared ? down_splits(d.inter_shared) : 1;
         if ((e = launch_down(a, s)) != hipSuccess) return hip_fail(e, "down launch");

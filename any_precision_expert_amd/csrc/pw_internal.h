@@ -45,7 +45,14 @@ struct FfnArgs {
     int32_t splits_shared;    // K splits per shared row tile
     int32_t hstride;          // max(I, Is)
     int32_t drows;            // rows of one dout split plane: T * k (+ T with a shared expert)
+    int32_t rg;               // 32-row groups per workgroup tile: 2 or 4
 };
+
+// 32-row groups per workgroup tile (two share one LUT set; four use both
+// halves of the LUT slots): gate_up tiles hold 16 * rg gate rows and their up
+// rows, down tiles 32 * rg output rows.
+constexpr int kGateUpRowGroups = 4;
+constexpr int kDownRowGroups = 2;
 
 // K splits of a down-projection row tile: about kChunksPerSplit 128-column
 // chunks per workgroup (two per wave), so long K ranges spread over the chip.

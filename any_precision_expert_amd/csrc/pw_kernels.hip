@@ -160,31 +160,33 @@ __device__ __forceinline__ void lookup(const Gathered<Q>& g, uint32_t lane_off, 
 // Step-wise form of gather + lookup used by the contraction: the planes are
 // rotated once (Rot), then each MFMA step P assembles only its own code
 // register(s) and looks up its 8 weights, which keeps few registers live.
-template <int Q>
+template <int Q, bool PAIR>
 struct Rot {
     uint32_t A[Q];
-    uint32_t B[Q <= 4 ? Q : 1];
+    uint32_t B[PAIR ? Q : 1];
 };
 
-template <int Q>
-__device__ __forceinline__ void rotate_planes(const uint32_t (&W)[Q], Rot<Q>& r)
+template <int Q, bool PAIR>
+__device__ __forceinline__ void rotate_planes(const uint32_t (&W)[Q], Rot<Q, PAIR>& r)
 {
 #pragma unroll
     for (int p = 0; p < Q; ++p) r.A[p] = rotl(W[p], Q - 1 - p);
-    if constexpr (Q <= 4) {
+    if constexpr (PAIR) {
 #pragma unroll
         for (int p = 0; p < Q; ++p) r.B[p] = rotl(W[p], 2 * Q - 5 - p);
     }
 }
 
 // Weights of columns 8P..8P+7 of the word as an MFMA A fragment (8 x fp16).
-template <int Q>
-__device__ __forceinline__ half8_t step_weights(const Rot<Q>& r, int P, const RepMasks& M, uint32_t lane_off,
-                                               const char* lutb)
+// Pair tables: acc0 seeds the code bytes (the LUT set bit of a two-set pair
+// table, pre-rotated so the final rotate puts it above the pair code).
+template <int Q, bool PAIR>
+__device__ __forceinline__ half8_t step_weights(const Rot<Q, PAIR>& r, int P, const RepMasks& M, uint32_t lane_off,
+                                               const char* lutb, uint32_t acc0)
 {
     half8_t f;
-    if constexpr (Q <= 4) {
-        uint32_t acc = 0;
+    if constexpr (PAIR) {
+        uint32_t acc = acc0;
 #pragma unroll
         for (int p = 0; p < Q; ++p) {
             acc = and_or(r.A[p], M.m[rep_index(P + Q - 1 - p)], acc);
@@ -256,6 +258,65 @@ struct LutPieces {
             for (int e = wave; e < NC * NC; e += NW) {
                 const int ea = e & (NC - 1), eb = e >> Q;
                 lds[(e << 6) | lane] = single[(ea << 6) | lane] | (single[(eb << 6) | lane] << 16);
+            }
+        }
+    }
+};
+
+// LUT staging of the contraction for a workgroup of RG row groups (32 rows
+// each).  Slot s (0..63) of set t holds the LUT of row group 2t + s / 32, row
+// s % 32.  Single tables: [code][64 slots] 32-bit slots, set t in half t (two
+// sets share every slot, so a 128-row workgroup needs no more LDS than a
+// 64-row one); a lookup adds 2t to the slot's byte offset.  Pair tables (the
+// 32-bit slot is full): [set][a | b << q][64 slots]; the set index sits above
+// the pair code in the look-up byte.  Pair tables are used for q <= 4 with one
+// set and for q = 3 with two (a two-set q = 4 pair table would not fit).
+template <int Q, int RG>
+struct LutStage {
+    static constexpr int NS = RG / 2;
+    static constexpr bool PAIR = RG == 2 ? Q <= 4 : Q <= 3;
+    static constexpr int NC = 1 << Q;
+    static constexpr int NP = NC / 8;                           // 16-byte pieces per row
+    static constexpr int PER = (NS * NP + kWaves - 1) / kWaves;  // pieces per lane
+    u32x4 u[PER];
+
+    __device__ __forceinline__ void issue(const uint16_t* lut, const int (&row)[NS], int wave)
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int jg = wave + j * kWaves;  // wave-uniform
+            if (jg < NS * NP) {
+                const int t = jg / NP, c8 = jg - t * NP;
+                u[j] = ((gu32x4p)(uintptr_t)(lut + (size_t)row[t] * NC))[c8];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void commit(uint32_t* lds, uint32_t* stage, int lane, int wave)
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int jg = wave + j * kWaves;
+            if (jg < NS * NP) {
+                const int t = jg / NP, c8 = jg - t * NP;
+                const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t v = (w4[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                    const int e = 8 * c8 + i;
+                    if constexpr (PAIR)
+                        stage[((t * NC + e) << 6) | lane] = v;
+                    else
+                        ((uint16_t*)lds)[(((e << 6) | lane) << 1) + t] = (uint16_t)v;
+                }
+            }
+        }
+        if constexpr (PAIR) {
+            __syncthreads();
+            for (int e = wave; e < NS * NC * NC; e += kWaves) {
+                const int t = e / (NC * NC), pe = e - t * NC * NC;
+                const int ea = pe & (NC - 1), eb = pe >> Q;
+                lds[(e << 6) | lane] = stage[((t * NC + ea) << 6) | lane] | (stage[((t * NC + eb) << 6) | lane] << 16);
             }
         }
     }
@@ -454,7 +515,7 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
 // Word pair u pairs word u (kh = 0) with word 2 + u (kh = 1) in one 16-deep
 // MFMA step set: step P takes columns 8P..8P+7 of each word, which is exactly
 // what the gather produces for register P.  The tokens of a pass (up to
-// kTokPass) are the MFMA's N columns; a weight is decoded once per pass.
+// 8 for gate_up, 4 for down) are the MFMA's N columns; a weight is decoded once per pass.
 //
 // Memory pipeline.  Each wave keeps D chunks of plane loads in flight (a
 // static ring, so no in-flight register is ever moved) and loads the next
@@ -472,9 +533,9 @@ typedef __attribute__((address_space(1))) const u32x2* gu32x2p;
 typedef __attribute__((address_space(1))) const u32x4* gcu32x4p;
 typedef __attribute__((address_space(4))) const int32_t* ci32p;
 
-constexpr int kTokPass = 4;               // tokens per pass
+constexpr int kTokPass = 8;               // most tokens per pass (gate_up; down: 4)
 constexpr int kKWaves = kWaves / 2;       // waves per row group (K split)
-constexpr int kSliceWords = 512;          // per-wave slice: [part 2][token 4][16 units of 16 B]
+constexpr int kSliceWords = 512;          // per-wave slice: 8 rows x 16 units of 16 B
 static_assert(kWaves * kSliceWords >= kStageWords, "pair staging lives in the slice region");
 static_assert(kWaves * 32 * kTokPass <= kWaves * kSliceWords, "reduction lives in the slice region");
 
@@ -502,52 +563,70 @@ __device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const BlockDesc*
     for (int p = 0; p < Q; ++p) pg[p] = __builtin_nontemporal_load((gu32x2p)(uintptr_t)cbd->planes[p] + at);
 }
 
-// 16-byte unit g (8 fp16 columns) of token t, part 0 (x or h hi) or 1 (h lo),
-// in a wave's slice.  The unit index is XOR-swizzled with the token so the B
-// reads of different tokens in one instruction fall in different banks.
-__device__ __forceinline__ int slice_unit(int part, int t, int g)
+// 16-byte unit g (8 fp16 columns) of row j of a wave's slice: gate_up rows
+// are the pass's tokens (up to 8), down rows are the tokens' h hi (0-3) and h
+// lo (4-7).  The unit index is XOR-swizzled with the token so the B reads of
+// different tokens in one instruction fall in different banks.
+__device__ __forceinline__ int slice_unit(int j, int t, int g)
 {
-    return (part * kTokPass + t) * 16 + (g ^ t);
+    return j * 16 + (g ^ t);
 }
 
-template <int MODE, int Q>
-__device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0, int ntok,
-                           int tile, int split, int nsplit, uint32_t* lds)
+template <int MODE, int Q, int RG>
+__device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
+                                           int ntok, int tile, int split, int nsplit, uint32_t* lds)
 {
     constexpr int D = Q <= 4 ? 2 : 1;      // chunks of plane loads in flight
-    constexpr int NPART = MODE == 0 ? 1 : 2;
+    constexpr int NPART = 2;               // activation loads per lane and chunk
+    constexpr int TP = MODE == 0 ? 8 : 4;  // tokens per pass
+    constexpr int KW = kWaves / RG;        // waves per row group (K split)
+    constexpr int NS = RG / 2;             // LUT sets
+    constexpr bool PAIR = LutStage<Q, RG>::PAIR;
+    constexpr int HR = 16 * RG;            // gate_up: h rows per tile (gate and up rows each)
+    constexpr int TR = 32 * RG;            // down: output rows per tile
     const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave / kKWaves, kw = wave % kKWaves;
+    const int grp = wave / KW, kw = wave % KW;
     const int R = bd->R;
     const int nchunks = bd->nchunks, kwords = bd->kwords;
     const int K = kwords * 32;
-    int row, srow;
-    bool rvalid, svalid;
-    if (MODE == 0) {
-        const int Iblk = R >> 1;
-        const int i = tile * 32 + rho;
-        rvalid = svalid = i < Iblk;
-        row = grp ? Iblk + i : i;
-        srow = kh ? Iblk + i : i;  // LDS slot `lane` holds the LUT of this row
-    } else {
-        row = tile * 64 + 32 * grp + rho;
-        rvalid = row < R;
-        srow = tile * 64 + lane;
-        svalid = srow < R;
-    }
+    const int Iblk = R >> 1;
+    // row of row group g, lane row r; gate_up: groups [0, RG/2) gate rows,
+    // [RG/2, RG) the matching up rows
+    auto group_row = [&](int g, int r, bool& valid) {
+        if (MODE == 0) {
+            const int sub = g % (RG / 2), up = g / (RG / 2);
+            const int i = tile * HR + 32 * sub + r;
+            valid = i < Iblk;
+            return up ? Iblk + i : i;
+        } else {
+            const int row = tile * TR + 32 * g + r;
+            valid = row < R;
+            return row;
+        }
+    };
+    bool rvalid;
+    const int row = group_row(grp, rho, rvalid);
     const int lrow = rvalid ? row : 0;  // in-range load row
+    int lut_rows[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+        bool v;
+        const int r = group_row(2 * t + (lane >> 5), lane & 31, v);
+        lut_rows[t] = v ? r : 0;  // rows past the block stage row 0 (never used)
+    }
     const int cps = (nchunks + nsplit - 1) / nsplit;
     const int c_begin = split * cps;
     const int c_end = min(nchunks, c_begin + cps);
     const int first = c_begin + kw;
-    const int nch = first < c_end ? (c_end - first + kKWaves - 1) / kKWaves : 0;
-    const int lastc = nch > 0 ? first + (nch - 1) * kKWaves : 0;  // chunk 0 always exists
+    const int nch = first < c_end ? (c_end - first + KW - 1) / KW : 0;
+    const int lastc = nch > 0 ? first + (nch - 1) * KW : 0;  // chunk 0 always exists
     const int TK = a.T * a.k;
 
     uint32_t* slice = lds + kLutBytes / 4 + wave * kSliceWords;
     u32x4* slice4 = (u32x4*)slice;
-    const uint32_t lane_off = (uint32_t)(32 * grp + rho) * 4u;
+    const int set = grp / 2;
+    const uint32_t lane_off = (uint32_t)(32 * (grp % 2) + rho) * 4u + (PAIR ? 0u : 2u * (uint32_t)set);
     const char* lutb = (const char*)lds;
     const RepMasks masks = make_masks();
 
@@ -559,29 +638,39 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
     const uint16_t* xsrc[NPART];
     int nt = 0;
 
-    // Activation rows of the pass starting at t0 (token xt; tokens past the
-    // pass repeat its first token, whose slots are never read).
+    // Activation rows of the pass starting at t0: gate_up tokens xt and
+    // xt + 4, down token xt's h hi and lo (tokens past the pass repeat its
+    // last token, whose slots are never read).
     auto set_sources = [&](int t0) {
-        nt = min(kTokPass, ntok - t0);
-        const int te = min(xt, nt - 1);
+        nt = min(TP, ntok - t0);
         if (MODE == 0) {
-            int tok;
+            int tok[2];
             if (shared) {
-                tok = t0 + te;
+                tok[0] = t0 + min(xt, nt - 1);
+                tok[1] = t0 + min(xt + 4, nt - 1);
             } else {
                 // the pass's assignment ids through scalar loads (lgkmcnt)
                 const ci32p srt = (ci32p)(uintptr_t)a.sorted;
                 const int base = p0 + t0;
-                const int s0 = srt[base], s1 = srt[base + min(1, nt - 1)];
-                const int s2 = srt[base + min(2, nt - 1)], s3 = srt[base + min(3, nt - 1)];
-                const int sa = te == 0 ? s0 : te == 1 ? s1 : te == 2 ? s2 : s3;
-                tok = sa / a.k;
+                int sa[TP];
+#pragma unroll
+                for (int j = 0; j < TP; ++j) sa[j] = srt[base + min(j, nt - 1)];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int te = xt + 4 * h;
+                    int v = sa[0];
+#pragma unroll
+                    for (int j = 1; j < TP; ++j) v = te == j ? sa[j] : v;
+                    tok[h] = v / a.k;
+                }
             }
-            xsrc[0] = a.x + (size_t)tok * a.H;
+            xsrc[0] = a.x + (size_t)tok[0] * a.H;
+            xsrc[1] = a.x + (size_t)tok[1] * a.H;
         } else {
+            const int te = min(xt, nt - 1);
             const int hrow = shared ? TK + t0 + te : p0 + t0 + te;
             xsrc[0] = a.h_hi + (size_t)hrow * a.hstride;
-            xsrc[NPART - 1] = a.h_lo + (size_t)hrow * a.hstride;
+            xsrc[1] = a.h_lo + (size_t)hrow * a.hstride;
         }
     };
     // activation unit of chunk c (column clamped into the row; the store zeroes it)
@@ -593,20 +682,20 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
     auto issue_ring = [&]() {
         issue_x(first);
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_pair_words<Q>(pg[d], bd, min(first + d * kKWaves, lastc), R, lrow, kh);
+        for (int d = 0; d < D; ++d) load_pair_words<Q>(pg[d], bd, min(first + d * KW, lastc), R, lrow, kh);
     };
 
     // pass 0: LUT loads first, then the ring's first loads, then LUT -> LDS
     {
-        LutPieces<Q, kWaves> lp;
-        lp.issue(bd->lut, srow, svalid, wave);
+        LutStage<Q, RG> ls;
+        ls.issue(bd->lut, lut_rows, wave);
         set_sources(0);
         if (ntok > 0) issue_ring();
-        lp.commit(lds, lds + kLutBytes / 4, lane, wave);
+        ls.commit(lds, lds + kLutBytes / 4, lane, wave);
         __syncthreads();
     }
 
-    for (int t0 = 0; t0 < ntok; t0 += kTokPass) {
+    for (int t0 = 0; t0 < ntok; t0 += TP) {
         if (t0 > 0) {
             set_sources(t0);
             issue_ring();
@@ -623,34 +712,36 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
                 __builtin_amdgcn_sched_barrier(0);
                 const int ci = ci0 + d;
                 const bool live = ci < nch;  // padding chunk of the ring: B = 0
-                const int c = min(first + ci * kKWaves, lastc);
+                const int c = min(first + ci * KW, lastc);
                 // this chunk's activations -> the wave's slice (zero past K and
                 // in padding chunks)
                 const bool ok = live && c * kChunkCols + 8 * xg < K;
 #pragma unroll
                 for (int pp = 0; pp < NPART; ++pp)
-                    slice4[slice_unit(pp, xt, xg)] = ok ? xv[pp] : u32x4{0, 0, 0, 0};
+                    slice4[slice_unit(4 * pp + xt, MODE == 0 ? 4 * pp + xt : xt, xg)] = ok ? xv[pp] : u32x4{0, 0, 0, 0};
                 // prefetch: next chunk's activations, then the planes D chunks on
                 u32x2 cur[Q];
 #pragma unroll
                 for (int p = 0; p < Q; ++p) cur[p] = pg[d][p];
-                issue_x(min(c + kKWaves, lastc));
-                load_pair_words<Q>(pg[d], bd, min(c + D * kKWaves, lastc), R, lrow, kh);
+                issue_x(min(c + KW, lastc));
+                load_pair_words<Q>(pg[d], bd, min(c + D * KW, lastc), R, lrow, kh);
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     uint32_t W[Q];
 #pragma unroll
                     for (int p = 0; p < Q; ++p) W[p] = cur[p][u];
-                    Rot<Q> rt;
-                    rotate_planes<Q>(W, rt);
+                    Rot<Q, PAIR> rt;
+                    rotate_planes<Q, PAIR>(W, rt);
 #pragma unroll
                     for (int P = 0; P < 4; ++P) {
-                        const half8 A = step_weights<Q>(rt, P, masks, lane_off, lutb);
+                        // two-set pair tables: set bit above the 2q-bit pair code
+                        const uint32_t acc0 = PAIR && NS == 2 && set ? rotl(0x01010101u << (2 * Q), P) : 0u;
+                        const half8 A = step_weights<Q, PAIR>(rt, P, masks, lane_off, lutb, acc0);
                         const int g = 4 * (2 * kh + u) + P;
-                        const half8 Bh = __builtin_bit_cast(half8, slice4[slice_unit(0, te, g)]);
+                        const half8 Bh = __builtin_bit_cast(half8, slice4[slice_unit(te, te, g)]);
                         C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh, C, 0, 0, 0);
                         if (MODE == 1) {
-                            const half8 Bl = __builtin_bit_cast(half8, slice4[slice_unit(1, te, g)]);
+                            const half8 Bl = __builtin_bit_cast(half8, slice4[slice_unit(4 + te, te, g)]);
                             C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl, C, 0, 0, 0);
                         }
                     }
@@ -660,26 +751,26 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
 
         // cross-wave reduction through the slice region
         __syncthreads();
-        float* red = (float*)(lds + kLutBytes / 4);  // [wave][row 32][token kTokPass]
+        float* red = (float*)(lds + kLutBytes / 4);  // [wave][row 32][token TP]
         if (nvalid) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = 8 * (i >> 2) + 4 * kh + (i & 3);
-                red[(wave * 32 + r) * kTokPass + rho] = C[i];
+                red[(wave * 32 + r) * TP + rho] = C[i];
             }
         }
         __syncthreads();
         if (MODE == 0) {
-            const int Iblk = R >> 1;
-            for (int idx = tid; idx < 32 * nt; idx += kThreads) {
-                const int r = idx / nt, n = idx - r * nt;
+            for (int idx = tid; idx < HR * nt; idx += kThreads) {
+                const int hr = idx / nt, n = idx - hr * nt;
+                const int sub = hr >> 5, r = hr & 31;
                 float g = 0.0f, u = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kKWaves; ++w) {
-                    g += red[(w * 32 + r) * kTokPass + n];
-                    u += red[((kKWaves + w) * 32 + r) * kTokPass + n];
+                for (int w = 0; w < KW; ++w) {
+                    g += red[((sub * KW + w) * 32 + r) * TP + n];
+                    u += red[(((RG / 2 + sub) * KW + w) * 32 + r) * TP + n];
                 }
-                const int i = tile * 32 + r;
+                const int i = tile * HR + hr;
                 if (i < Iblk) {
                     const float h = g / (1.0f + __expf(-g)) * u;
                     const _Float16 hi = (_Float16)h;
@@ -691,13 +782,13 @@ __device__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, boo
                 }
             }
         } else {
-            for (int idx = tid; idx < 64 * nt; idx += kThreads) {
-                const int r64 = idx / nt, n = idx - r64 * nt;
-                const int g = r64 >> 5, r = r64 & 31;
+            for (int idx = tid; idx < TR * nt; idx += kThreads) {
+                const int rt = idx / nt, n = idx - rt * nt;
+                const int g = rt >> 5, r = rt & 31;
                 float d = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kKWaves; ++w) d += red[((g * kKWaves + w) * 32 + r) * kTokPass + n];
-                const int orow_r = tile * 64 + r64;
+                for (int w = 0; w < KW; ++w) d += red[((g * KW + w) * 32 + r) * TP + n];
+                const int orow_r = tile * TR + rt;
                 if (orow_r < R) {
                     const int orow = shared ? TK + t0 + n : a.sorted[p0 + t0 + n];
                     a.dout[((size_t)split * a.drows + orow) * a.H + orow_r] = d;
@@ -761,7 +852,7 @@ __device__ __forceinline__ SlotExpert slot_expert(const int32_t* __restrict__ of
 // round-robin to the XCDs, so the workgroups that find work (slots below the
 // active-expert count) form one contiguous run and every XCD gets an equal
 // share of them.
-template <int MODE>
+template <int MODE, int RG>
 __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 {
     __shared__ uint32_t lds[kGemvLdsWords];
@@ -795,12 +886,12 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
     const BlockDesc* bd = a.table + (slot_e * 2 + MODE);
     KArgs& ka = kernel_args();
     switch (bd->q) {
-        case 3: mfma_block<MODE, 3>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 4: mfma_block<MODE, 4>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 5: mfma_block<MODE, 5>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 6: mfma_block<MODE, 6>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 7: mfma_block<MODE, 7>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 8: mfma_block<MODE, 8>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 3: mfma_block<MODE, 3, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 4: mfma_block<MODE, 4, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 5: mfma_block<MODE, 5, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 6: mfma_block<MODE, 6, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 7: mfma_block<MODE, 7, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
+        case 8: mfma_block<MODE, 8, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
         default: break;
     }
 }
@@ -922,7 +1013,10 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
 {
     const int grid = a.n_slots * a.tiles_routed * a.splits_routed + a.tiles_shared * a.splits_shared;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(ffn_gemv_kernel<0>, dim3(grid), dim3(kThreads), 0, s, a);
+    if (a.rg == 4)
+        hipLaunchKernelGGL((ffn_gemv_kernel<0, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((ffn_gemv_kernel<0, 2>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -930,7 +1024,10 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s)
 {
     const int grid = a.n_slots * a.tiles_routed * a.splits_routed + a.tiles_shared * a.splits_shared;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(ffn_gemv_kernel<1>, dim3(grid), dim3(kThreads), 0, s, a);
+    if (a.rg == 4)
+        hipLaunchKernelGGL((ffn_gemv_kernel<1, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((ffn_gemv_kernel<1, 2>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
