@@ -522,6 +522,32 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
     a.hstride = std::max(d.inter, d.inter_shared);
     a.drows = T * d.top_k + (d.inter_shared ? T : 0);
     hipStream_t s = (hipStream_t)stream;
+    if (T >= kPrefillMinT) {
+        // prefill: GEMM tiles of 128 weight rows x 512 tokens, full K, one
+        // dout plane
+        const int tt = (T + 511) / 512;
+        a.tok_tiles_shared = d.inter_shared ? tt : 0;
+        a.tok_tiles_routed = (T * d.top_k + 511) / 512 + std::min(E, T * d.top_k);
+        {
+            ProfScope ps(c, "gate_up", s);
+            a.tiles_routed = (d.inter + 63) / 64;
+            a.tiles_shared = d.inter_shared ? (d.inter_shared + 63) / 64 : 0;
+            if ((e = launch_prefill(a, 0, s)) != hipSuccess) return hip_fail(e, "prefill gate_up launch");
+        }
+        {
+            ProfScope ps(c, "down", s);
+            a.tiles_routed = (d.hidden + 127) / 128;
+            a.tiles_shared = d.inter_shared ? (d.hidden + 127) / 128 : 0;
+            if ((e = launch_prefill(a, 1, s)) != hipSuccess) return hip_fail(e, "prefill down launch");
+        }
+        {
+            ProfScope ps(c, "combine", s);
+            a.splits_routed = 1;
+            a.splits_shared = 1;
+            if ((e = launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
+        }
+        return ok();
+    }
     {
         ProfScope ps(c, "gate_up", s);
         a.rg = kGateUpRowGroups;

@@ -46,7 +46,14 @@ struct FfnArgs {
     int32_t hstride;          // max(I, Is)
     int32_t drows;            // rows of one dout split plane: T * k (+ T with a shared expert)
     int32_t rg;               // 32-row groups per workgroup tile: 2 or 4
+    // prefill launches: token tiles of the shared block, and an upper bound
+    // on the routed token tiles (sum over experts of ceil(tokens / 512))
+    int32_t tok_tiles_shared;
+    int32_t tok_tiles_routed;
 };
+
+// Tokens per call from which the prefill GEMM path runs.
+constexpr int kPrefillMinT = 256;
 
 // 32-row groups per workgroup tile (two share one LUT set; four use both
 // halves of the LUT slots): gate_up tiles hold 16 * rg gate rows and their up
@@ -78,6 +85,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
                           int32_t* sorted, hipStream_t s);
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
 hipError_t launch_debug_decode(const BlockDesc* entry, int R, int K, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s);

@@ -217,6 +217,47 @@ __device__ __forceinline__ half8_t step_weights(const Rot<Q, PAIR>& r, int P, co
     return f;
 }
 
+// step_weights for a wave-uniform unit index P known only at run time: the
+// masks 0x01010101 << s are formed with scalar shifts of P, so no register
+// array is indexed dynamically.
+template <int Q, bool PAIR>
+__device__ __forceinline__ half8_t step_weights_u(const Rot<Q, PAIR>& r, int P, uint32_t lane_off,
+                                                 const char* lutb, uint32_t acc0)
+{
+    auto mask = [&](int k) { return 0x01010101u << ((P + k) & 7); };
+    half8_t f;
+    if constexpr (PAIR) {
+        uint32_t acc = acc0;
+#pragma unroll
+        for (int p = 0; p < Q; ++p) {
+            acc = and_or(r.A[p], mask(Q - 1 - p), acc);
+            acc = and_or(r.B[p], mask(2 * Q - 1 - p), acc);
+        }
+        const uint32_t pr = rotr(acc, P);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h2 v = *(const h2*)(lutb + lut_addr(pr, lane_off, i));
+            f[2 * i] = v.x;
+            f[2 * i + 1] = v.y;
+        }
+    } else {
+        uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+        for (int p = 0; p < Q; ++p) {
+            c0 = and_or(r.A[p], mask(Q - 1 - p), c0);
+            c1 = and_or(r.A[p], mask(4 + Q - 1 - p), c1);
+        }
+        c0 = rotr(c0, P);
+        c1 = rotr(c1, 4 + P);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = *(const _Float16*)(lutb + lut_addr(c0, lane_off, i));
+            f[2 * i + 1] = *(const _Float16*)(lutb + lut_addr(c1, lane_off, i));
+        }
+    }
+    return f;
+}
+
 // LUT_q of this lane's row -> LDS slots [entry][lane] (32-bit each).
 // Single (q >= 5): entry = code, low half = LUT[code].  Pair (q <= 4):
 // entry = a | b << q, value = LUT[a] | LUT[b] << 16; the single table is
@@ -896,6 +937,306 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
     }
 }
 
+// ---------------------------------------------------------------- prefill GEMM
+//
+// Large token counts per expert (prefill): an expert's contraction is a GEMM
+// [tokens x K] x [rows x K]^T on the matrix cores.  One 8-wave workgroup per
+// CU owns 128 weight rows (gate_up: 64 gate rows and their 64 up rows; down:
+// 128 output rows) x 512 tokens and walks K in 32-column steps (one plane
+// word).  The weight and activation tiles of a step live in LDS, double
+// buffered: while the waves run the MFMAs of step s they decode step s + 1's
+// weights (each thread: one row, 8 columns, with the same gather and LUT
+// look-up as the decode path) and store the activations of step s + 1 (each
+// thread: one token row, gathered through the expert's assignment list), so
+// decode and matrix work overlap and one barrier ends a step.  Global loads
+// run two steps ahead.  Tiles are XOR-swizzled by row so the fragment reads
+// and the stores are conflict-free.  Each wave owns 64 rows x 128 tokens (2 x
+// 4 blocks of v_mfma_f32_32x32x16_f16); a weight is decoded once per 512
+// tokens.  gate_up writes h = silu(g) * u rounded to fp16 (the MFMA operand of
+// the down GEMM); down writes the fp32 expert outputs that the combine
+// weights and sums.
+
+constexpr int kPfRows = 128;   // weight rows per tile
+constexpr int kPfTok = 512;    // tokens per tile
+constexpr int kPfThreads = 512;
+constexpr int kPfStepCols = 32;  // columns per K step (one plane word)
+// LDS words: LUT (64 KB) | weight tiles 2 x [128 rows][4 units] | activation tiles 2 x [512 tokens][4 units]
+constexpr int kPfW = kLutBytes / 4;
+constexpr int kPfWWords = kPfRows * kPfStepCols / 2;
+constexpr int kPfX = kPfW + 2 * kPfWWords;
+constexpr int kPfXWords = kPfTok * kPfStepCols / 2;
+constexpr int kPfLdsWords = kPfX + 2 * kPfXWords;
+static_assert(kPfLdsWords * 4 == 144 * 1024, "prefill LDS: 144 KB");
+static_assert(64 * kPfTok <= kPfLdsWords, "gate_up epilogue exchange fits in LDS");
+
+// swizzled 16-byte unit u (columns 8u..8u+7 of the step) of tile row r
+__device__ __forceinline__ int pf_unit(int r, int u) { return r * 4 + (u ^ ((r >> 1) & 3)); }
+
+template <int MODE, int Q>
+__device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
+                                              int ntok, int mtile, int ntile, uint32_t* lds)
+{
+    constexpr bool PAIR = LutStage<Q, 4>::PAIR;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int R = bd->R;
+    const int kwords = bd->kwords;
+    const int K = kwords * 32;
+    const int nsteps = kwords;
+    const int Iblk = R >> 1;
+    const int TK = a.T * a.k;
+    auto tile_row = [&](int r, bool& valid) {
+        if (MODE == 0) {
+            const int i = mtile * 64 + (r & 63);
+            valid = i < Iblk;
+            return r < 64 ? i : Iblk + i;
+        } else {
+            const int row = mtile * kPfRows + r;
+            valid = row < R;
+            return row;
+        }
+    };
+    // LUT sets: set t holds tile rows 64 t .. 64 t + 63 in slots 0..63
+    int lut_rows[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        bool v;
+        const int r = tile_row(64 * t + lane, v);
+        lut_rows[t] = v ? r : 0;
+    }
+    // decoder: thread = (tile row dr, 8-column unit dP of the step's word)
+    const int dr = tid & (kPfRows - 1), dP = wave >> 1;  // dP is wave-uniform
+    bool dvalid;
+    const int drow = tile_row(dr, dvalid);
+    const int dlrow = dvalid ? drow : 0;
+    const int set = dr >> 6;
+    const uint32_t lane_off = (uint32_t)(dr & 63) * 4u + (PAIR ? 0u : 2u * (uint32_t)set);
+    const uint32_t acc0 = PAIR && set ? rotl(0x01010101u << (2 * Q), dP) : 0u;
+    // activation loader: thread = token row tid of the tile
+    const int n0 = ntile * kPfTok;
+    const int te = n0 + tid < ntok ? n0 + tid : n0;
+    const uint16_t* xsrc;
+    if (MODE == 0) {
+        const int tok = shared ? te : a.sorted[p0 + te] / a.k;
+        xsrc = a.x + (size_t)tok * a.H;
+    } else {
+        const int hrow = shared ? TK + te : p0 + te;
+        xsrc = a.h_hi + (size_t)hrow * a.hstride;
+    }
+
+    u32x4* wt = (u32x4*)(lds + kPfW);  // [buffer][128 rows x 4 units]
+    u32x4* xt = (u32x4*)(lds + kPfX);  // [buffer][512 tokens x 4 units]
+    const char* lutb = (const char*)lds;
+    const __attribute__((address_space(4))) BlockDesc* cbd =
+        (const __attribute__((address_space(4))) BlockDesc*)(uintptr_t)bd;
+
+    // loads of step s (columns 32 s .. 32 s + 31); two steps are in flight
+    u32x4 xr[2][4];
+    uint32_t pw[2][Q];
+    auto issue = [&](int st, int slot) {
+        const int s = min(st, nsteps - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xr[slot][j] = *(gcu32x4p)(uintptr_t)(xsrc + s * kPfStepCols + 8 * j);
+        const size_t at = ((size_t)(s >> 2) * R + dlrow) * 4 + (s & 3);
+#pragma unroll
+        for (int p = 0; p < Q; ++p)
+            pw[slot][p] = __builtin_nontemporal_load((__attribute__((address_space(1))) const uint32_t*)(uintptr_t)cbd->planes[p] + at);
+    };
+    // step s (loaded in `slot`) -> LDS buffer s & 1
+    auto stage = [&](int s, int slot) {
+        const int buf = s & 1;
+        Rot<Q, PAIR> rt;
+        rotate_planes<Q, PAIR>(pw[slot], rt);
+        const half8 A = step_weights_u<Q, PAIR>(rt, dP, lane_off, lutb, acc0);
+        wt[buf * (kPfWWords / 4) + pf_unit(dr, dP)] = __builtin_bit_cast(u32x4, A);
+        // steps past K (padding to an even count) multiply by zero activations
+        const bool live = s < nsteps;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xt[buf * (kPfXWords / 4) + pf_unit(tid, j)] = live ? xr[slot][j] : u32x4{0, 0, 0, 0};
+    };
+
+    {
+        LutStage<Q, 4> ls;
+        ls.issue(bd->lut, lut_rows, wave);
+        issue(0, 0);
+        issue(1, 1);
+        ls.commit(lds, lds + kPfW, lane, wave);  // pair staging in the (idle) weight tiles
+        __syncthreads();
+    }
+    stage(0, 0);
+    issue(2, 0);
+    __syncthreads();
+
+    const int rb = wave & 1, tb = wave >> 1;  // this wave: 64 rows x 128 tokens
+    f32x16 C[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) C[i][j] = f32x16{};
+
+    // K steps in pairs so the register slots of the loads stay static; the
+    // body is branch-free (a branch would make the compiler wait for every
+    // load in flight at its join)
+    for (int s = 0; s < nsteps; s += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int st = s + h;
+            {
+                const int buf = st & 1;
+                // matrix work of step st
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int u = 2 * kk + (lane >> 5);
+                    half8 Af[2], Bf[4];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        Af[i] = __builtin_bit_cast(half8, wt[buf * (kPfWWords / 4) + pf_unit(64 * rb + 32 * i + (lane & 31), u)]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        Bf[j] = __builtin_bit_cast(half8, xt[buf * (kPfXWords / 4) + pf_unit(128 * tb + 32 * j + (lane & 31), u)]);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i], Bf[j], C[i][j], 0, 0, 0);
+                }
+                // step st + 1 into the other buffer, then the loads of st + 3
+                // into the registers just consumed (kept in this order: a
+                // load hoisted above the stores would force register copies
+                // and a wait for every load in flight)
+                stage(st + 1, 1 - h);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(st + 3, 1 - h);
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue; C[i][j][e]: tile row 64 rb + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
+    // token n0 + 128 tb + 32 j + lane % 32
+    if (MODE == 0) {
+        float* up = (float*)lds;  // [64 rows][512 tokens]
+        if (rb == 1) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        up[r * kPfTok + 128 * tb + 32 * j + (lane & 31)] = C[i][j][e];
+                    }
+        }
+        __syncthreads();
+        if (rb == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const int t = 128 * tb + 32 * j + (lane & 31);
+                        const int hi = mtile * 64 + r;
+                        if (n0 + t < ntok && hi < Iblk) {
+                            const float g = C[i][j][e], u = up[r * kPfTok + t];
+                            const float h = g / (1.0f + __expf(-g)) * u;
+                            const int hrow = shared ? TK + n0 + t : p0 + n0 + t;
+                            a.h_hi[(size_t)hrow * a.hstride + hi] = __builtin_bit_cast(uint16_t, (_Float16)h);
+                        }
+                    }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 128 * tb + 32 * j + (lane & 31);
+            if (n0 + t >= ntok) continue;
+            const int orow = shared ? TK + n0 + t : a.sorted[p0 + n0 + t];
+            float* dst = a.dout + (size_t)orow * a.H + mtile * kPfRows;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int r = 64 * rb + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (mtile * kPfRows + r < R) dst[r] = C[i][j][e];
+                }
+        }
+    }
+}
+
+// Workgroups: the shared block's (token tile, row tile) pairs first, then the
+// routed ones.  Routed token tiles are numbered over the experts in index
+// order (expert e has ceil(ntok_e / 256) of them); workgroups past the last
+// tile return at once.  Row tiles are fastest so neighbouring workgroups share
+// an activation tile.
+template <int MODE>
+__global__ void __launch_bounds__(kPfThreads, 2) ffn_prefill_kernel(FfnArgs a)
+{
+    __shared__ uint32_t lds[kPfLdsWords];
+    KArgs& ka = kernel_args();
+    const int wg = blockIdx.x;
+    const int shared_wgs = a.tiles_shared * a.tok_tiles_shared;
+    bool shared;
+    int mtile, ntile, p0, ntok, e;
+    if (wg < shared_wgs) {
+        shared = true;
+        ntile = wg / a.tiles_shared;
+        mtile = wg - ntile * a.tiles_shared;
+        p0 = 0;
+        ntok = a.T;
+        e = a.E;
+    } else {
+        shared = false;
+        const int r = wg - shared_wgs;
+        const int gn = r / a.tiles_routed;
+        mtile = r - gn * a.tiles_routed;
+        // expert of routed token tile gn: inclusive scan of the tile counts
+        const int lane = threadIdx.x & 63;
+        int base = 0;
+        e = -1;
+        ntile = 0;
+        p0 = 0;
+        ntok = 0;
+        for (int g = 0; g < (a.E + 63) / 64; ++g) {
+            const int ee = 64 * g + lane;
+            const int lo = ee < a.E ? a.offsets[ee] : 0, hi = ee < a.E ? a.offsets[ee + 1] : 0;
+            const int cnt = (hi - lo + kPfTok - 1) / kPfTok;
+            int incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(incl, d);
+                if (lane >= d) incl += v;
+            }
+            const int excl = base + incl - cnt;
+            const uint64_t hit = __ballot(cnt > 0 && gn >= excl && gn < excl + cnt);
+            if (hit) {
+                const int h = __ffsll((long long)hit) - 1;
+                e = 64 * g + h;
+                ntile = gn - __shfl(excl, h);
+                p0 = __shfl(lo, h);
+                ntok = __shfl(hi, h) - p0;
+                break;
+            }
+            base += __shfl(incl, 63);
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
+        if (e < 0) return;
+        ntile = __builtin_amdgcn_readfirstlane(ntile);
+        p0 = __builtin_amdgcn_readfirstlane(p0);
+        ntok = __builtin_amdgcn_readfirstlane(ntok);
+    }
+    const BlockDesc* bd = a.table + (e * 2 + MODE);
+    switch (bd->q) {
+        case 3: prefill_block<MODE, 3>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 4: prefill_block<MODE, 4>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 5: prefill_block<MODE, 5>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 6: prefill_block<MODE, 6>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 7: prefill_block<MODE, 7>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 8: prefill_block<MODE, 8>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        default: break;
+    }
+}
+
 // y[t][o] = sum_j w[t][j] * (sum over splits of d_(t,j)[o]) (+ shared d), rounded once to fp16.
 __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a)
 {
@@ -1028,6 +1369,17 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s)
         hipLaunchKernelGGL((ffn_gemv_kernel<1, 4>), dim3(grid), dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((ffn_gemv_kernel<1, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s)
+{
+    const int grid = a.tiles_shared * a.tok_tiles_shared + a.tiles_routed * a.tok_tiles_routed;
+    if (grid == 0) return hipSuccess;
+    if (module == 0)
+        hipLaunchKernelGGL(ffn_prefill_kernel<0>, dim3(grid), dim3(kPfThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(ffn_prefill_kernel<1>, dim3(grid), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
 

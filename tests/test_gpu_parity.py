@@ -107,6 +107,24 @@ def test_ffn_k_equals_E_and_large_tiles():
     check_layer(w, a, label="k=E")
 
 
+# ------------------------------------------------------------------ prefill GEMM path (T >= 256)
+
+@pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
+def test_prefill_each_width(q):
+    """128-row x 256-token MFMA tiles over weights decoded into LDS; ragged
+    rows (I = 352 is not a multiple of 64), ragged K and partial token tiles."""
+    w, a = pw_synth.make_small(H=416, I=352, E=4, top_k=2, T=300, I_shared=160, seed=700 + q, q_fixed=q)
+    check_layer(w, a, label="prefill q=%d" % q)
+
+
+def test_prefill_mixed_widths_hot_expert():
+    """Mixed widths and one expert with every token: 600 tokens -> three
+    token tiles for that expert, empty experts skipped."""
+    w, a = pw_synth.make_small(H=256, I=192, E=6, top_k=2, T=600, seed=710)
+    a.logits[:, 4] += 100.0
+    check_layer(w, a, label="prefill hot expert")
+
+
 def test_zero_tokens_enqueues_nothing():
     import torch
     w, a = pw_synth.make_small(H=64, I=32, E=2, top_k=1, T=1, seed=404)
