@@ -27,7 +27,7 @@ LUT_HALVES_PER_ROW = sum(1 << k for k in range(QMIN, QMAX + 1))
 # every function declared in include/pw.h
 EXPORTS = (
     "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
-    "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert",
+    "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
     "pw_moe_ffn_bitplane", "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
     "pw_resident_bytes", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
     "pw_profile_read",
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.pw_workspace_size.restype = sz
         L.pw_route_topk.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
         L.pw_permute_by_expert.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
+        L.pw_route_permute.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
         L.pw_moe_ffn_bitplane.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pw_set_committed_bits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
         L.pw_get_committed_bits.argtypes = [vp, i32, ctypes.POINTER(i32)]
@@ -211,6 +212,10 @@ class Context:
     def permute_by_expert(self, topk_idx, T: int, offsets, sorted_assign, stream=None) -> None:
         _check(lib().pw_permute_by_expert(self.h, _ptr(topk_idx), T, _ptr(offsets), _ptr(sorted_assign),
                                           _stream(stream)))
+
+    def route_permute(self, logits, T: int, topk_idx, topk_w, offsets, sorted_assign, stream=None) -> None:
+        _check(lib().pw_route_permute(self.h, _ptr(logits), T, _ptr(topk_idx), _ptr(topk_w), _ptr(offsets),
+                                      _ptr(sorted_assign), _stream(stream)))
 
     def moe_ffn_bitplane(self, layer: int, x, T: int, topk_idx, topk_w, offsets, sorted_assign, y,
                          workspace, ws_bytes: Optional[int] = None, stream=None) -> None:

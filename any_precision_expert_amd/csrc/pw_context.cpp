@@ -454,6 +454,27 @@ pw_status pw_route_topk(pw_ctx* c, const float* logits, int T, int32_t* idx, flo
     return e == hipSuccess ? ok() : hip_fail(e, "route_topk launch");
 }
 
+pw_status pw_route_permute(pw_ctx* c, const float* logits, int T, int32_t* idx, float* w, int32_t* offsets,
+                           int32_t* sorted, pw_stream stream)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_route_permute: null context");
+    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_route_permute: T=%d out of range", T);
+    if (!offsets) return fail(PW_ERR_INVALID, "pw_route_permute: null offsets");
+    if (T > 0 && (!logits || !idx || !w || !sorted)) return fail(PW_ERR_INVALID, "pw_route_permute: null pointer");
+    if (!aligned4(offsets) || (T > 0 && (!aligned4(logits) || !aligned4(idx) || !aligned4(w) || !aligned4(sorted))))
+        return fail(PW_ERR_INVALID, "pw_route_permute: device pointers must be 4-byte aligned");
+    const int k = c->d.top_k, E = c->d.num_experts;
+    if ((long long)T * k > kFusedMaxAssign) {
+        pw_status st = pw_route_topk(c, logits, T, idx, w, stream);
+        return st != PW_OK ? st : pw_permute_by_expert(c, idx, T, offsets, sorted, stream);
+    }
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    ProfScope ps(c, "route", (hipStream_t)stream);
+    e = launch_route_permute(logits, T, E, k, idx, w, offsets, sorted, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "route_permute launch");
+}
+
 pw_status pw_permute_by_expert(pw_ctx* c, const int32_t* idx, int T, int32_t* offsets, int32_t* sorted,
                                pw_stream stream)
 {

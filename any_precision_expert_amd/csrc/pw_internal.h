@@ -83,6 +83,10 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
                              hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted, hipStream_t s);
+// one workgroup routes and sorts (T * k <= kFusedMaxAssign)
+constexpr int kFusedMaxAssign = 4096;
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                                int32_t* offsets, int32_t* sorted, hipStream_t s);
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s);

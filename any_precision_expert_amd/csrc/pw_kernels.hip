@@ -395,13 +395,11 @@ __device__ __forceinline__ bool route_better(float av, int ai, float bv, int bi)
     return av > bv || (av == bv && ai < bi);
 }
 
-__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                         int k, int32_t* __restrict__ idx,
-                                                         float* __restrict__ w)
+// Top-k of token t's logits by one wave; lanes j < k hold the j-th expert
+// and its gate weight (returned; other lanes return -1).
+__device__ __forceinline__ int route_token(const float* __restrict__ logits, int t, int E, int k, float& wout)
 {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;  // whole wave
     const float* l = logits + (size_t)t * E;
     float v[4];
     bool live[4];
@@ -451,25 +449,38 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
         ex[j] = j < k ? expf(sv[j] - m) : 0.0f;
         s += ex[j];
     }
+    int out = -1;
+    wout = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (j < k && lane == j) {
-            idx[(size_t)t * k + j] = si[j];
-            w[(size_t)t * k + j] = ex[j] / s;
+            out = si[j];
+            wout = ex[j] / s;
         }
+    }
+    return out;
+}
+
+__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                         int k, int32_t* __restrict__ idx,
+                                                         float* __restrict__ w)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // whole wave
+    float wv;
+    const int e = route_token(logits, t, E, k, wv);
+    if (lane < k) {
+        idx[(size_t)t * k + lane] = e;
+        w[(size_t)t * k + lane] = wv;
     }
 }
 
-// One workgroup: count per expert, exclusive scan, then a stable placement of
-// assignments chunk by chunk (rank inside a wave from a ballot match, rank
-// across waves from per-wave counts).
-__global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict__ idx, int n, int E,
-                                                       int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ sorted)
+// Stable counting sort of the n assignments by expert (one 1024-thread
+// workgroup); idx may point to global memory or LDS.
+__device__ __forceinline__ void permute_body(const int32_t* idx, int n, int E, int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ sorted, int* cnt, int* base, int (*wcnt)[256])
 {
-    __shared__ int cnt[256];
-    __shared__ int base[256];
-    __shared__ int wcnt[16][256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     __syncthreads();
@@ -535,6 +546,88 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
         }
         __syncthreads();
     }
+}
+
+__global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict__ idx, int n, int E,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted)
+{
+    __shared__ int cnt[256];
+    __shared__ int base[256];
+    __shared__ int wcnt[16][256];
+    permute_body(idx, n, E, offsets, sorted, cnt, base, wcnt);
+}
+
+// Routing and permutation of a decode-sized batch in one workgroup: the 16
+// waves route the tokens (one token per wave at a time), the assignments stay
+// in LDS, and the same workgroup sorts them.  Results equal those of the two
+// separate kernels.
+__global__ void __launch_bounds__(1024) route_permute_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                             int32_t* __restrict__ idx, float* __restrict__ w,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted)
+{
+    __shared__ int cnt[256];
+    __shared__ int base[256];
+    __shared__ int wcnt[16][256];
+    __shared__ int sidx[kFusedMaxAssign];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += 16) {
+        float wv;
+        const int e = route_token(logits, t, E, k, wv);
+        if (lane < k) {
+            idx[(size_t)t * k + lane] = e;
+            w[(size_t)t * k + lane] = wv;
+            sidx[t * k + lane] = e;
+        }
+    }
+    __syncthreads();
+    const int n = T * k;
+    if (n > 64) {
+        permute_body(sidx, n, E, offsets, sorted, cnt, base, wcnt);
+        return;
+    }
+    // up to 64 assignments: wave 0 alone, one assignment per lane (LDS
+    // operations of one wave complete in order, so no barrier is needed)
+    if (wave != 0) return;
+    int e = lane < n ? sidx[lane] : 511;
+    if (e < 0 || e >= E) e = 511;
+    for (int x = lane; x < E; x += 64) cnt[x] = 0;
+    if (e < E) atomicAdd(&cnt[e], 1);
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int x = lane * 4 + i;
+        c[i] = x < E ? cnt[x] : 0;
+        sum += c[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int nb = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += nb;
+    }
+    int ex = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int x = lane * 4 + i;
+        if (x < E) {
+            base[x] = ex;
+            offsets[x] = ex;
+        }
+        ex += c[i];
+    }
+    if (lane == 63) offsets[E] = incl;
+    // rank among the lanes with the same expert (lanes = assignments in order)
+    unsigned long long m = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+        const int bit = (e >> b) & 1;
+        const unsigned long long bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (e < E) sorted[base[e] + rank] = lane;
 }
 
 // ---------------------------------------------------------------- FFN GEMV
@@ -969,8 +1062,11 @@ constexpr int kPfLdsWords = kPfX + 2 * kPfXWords;
 static_assert(kPfLdsWords * 4 == 144 * 1024, "prefill LDS: 144 KB");
 static_assert(64 * kPfTok <= kPfLdsWords, "gate_up epilogue exchange fits in LDS");
 
-// swizzled 16-byte unit u (columns 8u..8u+7 of the step) of tile row r
-__device__ __forceinline__ int pf_unit(int r, int u) { return r * 4 + (u ^ ((r >> 1) & 3)); }
+// swizzled 16-byte unit u (columns 8u..8u+7 of the step) of tile row r: any
+// 8 (16) consecutive rows put a given unit in 8 (16) distinct 16-byte bank
+// groups, so fragment reads and tile stores are conflict-free with 32 or 64
+// LDS banks
+__device__ __forceinline__ int pf_unit(int r, int u) { return r * 4 + (u ^ (((r >> 1) ^ (r >> 3)) & 3)); }
 
 template <int MODE, int Q>
 __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
@@ -1340,6 +1436,13 @@ __global__ void __launch_bounds__(64) debug_decode_kernel(const BlockDesc* __res
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s)
 {
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* offsets,
+                                int32_t* sorted, hipStream_t s)
+{
+    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(1024), 0, s, logits, T, E, k, idx, w, offsets, sorted);
     return hipGetLastError();
 }
 

@@ -49,9 +49,12 @@ class Batch:
         self.logits.copy_(torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)))
         self.x.copy_(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float16)))
 
-    def route(self, stream=None) -> None:
-        self.ctx.route_topk(self.logits, self.T, self.idx, self.w, stream)
-        self.ctx.permute_by_expert(self.idx, self.T, self.offsets, self.sorted, stream)
+    def route(self, stream=None, fused: bool = True) -> None:
+        if fused:
+            self.ctx.route_permute(self.logits, self.T, self.idx, self.w, self.offsets, self.sorted, stream)
+        else:
+            self.ctx.route_topk(self.logits, self.T, self.idx, self.w, stream)
+            self.ctx.permute_by_expert(self.idx, self.T, self.offsets, self.sorted, stream)
 
     def ffn(self, layer: int, stream=None, x=None, y=None) -> None:
         self.ctx.moe_ffn_bitplane(layer, self.x if x is None else x, self.T, self.idx, self.w,

@@ -51,8 +51,7 @@ class StackDriver:
 
     def layer_step(self, s: int, l: int) -> None:
         c, st = self.ctx, self.compute
-        c.route_topk(self.logits[s, l], self.T, self.idx[s, l], self.w[s, l], st)
-        c.permute_by_expert(self.idx[s, l], self.T, self.offsets[l], self.sorted[l], st)
+        c.route_permute(self.logits[s, l], self.T, self.idx[s, l], self.w[s, l], self.offsets[l], self.sorted[l], st)
         c.moe_ffn_bitplane(l, self.x[s, l], self.T, self.idx[s, l], self.w[s, l], self.offsets[l],
                            self.sorted[l], self.y[l], self.ws, self.ws_bytes, st)
 

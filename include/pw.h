@@ -22,7 +22,8 @@
  *    aligned, every other device array 4-byte aligned.  Nothing the caller passes is
  *    retained after the call returns, except through work enqueued on the
  *    given stream.
- *  - Hot-path calls (pw_route_topk, pw_permute_by_expert, pw_moe_ffn_bitplane)
+ *  - Hot-path calls (pw_route_topk, pw_permute_by_expert, pw_route_permute,
+ *    pw_moe_ffn_bitplane)
  *    are asynchronous on `stream`: no host synchronisation, no allocation.
  *    Kernel faults surface at the caller's next synchronisation.
  *  - A context is not thread-safe: drive it from one host thread.
@@ -143,6 +144,14 @@ pw_status pw_route_topk(pw_ctx *ctx, const float *logits, int T, int32_t *topk_i
  * 0..E-1. */
 pw_status pw_permute_by_expert(pw_ctx *ctx, const int32_t *topk_idx, int T,
                                int32_t *expert_offsets, int32_t *sorted_assign, pw_stream stream);
+
+/* pw_route_topk followed by pw_permute_by_expert in one call, with the same
+ * outputs (bit for bit).  For T * k <= 4096 a single workgroup routes the
+ * tokens and sorts the assignments without a round trip through memory (one
+ * launch instead of two, for decode-sized batches); larger batches run the
+ * two kernels.  Arguments and errors as for the two calls. */
+pw_status pw_route_permute(pw_ctx *ctx, const float *logits, int T, int32_t *topk_idx, float *topk_w,
+                           int32_t *expert_offsets, int32_t *sorted_assign, pw_stream stream);
 
 /* The fused mixed-precision MoE FFN of one layer (Core components 3: "fused
  * mixed-precision kernel" reading planes and LUTs directly, a different width

@@ -64,15 +64,22 @@ def test_route_and_permute_bit_exact(T, E, k):
         wt = torch.zeros((T, k), dtype=torch.float32, device="cuda")
         offs = torch.zeros((E + 1,), dtype=torch.int32, device="cuda")
         srt = torch.zeros((T * k,), dtype=torch.int32, device="cuda")
-        ctx.route_topk(lg, T, idx, wt)
-        ctx.permute_by_expert(idx, T, offs, srt)
-        torch.cuda.synchronize()
         ridx, rw = oracle.route_topk(logits, k)
         roff, rsrt = oracle.permute(ridx, E)
-        assert np.array_equal(idx.cpu().numpy(), ridx)
-        assert np.max(np.abs(wt.cpu().numpy() - rw)) <= 1e-6
-        assert np.array_equal(offs.cpu().numpy(), roff)
-        assert np.array_equal(srt.cpu().numpy(), rsrt)
+        # the two calls, then the fused call (one workgroup for T * k <= 4096)
+        for fused in (False, True):
+            for b in (idx, wt, offs, srt):
+                b.fill_(-7)
+            if fused:
+                ctx.route_permute(lg, T, idx, wt, offs, srt)
+            else:
+                ctx.route_topk(lg, T, idx, wt)
+                ctx.permute_by_expert(idx, T, offs, srt)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy(), ridx), "fused=%s" % fused
+            assert np.max(np.abs(wt.cpu().numpy() - rw)) <= 1e-6, "fused=%s" % fused
+            assert np.array_equal(offs.cpu().numpy(), roff), "fused=%s" % fused
+            assert np.array_equal(srt.cpu().numpy(), rsrt), "fused=%s" % fused
     finally:
         ctx.close()
 
