@@ -62,7 +62,7 @@ def step_bytes(shape, wq, offsets, T):
 
 KERNEL_SRC = os.path.join(ROOT, "any_precision_expert_amd", "csrc", "pw_kernels.hip")
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "gate_up_qwen_decode_traffic.md")
-GATE_UP_NAME = "ffn_gemv_kernel<0>"
+GATE_UP_NAME = "ffn_gemv_kernel<0,"  # demangled prefix of the gate_up decode kernel
 COPY_NAME = "copyBuffer"
 
 
@@ -103,7 +103,7 @@ def _find(d, suffix):
 def summarize_trace(trace_dir, out, command):
     """Kernel-trace statistics (rocprofv3 --kernel-trace --stats) -> markdown."""
     rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
-    lines = ["# Kernel time, Qwen-shaped decode layer (bench.py)", "",
+    lines = ["# Kernel time of bench.py: Qwen-shaped decode layer steps and the Mixtral-shaped prefill leg", "",
              "Command: `%s`" % command, "",
              "| kernel | calls | average us | total ms | share % |", "|---|---|---|---|---|"]
     for r in rows:
@@ -163,6 +163,67 @@ def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, copy_
     print("\n".join(lines))
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+PREFILL_CFG = 3
+
+
+def prefill_leg(steps):
+    """The prefill path on a Mixtral-8x7B-shaped layer (4096 tokens, 8 experts,
+    top-2, widths 3..8 per block): layer step time, and the gate_up / down
+    GEMMs against the fp16 dense MFMA peak (2 flops per multiply-add)."""
+    import torch
+    import any_precision_expert_amd as pw
+    import pw_synth
+    from any_precision_expert_amd.layer import Batch, register_layer
+    spec = pw_synth.CONFIGS[PREFILL_CFG]
+    shape, T = spec.shape, spec.tokens[0]
+    seed = pw_synth.config_seed(PREFILL_CFG)
+    t0 = time.time()
+    w = pw_synth.make_weights(shape, seed, 0, spec.q_policy, spec.logits)
+    a = pw_synth.make_activations(shape, T, seed, 0, 0, spec.logits, w.rank)
+    ctx = pw.Context(0, 1, shape.E, shape.H, shape.I, shape.top_k, shape.I_shared, keep_host_masters=False)
+    register_layer(ctx, 0, w)
+    b = Batch(ctx, T)
+    b.load(a.logits, a.x)
+    log("prefill: set up %s in %.1fs" % (spec.name, time.time() - t0))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            b.step(0, stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(steps):
+            b.step(0, stream)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    ctx.profile_enable(True)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            b.step(0, stream)
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ("route", "gate_up", "down", "combine"):
+        kms, cnt = ctx.profile_read(name)
+        kern[name] = kms / max(cnt, 1) * 1e3
+    ctx.profile_enable(False)
+    assign = int(b.offsets[-1].item())
+    gu_tf = 2.0 * assign * 2 * shape.I * shape.H / (kern["gate_up"] * 1e-6) / 1e12
+    dn_tf = 2.0 * assign * shape.H * shape.I / (kern["down"] * 1e-6) / 1e12
+    all_tf = 2.0 * assign * 3 * shape.I * shape.H / (ms * 1e-3) / 1e12
+    ctx.close()
+    log("prefill: %.3f ms/step, gate_up %.1f TFLOP/s, down %.1f TFLOP/s" % (ms, gu_tf, dn_tf))
+    return {"workload": spec.name, "tokens_per_batch": T, "H": shape.H, "I": shape.I, "E": shape.E,
+            "top_k": shape.top_k, "q": "uniform 3..8 per block", "steps": steps,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "layer_tflops": round(all_tf, 1), "kernels_us": {k: round(v, 1) for k, v in kern.items()},
+            "roofline": {"bound": "mfma", "kernel": "gate_up", "achieved": round(gu_tf, 1),
+                         "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(gu_tf / MFMA_F16_PEAK_TFLOPS, 4), "down_achieved": round(dn_tf, 1)}}
+
+
 def cpu_baseline(weights, acts_list, budget_s):
     import oracle
     P = oracle.PreparedLayer(weights)
@@ -187,6 +248,8 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="distinct weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the Mixtral-shaped prefill leg")
+    ap.add_argument("--prefill-steps", type=int, default=8)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the bench, copy this many MiB device-to-device (PMC scale reference)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"))
@@ -313,6 +376,7 @@ def main():
 
     tr = stored_traffic()
     traffic = int(tr["traffic_bytes"]) if tr else None  # HBM bytes per launch (PMC, scaled)
+    prefill = None if args.no_prefill else prefill_leg(args.prefill_steps)
 
     out = {
         "metric": "routed tokens/s per MoE layer at mixed 3-8 bit + achieved HBM GB/s vs peak",
@@ -340,6 +404,7 @@ def main():
                      "traffic": traffic, "bytes_per_launch": int(mean_b["gate_up"]),
                      "down_achieved": round(dn_gbps, 1)},
         "cpu_baseline": cpu,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
     if args.copy_calibration_mib > 0:
