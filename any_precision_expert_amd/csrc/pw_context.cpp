@@ -172,6 +172,7 @@ struct pw_ctx {
     };
     std::vector<Staging> staging;
     std::vector<hipEvent_t> events;  // owned events (released at destroy)
+    int num_cus = 256;  // compute units of the device (decode tile schedule)
     bool profiling = false;
     std::map<std::string, std::vector<ProfRec>> prof;
     std::vector<hipEvent_t> prof_pool;
@@ -338,6 +339,9 @@ pw_status pw_create(pw_ctx** out, int hip_device, const pw_model_desc* d)
         delete c;
         return hip_fail(e, "hipMemset(page table)");
     }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess && cus > 0)
+        c->num_cus = cus;
     *out = c;
     return ok();
 }
@@ -572,6 +576,7 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
     {
         ProfScope ps(c, "gate_up", s);
         a.rg = kGateUpRowGroups;
+        a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         a.tiles_routed = (d.inter + 16 * a.rg - 1) / (16 * a.rg);
         a.tiles_shared = (d.inter_shared + 16 * a.rg - 1) / (16 * a.rg);
         a.splits_routed = 1;
@@ -581,6 +586,7 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
     {
         ProfScope ps(c, "down", s);
         a.rg = kDownRowGroups;
+        a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         a.tiles_routed = (d.hidden + 32 * a.rg - 1) / (32 * a.rg);
         a.tiles_shared = d.inter_shared ? (d.hidden + 32 * a.rg - 1) / (32 * a.rg) : 0;
         a.splits_routed = down_splits(d.inter);

@@ -46,6 +46,7 @@ struct FfnArgs {
     int32_t hstride;          // max(I, Is)
     int32_t drows;            // rows of one dout split plane: T * k (+ T with a shared expert)
     int32_t rg;               // 32-row groups per workgroup tile: 2 or 4
+    int32_t big_wgs;          // rg 4: workgroups taking whole tiles before tiles split in halves (0: all whole)
     // prefill launches: token tiles of the shared block, and an upper bound
     // on the routed token tiles (sum over experts of ceil(tokens / 512))
     int32_t tok_tiles_shared;

@@ -986,17 +986,28 @@ __device__ __forceinline__ SlotExpert slot_expert(const int32_t* __restrict__ of
 // round-robin to the XCDs, so the workgroups that find work (slots below the
 // active-expert count) form one contiguous run and every XCD gets an equal
 // share of them.
+// Work units are (row tile, K split) of the shared block, then of the routed
+// slots.  With a.big_wgs > 0 (RG = 4 only) the first big_wgs workgroups - one
+// per CU - take whole units and every later unit is split into its two 64-row
+// halves (RG = 2 tiles) taken by two workgroups: the CUs that get a second
+// workgroup then carry half a unit more, not a whole one.
 template <int MODE, int RG>
 __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 {
     __shared__ uint32_t lds[kGemvLdsWords];
     const int wg = blockIdx.x;
-    const int shared_wgs = a.tiles_shared * a.splits_shared;
+    int unit = wg, half = -1;
+    if (RG == 4 && a.big_wgs > 0 && wg >= a.big_wgs) {
+        const int j = wg - a.big_wgs;
+        unit = a.big_wgs + (j >> 1);
+        half = j & 1;
+    }
+    const int shared_units = a.tiles_shared * a.splits_shared;
     bool shared;
     int tile, split, nsplit, p0, ntok, slot_e;
-    if (wg >= shared_wgs) {
+    if (unit >= shared_units) {
         shared = false;
-        const int rem = wg - shared_wgs;
+        const int rem = unit - shared_units;
         const int per_slot = a.tiles_routed * a.splits_routed;
         const int slot = rem / per_slot;
         const int ts = rem - slot * per_slot;
@@ -1010,8 +1021,8 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
         slot_e = se.e;
     } else {
         shared = true;
-        tile = wg / a.splits_shared;
-        split = wg - tile * a.splits_shared;
+        tile = unit / a.splits_shared;
+        split = unit - tile * a.splits_shared;
         nsplit = a.splits_shared;
         p0 = 0;
         ntok = a.T;
@@ -1019,6 +1030,21 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
     }
     const BlockDesc* bd = a.table + (slot_e * 2 + MODE);
     KArgs& ka = kernel_args();
+    if constexpr (RG == 4) {
+        if (half >= 0) {
+            const int t2 = 2 * tile + half;
+            switch (bd->q) {
+                case 3: mfma_block<MODE, 3, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
+                case 4: mfma_block<MODE, 4, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
+                case 5: mfma_block<MODE, 5, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
+                case 6: mfma_block<MODE, 6, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
+                case 7: mfma_block<MODE, 7, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
+                case 8: mfma_block<MODE, 8, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
+                default: break;
+            }
+            return;
+        }
+    }
     switch (bd->q) {
         case 3: mfma_block<MODE, 3, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
         case 4: mfma_block<MODE, 4, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
@@ -1453,9 +1479,18 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
     return hipGetLastError();
 }
 
+// workgroups of a decode launch: every unit, plus one more per unit past the
+// first big_wgs when those units are split in halves
+static int gemv_grid(const FfnArgs& a)
+{
+    const int units = a.n_slots * a.tiles_routed * a.splits_routed + a.tiles_shared * a.splits_shared;
+    if (a.rg == 4 && a.big_wgs > 0 && units > a.big_wgs) return a.big_wgs + 2 * (units - a.big_wgs);
+    return units;
+}
+
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
 {
-    const int grid = a.n_slots * a.tiles_routed * a.splits_routed + a.tiles_shared * a.splits_shared;
+    const int grid = gemv_grid(a);
     if (grid == 0) return hipSuccess;
     if (a.rg == 4)
         hipLaunchKernelGGL((ffn_gemv_kernel<0, 4>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -1466,7 +1501,7 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
 
 hipError_t launch_down(const FfnArgs& a, hipStream_t s)
 {
-    const int grid = a.n_slots * a.tiles_routed * a.splits_routed + a.tiles_shared * a.splits_shared;
+    const int grid = gemv_grid(a);
     if (grid == 0) return hipSuccess;
     if (a.rg == 4)
         hipLaunchKernelGGL((ffn_gemv_kernel<1, 4>), dim3(grid), dim3(kThreads), 0, s, a);
