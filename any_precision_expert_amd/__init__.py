@@ -28,7 +28,7 @@ LUT_HALVES_PER_ROW = sum(1 << k for k in range(QMIN, QMAX + 1))
 EXPORTS = (
     "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
     "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
-    "pw_moe_ffn_bitplane", "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
+    "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
     "pw_resident_bytes", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
     "pw_profile_read",
 )
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.pw_permute_by_expert.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
         L.pw_route_permute.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
         L.pw_moe_ffn_bitplane.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pw_moe_layer.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pw_set_committed_bits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
         L.pw_get_committed_bits.argtypes = [vp, i32, ctypes.POINTER(i32)]
         L.pw_block_id.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -224,6 +225,14 @@ class Context:
         _check(lib().pw_moe_ffn_bitplane(self.h, layer, _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
                                          _ptr(offsets), _ptr(sorted_assign), _ptr(y), _ptr(workspace),
                                          ws_bytes, _stream(stream)))
+
+    def moe_layer(self, layer: int, logits, x, T: int, topk_idx, topk_w, offsets, sorted_assign, y,
+                  workspace, ws_bytes: Optional[int] = None, stream=None) -> None:
+        if ws_bytes is None:
+            ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib().pw_moe_layer(self.h, layer, _ptr(logits), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
+                                  _ptr(offsets), _ptr(sorted_assign), _ptr(y), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))
 
     # test exports and profiling ----------------------------------------
     def debug_decode_codes(self, block_id: int, out, stream=None) -> None:

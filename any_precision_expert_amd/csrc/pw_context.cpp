@@ -495,34 +495,51 @@ pw_status pw_permute_by_expert(pw_ctx* c, const int32_t* idx, int T, int32_t* of
     return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
 }
 
-pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, const int32_t* idx,
-                              const float* w, const int32_t* offsets, const int32_t* sorted, uint16_t* y,
-                              void* workspace, size_t ws_bytes, pw_stream stream)
+// Argument checks of the FFN (fn names the entry point in messages).
+static pw_status ffn_check(const pw_ctx* c, const char* fn, int layer, const uint16_t* x, int T, const int32_t* idx,
+                           const float* w, const int32_t* offsets, const int32_t* sorted, const uint16_t* y,
+                           const void* workspace, size_t ws_bytes)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: null context");
-    if (layer < 0 || layer >= c->d.num_layers) return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: layer %d out of range", layer);
-    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: T=%d out of range", T);
+    if (!c) return fail(PW_ERR_INVALID, "%s: null context", fn);
+    if (layer < 0 || layer >= c->d.num_layers) return fail(PW_ERR_INVALID, "%s: layer %d out of range", fn, layer);
+    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "%s: T=%d out of range", fn, T);
     if (T == 0) return ok();
-    if (!x || !idx || !w || !offsets || !sorted || !y || !workspace)
-        return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: null pointer");
+    if (!x || !idx || !w || !offsets || !sorted || !y || !workspace) return fail(PW_ERR_INVALID, "%s: null pointer", fn);
     if (!aligned16(x) || !aligned4(idx) || !aligned4(w) || !aligned4(offsets) || !aligned4(sorted) ||
         !aligned16(y) || ((uintptr_t)workspace & 255u))
-        return fail(PW_ERR_INVALID,
-                    "pw_moe_ffn_bitplane: misaligned pointer (x, y 16 B; index arrays 4 B; workspace 256 B)");
+        return fail(PW_ERR_INVALID, "%s: misaligned pointer (x, y 16 B; index arrays 4 B; workspace 256 B)", fn);
     const pw_model_desc& d = c->d;
     const WsLayout L = ws_layout(T, d.top_k, d.hidden, d.inter, d.inter_shared);
-    if (ws_bytes < L.total)
-        return fail(PW_ERR_INVALID, "pw_moe_ffn_bitplane: workspace %zu B < %zu B needed", ws_bytes, L.total);
+    if (ws_bytes < L.total) return fail(PW_ERR_INVALID, "%s: workspace %zu B < %zu B needed", fn, ws_bytes, L.total);
     const int E = d.num_experts;
     for (int s = 0; s <= E; ++s) {
         if (s == E && d.inter_shared == 0) break;
         for (int m = 0; m < 2; ++m) {
             const int id = (layer * (E + 1) + s) * 2 + m;
             if (!c->blocks[id].registered)
-                return fail(PW_ERR_STATE, "pw_moe_ffn_bitplane: block (layer %d, slot %d, module %d) not registered",
-                            layer, s, m);
+                return fail(PW_ERR_STATE, "%s: block (layer %d, slot %d, module %d) not registered", fn, layer, s, m);
         }
     }
+    return ok();
+}
+
+// Routing results computed by the decode gate_up launch itself.
+struct LayerRoute {
+    const float* logits;
+    int32_t* idx;
+    float* w;
+    int32_t* offsets;
+    int32_t* sorted;
+};
+
+// Enqueues the FFN of checked arguments (T > 0).
+static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, const float* w, const int32_t* offsets,
+                            const int32_t* sorted, uint16_t* y, void* workspace, pw_stream stream,
+                            const LayerRoute* route)
+{
+    const pw_model_desc& d = c->d;
+    const WsLayout L = ws_layout(T, d.top_k, d.hidden, d.inter, d.inter_shared);
+    const int E = d.num_experts;
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
     char* ws = (char*)workspace;
@@ -581,7 +598,15 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
         a.tiles_shared = (d.inter_shared + 16 * a.rg - 1) / (16 * a.rg);
         a.splits_routed = 1;
         a.splits_shared = 1;
+        if (route) {
+            a.logits = route->logits;
+            a.idx_out = route->idx;
+            a.w_out = route->w;
+            a.offsets_out = route->offsets;
+            a.sorted_out = route->sorted;
+        }
         if ((e = launch_gate_up(a, s)) != hipSuccess) return hip_fail(e, "gate_up launch");
+        a.logits = nullptr;
     }
     {
         ProfScope ps(c, "down", s);
@@ -598,6 +623,38 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
         if ((e = launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
     }
     return ok();
+}
+
+pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, const int32_t* idx,
+                              const float* w, const int32_t* offsets, const int32_t* sorted, uint16_t* y,
+                              void* workspace, size_t ws_bytes, pw_stream stream)
+{
+    const pw_status st =
+        ffn_check(c, "pw_moe_ffn_bitplane", layer, x, T, idx, w, offsets, sorted, y, workspace, ws_bytes);
+    if (st != PW_OK || T == 0) return st;
+    return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, nullptr);
+}
+
+pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t* x, int T, int32_t* idx, float* w,
+                       int32_t* offsets, int32_t* sorted, uint16_t* y, void* workspace, size_t ws_bytes,
+                       pw_stream stream)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_moe_layer: null context");
+    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_layer: T=%d out of range", T);
+    if (!offsets) return fail(PW_ERR_INVALID, "pw_moe_layer: null offsets");
+    if (!aligned4(offsets) || (T > 0 && (!logits || !aligned4(logits))))
+        return fail(PW_ERR_INVALID, "pw_moe_layer: null or misaligned logits / offsets (4 B)");
+    pw_status st = ffn_check(c, "pw_moe_layer", layer, x, T, idx, w, offsets, sorted, y, workspace, ws_bytes);
+    if (st != PW_OK) return st;
+    const long long n = (long long)T * c->d.top_k;
+    if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign) {
+        // the separate routing launch, then the FFN (identical results)
+        st = pw_route_permute(c, logits, T, idx, w, offsets, sorted, stream);
+        if (st != PW_OK || T == 0) return st;
+        return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, nullptr);
+    }
+    const LayerRoute r{logits, idx, w, offsets, sorted};
+    return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, &r);
 }
 
 pw_status pw_get_committed_bits(const pw_ctx* c, int32_t id, int32_t* q_out)

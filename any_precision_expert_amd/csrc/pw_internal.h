@@ -51,7 +51,19 @@ struct FfnArgs {
     // on the routed token tiles (sum over experts of ceil(tokens / 512))
     int32_t tok_tiles_shared;
     int32_t tok_tiles_routed;
+    // routing inside the decode gate_up launch (logits non-null; T * k <=
+    // kLayerRouteMaxAssign): every routed workgroup routes and sorts the batch
+    // in LDS, and one of them writes the results that the down and combine
+    // launches read (offsets, sorted, topk_w above point at the same buffers)
+    const float* logits;
+    int32_t* idx_out;
+    float* w_out;
+    int32_t* offsets_out;
+    int32_t* sorted_out;
 };
+
+// Most assignments (T * k) a gate_up launch routes by itself.
+constexpr int kLayerRouteMaxAssign = 64;
 
 // Tokens per call from which the prefill GEMM path runs.
 constexpr int kPrefillMinT = 256;
@@ -88,7 +100,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 constexpr int kFusedMaxAssign = 4096;
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                 int32_t* offsets, int32_t* sorted, hipStream_t s);
-hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);  // routes first when a.logits is set
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s);

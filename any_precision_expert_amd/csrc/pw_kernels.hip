@@ -461,19 +461,48 @@ __device__ __forceinline__ int route_token(const float* __restrict__ logits, int
     return out;
 }
 
+// One token's picks in the form the callers store: lane j < k holds pick j.
+struct RoutePick {
+    int j;    // pick index 0..k-1, or -1 on lanes >= k
+    int e;    // the picked expert
+    float w;  // its gate weight
+};
+
+__device__ __forceinline__ RoutePick route_pick(const float* __restrict__ logits, int t, int E, int k)
+{
+    float wv;
+    const int e = route_token(logits, t, E, k, wv);
+    const int lane = threadIdx.x & 63;
+    return RoutePick{lane < k ? lane : -1, e, wv};
+}
+
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T, int E,
                                                          int k, int32_t* __restrict__ idx,
                                                          float* __restrict__ w)
 {
-    const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave
-    float wv;
-    const int e = route_token(logits, t, E, k, wv);
-    if (lane < k) {
-        idx[(size_t)t * k + lane] = e;
-        w[(size_t)t * k + lane] = wv;
+    const RoutePick p = route_pick(logits, t, E, k);
+    if (p.j >= 0) {
+        idx[(size_t)t * k + p.j] = p.e;
+        w[(size_t)t * k + p.j] = p.w;
     }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips): shifts 1, 2, 4, 8 inside each 16-lane
+// row, then lane 15 of rows 0 / 2 into rows 1 / 3, then lane 31 into rows 2
+// and 3.  Lanes whose DPP source is outside the row, or whose row is masked
+// off, add 0.
+__device__ __forceinline__ int wave_inclusive_sum(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
 }
 
 // Stable counting sort of the n assignments by expert (one 1024-thread
@@ -489,7 +518,7 @@ __device__ __forceinline__ void permute_body(const int32_t* idx, int n, int E, i
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    if (wave == 0) {  // exclusive scan of the counts: 4 experts per lane + a shuffle scan
+    if (wave == 0) {  // exclusive scan of the counts: 4 experts per lane + a wave scan
         int c[4], s = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -497,12 +526,7 @@ __device__ __forceinline__ void permute_body(const int32_t* idx, int n, int E, i
             c[i] = e < E ? cnt[e] : 0;
             s += c[i];
         }
-        int incl = s;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int nb = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += nb;
-        }
+        const int incl = wave_inclusive_sum(s);
         int ex = incl - s;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -558,38 +582,14 @@ __global__ void __launch_bounds__(1024) permute_kernel(const int32_t* __restrict
     permute_body(idx, n, E, offsets, sorted, cnt, base, wcnt);
 }
 
-// Routing and permutation of a decode-sized batch in one workgroup: the 16
-// waves route the tokens (one token per wave at a time), the assignments stay
-// in LDS, and the same workgroup sorts them.  Results equal those of the two
-// separate kernels.
-__global__ void __launch_bounds__(1024) route_permute_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                             int32_t* __restrict__ idx, float* __restrict__ w,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ sorted)
+// Stable counting sort of n <= 64 assignments by wave 0 alone, one
+// assignment per lane (LDS operations of one wave complete in order, so no
+// barrier is needed).  sidx, cnt and base are LDS; offsets and sorted may be
+// global memory or LDS.
+__device__ __forceinline__ void sort_small(const int* sidx, int n, int E, int32_t* offsets, int32_t* sorted,
+                                           int* cnt, int* base)
 {
-    __shared__ int cnt[256];
-    __shared__ int base[256];
-    __shared__ int wcnt[16][256];
-    __shared__ int sidx[kFusedMaxAssign];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += 16) {
-        float wv;
-        const int e = route_token(logits, t, E, k, wv);
-        if (lane < k) {
-            idx[(size_t)t * k + lane] = e;
-            w[(size_t)t * k + lane] = wv;
-            sidx[t * k + lane] = e;
-        }
-    }
-    __syncthreads();
-    const int n = T * k;
-    if (n > 64) {
-        permute_body(sidx, n, E, offsets, sorted, cnt, base, wcnt);
-        return;
-    }
-    // up to 64 assignments: wave 0 alone, one assignment per lane (LDS
-    // operations of one wave complete in order, so no barrier is needed)
-    if (wave != 0) return;
+    const int lane = threadIdx.x & 63;
     int e = lane < n ? sidx[lane] : 511;
     if (e < 0 || e >= E) e = 511;
     for (int x = lane; x < E; x += 64) cnt[x] = 0;
@@ -601,12 +601,7 @@ __global__ void __launch_bounds__(1024) route_permute_kernel(const float* __rest
         c[i] = x < E ? cnt[x] : 0;
         sum += c[i];
     }
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int nb = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += nb;
-    }
+    const int incl = wave_inclusive_sum(sum);
     int ex = incl - sum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -628,6 +623,39 @@ __global__ void __launch_bounds__(1024) route_permute_kernel(const float* __rest
     }
     const int rank = __popcll(m & ((1ull << lane) - 1ull));
     if (e < E) sorted[base[e] + rank] = lane;
+}
+
+// Routing and permutation of a decode-sized batch in one workgroup: the 16
+// waves route the tokens (one token per wave at a time), the assignments stay
+// in LDS, and the same workgroup sorts them.  Results equal those of the two
+// separate kernels.
+__global__ void __launch_bounds__(1024) route_permute_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                             int32_t* __restrict__ idx, float* __restrict__ w,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted)
+{
+    __shared__ int cnt[256];
+    __shared__ int base[256];
+    __shared__ int wcnt[16][256];
+    __shared__ int sidx[kFusedMaxAssign];
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += 16) {
+        const RoutePick p = route_pick(logits, t, E, k);
+        if (p.j >= 0) {
+            idx[(size_t)t * k + p.j] = p.e;
+            w[(size_t)t * k + p.j] = p.w;
+            sidx[t * k + p.j] = p.e;
+        }
+    }
+    __syncthreads();
+    const int n = T * k;
+    if (n > 64) {
+        permute_body(sidx, n, E, offsets, sorted, cnt, base, wcnt);
+        return;
+    }
+    // up to 64 assignments: wave 0 alone (see sort_small)
+    if (wave != 0) return;
+    sort_small(sidx, n, E, offsets, sorted, cnt, base);
 }
 
 // ---------------------------------------------------------------- FFN GEMV
@@ -706,9 +734,11 @@ __device__ __forceinline__ int slice_unit(int j, int t, int g)
     return j * 16 + (g ^ t);
 }
 
-template <int MODE, int Q, int RG>
+// FUSED (gate_up of a launch that routed the batch itself): lane i of tokreg
+// holds the slot's i-th sorted assignment instead of a.sorted in memory.
+template <int MODE, int Q, int RG, bool FUSED = false>
 __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
-                                           int ntok, int tile, int split, int nsplit, uint32_t* lds)
+                                           int ntok, int tile, int split, int nsplit, uint32_t* lds, int tokreg = 0)
 {
     constexpr int D = Q <= 4 ? 2 : 1;      // chunks of plane loads in flight
     constexpr int NPART = 2;               // activation loads per lane and chunk
@@ -783,12 +813,17 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 tok[0] = t0 + min(xt, nt - 1);
                 tok[1] = t0 + min(xt + 4, nt - 1);
             } else {
-                // the pass's assignment ids through scalar loads (lgkmcnt)
-                const ci32p srt = (ci32p)(uintptr_t)a.sorted;
-                const int base = p0 + t0;
                 int sa[TP];
+                if constexpr (FUSED) {
 #pragma unroll
-                for (int j = 0; j < TP; ++j) sa[j] = srt[base + min(j, nt - 1)];
+                    for (int j = 0; j < TP; ++j) sa[j] = __builtin_amdgcn_readlane(tokreg, t0 + min(j, nt - 1));
+                } else {
+                    // the pass's assignment ids through scalar loads (lgkmcnt)
+                    const ci32p srt = (ci32p)(uintptr_t)a.sorted;
+                    const int base = p0 + t0;
+#pragma unroll
+                    for (int j = 0; j < TP; ++j) sa[j] = srt[base + min(j, nt - 1)];
+                }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int te = xt + 4 * h;
@@ -945,20 +980,32 @@ struct SlotExpert {
     int e, p0, ntok;
 };
 
-__device__ __forceinline__ SlotExpert slot_expert(const int32_t* __restrict__ offsets,
-                                                  const BlockDesc* __restrict__ table, int module, int E, int slot)
+// Committed widths of the E blocks of one module, experts lane + 64 g.
+__device__ __forceinline__ void load_widths(const BlockDesc* __restrict__ table, int module, int E, int (&q)[4])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int e = 64 * g + lane;
+        q[g] = table[(e < E ? e : 0) * 2 + module].q;  // in-range address for every lane
+    }
+}
+
+// Expert of a routed slot: the active experts (offsets[e + 1] > offsets[e])
+// ordered by decreasing width, then by index.  offsets may be global memory
+// or LDS.
+__device__ __forceinline__ SlotExpert find_slot(const int32_t* offsets, const int (&q)[4], int E, int slot)
 {
     const int lane = threadIdx.x & 63;
     const uint64_t below = (1ull << lane) - 1ull;
-    int lo[4], hi[4], q[4];
+    int lo[4], hi[4];
     bool act[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int e = 64 * g + lane;
-        const int ec = e < E ? e : 0;  // in-range address for every lane
+        const int ec = e < E ? e : 0;
         lo[g] = offsets[ec];
         hi[g] = offsets[ec + 1];
-        q[g] = table[ec * 2 + module].q;
         act[g] = e < E && hi[g] > lo[g];
     }
     int base = 0;
@@ -980,21 +1027,43 @@ __device__ __forceinline__ SlotExpert slot_expert(const int32_t* __restrict__ of
     return SlotExpert{-1, 0, 0};
 }
 
-// Workgroup order: the shared expert's tiles first (its work is known to
-// exist and is at the widest width), then the routed tiles slot by slot (slots
-// in decreasing width).  The dispatcher deals consecutive workgroups
-// round-robin to the XCDs, so the workgroups that find work (slots below the
-// active-expert count) form one contiguous run and every XCD gets an equal
-// share of them.
-// Work units are (row tile, K split) of the shared block, then of the routed
-// slots.  With a.big_wgs > 0 (RG = 4 only) the first big_wgs workgroups - one
-// per CU - take whole units and every later unit is split into its two 64-row
-// halves (RG = 2 tiles) taken by two workgroups: the CUs that get a second
-// workgroup then carry half a unit more, not a whole one.
-template <int MODE, int RG>
+// Routing of the whole batch inside a gate_up workgroup (n = T * k <= 64):
+// the waves route the tokens, wave 0 sorts the assignments.  LDS layout of rt
+// (words): idx [64] | w [64] | offsets [257] | sorted [64] | cnt [256] | base [256].
+constexpr int kRtIdx = 0, kRtW = 64, kRtOff = 128, kRtSorted = 385, kRtCnt = 449, kRtBase = 705, kRtWords = 961;
+static_assert(kRtWords <= kWaves * kSliceWords, "routing scratch lives in the slice region");
+
+__device__ __forceinline__ void route_in_workgroup(const FfnArgs& a, int* rt)
+{
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < a.T; t += kWaves) {
+        const RoutePick p = route_pick(a.logits, t, a.E, a.k);
+        if (p.j >= 0) {
+            rt[kRtIdx + t * a.k + p.j] = p.e;
+            ((float*)rt)[kRtW + t * a.k + p.j] = p.w;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) sort_small(rt + kRtIdx, a.T * a.k, a.E, rt + kRtOff, rt + kRtSorted, rt + kRtCnt, rt + kRtBase);
+    __syncthreads();
+}
+
+// Workgroup order: work units are (row tile, K split) of the shared expert
+// first (its work is known to exist and is at the widest width), then of the
+// routed slots, slot by slot (slots in decreasing width).  The dispatcher deals
+// consecutive workgroups round-robin to the XCDs, so the workgroups that find
+// work (slots below the active-expert count) form one contiguous run and every
+// XCD gets an equal share of them.  With a.big_wgs > 0 (RG = 4 only) the first
+// big_wgs workgroups - one per CU - take whole units and every later unit is
+// split into its two 64-row halves (RG = 2 tiles) taken by two workgroups: the
+// CUs that get a second workgroup then carry half a unit more, not a whole one.
+// FUSED (gate_up only): the launch routes the batch itself (a.logits); the
+// workgroup of the first routed unit writes the routing results for the caller
+// and for the down and combine launches.
+template <int MODE, int RG, bool FUSED = false>
 __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 {
-    __shared__ uint32_t lds[kGemvLdsWords];
+    __shared__ __align__(16) uint32_t lds[kGemvLdsWords];
     const int wg = blockIdx.x;
     int unit = wg, half = -1;
     if (RG == 4 && a.big_wgs > 0 && wg >= a.big_wgs) {
@@ -1004,7 +1073,7 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
     }
     const int shared_units = a.tiles_shared * a.splits_shared;
     bool shared;
-    int tile, split, nsplit, p0, ntok, slot_e;
+    int tile, split, nsplit, p0, ntok, slot_e, tokreg = 0;
     if (unit >= shared_units) {
         shared = false;
         const int rem = unit - shared_units;
@@ -1014,7 +1083,27 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
         tile = ts / a.splits_routed;
         split = ts - tile * a.splits_routed;
         nsplit = a.splits_routed;
-        const SlotExpert se = slot_expert(a.offsets, a.table, MODE, a.E, slot);
+        int qw[4];
+        load_widths(a.table, MODE, a.E, qw);
+        SlotExpert se;
+        if constexpr (FUSED) {
+            int* rt = (int*)(lds + kLutBytes / 4);
+            route_in_workgroup(a, rt);
+            const int n = a.T * a.k;
+            if (rem == 0 && half <= 0) {
+                for (int i = threadIdx.x; i < n; i += kThreads) {
+                    a.idx_out[i] = rt[kRtIdx + i];
+                    a.w_out[i] = ((const float*)rt)[kRtW + i];
+                    a.sorted_out[i] = rt[kRtSorted + i];
+                }
+                for (int i = threadIdx.x; i <= a.E; i += kThreads) a.offsets_out[i] = rt[kRtOff + i];
+            }
+            se = find_slot(rt + kRtOff, qw, a.E, slot);
+            tokreg = rt[kRtSorted + min(se.p0 + (int)(threadIdx.x & 63), n - 1)];
+            __syncthreads();  // the slice region is reused from here on
+        } else {
+            se = find_slot(a.offsets, qw, a.E, slot);
+        }
         if (se.e < 0) return;
         p0 = se.p0;
         ntok = se.ntok;
@@ -1030,30 +1119,25 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
     }
     const BlockDesc* bd = a.table + (slot_e * 2 + MODE);
     KArgs& ka = kernel_args();
+#define PW_GEMV_CASES(RGX, TILE)                                                                                  \
+    switch (bd->q) {                                                                                             \
+        case 3: mfma_block<MODE, 3, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 4: mfma_block<MODE, 4, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 5: mfma_block<MODE, 5, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 6: mfma_block<MODE, 6, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 7: mfma_block<MODE, 7, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 8: mfma_block<MODE, 8, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        default: break;                                                                                          \
+    }
     if constexpr (RG == 4) {
         if (half >= 0) {
             const int t2 = 2 * tile + half;
-            switch (bd->q) {
-                case 3: mfma_block<MODE, 3, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
-                case 4: mfma_block<MODE, 4, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
-                case 5: mfma_block<MODE, 5, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
-                case 6: mfma_block<MODE, 6, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
-                case 7: mfma_block<MODE, 7, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
-                case 8: mfma_block<MODE, 8, 2>(ka, bd, shared, p0, ntok, t2, split, nsplit, lds); break;
-                default: break;
-            }
+            PW_GEMV_CASES(2, t2)
             return;
         }
     }
-    switch (bd->q) {
-        case 3: mfma_block<MODE, 3, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 4: mfma_block<MODE, 4, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 5: mfma_block<MODE, 5, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 6: mfma_block<MODE, 6, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 7: mfma_block<MODE, 7, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        case 8: mfma_block<MODE, 8, RG>(ka, bd, shared, p0, ntok, tile, split, nsplit, lds); break;
-        default: break;
-    }
+    PW_GEMV_CASES(RG, tile)
+#undef PW_GEMV_CASES
 }
 
 // ---------------------------------------------------------------- prefill GEMM
@@ -1294,7 +1378,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
 template <int MODE>
 __global__ void __launch_bounds__(kPfThreads, 2) ffn_prefill_kernel(FfnArgs a)
 {
-    __shared__ uint32_t lds[kPfLdsWords];
+    __shared__ __align__(16) uint32_t lds[kPfLdsWords];
     KArgs& ka = kernel_args();
     const int wg = blockIdx.x;
     const int shared_wgs = a.tiles_shared * a.tok_tiles_shared;
@@ -1323,12 +1407,7 @@ __global__ void __launch_bounds__(kPfThreads, 2) ffn_prefill_kernel(FfnArgs a)
             const int ee = 64 * g + lane;
             const int lo = ee < a.E ? a.offsets[ee] : 0, hi = ee < a.E ? a.offsets[ee + 1] : 0;
             const int cnt = (hi - lo + kPfTok - 1) / kPfTok;
-            int incl = cnt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int v = __shfl_up(incl, d);
-                if (lane >= d) incl += v;
-            }
+            const int incl = wave_inclusive_sum(cnt);
             const int excl = base + incl - cnt;
             const uint64_t hit = __ballot(cnt > 0 && gn >= excl && gn < excl + cnt);
             if (hit) {
@@ -1444,7 +1523,7 @@ __device__ void debug_block(const BlockDesc* __restrict__ bd, int R, int K, uint
 __global__ void __launch_bounds__(64) debug_decode_kernel(const BlockDesc* __restrict__ bd, int R, int K,
                                                           uint8_t* codes_out, uint16_t* w_out)
 {
-    __shared__ uint32_t lds[kDebugLdsWords];
+    __shared__ __align__(16) uint32_t lds[kDebugLdsWords];
     switch (bd->q) {
         case 3: debug_block<3>(bd, R, K, codes_out, w_out, lds); break;
         case 4: debug_block<4>(bd, R, K, codes_out, w_out, lds); break;
@@ -1492,10 +1571,14 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
 {
     const int grid = gemv_grid(a);
     if (grid == 0) return hipSuccess;
-    if (a.rg == 4)
+    if (a.logits) {
+        if (a.rg != 4 || a.T * a.k > kLayerRouteMaxAssign || a.E > 256) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((ffn_gemv_kernel<0, 4, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    } else if (a.rg == 4) {
         hipLaunchKernelGGL((ffn_gemv_kernel<0, 4>), dim3(grid), dim3(kThreads), 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((ffn_gemv_kernel<0, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -61,7 +61,13 @@ class Batch:
                                   self.offsets, self.sorted, self.y if y is None else y, self.ws,
                                   self.ws_bytes, stream)
 
-    def step(self, layer: int, stream=None) -> None:
-        """One pass of the hot path: route -> permute -> FFN -> combine."""
-        self.route(stream)
-        self.ffn(layer, stream)
+    def step(self, layer: int, stream=None, separate: bool = False) -> None:
+        """One pass of the hot path: route -> permute -> FFN -> combine, as one
+        pw_moe_layer call (routing inside the gate_up launch for decode-sized
+        batches) or, with `separate`, as pw_route_permute + pw_moe_ffn_bitplane."""
+        if separate:
+            self.route(stream)
+            self.ffn(layer, stream)
+            return
+        self.ctx.moe_layer(layer, self.logits, self.x, self.T, self.idx, self.w, self.offsets, self.sorted,
+                           self.y, self.ws, self.ws_bytes, stream)

@@ -51,9 +51,8 @@ class StackDriver:
 
     def layer_step(self, s: int, l: int) -> None:
         c, st = self.ctx, self.compute
-        c.route_permute(self.logits[s, l], self.T, self.idx[s, l], self.w[s, l], self.offsets[l], self.sorted[l], st)
-        c.moe_ffn_bitplane(l, self.x[s, l], self.T, self.idx[s, l], self.w[s, l], self.offsets[l],
-                           self.sorted[l], self.y[l], self.ws, self.ws_bytes, st)
+        c.moe_layer(l, self.logits[s, l], self.x[s, l], self.T, self.idx[s, l], self.w[s, l], self.offsets[l],
+                    self.sorted[l], self.y[l], self.ws, self.ws_bytes, st)
 
     def step(self, s: int) -> None:
         for l in range(self.L):

@@ -23,7 +23,7 @@
  *    retained after the call returns, except through work enqueued on the
  *    given stream.
  *  - Hot-path calls (pw_route_topk, pw_permute_by_expert, pw_route_permute,
- *    pw_moe_ffn_bitplane)
+ *    pw_moe_ffn_bitplane, pw_moe_layer)
  *    are asynchronous on `stream`: no host synchronisation, no allocation.
  *    Kernel faults surface at the caller's next synchronisation.
  *  - A context is not thread-safe: drive it from one host thread.
@@ -167,6 +167,22 @@ pw_status pw_moe_ffn_bitplane(pw_ctx *ctx, int layer, const uint16_t *x, int T,
                               const int32_t *topk_idx, const float *topk_w,
                               const int32_t *expert_offsets, const int32_t *sorted_assign,
                               uint16_t *y, void *workspace, size_t ws_bytes, pw_stream stream);
+
+/* One whole MoE layer step: pw_route_permute followed by pw_moe_ffn_bitplane,
+ * with the same outputs (topk_idx, topk_w, expert_offsets, sorted_assign and
+ * y, bit for bit).  For decode-sized batches (T * k <= 64 and T below the
+ * prefill crossover of 256 tokens) the routing runs inside the gate_up launch:
+ * every workgroup with routed work routes and sorts the batch in LDS (a
+ * fraction of a microsecond of its start-up) instead of waiting for a separate
+ * routing launch, and one of them writes the routing outputs for the caller
+ * and for the down and combine launches.  Larger batches run the separate
+ * launches.  logits: dev fp32 [T][E]; the other arguments, the errors and the
+ * workspace rule are those of the two calls.  T = 0 sets expert_offsets to
+ * zero and enqueues nothing else. */
+pw_status pw_moe_layer(pw_ctx *ctx, int layer, const float *logits, const uint16_t *x, int T,
+                       int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                       int32_t *sorted_assign, uint16_t *y, void *workspace, size_t ws_bytes,
+                       pw_stream stream);
 
 /* Change the committed width of n blocks (Core components 3: asynchronous page
  * movement; widths committed only at safe boundaries).  block_ids: host, each

@@ -24,12 +24,18 @@ def make_ctx(shape, layers=1, keep_host_masters=True):
     return pw.Context(0, layers, shape.E, shape.H, shape.I, shape.top_k, shape.I_shared, keep_host_masters)
 
 
-def run_gpu(ctx, layer, acts):
+def run_gpu(ctx, layer, acts, separate=False):
+    """One layer step; outputs are pre-filled with a poison value so that a
+    result the path fails to write shows up."""
     import torch
     T = acts.x.shape[0]
     b = Batch(ctx, T)
     b.load(acts.logits, acts.x)
-    b.step(layer)
+    for t in (b.idx, b.offsets, b.sorted):
+        t.fill_(-7)
+    b.w.fill_(-7.0)
+    b.y.fill_(-7.0)
+    b.step(layer, separate=separate)
     torch.cuda.synchronize()
     return dict(idx=b.idx.cpu().numpy(), w=b.w.cpu().numpy(), offsets=b.offsets.cpu().numpy(),
                 sorted=b.sorted.cpu().numpy()[:T * ctx.desc.top_k],

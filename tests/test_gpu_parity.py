@@ -187,3 +187,52 @@ def test_config3_mixtral_prefill_sampled():
     rng = np.random.default_rng(3)
     tokens = sorted(set(rng.choice(4096, size=8, replace=False).tolist()) | {0, 4095})
     check_layer(w, a, tokens=tokens, label="cfg3 prefill")
+
+
+# ------------------------------------------------------------------ one call per layer
+
+@pytest.fixture(scope="module")
+def qwen():
+    from any_precision_expert_amd.layer import register_layer
+    spec = pw_synth.CONFIGS[1]
+    w = pw_synth.make_weights(spec.shape, pw_synth.config_seed(1), 0, spec.q_policy, spec.logits)
+    ctx = make_ctx(w.shape)
+    register_layer(ctx, 0, w)
+    yield w, ctx
+    ctx.close()
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 17])
+def test_layer_call_equals_separate_calls_qwen(qwen, T):
+    """pw_moe_layer (routing inside the gate_up launch up to T*k = 64, the
+    separate launches above) gives bit for bit the outputs of pw_route_permute
+    + pw_moe_ffn_bitplane, and both match the oracle."""
+    from tests.gpu_util import run_gpu
+    import oracle
+    w, ctx = qwen
+    spec = pw_synth.CONFIGS[1]
+    a = pw_synth.make_activations(spec.shape, T, pw_synth.config_seed(1), 0, 3, spec.logits, w.rank)
+    sep = run_gpu(ctx, 0, a, separate=True)
+    one = run_gpu(ctx, 0, a)
+    for key in ("idx", "w", "offsets", "sorted", "y"):
+        assert np.array_equal(one[key], sep[key]), "T=%d: %s differs from the separate calls" % (T, key)
+    compare(one, oracle.moe_layer(w, a), label="layer call T=%d" % T)
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_layer_call_equals_separate_calls_toy(T):
+    from any_precision_expert_amd.layer import register_layer
+    from tests.gpu_util import run_gpu
+    w, a = pw_synth.make_config(0)
+    if T != a.x.shape[0]:
+        spec = pw_synth.CONFIGS[0]
+        a = pw_synth.make_activations(spec.shape, T, pw_synth.config_seed(0), 0, 1, spec.logits)
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        sep = run_gpu(ctx, 0, a, separate=True)
+        one = run_gpu(ctx, 0, a)
+    finally:
+        ctx.close()
+    for key in ("idx", "w", "offsets", "sorted", "y"):
+        assert np.array_equal(one[key], sep[key]), "T=%d: %s differs from the separate calls" % (T, key)
