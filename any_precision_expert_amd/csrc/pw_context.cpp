@@ -646,8 +646,16 @@ pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t
         return fail(PW_ERR_INVALID, "pw_moe_layer: null or misaligned logits / offsets (4 B)");
     pw_status st = ffn_check(c, "pw_moe_layer", layer, x, T, idx, w, offsets, sorted, y, workspace, ws_bytes);
     if (st != PW_OK) return st;
-    const long long n = (long long)T * c->d.top_k;
-    if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign) {
+    // In-launch routing pays off only when every gate_up work unit gets a
+    // workgroup slot at once (two per CU): each routed workgroup routes the
+    // batch itself, so a launch with several rounds of workgroups would repeat
+    // it per round.
+    const pw_model_desc& d = c->d;
+    const long long n = (long long)T * d.top_k;
+    const long long gu_rows = 16LL * kGateUpRowGroups;
+    const long long gu_units = (d.inter_shared + gu_rows - 1) / gu_rows +
+                               std::min<long long>(d.num_experts, n) * ((d.inter + gu_rows - 1) / gu_rows);
+    if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus) {
         // the separate routing launch, then the FFN (identical results)
         st = pw_route_permute(c, logits, T, idx, w, offsets, sorted, stream);
         if (st != PW_OK || T == 0) return st;

@@ -217,6 +217,63 @@ __device__ __forceinline__ half8_t step_weights(const Rot<Q, PAIR>& r, int P, co
     return f;
 }
 
+// step_weights split in three so that a step's look-ups can be in flight
+// while the previous step waits and multiplies: step_codes assembles the
+// code register(s) of step P, step_lookup issues the LDS reads, step_pack
+// forms the A fragment once they have arrived.
+struct StepCodes {
+    uint32_t c0, c1;  // pair tables: c0 = the four pair codes; single: codes of registers P and 4 + P
+};
+
+struct StepRaw {
+    uint32_t v[8];  // pair tables: v[0..3] = four fp16 pairs; single: v[0..7] = eight fp16 (low halves)
+};
+
+template <int Q, bool PAIR>
+__device__ __forceinline__ StepCodes step_codes(const Rot<Q, PAIR>& r, int P, const RepMasks& M, uint32_t acc0)
+{
+    if constexpr (PAIR) {
+        uint32_t acc = acc0;
+#pragma unroll
+        for (int p = 0; p < Q; ++p) {
+            acc = and_or(r.A[p], M.m[rep_index(P + Q - 1 - p)], acc);
+            acc = and_or(r.B[p], M.m[rep_index(P + 2 * Q - 1 - p)], acc);
+        }
+        return StepCodes{rotr(acc, P), 0u};
+    } else {
+        uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+        for (int p = 0; p < Q; ++p) {
+            c0 = and_or(r.A[p], M.m[rep_index(P + Q - 1 - p)], c0);
+            c1 = and_or(r.A[p], M.m[rep_index(4 + P + Q - 1 - p)], c1);
+        }
+        return StepCodes{rotr(c0, P), rotr(c1, 4 + P)};
+    }
+}
+
+template <bool PAIR>
+__device__ __forceinline__ void step_lookup(const StepCodes& c, uint32_t lane_off, const char* lutb, StepRaw& raw)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (PAIR) {
+            raw.v[i] = *(const uint32_t*)(lutb + lut_addr(c.c0, lane_off, i));
+        } else {
+            raw.v[2 * i] = *(const uint16_t*)(lutb + lut_addr(c.c0, lane_off, i));
+            raw.v[2 * i + 1] = *(const uint16_t*)(lutb + lut_addr(c.c1, lane_off, i));
+        }
+    }
+}
+
+template <bool PAIR>
+__device__ __forceinline__ half8_t step_pack(const StepRaw& raw)
+{
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = PAIR ? raw.v[i] : (raw.v[2 * i] | (raw.v[2 * i + 1] << 16));
+    return __builtin_bit_cast(half8_t, w);
+}
+
 // step_weights for a wave-uniform unit index P known only at run time: the
 // masks 0x01010101 << s are formed with scalar shifts of P, so no register
 // array is indexed dynamically.
@@ -894,25 +951,46 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 for (int p = 0; p < Q; ++p) cur[p] = pg[d][p];
                 issue_x(min(c + KW, lastc));
                 load_pair_words<Q>(pg[d], bd, min(c + D * KW, lastc), R, lrow, kh);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                // the 8 MFMA steps s = 4u + P of the chunk (word pair u,
+                // columns 8P..8P+7), pipelined by one step: the B read and the
+                // LUT look-ups of step s + 1 are issued before step s's MFMA
+                // finishes, and step s + 1's code gather runs while step s's
+                // reads are in flight.  Two-set pair tables carry the set bit
+                // above the 2q-bit pair code (acc0).
+                auto acc0 = [&](int P) {
+                    return PAIR && NS == 2 && set ? rotl(0x01010101u << (2 * Q), P) : 0u;
+                };
+                auto b_unit = [&](int s, int row) { return slice_unit(row, te, 4 * (2 * kh + (s >> 2)) + (s & 3)); };
+                Rot<Q, PAIR> rt;
+                {
                     uint32_t W[Q];
 #pragma unroll
-                    for (int p = 0; p < Q; ++p) W[p] = cur[p][u];
-                    Rot<Q, PAIR> rt;
+                    for (int p = 0; p < Q; ++p) W[p] = cur[p][0];
                     rotate_planes<Q, PAIR>(W, rt);
+                }
+                u32x4 bh = slice4[b_unit(0, te)], bl = {0, 0, 0, 0};
+                if (MODE == 1) bl = slice4[b_unit(0, 4 + te)];
+                StepRaw raw;
+                step_lookup<PAIR>(step_codes<Q, PAIR>(rt, 0, masks, acc0(0)), lane_off, lutb, raw);
 #pragma unroll
-                    for (int P = 0; P < 4; ++P) {
-                        // two-set pair tables: set bit above the 2q-bit pair code
-                        const uint32_t acc0 = PAIR && NS == 2 && set ? rotl(0x01010101u << (2 * Q), P) : 0u;
-                        const half8 A = step_weights<Q, PAIR>(rt, P, masks, lane_off, lutb, acc0);
-                        const int g = 4 * (2 * kh + u) + P;
-                        const half8 Bh = __builtin_bit_cast(half8, slice4[slice_unit(te, te, g)]);
-                        C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bh, C, 0, 0, 0);
-                        if (MODE == 1) {
-                            const half8 Bl = __builtin_bit_cast(half8, slice4[slice_unit(4 + te, te, g)]);
-                            C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bl, C, 0, 0, 0);
+                for (int s = 0; s < 8; ++s) {
+                    StepCodes next{0u, 0u};
+                    if (s < 7) {
+                        if (s == 3) {  // word pair 1 (pair 0's rotated words are no longer needed)
+                            uint32_t W[Q];
+#pragma unroll
+                            for (int p = 0; p < Q; ++p) W[p] = cur[p][1];
+                            rotate_planes<Q, PAIR>(W, rt);
                         }
+                        next = step_codes<Q, PAIR>(rt, (s + 1) & 3, masks, acc0((s + 1) & 3));
+                    }
+                    const half8 A = step_pack<PAIR>(raw);
+                    C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bh), C, 0, 0, 0);
+                    if (MODE == 1) C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bl), C, 0, 0, 0);
+                    if (s < 7) {
+                        bh = slice4[b_unit(s + 1, te)];
+                        if (MODE == 1) bl = slice4[b_unit(s + 1, 4 + te)];
+                        step_lookup<PAIR>(next, lane_off, lutb, raw);
                     }
                 }
             }

@@ -170,8 +170,11 @@ pw_status pw_moe_ffn_bitplane(pw_ctx *ctx, int layer, const uint16_t *x, int T,
 
 /* One whole MoE layer step: pw_route_permute followed by pw_moe_ffn_bitplane,
  * with the same outputs (topk_idx, topk_w, expert_offsets, sorted_assign and
- * y, bit for bit).  For decode-sized batches (T * k <= 64 and T below the
- * prefill crossover of 256 tokens) the routing runs inside the gate_up launch:
+ * y, bit for bit).  For decode-sized batches (T * k <= 64, T below the
+ * prefill crossover of 256 tokens, and few enough gate_up work units that
+ * all of them run at once: at most two per compute unit, counting the
+ * shared expert's 64-row tiles and min(E, T*k) routed blocks' 64-row tiles)
+ * the routing runs inside the gate_up launch:
  * every workgroup with routed work routes and sorts the batch in LDS (a
  * fraction of a microsecond of its start-up) instead of waiting for a separate
  * routing launch, and one of them writes the routing outputs for the caller
