@@ -224,6 +224,132 @@ def prefill_leg(steps):
                          "frac": round(gu_tf / MFMA_F16_PEAK_TFLOPS, 4), "down_achieved": round(dn_tf, 1)}}
 
 
+BASELINE_TOKENS = (1, 4, 16)
+UNIFORM_WIDTHS = (4, 5, 8)
+
+
+def _graph_ms(run_steps, L, steps, stream):
+    """ms per step of `run_steps(L)` captured in one HIP graph and replayed."""
+    import torch
+    with torch.cuda.stream(stream):
+        run_steps(L)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run_steps(L)
+    torch.cuda.synchronize()
+    reps = max(1, steps // L)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            graph.replay()
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / (reps * L)
+
+
+def baselines_leg(w, packed, steps, L):
+    """The pages' comparison (mixed widths against uniform quantization, batch
+    1 / 4 / 16) on the same Qwen-shaped layer: the same kernels with every
+    routed block at one width (4, 5 or 8; the shared expert stays at 8), and an
+    fp16 dense expert FFN in torch (batched GEMMs over the active experts'
+    fp16 weights, the routing fixed when the graph is captured, so its time
+    excludes routing).  Steps rotate over L weight copies as in the main leg."""
+    import torch
+    import any_precision_expert_amd as pw
+    import pw_synth
+    from any_precision_expert_amd.layer import Batch
+    spec = pw_synth.CONFIGS[CFG]
+    shape, seed = spec.shape, pw_synth.config_seed(CFG)
+    H, I, Is, E, k = shape.H, shape.I, shape.I_shared, shape.E, shape.top_k
+    stream = torch.cuda.Stream()
+    acts = {T: [pw_synth.make_activations(shape, T, seed, 0, s, spec.logits, w.rank) for s in range(L)]
+            for T in BASELINE_TOKENS}
+    out = {"T=%d" % T: {} for T in BASELINE_TOKENS}
+    routing = {}
+    for variant in ["mixed"] + ["uniform_q%d" % q for q in UNIFORM_WIDTHS]:
+        qu = None if variant == "mixed" else int(variant[len("uniform_q"):])
+        ctx = pw.Context(0, L, E, H, I, k, Is, keep_host_masters=False)
+        wq = np.zeros((E, 2), dtype=int)
+        for (e, m), (planes, luts, qm) in packed.items():
+            q = qm if (qu is None or e == pw.EXPERT_SHARED) else qu
+            if e != pw.EXPERT_SHARED:
+                wq[e, m] = q
+            for l in range(L):
+                ctx.register_block(l, e, m, planes, luts, q)
+        for T in BASELINE_TOKENS:
+            batches = []
+            for l in range(L):
+                b = Batch(ctx, T)
+                b.load(acts[T][l].logits, acts[T][l].x)
+                batches.append(b)
+
+            def run_steps(n):
+                for i in range(n):
+                    batches[i % L].step(i % L, stream)
+            ms = _graph_ms(run_steps, L, steps, stream)
+            offs = [b.offsets.cpu().numpy() for b in batches]
+            if variant == "mixed":
+                routing[T] = [(b.idx.cpu().numpy(), b.w.cpu().numpy(), o) for b, o in zip(batches, offs)]
+            pb = float(np.mean([step_bytes(shape, wq, o, T)["path"] for o in offs]))
+            out["T=%d" % T][variant] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                                        "path_gbps": round(pb / (ms * 1e-3) / 1e9, 1),
+                                        "path_bytes_per_step": int(pb)}
+            del batches
+        ctx.close()
+        torch.cuda.synchronize()
+    # fp16 dense: per copy, the active experts' weights stacked [n, H, 2I] and
+    # [n, I, H]; tokens gathered per expert (padded with weight-0 rows)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for T in BASELINE_TOKENS:
+        copies = []
+        for l in range(L):
+            idx, gw, offs = routing[T][l]
+            act = [e for e in range(E) if offs[e + 1] > offs[e]]
+            tm = max(int(offs[e + 1] - offs[e]) for e in act)
+            tok = np.zeros((len(act), tm), dtype=np.int64)
+            wt = np.zeros((len(act), tm), dtype=np.float32)
+            for n, e in enumerate(act):
+                ts, js = np.nonzero(idx == e)
+                tok[n, :len(ts)] = ts
+                wt[n, :len(ts)] = gw[ts, js]
+            mk = lambda *sh: (torch.randn(*sh, device="cuda", dtype=torch.float16, generator=g) * 0.02).contiguous()
+            copies.append(dict(
+                x=torch.from_numpy(acts[T][l].x.astype(np.float16)).cuda(),
+                tok=torch.from_numpy(tok.reshape(-1)).cuda(), wt=torch.from_numpy(wt).cuda()[..., None],
+                wgu=mk(len(act), H, 2 * I), wd=mk(len(act), I, H), sgu=mk(H, 2 * Is), sd=mk(Is, H),
+                y=torch.zeros(T, H, device="cuda", dtype=torch.float32), n=len(act), tm=tm,
+                bytes=(len(act) * 3 * I * H + 3 * Is * H) * 2))
+
+        def run_dense(n):
+            for i in range(n):
+                c = copies[i % L]
+                xe = c["x"].index_select(0, c["tok"]).view(c["n"], c["tm"], H)
+                gu = torch.bmm(xe, c["wgu"])
+                h = (torch.nn.functional.silu(gu[..., :I].float()) * gu[..., I:].float()).half()
+                d = torch.bmm(h, c["wd"]).float() * c["wt"]
+                c["y"].zero_()
+                c["y"].index_add_(0, c["tok"], d.view(-1, H))
+                hs = c["x"] @ c["sgu"]
+                hs = (torch.nn.functional.silu(hs[:, :Is].float()) * hs[:, Is:].float()).half()
+                c["y"] += (hs @ c["sd"]).float()
+        ms = _graph_ms(run_dense, L, steps, stream)
+        db = float(np.mean([c["bytes"] for c in copies]))
+        out["T=%d" % T]["fp16_dense_torch"] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                                              "weight_gbps": round(db / (ms * 1e-3) / 1e9, 1),
+                                              "weight_bytes_per_step": int(db)}
+        del copies
+        torch.cuda.synchronize()
+    for T in BASELINE_TOKENS:
+        r = out["T=%d" % T]
+        log("baselines T=%d: " % T + ", ".join("%s %.4f ms" % (v, d["ms_per_step"]) for v, d in r.items()))
+    return out
+
+
 def cpu_baseline(weights, acts_list, budget_s):
     import oracle
     P = oracle.PreparedLayer(weights)
@@ -250,6 +376,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the Mixtral-shaped prefill leg")
     ap.add_argument("--prefill-steps", type=int, default=8)
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the uniform-width and fp16-dense comparison at 1 / 4 / 16 tokens")
+    ap.add_argument("--baseline-steps", type=int, default=160)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the bench, copy this many MiB device-to-device (PMC scale reference)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"))
@@ -293,9 +422,11 @@ def main():
              [(e, pw.MODULE_DOWN, w.down[e]) for e in range(shape.E)] + \
              [(pw.EXPERT_SHARED, pw.MODULE_GATE_UP, w.shared_gate_up),
               (pw.EXPERT_SHARED, pw.MODULE_DOWN, w.shared_down)]
+    packed = {}
     for e, m, b in blocks:
         planes, luts = pw.pack_bitplanes(b.code8), pw.concat_luts(b.luts)
         q = b.q if e != pw.EXPERT_SHARED else 8
+        packed[(e, m)] = (planes, luts, q)
         for l in range(L):
             ctx.register_block(l, e, m, planes, luts, q)
     log("registered %d layer copies in %.1fs, resident %.2f GB"
@@ -377,6 +508,11 @@ def main():
     tr = stored_traffic()
     traffic = int(tr["traffic_bytes"]) if tr else None  # HBM bytes per launch (PMC, scaled)
     prefill = None if args.no_prefill else prefill_leg(args.prefill_steps)
+    baselines = None
+    if not args.no_baselines:
+        ctx.close()
+        ctx = None
+        baselines = baselines_leg(w, packed, args.baseline_steps, L)
 
     out = {
         "metric": "routed tokens/s per MoE layer at mixed 3-8 bit + achieved HBM GB/s vs peak",
@@ -405,6 +541,7 @@ def main():
                      "down_achieved": round(dn_gbps, 1)},
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "baselines": baselines,
     }
     print(json.dumps(out), flush=True)
     if args.copy_calibration_mib > 0:
@@ -415,7 +552,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copy calibration: 5 x %d MiB device-to-device" % args.copy_calibration_mib)
-    ctx.close()
+    if ctx is not None:
+        ctx.close()
 
 
 if __name__ == "__main__":
