@@ -445,11 +445,25 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int ww)
 
 // One wave per token: lane l holds the logits of experts l, l+64, l+128,
 // l+192.  Each of the k rounds takes the wave-wide best entry by the key
-// (value descending, expert index ascending) with a butterfly of shuffles and
+// (value descending, expert index ascending) with DPP reduction steps and
 // retires it; the softmax runs over the k selected logits.
 __device__ __forceinline__ bool route_better(float av, int ai, float bv, int bi)
 {
     return av > bv || (av == bv && ai < bi);
+}
+
+// One DPP step of the wave-wide best: take the (value, index) the DPP pattern
+// brings in if it is better; lanes whose row is masked off keep their own.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void route_dpp_step(float& bv, int& bi)
+{
+    const float ov = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), CTRL, ROW_MASK, 0xf, false));
+    const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, ROW_MASK, 0xf, false);
+    if (oi != 0x7fffffff && (bi == 0x7fffffff || route_better(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+    }
 }
 
 // Top-k of token t's logits by one wave; lanes j < k hold the j-th expert
@@ -483,15 +497,17 @@ __device__ __forceinline__ int route_token(const float* __restrict__ logits, int
                     bi = e;
                 }
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, 64);
-                const int oi = __shfl_xor(bi, off, 64);
-                if (oi != 0x7fffffff && (bi == 0x7fffffff || route_better(ov, oi, bv, bi))) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
+            // wave-wide best by DPP steps (no LDS round trips): pairs and
+            // quads, mirrored halves of 8, mirrored rows of 16, then rows 0 / 2
+            // into 1 / 3 and row 1 into 2 / 3; lane 63 ends with the best
+            route_dpp_step<0xB1, 0xf>(bv, bi);   // quad_perm [1,0,3,2]
+            route_dpp_step<0x4E, 0xf>(bv, bi);   // quad_perm [2,3,0,1]
+            route_dpp_step<0x141, 0xf>(bv, bi);  // row_half_mirror
+            route_dpp_step<0x140, 0xf>(bv, bi);  // row_mirror
+            route_dpp_step<0x142, 0xa>(bv, bi);  // row_bcast:15
+            route_dpp_step<0x143, 0xc>(bv, bi);  // row_bcast:31
+            bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 63));
+            bi = __builtin_amdgcn_readlane(bi, 63);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (lane + 64 * i == bi) live[i] = false;
