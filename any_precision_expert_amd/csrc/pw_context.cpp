@@ -140,15 +140,17 @@ private:
 struct HostBlock {
     bool registered = false;
     int R = 0, K = 0, q = 0;
+    int S = 0;       // LUT slots
     int64_t pw = 0;  // words per plane
     void* dplanes[8] = {};
     void* dlut = nullptr;
     uint32_t* hplanes = nullptr;  // pinned master: 8 planes
-    uint16_t* hluts = nullptr;    // pinned master: LUT_3..LUT_8
+    uint32_t* hluts = nullptr;    // pinned master: LUT_3..LUT_8, each in the device slot layout
 };
 
-size_t lut_bytes(int R, int q) { return (size_t)R * ((size_t)1 << q) * 2; }
-size_t lut_offset_halves(int R, int q) { return (size_t)R * (((size_t)1 << q) - 8); }
+// device LUT_q in the slot layout, and its offset in the host master (words)
+size_t lut_bytes(int S, int q) { return (size_t)S * ((size_t)1 << q) * 4; }
+size_t lut_offset_words(int S, int q) { return (size_t)S * (((size_t)1 << q) - 8); }
 
 struct ProfRec {
     hipEvent_t a, b;
@@ -225,7 +227,8 @@ BlockDesc make_desc(const HostBlock& b)
     BlockDesc d;
     std::memset(&d, 0, sizeof d);
     for (int p = 0; p < 8; ++p) d.planes[p] = p < b.q ? (const uint32_t*)b.dplanes[p] : nullptr;
-    d.lut = (const uint16_t*)b.dlut;
+    d.lut = (const uint32_t*)b.dlut;
+    d.slots = b.S;
     d.q = b.q;
     d.R = b.R;
     d.K = b.K;
@@ -240,7 +243,7 @@ void free_block_now(pw_ctx* c, HostBlock& b)
         c->pool.release_now(b.dplanes[p], (size_t)b.pw * 4);
         b.dplanes[p] = nullptr;
     }
-    c->pool.release_now(b.dlut, lut_bytes(b.R, b.q));
+    c->pool.release_now(b.dlut, lut_bytes(b.S, b.q));
     b.dlut = nullptr;
     if (b.hplanes) (void)hipHostFree(b.hplanes);
     if (b.hluts) (void)hipHostFree(b.hluts);
@@ -384,12 +387,13 @@ pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const 
     nb.R = R;
     nb.K = K;
     nb.q = q_init;
+    nb.S = lut_slots(R, module);
     nb.pw = plane_words(R, K);
     const size_t plane_b = (size_t)nb.pw * 4;
-    const size_t luts_b = (size_t)R * kLutHalvesPerRow * 2;
+    const size_t luts_b = lut_offset_words(nb.S, PW_QMAX + 1) * 4;  // LUT_3..LUT_8, slot layout
     auto undo = [&]() {
         for (int p = 0; p < 8; ++p) c->pool.release_now(nb.dplanes[p], plane_b);
-        c->pool.release_now(nb.dlut, lut_bytes(R, q_init));
+        c->pool.release_now(nb.dlut, lut_bytes(nb.S, q_init));
         if (nb.hplanes) (void)hipHostFree(nb.hplanes);
         if (nb.hluts) (void)hipHostFree(nb.hluts);
     };
@@ -399,7 +403,7 @@ pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const 
             return fail(PW_ERR_OOM, "pw_register_block: device plane: %s", hipGetErrorString(e));
         }
     }
-    if ((e = c->pool.alloc(lut_bytes(R, q_init), &nb.dlut)) != hipSuccess) {
+    if ((e = c->pool.alloc(lut_bytes(nb.S, q_init), &nb.dlut)) != hipSuccess) {
         undo();
         return fail(PW_ERR_OOM, "pw_register_block: device LUT: %s", hipGetErrorString(e));
     }
@@ -411,12 +415,16 @@ pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const 
             return fail(PW_ERR_OOM, "pw_register_block: pinned host master");
         }
         std::memcpy(nb.hplanes, host_planes, plane_b * 8);
-        std::memcpy(nb.hluts, host_luts, luts_b);
+        for (int q = PW_QMIN; q <= PW_QMAX; ++q)
+            convert_lut(host_luts, R, module, q, nb.hluts + lut_offset_words(nb.S, q));
     }
     for (int p = 0; p < q_init && e == hipSuccess; ++p)
         e = hipMemcpy(nb.dplanes[p], host_planes + (size_t)p * nb.pw, plane_b, hipMemcpyHostToDevice);
-    if (e == hipSuccess)
-        e = hipMemcpy(nb.dlut, host_luts + lut_offset_halves(R, q_init), lut_bytes(R, q_init), hipMemcpyHostToDevice);
+    if (e == hipSuccess) {
+        std::vector<uint32_t> lq(lut_bytes(nb.S, q_init) / 4);
+        convert_lut(host_luts, R, module, q_init, lq.data());
+        e = hipMemcpy(nb.dlut, lq.data(), lut_bytes(nb.S, q_init), hipMemcpyHostToDevice);
+    }
     if (e != hipSuccess) {
         undo();
         return hip_fail(e, "pw_register_block: copy to device");
@@ -714,7 +722,7 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
         for (auto& p : plans) {
             const HostBlock& b = c->blocks[p.id];
             for (int j = p.qo; j < p.qn; ++j) c->pool.release_now(p.planes[j], (size_t)b.pw * 4);
-            c->pool.release_now(p.lut, lut_bytes(b.R, p.qn));
+            c->pool.release_now(p.lut, lut_bytes(b.S, p.qn));
         }
     };
     for (int i : changed) {
@@ -732,7 +740,7 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
                 return fail(PW_ERR_OOM, "pw_set_committed_bits: device plane: %s", hipGetErrorString(e));
             }
         }
-        if ((e = c->pool.alloc(lut_bytes(b.R, pr.qn), &pr.lut)) != hipSuccess) {
+        if ((e = c->pool.alloc(lut_bytes(b.S, pr.qn), &pr.lut)) != hipSuccess) {
             rollback();
             return fail(PW_ERR_OOM, "pw_set_committed_bits: device LUT: %s", hipGetErrorString(e));
         }
@@ -765,7 +773,7 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
         for (int j = p.qo; j < p.qn && e == hipSuccess; ++j)
             e = hipMemcpyAsync(p.planes[j], b.hplanes + (size_t)j * b.pw, (size_t)b.pw * 4, hipMemcpyHostToDevice, xs);
         if (e == hipSuccess)
-            e = hipMemcpyAsync(p.lut, b.hluts + lut_offset_halves(b.R, p.qn), lut_bytes(b.R, p.qn),
+            e = hipMemcpyAsync(p.lut, b.hluts + lut_offset_words(b.S, p.qn), lut_bytes(b.S, p.qn),
                                hipMemcpyHostToDevice, xs);
         if (e != hipSuccess) break;
     }
@@ -816,7 +824,7 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
             b.dplanes[j] = nullptr;
         }
         for (int j = plans[i].qo; j < plans[i].qn; ++j) b.dplanes[j] = plans[i].planes[j];
-        c->pool.release_after(b.dlut, lut_bytes(b.R, b.q), updated);
+        c->pool.release_after(b.dlut, lut_bytes(b.S, b.q), updated);
         b.dlut = plans[i].lut;
         b.q = plans[i].qn;
         c->h_table[plans[i].id] = newdesc[i];
@@ -832,7 +840,7 @@ pw_status pw_debug_decode_codes(pw_ctx* c, int32_t id, uint8_t* out, pw_stream s
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
     const HostBlock& b = c->blocks[id];
-    e = launch_debug_decode(c->d_table + id, b.R, b.K, out, nullptr, (hipStream_t)stream);
+    e = launch_debug_decode(c->d_table + id, id & 1, b.R, b.K, out, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "debug decode launch");
 }
 
@@ -844,7 +852,7 @@ pw_status pw_debug_dequant(pw_ctx* c, int32_t id, uint16_t* out, pw_stream strea
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
     const HostBlock& b = c->blocks[id];
-    e = launch_debug_decode(c->d_table + id, b.R, b.K, nullptr, out, (hipStream_t)stream);
+    e = launch_debug_decode(c->d_table + id, id & 1, b.R, b.K, nullptr, out, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "debug dequant launch");
 }
 

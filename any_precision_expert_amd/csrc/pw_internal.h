@@ -13,16 +13,19 @@ constexpr int kChunkCols = 128;  // columns per plane chunk (4 words of 32)
 constexpr int kLutHalvesPerRow = 8 + 16 + 32 + 64 + 128 + 256;  // LUT_3..LUT_8
 
 // One entry of the device weight page table: a linear block at its committed
-// width q.  planes[p] is valid for p < q; lut points at LUT_q [R][2^q] fp16.
+// width q.  planes[p] is valid for p < q; lut points at LUT_q in the slot
+// layout [2^q][slots] (two rows' fp16 entries per 32-bit slot, see
+// convert_lut).
 struct alignas(128) BlockDesc {
     const uint32_t* planes[8];
-    const uint16_t* lut;
+    const uint32_t* lut;
     int32_t q;
     int32_t R;
     int32_t K;
     int32_t nchunks;  // ceil(K / 128)
     int32_t kwords;   // K / 32
-    int32_t pad[9];
+    int32_t slots;    // LUT slots (a multiple of 64)
+    int32_t pad[8];
 };
 static_assert(sizeof(BlockDesc) == 128, "page-table entry must be 128 bytes");
 
@@ -104,11 +107,17 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);  // routes first whe
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
-hipError_t launch_debug_decode(const BlockDesc* entry, int R, int K, uint8_t* codes_out,
+hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int K, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s);
 
 // Host packer (pw_pack.cpp).
 void pack_bitplanes(const uint8_t* codes, int64_t R, int64_t K, uint32_t* planes);
 int64_t plane_words(int64_t R, int64_t K);
+// Device LUT slot layout (pw_pack.cpp): slots of a block, the two rows of a
+// slot (-1 past the block), and LUT_q of the concatenated k = 3..8 host
+// arrays [R][2^k] rewritten as [2^q][slots] uint32.
+int lut_slots(int R, int module);
+void lut_slot_rows(int R, int module, int j, int* a, int* b);
+void convert_lut(const uint16_t* luts, int R, int module, int q, uint32_t* out);
 
 }  // namespace pw

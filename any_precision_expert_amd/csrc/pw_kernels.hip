@@ -315,118 +315,88 @@ __device__ __forceinline__ half8_t step_weights_u(const Rot<Q, PAIR>& r, int P, 
     return f;
 }
 
-// LUT_q of this lane's row -> LDS slots [entry][lane] (32-bit each).
-// Single (q >= 5): entry = code, low half = LUT[code].  Pair (q <= 4):
-// entry = a | b << q, value = LUT[a] | LUT[b] << 16; the single table is
-// staged first in `stage` (2^q x 64 slots) and the caller's barrier follows.
-// The NW waves share the 2^q / 8 16-byte pieces of each row.  Staging is split
+// LUT staging of a decode tile.  The block's LUT_q is stored in the slot
+// layout [2^q][S] uint32 (slot j: entries of two rows in the low and high 16
+// bits, see convert_lut); a tile of RG row groups owns NSLOT = 16 * RG
+// consecutive slots from s0.  Single tables (q >= 5, and q = 4 with RG = 4):
+// the tile's slots are copied to LDS as [entry][64 slots] (256-byte entry
+// rows, RG = 2 tiles fill slots 0..31), so a look-up address is one v_perm of
+// the code byte and the lane's byte offset 4 * slot + 2 * half.  Pair tables
+// (RG = 2: q <= 4; RG = 4: q = 3; two weights per look-up) are built in LDS
+// from the staged entries: entry a | b << q of a row holds LUT[a] |
+// LUT[b] << 16.  RG = 2 keeps the row of half h of slot s at pair slot 32 h + s;
+// RG = 4 keeps the slot and puts h above the pair code (a two-set q = 4 pair
+// table would not fit).  Global reads are coalesced (a wave reads whole 128-
+// or 256-byte runs of one entry) and LDS writes are 16 bytes per lane.  Split
 // in two so callers can put other loads between the LUT loads and their first
-// use: issue() starts every load of the wave, commit() writes LDS.  Lanes
-// whose row is past the block load row 0 (their slots are never used).
-template <int Q, int NW>
-struct LutPieces {
-    static constexpr int NC = 1 << Q;
-    static constexpr int NP = NC / 8;               // 16-byte pieces per row
-    static constexpr int PER = (NP + NW - 1) / NW;  // pieces per wave
-    u32x4 u[PER];
-
-    __device__ __forceinline__ void issue(const uint16_t* lut, int row, bool valid, int wave)
-    {
-        gu32x4p src = (gu32x4p)(uintptr_t)(lut + (size_t)(valid ? row : 0) * NC);
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (wave + j * NW < NP) u[j] = src[wave + j * NW];  // wave-uniform condition
-    }
-
-    __device__ __forceinline__ void commit(uint32_t* lds, uint32_t* stage, int lane, int wave)
-    {
-        uint32_t* single = Q <= 4 ? stage : lds;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int c8 = wave + j * NW;
-            if (c8 < NP) {
-                const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    single[((8 * c8 + i) << 6) | lane] = (w4[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-            }
-        }
-        if constexpr (Q <= 4) {
-            __syncthreads();
-            for (int e = wave; e < NC * NC; e += NW) {
-                const int ea = e & (NC - 1), eb = e >> Q;
-                lds[(e << 6) | lane] = single[(ea << 6) | lane] | (single[(eb << 6) | lane] << 16);
-            }
-        }
-    }
-};
-
-// LUT staging of the contraction for a workgroup of RG row groups (32 rows
-// each).  Slot s (0..63) of set t holds the LUT of row group 2t + s / 32, row
-// s % 32.  Single tables: [code][64 slots] 32-bit slots, set t in half t (two
-// sets share every slot, so a 128-row workgroup needs no more LDS than a
-// 64-row one); a lookup adds 2t to the slot's byte offset.  Pair tables (the
-// 32-bit slot is full): [set][a | b << q][64 slots]; the set index sits above
-// the pair code in the look-up byte.  Pair tables are used for q <= 4 with one
-// set and for q = 3 with two (a two-set q = 4 pair table would not fit).
-template <int Q, int RG>
-struct LutStage {
-    static constexpr int NS = RG / 2;
+// use: issue() starts every load of the wave, commit() writes LDS (pair
+// tables: with a barrier between staging and building; the caller's barrier
+// follows).
+template <int Q, int RG, int NT = kThreads>
+struct LutLoad {
+    static constexpr int NSLOT = 16 * RG;
     static constexpr bool PAIR = RG == 2 ? Q <= 4 : Q <= 3;
     static constexpr int NC = 1 << Q;
-    static constexpr int NP = NC / 8;                           // 16-byte pieces per row
-    static constexpr int PER = (NS * NP + kWaves - 1) / kWaves;  // pieces per lane
+    static constexpr int PPE = NSLOT / 4;         // 16-byte pieces per entry
+    static constexpr int BLOCKS = NC * PPE / 64;  // 64-piece blocks, one per wave load
+    static constexpr int NW = NT / 64;
+    static constexpr int PER = (BLOCKS + NW - 1) / NW;
+    static_assert(NC * PPE % 64 == 0, "whole 64-piece blocks");
     u32x4 u[PER];
 
-    __device__ __forceinline__ void issue(const uint16_t* lut, const int (&row)[NS], int wave)
+    __device__ __forceinline__ void issue(const uint32_t* lut, int S, int s0, int lane, int wave)
     {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int jg = wave + j * kWaves;  // wave-uniform
-            if (jg < NS * NP) {
-                const int t = jg / NP, c8 = jg - t * NP;
-                u[j] = ((gu32x4p)(uintptr_t)(lut + (size_t)row[t] * NC))[c8];
+            const int blk = wave + j * NW;  // wave-uniform
+            if (blk < BLOCKS) {
+                const int pc = blk * 64 + lane, e = pc / PPE, c = pc - e * PPE;
+                u[j] = *(gu32x4p)(uintptr_t)(lut + (size_t)e * S + s0 + 4 * c);
             }
         }
     }
 
     __device__ __forceinline__ void commit(uint32_t* lds, uint32_t* stage, int lane, int wave)
     {
+        uint32_t* dst = PAIR ? stage : lds;
+        constexpr int STRIDE = PAIR ? NSLOT : 64;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int jg = wave + j * kWaves;
-            if (jg < NS * NP) {
-                const int t = jg / NP, c8 = jg - t * NP;
-                const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t v = (w4[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-                    const int e = 8 * c8 + i;
-                    if constexpr (PAIR)
-                        stage[((t * NC + e) << 6) | lane] = v;
-                    else
-                        ((uint16_t*)lds)[(((e << 6) | lane) << 1) + t] = (uint16_t)v;
-                }
+            const int blk = wave + j * NW;
+            if (blk < BLOCKS) {
+                const int pc = blk * 64 + lane, e = pc / PPE, c = pc - e * PPE;
+                *(u32x4*)(dst + e * STRIDE + 4 * c) = u[j];
             }
         }
         if constexpr (PAIR) {
             __syncthreads();
-            for (int e = wave; e < NS * NC * NC; e += kWaves) {
-                const int t = e / (NC * NC), pe = e - t * NC * NC;
-                const int ea = pe & (NC - 1), eb = pe >> Q;
-                lds[(e << 6) | lane] = stage[((t * NC + ea) << 6) | lane] | (stage[((t * NC + eb) << 6) | lane] << 16);
+            constexpr int NPE = NC * NC;
+            auto half16 = [](uint32_t v, int h) { return (v >> (16 * h)) & 0xffffu; };
+            if constexpr (RG == 2) {
+                for (int pe = wave; pe < NPE; pe += NW) {
+                    const int h = lane >> 5, sl = lane & 31;
+                    const int a = pe & (NC - 1), b = pe >> Q;
+                    lds[(pe << 6) | lane] = half16(stage[a * NSLOT + sl], h) | (half16(stage[b * NSLOT + sl], h) << 16);
+                }
+            } else {
+                for (int x = wave; x < 2 * NPE; x += NW) {
+                    const int h = x / NPE, pe = x - h * NPE;
+                    const int a = pe & (NC - 1), b = pe >> Q;
+                    lds[(x << 6) | lane] = half16(stage[a * NSLOT + lane], h) | (half16(stage[b * NSLOT + lane], h) << 16);
+                }
             }
         }
     }
 };
 
-template <int Q, int NW>
-__device__ __forceinline__ void load_lut(uint32_t* lds, uint32_t* stage, const uint16_t* lut, int row,
-                                         bool valid, int lane, int wave)
+// LDS byte offset of a look-up for the row held in half `h` of tile slot
+// `sl` (pair tables: RG = 2 uses pair slot 32 h + sl, RG = 4 the slot with h
+// carried in the code byte).
+template <int Q, int RG>
+__device__ __forceinline__ uint32_t lut_lane_off(int sl, int h)
 {
-    LutPieces<Q, NW> lp;
-    lp.issue(lut, row, valid, wave);
-    lp.commit(lds, stage, lane, wave);
+    if constexpr (LutLoad<Q, RG>::PAIR) return (uint32_t)(RG == 2 ? 32 * h + sl : sl) * 4u;
+    return (uint32_t)sl * 4u + 2u * (uint32_t)h;
 }
 
 __device__ __forceinline__ uint4 load_planes_chunk(const uint32_t* plane, int c, int R, int row, bool valid)
@@ -817,8 +787,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     constexpr int NPART = 2;               // activation loads per lane and chunk
     constexpr int TP = MODE == 0 ? 8 : 4;  // tokens per pass
     constexpr int KW = kWaves / RG;        // waves per row group (K split)
-    constexpr int NS = RG / 2;             // LUT sets
-    constexpr bool PAIR = LutStage<Q, RG>::PAIR;
+    constexpr bool PAIR = LutLoad<Q, RG>::PAIR;
     constexpr int HR = 16 * RG;            // gate_up: h rows per tile (gate and up rows each)
     constexpr int TR = 32 * RG;            // down: output rows per tile
     const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
@@ -845,13 +814,11 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     bool rvalid;
     const int row = group_row(grp, rho, rvalid);
     const int lrow = rvalid ? row : 0;  // in-range load row
-    int lut_rows[NS];
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-        bool v;
-        const int r = group_row(2 * t + (lane >> 5), lane & 31, v);
-        lut_rows[t] = v ? r : 0;  // rows past the block stage row 0 (never used)
-    }
+    // LUT slot and half of this lane's row (slot layout: gate_up slot = h-row
+    // with gate / up in the halves; down slot 32 m + r holds rows 64 m + r and
+    // 64 m + 32 + r)
+    const int half = (MODE == 0 && RG == 4) ? grp / 2 : grp % 2;
+    const int lslot = (MODE == 0 && RG == 4) ? 32 * (grp % 2) + rho : (RG == 4 ? 32 * (grp / 2) + rho : rho);
     const int cps = (nchunks + nsplit - 1) / nsplit;
     const int c_begin = split * cps;
     const int c_end = min(nchunks, c_begin + cps);
@@ -862,8 +829,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
 
     uint32_t* slice = lds + kLutBytes / 4 + wave * kSliceWords;
     u32x4* slice4 = (u32x4*)slice;
-    const int set = grp / 2;
-    const uint32_t lane_off = (uint32_t)(32 * (grp % 2) + rho) * 4u + (PAIR ? 0u : 2u * (uint32_t)set);
+    const uint32_t lane_off = lut_lane_off<Q, RG>(lslot, half);
     const char* lutb = (const char*)lds;
     const RepMasks masks = make_masks();
 
@@ -929,8 +895,8 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
 
     // pass 0: LUT loads first, then the ring's first loads, then LUT -> LDS
     {
-        LutStage<Q, RG> ls;
-        ls.issue(bd->lut, lut_rows, wave);
+        LutLoad<Q, RG> ls;
+        ls.issue(bd->lut, bd->slots, tile * LutLoad<Q, RG>::NSLOT, lane, wave);
         set_sources(0);
         if (ntok > 0) issue_ring();
         ls.commit(lds, lds + kLutBytes / 4, lane, wave);
@@ -974,7 +940,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 // reads are in flight.  Two-set pair tables carry the set bit
                 // above the 2q-bit pair code (acc0).
                 auto acc0 = [&](int P) {
-                    return PAIR && NS == 2 && set ? rotl(0x01010101u << (2 * Q), P) : 0u;
+                    return PAIR && RG == 4 && half ? rotl(0x01010101u << (2 * Q), P) : 0u;
                 };
                 auto b_unit = [&](int s, int row) { return slice_unit(row, te, 4 * (2 * kh + (s >> 2)) + (s & 3)); };
                 Rot<Q, PAIR> rt;
@@ -1276,7 +1242,7 @@ template <int MODE, int Q>
 __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
                                               int ntok, int mtile, int ntile, uint32_t* lds)
 {
-    constexpr bool PAIR = LutStage<Q, 4>::PAIR;
+    constexpr bool PAIR = LutLoad<Q, 4>::PAIR;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int R = bd->R;
@@ -1296,22 +1262,17 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
             return row;
         }
     };
-    // LUT sets: set t holds tile rows 64 t .. 64 t + 63 in slots 0..63
-    int lut_rows[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        bool v;
-        const int r = tile_row(64 * t + lane, v);
-        lut_rows[t] = v ? r : 0;
-    }
     // decoder: thread = (tile row dr, 8-column unit dP of the step's word)
     const int dr = tid & (kPfRows - 1), dP = wave >> 1;  // dP is wave-uniform
     bool dvalid;
     const int drow = tile_row(dr, dvalid);
     const int dlrow = dvalid ? drow : 0;
-    const int set = dr >> 6;
-    const uint32_t lane_off = (uint32_t)(dr & 63) * 4u + (PAIR ? 0u : 2u * (uint32_t)set);
-    const uint32_t acc0 = PAIR && set ? rotl(0x01010101u << (2 * Q), dP) : 0u;
+    // LUT slot / half of the row (gate_up: slot = h-row, up rows in the high
+    // half; down: slot 32 m + r holds tile rows 64 m + r and 64 m + 32 + r)
+    const int half = MODE == 0 ? dr >> 6 : (dr >> 5) & 1;
+    const int lslot = MODE == 0 ? dr & 63 : 32 * (dr >> 6) + (dr & 31);
+    const uint32_t lane_off = lut_lane_off<Q, 4>(lslot, half);
+    const uint32_t acc0 = PAIR && half ? rotl(0x01010101u << (2 * Q), dP) : 0u;
     // activation loader: thread = token row tid of the tile
     const int n0 = ntile * kPfTok;
     const int te = n0 + tid < ntok ? n0 + tid : n0;
@@ -1356,8 +1317,8 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     };
 
     {
-        LutStage<Q, 4> ls;
-        ls.issue(bd->lut, lut_rows, wave);
+        LutLoad<Q, 4> ls;
+        ls.issue(bd->lut, bd->slots, mtile * LutLoad<Q, 4>::NSLOT, lane, wave);
         issue(0, 0);
         issue(1, 1);
         ls.commit(lds, lds + kPfW, lane, wave);  // pair staging in the (idle) weight tiles
@@ -1558,18 +1519,32 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a)
 
 // ---------------------------------------------------------------- debug export
 
-// Same LUT staging, gather and look-up as the FFN: one wave per 64 rows.
+// Same LUT staging, gather and look-up as the FFN: one wave per tile of 32
+// LUT slots (RG = 2 geometry: lane = half * 32 + slot, the rows of
+// lut_slot_rows), writing each row's child codes and/or decoded weights.
 template <int Q>
-__device__ void debug_block(const BlockDesc* __restrict__ bd, int R, int K, uint8_t* codes_out,
+__device__ void debug_block(const BlockDesc* __restrict__ bd, int module, int R, int K, uint8_t* codes_out,
                             uint16_t* w_out, uint32_t* lds)
 {
     const int lane = threadIdx.x;
-    const int row = blockIdx.x * 64 + lane;
-    const bool valid = row < R;
-    load_lut<Q, 1>(lds, lds + kLutBytes / 4, bd->lut, row, valid, lane, 0);
+    const int sl = lane & 31, h = lane >> 5;
+    const int j = blockIdx.x * 32 + sl;
+    int row;
+    if (module == 0) {
+        row = j < R / 2 ? j + h * (R / 2) : -1;
+    } else {
+        row = 64 * (j / 32) + 32 * h + j % 32;
+        if (row >= R) row = -1;
+    }
+    const bool valid = row >= 0;
+    {
+        LutLoad<Q, 2, 64> ls;
+        ls.issue(bd->lut, bd->slots, blockIdx.x * 32, lane, 0);
+        ls.commit(lds, lds + kLutBytes / 4, lane, 0);
+    }
     __syncthreads();
     const char* lutb = (const char*)lds;
-    const uint32_t lane_off = (uint32_t)lane * 4u;
+    const uint32_t lane_off = lut_lane_off<Q, 2>(sl, h);
     const RepMasks masks = make_masks();
     for (int c = 0; c < bd->nchunks; ++c) {
         uint4 pv[Q];
@@ -1614,17 +1589,17 @@ __device__ void debug_block(const BlockDesc* __restrict__ bd, int R, int K, uint
     }
 }
 
-__global__ void __launch_bounds__(64) debug_decode_kernel(const BlockDesc* __restrict__ bd, int R, int K,
-                                                          uint8_t* codes_out, uint16_t* w_out)
+__global__ void __launch_bounds__(64) debug_decode_kernel(const BlockDesc* __restrict__ bd, int module, int R,
+                                                          int K, uint8_t* codes_out, uint16_t* w_out)
 {
     __shared__ __align__(16) uint32_t lds[kDebugLdsWords];
     switch (bd->q) {
-        case 3: debug_block<3>(bd, R, K, codes_out, w_out, lds); break;
-        case 4: debug_block<4>(bd, R, K, codes_out, w_out, lds); break;
-        case 5: debug_block<5>(bd, R, K, codes_out, w_out, lds); break;
-        case 6: debug_block<6>(bd, R, K, codes_out, w_out, lds); break;
-        case 7: debug_block<7>(bd, R, K, codes_out, w_out, lds); break;
-        case 8: debug_block<8>(bd, R, K, codes_out, w_out, lds); break;
+        case 3: debug_block<3>(bd, module, R, K, codes_out, w_out, lds); break;
+        case 4: debug_block<4>(bd, module, R, K, codes_out, w_out, lds); break;
+        case 5: debug_block<5>(bd, module, R, K, codes_out, w_out, lds); break;
+        case 6: debug_block<6>(bd, module, R, K, codes_out, w_out, lds); break;
+        case 7: debug_block<7>(bd, module, R, K, codes_out, w_out, lds); break;
+        case 8: debug_block<8>(bd, module, R, K, codes_out, w_out, lds); break;
         default: break;
     }
 }
@@ -1706,11 +1681,11 @@ hipError_t launch_combine(const FfnArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_debug_decode(const BlockDesc* entry, int R, int K, uint8_t* codes_out, uint16_t* w_out,
-                               hipStream_t s)
+hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int K, uint8_t* codes_out,
+                               uint16_t* w_out, hipStream_t s)
 {
-    hipLaunchKernelGGL(debug_decode_kernel, dim3((R + 63) / 64), dim3(64), 0, s, entry, R, K, codes_out,
-                       w_out);
+    const int tiles = lut_slots(R, module) / 32;
+    hipLaunchKernelGGL(debug_decode_kernel, dim3(tiles), dim3(64), 0, s, entry, module, R, K, codes_out, w_out);
     return hipGetLastError();
 }
 

@@ -58,4 +58,43 @@ void pack_bitplanes(const uint8_t* codes, int64_t R, int64_t K, uint32_t* planes
     for (auto& x : th) x.join();
 }
 
+// Device LUT layout ("slot layout"): LUT_q of a block as [2^q][S] uint32,
+// where slot j holds the entries of two rows, row_a(j) in the low and
+// row_b(j) in the high 16 bits.  gate_up pairs h-row i's gate row i with its
+// up row I + i; down pairs row 64 m + r with row 64 m + 32 + r (r < 32).  S is
+// rounded up to a multiple of 64; slots past the block hold zeros.  A decode
+// tile of 16 * RG slots is then one contiguous run of 64 * RG bytes per entry.
+int lut_slots(int R, int module)
+{
+    const int s = module == 0 ? R / 2 : (R + 63) / 64 * 32;
+    return (s + 63) / 64 * 64;
+}
+
+void lut_slot_rows(int R, int module, int j, int* a, int* b)
+{
+    if (module == 0) {
+        *a = j < R / 2 ? j : -1;
+        *b = j < R / 2 ? R / 2 + j : -1;
+    } else {
+        const int ra = 64 * (j / 32) + j % 32;
+        *a = ra < R ? ra : -1;
+        *b = ra + 32 < R ? ra + 32 : -1;
+    }
+}
+
+void convert_lut(const uint16_t* luts, int R, int module, int q, uint32_t* out)
+{
+    const int S = lut_slots(R, module), nc = 1 << q;
+    const uint16_t* lq = luts + (size_t)R * (nc - 8);  // LUT_q [R][2^q] in the concatenated k = 3..8 arrays
+    for (int j = 0; j < S; ++j) {
+        int a, b;
+        lut_slot_rows(R, module, j, &a, &b);
+        for (int e = 0; e < nc; ++e) {
+            const uint32_t lo = a >= 0 ? lq[(size_t)a * nc + e] : 0u;
+            const uint32_t hi = b >= 0 ? lq[(size_t)b * nc + e] : 0u;
+            out[(size_t)e * S + j] = lo | (hi << 16);
+        }
+    }
+}
+
 }  // namespace pw
