@@ -28,10 +28,17 @@ LUT_HALVES_PER_ROW = sum(1 << k for k in range(QMIN, QMAX + 1))
 EXPORTS = (
     "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
     "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
-    "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
+    "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_routing_mass_enable", "pw_routing_mass_reset",
+    "pw_routing_mass_read", "pw_plan_widths", "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
     "pw_resident_bytes", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
     "pw_profile_read",
 )
+
+
+class PlanParams(ctypes.Structure):
+    """pw_plan_params: width floors, hot-expert threshold and multiplier."""
+    _fields_ = [("q_min", ctypes.c_int), ("q_max", ctypes.c_int), ("hot_floor", ctypes.c_int),
+                ("hot_share", ctypes.c_double), ("hot_mult", ctypes.c_double), ("mass_eps", ctypes.c_double)]
 
 
 class PwError(RuntimeError):
@@ -72,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.pw_route_permute.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
         L.pw_moe_ffn_bitplane.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pw_moe_layer.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pw_routing_mass_enable.argtypes = [vp, ctypes.c_int]
+        L.pw_routing_mass_reset.argtypes = [vp, vp]
+        L.pw_routing_mass_read.argtypes = [vp, vp, vp]
+        L.pw_plan_widths.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                     ctypes.POINTER(PlanParams), i64, vp, ctypes.POINTER(i64)]
         L.pw_set_committed_bits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
         L.pw_get_committed_bits.argtypes = [vp, i32, ctypes.POINTER(i32)]
         L.pw_block_id.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -234,6 +246,19 @@ class Context:
                                   _ptr(offsets), _ptr(sorted_assign), _ptr(y), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
 
+    def routing_mass_enable(self, on: bool = True) -> None:
+        _check(lib().pw_routing_mass_enable(self.h, 1 if on else 0))
+
+    def routing_mass_reset(self, stream=None) -> None:
+        _check(lib().pw_routing_mass_reset(self.h, _stream(stream)))
+
+    def routing_mass(self, stream=None) -> np.ndarray:
+        """The accumulated routing mass [L][E] (fp64) after the work on `stream`."""
+        d = self.desc
+        out = np.zeros((d.num_layers, d.num_experts), dtype=np.float64)
+        _check(lib().pw_routing_mass_read(self.h, out.ctypes.data_as(ctypes.c_void_p), _stream(stream)))
+        return out
+
     # test exports and profiling ----------------------------------------
     def debug_decode_codes(self, block_id: int, out, stream=None) -> None:
         _check(lib().pw_debug_decode_codes(self.h, block_id, _ptr(out), _stream(stream)))
@@ -249,3 +274,22 @@ class Context:
         n = ctypes.c_int64()
         _check(lib().pw_profile_read(self.h, kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
         return float(ms.value), int(n.value)
+
+
+def plan_widths(H: int, I: int, q_cur: np.ndarray, mass: np.ndarray, sensitivity: np.ndarray,
+                byte_target: int, q_min: int = 3, q_max: int = 8, hot_floor: int = 6, hot_share: float = 0.1,
+                hot_mult: float = 4.0, mass_eps: float = 1e-3):
+    """pw_plan_widths: new widths [L][E][2] (uint8) and the routed blocks'
+    bytes at those widths.  q_cur: [L][E][2]; mass: [L][E]; sensitivity:
+    [L][E][2]."""
+    q_cur = np.ascontiguousarray(q_cur, dtype=np.uint8)
+    L, E = q_cur.shape[0], q_cur.shape[1]
+    mass = np.ascontiguousarray(mass, dtype=np.float64).reshape(L, E)
+    sens = np.ascontiguousarray(sensitivity, dtype=np.float32).reshape(L, E, 2)
+    out = np.zeros_like(q_cur)
+    total = ctypes.c_int64(0)
+    p = PlanParams(q_min, q_max, hot_floor, hot_share, hot_mult, mass_eps)
+    _check(lib().pw_plan_widths(L, E, H, I, q_cur.ctypes.data_as(ctypes.c_void_p), mass.ctypes.data_as(ctypes.c_void_p),
+                                sens.ctypes.data_as(ctypes.c_void_p), ctypes.byref(p), int(byte_target),
+                                out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(total)))
+    return out, int(total.value)

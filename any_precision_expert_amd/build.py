@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpw.so")
-SOURCES = ["pw_kernels.hip", "pw_context.cpp", "pw_pack.cpp"]
+SOURCES = ["pw_kernels.hip", "pw_context.cpp", "pw_pack.cpp", "pw_planner.cpp"]
 ARCH = "gfx950"
 
 

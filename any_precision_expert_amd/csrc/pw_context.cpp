@@ -158,6 +158,11 @@ struct ProfRec {
 
 }  // namespace
 
+namespace pw {
+// error path of the host planner (pw_planner.cpp): the thread-local message
+pw_status plan_fail(const char* msg) { return fail(PW_ERR_INVALID, "%s", msg); }
+}  // namespace pw
+
 struct pw_ctx {
     int device = 0;
     pw_model_desc d{};
@@ -175,6 +180,8 @@ struct pw_ctx {
     std::vector<Staging> staging;
     std::vector<hipEvent_t> events;  // owned events (released at destroy)
     int num_cus = 256;  // compute units of the device (decode tile schedule)
+    double* d_mass = nullptr;  // routing-mass accumulator [L][E] fp64 (pw_routing_mass_enable)
+    bool mass_on = false;
     bool profiling = false;
     std::map<std::string, std::vector<ProfRec>> prof;
     std::vector<hipEvent_t> prof_pool;
@@ -361,6 +368,7 @@ pw_status pw_destroy(pw_ctx* c)
     for (auto ev : c->events) (void)hipEventDestroy(ev);
     c->pool.clear();
     (void)hipFree(c->d_table);
+    if (c->d_mass) (void)hipFree(c->d_mass);
     delete c;
     return ok();
 }
@@ -538,6 +546,7 @@ struct LayerRoute {
     float* w;
     int32_t* offsets;
     int32_t* sorted;
+    double* mass;  // this layer's routing-mass row, or null
 };
 
 // Enqueues the FFN of checked arguments (T > 0).
@@ -612,9 +621,11 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
             a.w_out = route->w;
             a.offsets_out = route->offsets;
             a.sorted_out = route->sorted;
+            a.mass = route->mass;
         }
         if ((e = launch_gate_up(a, s)) != hipSuccess) return hip_fail(e, "gate_up launch");
         a.logits = nullptr;
+        a.mass = nullptr;
     }
     {
         ProfScope ps(c, "down", s);
@@ -663,14 +674,60 @@ pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t
     const long long gu_rows = 16LL * kGateUpRowGroups;
     const long long gu_units = (d.inter_shared + gu_rows - 1) / gu_rows +
                                std::min<long long>(d.num_experts, n) * ((d.inter + gu_rows - 1) / gu_rows);
+    double* mass = c->mass_on ? c->d_mass + (size_t)layer * d.num_experts : nullptr;
     if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus) {
         // the separate routing launch, then the FFN (identical results)
         st = pw_route_permute(c, logits, T, idx, w, offsets, sorted, stream);
         if (st != PW_OK || T == 0) return st;
+        if (mass) {
+            const hipError_t e = launch_routing_mass(offsets, sorted, w, d.num_experts, mass, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "routing mass launch");
+        }
         return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, nullptr);
     }
-    const LayerRoute r{logits, idx, w, offsets, sorted};
+    const LayerRoute r{logits, idx, w, offsets, sorted, mass};
     return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, &r);
+}
+
+pw_status pw_routing_mass_enable(pw_ctx* c, int on)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_routing_mass_enable: null context");
+    if (on && !c->d_mass) {
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
+        double* p = nullptr;
+        if ((e = hipMalloc((void**)&p, bytes)) != hipSuccess) return fail(PW_ERR_OOM, "pw_routing_mass_enable: %s", hipGetErrorString(e));
+        if ((e = hipMemset(p, 0, bytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "pw_routing_mass_enable: zero");
+        }
+        c->d_mass = p;
+    }
+    c->mass_on = on != 0;
+    return ok();
+}
+
+pw_status pw_routing_mass_reset(pw_ctx* c, pw_stream stream)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_routing_mass_reset: null context");
+    if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_reset: routing mass was never enabled");
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    e = launch_fill_f64(c->d_mass, (int64_t)c->d.num_layers * c->d.num_experts, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "routing mass reset launch");
+}
+
+pw_status pw_routing_mass_read(pw_ctx* c, double* host_out, pw_stream stream)
+{
+    if (!c || !host_out) return fail(PW_ERR_INVALID, "pw_routing_mass_read: null pointer");
+    if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_read: routing mass was never enabled");
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
+    e = hipMemcpyAsync(host_out, c->d_mass, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "pw_routing_mass_read: copy");
 }
 
 pw_status pw_get_committed_bits(const pw_ctx* c, int32_t id, int32_t* q_out)

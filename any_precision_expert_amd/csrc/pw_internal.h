@@ -63,6 +63,8 @@ struct FfnArgs {
     float* w_out;
     int32_t* offsets_out;
     int32_t* sorted_out;
+    // routing-mass accumulator row of this layer ([E] fp64) or null
+    double* mass;
 };
 
 // Most assignments (T * k) a gate_up launch routes by itself.
@@ -107,6 +109,11 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);  // routes first whe
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
+// mass[e] += sum of w[sorted[p]] over p in [offsets[e], offsets[e+1]), fp64 in
+// that order (one workgroup)
+hipError_t launch_routing_mass(const int32_t* offsets, const int32_t* sorted, const float* w, int E, double* mass,
+                               hipStream_t s);
+hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s);
 hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int K, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s);
 

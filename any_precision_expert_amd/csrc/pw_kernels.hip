@@ -1087,6 +1087,35 @@ __device__ __forceinline__ SlotExpert find_slot(const int32_t* offsets, const in
     return SlotExpert{-1, 0, 0};
 }
 
+// Routing mass of one step (PagedWeight pages, Core components 2: online
+// routing statistics): expert e's gate weights summed in fp64 in sorted
+// (ascending assignment) order, added to mass[e].  Threads take experts;
+// offsets, sorted and w may be global memory or LDS.
+__device__ __forceinline__ void add_routing_mass(const int32_t* offsets, const int32_t* sorted, const float* w,
+                                                 int E, double* mass)
+{
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int p0 = offsets[e], p1 = offsets[e + 1];
+        if (p1 <= p0) continue;
+        double s = 0.0;
+        for (int p = p0; p < p1; ++p) s += (double)w[sorted[p]];
+        mass[e] += s;
+    }
+}
+
+__global__ void __launch_bounds__(256) routing_mass_kernel(const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ sorted,
+                                                           const float* __restrict__ w, int E, double* mass)
+{
+    add_routing_mass(offsets, sorted, w, E, mass);
+}
+
+__global__ void __launch_bounds__(256) fill_f64_kernel(double* p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0;
+}
+
 // Routing of the whole batch inside a gate_up workgroup (n = T * k <= 64):
 // the waves route the tokens, wave 0 sorts the assignments.  LDS layout of rt
 // (words): idx [64] | w [64] | offsets [257] | sorted [64] | cnt [256] | base [256].
@@ -1157,6 +1186,7 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
                     a.sorted_out[i] = rt[kRtSorted + i];
                 }
                 for (int i = threadIdx.x; i <= a.E; i += kThreads) a.offsets_out[i] = rt[kRtOff + i];
+                if (a.mass) add_routing_mass(rt + kRtOff, rt + kRtSorted, (const float*)rt + kRtW, a.E, a.mass);
             }
             se = find_slot(rt + kRtOff, qw, a.E, slot);
             tokreg = rt[kRtSorted + min(se.p0 + (int)(threadIdx.x & 63), n - 1)];
@@ -1678,6 +1708,20 @@ hipError_t launch_combine(const FfnArgs& a, hipStream_t s)
     const size_t n = (size_t)a.T * a.H;
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_routing_mass(const int32_t* offsets, const int32_t* sorted, const float* w, int E, double* mass,
+                               hipStream_t s)
+{
+    hipLaunchKernelGGL(routing_mass_kernel, dim3(1), dim3(256), 0, s, offsets, sorted, w, E, mass);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_f64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

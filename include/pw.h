@@ -187,6 +187,57 @@ pw_status pw_moe_layer(pw_ctx *ctx, int layer, const float *logits, const uint16
                        int32_t *sorted_assign, uint16_t *y, void *workspace, size_t ws_bytes,
                        pw_stream stream);
 
+/* Routing-mass accumulator (Core components 2: online routing statistics,
+ * the routing mass of an expert = how often and how strongly it is chosen).
+ * pw_routing_mass_enable(ctx, 1) allocates a device array mass [L][E] fp64,
+ * zeroed (synchronous, the first time only); while enabled, every
+ * pw_moe_layer call adds to mass[layer][e], for each expert e, the sum of the
+ * gate weights of the assignments routed to e in that call, summed in fp64 in
+ * sorted (ascending assignment) order.  Decode-sized calls do it inside the
+ * routing gate_up launch, others with one extra one-workgroup launch.
+ * enable(ctx, 0) stops accumulating and keeps the values.  _reset zeroes the
+ * array (asynchronous on `stream`, a fill kernel, so it may be captured);
+ * _read copies it to host_out [L * E] after the work enqueued on `stream` and
+ * waits for that copy.  Errors: INVALID, OOM, HIP, STATE (reset / read before
+ * the first enable). */
+pw_status pw_routing_mass_enable(pw_ctx *ctx, int on);
+pw_status pw_routing_mass_reset(pw_ctx *ctx, pw_stream stream);
+pw_status pw_routing_mass_read(pw_ctx *ctx, double *host_out, pw_stream stream);
+
+/* Parameters of pw_plan_widths. */
+typedef struct {
+    int q_min;        /* lowest width of a block (3..8) */
+    int q_max;        /* highest width (q_min..8) */
+    int hot_floor;    /* lowest width of a hot expert's blocks */
+    double hot_share; /* an expert is hot if its share of its layer's routing mass is >= hot_share (0: none) */
+    double hot_mult;  /* damage multiplier of a hot expert's blocks */
+    double mass_eps;  /* added to every share, so unrouted experts still count */
+} pw_plan_params;
+
+/* Quality-aware width planner (Core components 2: greedy lowest damage per
+ * byte under a memory target; hot experts protected by a higher width floor
+ * and a damage multiplier).  Pure host function, no context or device.
+ * Routed blocks b = (layer * E + expert) * 2 + module (gate_up R = 2I x K = H,
+ * down R = H x K = I) at width q hold q planes plus LUT_q as the library
+ * stores them (q * 4 * ceil(K/128) * R * 4 bytes of planes, S * 2^q * 4 of LUT
+ * with S the LUT slots of the block).  With share = mass[l][e] / sum over the
+ * layer (0 if the layer has none) and hot = share >= hot_share, block b's
+ * weight is sensitivity[b] * (share + mass_eps) * (hot ? hot_mult : 1), its
+ * floor max(q_min, hot_floor) if hot else q_min, and lowering it from q to
+ * q - 1 adds damage weight * 3 * 4^(8 - q) (error power about 4x per dropped
+ * bit).  Steps: clamp q_cur into [floor, q_max]; if the total bytes exceed
+ * byte_target, repeatedly lower the block with the least damage per byte
+ * saved (ties: lower b) until the total fits or every block is at its floor;
+ * otherwise repeatedly raise the block with the most damage removed per byte
+ * added among those that still fit the target (ties: lower b).  The planner
+ * ignores shared experts (their bytes are outside byte_target).
+ * q_cur, q_out: uint8 [L][E][2]; mass: [L][E]; sensitivity: [L][E][2], >= 0;
+ * bytes_out (may be NULL): total bytes of the routed blocks at q_out.
+ * Errors: INVALID. */
+pw_status pw_plan_widths(int L, int E, int H, int I, const uint8_t *q_cur, const double *mass,
+                         const float *sensitivity, const pw_plan_params *params, int64_t byte_target,
+                         uint8_t *q_out, int64_t *bytes_out);
+
 /* Change the committed width of n blocks (Core components 3: asynchronous page
  * movement; widths committed only at safe boundaries).  block_ids: host, each
  * = (layer * (E + 1) + slot) * 2 + module with slot = expert or E for the

@@ -1,0 +1,111 @@
+"""Oracle of the width planner and the routing-mass accumulator.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py): plain Python loops over
+Python floats (IEEE fp64), written from the description of the
+quality-aware runtime planner in "Technical summary: PagedWeight", Core
+components 2: the planner scores each possible width reduction by its
+damage and, when a memory target must be met, greedily takes the reductions
+with the lowest damage per byte saved; frequently routed ("hot") experts get
+a higher width floor and a damage multiplier; the routing mass of an expert
+counts how often and how strongly it is selected.  The pages' Hessian
+sensitivity is an input here and their prompt residuals are left out (both
+need trained models).  Readings (stated in the library header too):
+routing mass = sum of gate weights, per call summed in ascending assignment
+order; damage of lowering q -> q - 1 = weight * 3 * 4^(8 - q); the block
+byte model is the library's storage (q planes + LUT_q in the slot layout).
+"""
+from __future__ import annotations
+
+from typing import List, Sequence, Tuple
+
+
+def lut_slots(R: int, module: int) -> int:
+    """Slots of a block's slot-layout LUT: gate_up pairs row i with row R/2 + i,
+    down pairs rows 64m + r and 64m + 32 + r; rounded up to 64."""
+    s = R // 2 if module == 0 else (R + 63) // 64 * 32
+    return (s + 63) // 64 * 64
+
+
+def block_bytes(R: int, K: int, module: int, q: int) -> int:
+    plane = ((K + 127) // 128) * R * 4 * 4          # ceil(K/128) chunks x R rows x 4 words x 4 bytes
+    return q * plane + lut_slots(R, module) * (1 << q) * 4
+
+
+def block_shape(module: int, H: int, I: int) -> Tuple[int, int]:
+    return (2 * I, H) if module == 0 else (H, I)
+
+
+def routing_mass_add(mass_row: List[float], idx: Sequence[Sequence[int]], w: Sequence[Sequence[float]]) -> None:
+    """One call's routing mass: for each expert, the gate weights of its
+    assignments a = t * k + j in ascending a, summed from 0.0, then added to
+    the running total."""
+    T = len(idx)
+    k = len(idx[0]) if T else 0
+    per = {}
+    for a in range(T * k):
+        t, j = divmod(a, k)
+        e = int(idx[t][j])
+        per[e] = per.get(e, 0.0) + float(w[t][j])
+    for e, s in per.items():
+        mass_row[e] += s
+
+
+def plan_widths(L: int, E: int, H: int, I: int, q_cur, mass, sens, q_min: int, q_max: int, hot_floor: int,
+                hot_share: float, hot_mult: float, mass_eps: float, target: int):
+    """Greedy planner; q_cur, sens: [L][E][2]; mass: [L][E].  Returns
+    (q [L][E][2] as nested lists, total bytes of the routed blocks)."""
+    blocks = []  # (layer, expert, module, weight, floor)
+    for l in range(L):
+        tot = 0.0
+        for e in range(E):
+            tot += float(mass[l][e])
+        for e in range(E):
+            share = float(mass[l][e]) / tot if tot > 0.0 else 0.0
+            hot = hot_share > 0.0 and share >= hot_share
+            for m in range(2):
+                weight = float(sens[l][e][m]) * (share + mass_eps) * (hot_mult if hot else 1.0)
+                floor = max(q_min, hot_floor) if hot else q_min
+                blocks.append((l, e, m, weight, floor))
+    q = []
+    for (l, e, m, weight, floor) in blocks:
+        q.append(min(max(int(q_cur[l][e][m]), floor), q_max))
+
+    def nbytes(b, qq):
+        R, K = block_shape(blocks[b][2], H, I)
+        return block_bytes(R, K, blocks[b][2], qq)
+
+    def drop(b, qq):  # damage added by lowering from qq to qq - 1
+        return blocks[b][3] * (3.0 * float(4 ** (8 - qq)))
+
+    total = sum(nbytes(b, q[b]) for b in range(len(blocks)))
+    if total > target:
+        while total > target:
+            best, best_key = -1, 0.0
+            for b in range(len(blocks)):
+                if q[b] > blocks[b][4]:
+                    key = drop(b, q[b]) / float(nbytes(b, q[b]) - nbytes(b, q[b] - 1))
+                    if best < 0 or key < best_key:
+                        best, best_key = b, key
+            if best < 0:
+                break
+            total -= nbytes(best, q[best]) - nbytes(best, q[best] - 1)
+            q[best] -= 1
+    else:
+        while True:
+            best, best_key = -1, 0.0
+            for b in range(len(blocks)):
+                if q[b] < q_max:
+                    add = nbytes(b, q[b] + 1) - nbytes(b, q[b])
+                    if total + add > target:
+                        continue
+                    key = drop(b, q[b] + 1) / float(add)
+                    if best < 0 or key > best_key:
+                        best, best_key = b, key
+            if best < 0:
+                break
+            total += nbytes(best, q[best] + 1) - nbytes(best, q[best])
+            q[best] += 1
+    out = [[[0, 0] for _ in range(E)] for _ in range(L)]
+    for b, (l, e, m, _, _) in enumerate(blocks):
+        out[l][e][m] = q[b]
+    return out, total

@@ -110,6 +110,10 @@ def test_null_context_calls_are_invalid():
     assert L.pw_route_permute(None, None, 1, None, None, None, None, None) == pw.PW_ERR_INVALID
     assert L.pw_moe_ffn_bitplane(None, 0, None, 1, None, None, None, None, None, None, 0, None) == pw.PW_ERR_INVALID
     assert L.pw_moe_layer(None, 0, None, None, 1, None, None, None, None, None, None, 0, None) == pw.PW_ERR_INVALID
+    assert L.pw_routing_mass_enable(None, 1) == pw.PW_ERR_INVALID
+    assert L.pw_routing_mass_reset(None, None) == pw.PW_ERR_INVALID
+    assert L.pw_routing_mass_read(None, None, None) == pw.PW_ERR_INVALID
+    assert L.pw_plan_widths(1, 1, 32, 32, None, None, None, None, 0, None, None) == pw.PW_ERR_INVALID
     assert L.pw_set_committed_bits(None, 1, None, None, None, None) == pw.PW_ERR_INVALID
     assert L.pw_destroy(None) == pw.PW_OK
     assert L.pw_workspace_size(None, 4) == 0

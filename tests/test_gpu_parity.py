@@ -236,3 +236,51 @@ def test_layer_call_equals_separate_calls_toy(T):
         ctx.close()
     for key in ("idx", "w", "offsets", "sorted", "y"):
         assert np.array_equal(one[key], sep[key]), "T=%d: %s differs from the separate calls" % (T, key)
+
+
+# ------------------------------------------------------------------ routing mass (Core components 2)
+
+def test_routing_mass_accumulates_like_the_oracle():
+    """Mass over pw_moe_layer calls on two layers (in-launch routing at T = 16,
+    the separate launches at T = 5 with a prefill-sized T = 300) against the
+    oracle's fp64 routing; rerunning the same calls gives the same bits; reset
+    zeroes it.  Also pins the byte model the planner uses against the
+    library's own resident-byte count."""
+    import oracle
+    import oracle.plan as op
+    from any_precision_expert_amd.layer import Batch, register_layer
+    import torch
+    spec = pw_synth.CONFIGS[0]
+    shape, seed = spec.shape, pw_synth.config_seed(0)
+    w = pw_synth.make_weights(shape, seed, 0, spec.q_policy, spec.logits)
+    ctx = make_ctx(shape, layers=2)
+    try:
+        for l in range(2):
+            register_layer(ctx, l, w)
+        want_bytes = 2 * sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), m, int(b.q))
+                             for m, blocks in ((0, w.gate_up), (1, w.down)) for b in blocks)
+        assert ctx.resident_bytes() == want_bytes
+        calls = [(0, 16), (1, 16), (0, 300), (1, 5), (0, 16)]
+        runs = []
+        for rep in range(2):
+            ctx.routing_mass_enable(True)
+            ctx.routing_mass_reset()
+            expected = [[0.0] * shape.E for _ in range(2)]
+            for step, (layer, T) in enumerate(calls):
+                a = pw_synth.make_activations(shape, T, seed, layer, step, spec.logits)
+                b = Batch(ctx, T)
+                b.load(a.logits, a.x)
+                b.step(layer)
+                idx, gw = oracle.route_topk(a.logits, shape.top_k)
+                op.routing_mass_add(expected[layer], idx.tolist(), gw.tolist())
+            torch.cuda.synchronize()
+            got = ctx.routing_mass()
+            say("routing mass max |gpu - oracle| = %.3e" % np.max(np.abs(got - np.array(expected))))
+            assert np.max(np.abs(got - np.array(expected))) <= 1e-6 * sum(T for _, T in calls)
+            runs.append(got)
+        assert np.array_equal(runs[0], runs[1])
+        ctx.routing_mass_reset()
+        ctx.routing_mass_enable(False)
+        assert np.all(ctx.routing_mass() == 0.0)
+    finally:
+        ctx.close()
