@@ -96,3 +96,84 @@ def test_config4_stack_with_commit_events():
                                                               len(CHECK_LAYERS) * len(CHECK_STEPS)))
     finally:
         ctx.close()
+
+
+def test_budget_planner_stack():
+    """Three Zipf-routed layers (H=256, I=256, 16 experts, top-2, batch 8),
+    16 steps, an event every 4 steps with a routed-byte target (the bytes of
+    every block at 4, then 7, then 5 bits): the device routing mass feeds pw_plan_widths and
+    the event commits its widths.  Checks: committed widths and resident
+    bytes equal the plan, the plan fits its target, hot experts stay at or
+    above their floor, and every step matches the oracle at the widths
+    committed for it."""
+    import torch
+    import oracle
+    import oracle.plan as op
+    import any_precision_expert_amd as pw
+    from any_precision_expert_amd.layer import register_layer
+    from any_precision_expert_amd.stack import StackDriver
+    shape = pw_synth.LayerShape(H=256, I=256, E=16, top_k=2)
+    L, S, T, seed = 3, 16, 8, 4242
+    ctx = pw.Context(0, L, shape.E, shape.H, shape.I, shape.top_k, shape.I_shared, keep_host_masters=True)
+    try:
+        ws, q0, ranks = [], np.zeros((L, shape.E, 2), np.int64), []
+        for l in range(L):
+            w = pw_synth.make_weights(shape, seed, l, "zipf_tiers", "zipf")
+            register_layer(ctx, l, w)
+            q0[l] = [[g.q, d.q] for g, d in zip(w.gate_up, w.down)]
+            ws.append(w)
+            ranks.append(w.rank)
+        init = ctx.resident_bytes()
+        logits = np.zeros((S, L, T, shape.E), np.float32)
+        x = np.zeros((S, L, T, shape.H), np.float16)
+        for s in range(S):
+            for l in range(L):
+                a = pw_synth.make_activations(shape, T, seed, l, s, "zipf", ranks[l])
+                logits[s, l], x[s, l] = a.logits, a.x
+        sens = np.random.default_rng(seed).uniform(0.5, 1.5, size=(L, shape.E, 2)).astype(np.float32)
+        params = dict(q_min=3, q_max=8, hot_floor=6, hot_share=0.15, hot_mult=4.0, mass_eps=1e-3)
+        def uniform_bytes(qq):
+            return L * shape.E * sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), m, qq) for m in (0, 1))
+        assert init == sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), m, int(q0[l, e, m]))
+                           for l in range(L) for e in range(shape.E) for m in (0, 1))
+        targets = [uniform_bytes(4), uniform_bytes(7), uniform_bytes(5)]
+        drv = StackDriver(ctx, q0, logits, x, commit_every=4, byte_targets=targets, sensitivity=sens,
+                          plan_params=params)
+        mass_host = np.zeros((L, shape.E))
+        worst = [0.0]
+
+        def check(s, l):
+            drv.compute.synchronize()
+            k = shape.top_k
+            gpu = dict(idx=drv.idx[s, l].cpu().numpy(), w=drv.w[s, l].cpu().numpy(),
+                       offsets=drv.offsets[l].cpu().numpy(), sorted=drv.sorted[l].cpu().numpy()[:T * k],
+                       y=drv.y[l].cpu().numpy().astype(np.float64))
+            acts = pw_synth.Activations(x=x[s, l], logits=logits[s, l])
+            rel, _ = compare(gpu, oracle.moe_layer(_with_q(ws[l], drv.q[l]), acts), label="step %d layer %d" % (s, l))
+            worst[0] = max(worst[0], rel)
+
+        drv.run(on_layer=check)
+        torch.cuda.synchronize()
+        assert len(drv.plans) == 3
+        for (s, target, total, q), ev in zip(drv.plans, drv.events):
+            say("event before step %d: target %.2f MB, planned %.2f MB, resident %.2f MB, %d blocks changed"
+                % (s, target / 1e6, total / 1e6, ev[3] / 1e6, ev[2]))
+            assert total <= target and ev[3] == total
+            # hot experts (share of their layer's mass up to this event) keep the floor
+            for l in range(L):
+                mass_host[l] = 0.0
+                for s2 in range(s):
+                    idx, gw = oracle.route_topk(logits[s2, l], shape.top_k)
+                    row = list(mass_host[l])
+                    op.routing_mass_add(row, idx.tolist(), gw.tolist())
+                    mass_host[l] = row
+                share = mass_host[l] / mass_host[l].sum()
+                for e in np.nonzero(share >= params["hot_share"] + 1e-6)[0]:
+                    assert np.all(q[l, e] >= params["hot_floor"]), (l, e)
+        for l in range(L):
+            for e in range(shape.E):
+                for m in (0, 1):
+                    assert ctx.committed_bits(ctx.block_id(l, e, m)) == drv.q[l, e, m]
+        say("worst rel_l2 %.3e over %d checks" % (worst[0], S * L))
+    finally:
+        ctx.close()
