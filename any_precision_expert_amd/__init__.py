@@ -29,10 +29,14 @@ EXPORTS = (
     "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
     "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
     "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_routing_mass_enable", "pw_routing_mass_reset",
-    "pw_routing_mass_read", "pw_plan_widths", "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
+    "pw_routing_mass_read", "pw_plan_widths", "pw_request_widths", "pw_commit_ready", "pw_block_state",
+    "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
     "pw_resident_bytes", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
     "pw_profile_read",
 )
+
+
+PAGE_RESIDENT, PAGE_IN_TRANSFER, PAGE_READY = 0, 1, 2
 
 
 class PlanParams(ctypes.Structure):
@@ -79,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.pw_route_permute.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
         L.pw_moe_ffn_bitplane.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pw_moe_layer.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pw_request_widths.argtypes = [vp, ctypes.c_int, vp, vp, vp]
+        L.pw_commit_ready.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int)]
+        L.pw_block_state.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.pw_routing_mass_enable.argtypes = [vp, ctypes.c_int]
         L.pw_routing_mass_reset.argtypes = [vp, vp]
         L.pw_routing_mass_read.argtypes = [vp, vp, vp]
@@ -245,6 +252,24 @@ class Context:
         _check(lib().pw_moe_layer(self.h, layer, _ptr(logits), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
                                   _ptr(offsets), _ptr(sorted_assign), _ptr(y), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
+
+    def request_widths(self, block_ids, q_desired, copy_stream=None) -> None:
+        ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+        q = np.ascontiguousarray(q_desired, dtype=np.uint8)
+        assert ids.shape == q.shape
+        _check(lib().pw_request_widths(self.h, int(ids.size), ids.ctypes.data_as(ctypes.c_void_p),
+                                       q.ctypes.data_as(ctypes.c_void_p), _stream(copy_stream)))
+
+    def commit_ready(self, compute_stream=None) -> int:
+        n = ctypes.c_int(0)
+        _check(lib().pw_commit_ready(self.h, _stream(compute_stream), ctypes.byref(n)))
+        return n.value
+
+    def block_state(self, block_id: int):
+        """(committed q, desired q, state) with state PAGE_RESIDENT / PAGE_IN_TRANSFER / PAGE_READY."""
+        qc, qd, st = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pw_block_state(self.h, block_id, ctypes.byref(qc), ctypes.byref(qd), ctypes.byref(st)))
+        return qc.value, qd.value, st.value
 
     def routing_mass_enable(self, on: bool = True) -> None:
         _check(lib().pw_routing_mass_enable(self.h, 1 if on else 0))

@@ -148,6 +148,16 @@ struct HostBlock {
     uint32_t* hluts = nullptr;    // pinned master: LUT_3..LUT_8, each in the device slot layout
 };
 
+// A width change of one block: its new slabs (planes q_old..q_new-1 and
+// LUT_{q_new}) and the event behind their copies.
+struct WidthChange {
+    int id;
+    int qo, qn;
+    void* planes[8];
+    void* lut;
+    hipEvent_t copied;
+};
+
 // device LUT_q in the slot layout, and its offset in the host master (words)
 size_t lut_bytes(int S, int q) { return (size_t)S * ((size_t)1 << q) * 4; }
 size_t lut_offset_words(int S, int q) { return (size_t)S * (((size_t)1 << q) - 8); }
@@ -180,6 +190,7 @@ struct pw_ctx {
     std::vector<Staging> staging;
     std::vector<hipEvent_t> events;  // owned events (released at destroy)
     int num_cus = 256;  // compute units of the device (decode tile schedule)
+    std::map<int, WidthChange> pending;  // width requests whose commit has not happened
     double* d_mass = nullptr;  // routing-mass accumulator [L][E] fp64 (pw_routing_mass_enable)
     bool mass_on = false;
     bool profiling = false;
@@ -386,6 +397,7 @@ pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const 
     if (id < 0) return fail(PW_ERR_INVALID, "pw_register_block: (layer %d, expert %d, module %d) out of range",
                             layer, expert, module);
     if (!host_planes || !host_luts) return fail(PW_ERR_INVALID, "pw_register_block: null pointer");
+    if (c->pending.count(id)) return fail(PW_ERR_STATE, "pw_register_block: block has a width request in flight");
     if (q_init < PW_QMIN || q_init > PW_QMAX) return fail(PW_ERR_INVALID, "pw_register_block: q_init %d not in 3..8", q_init);
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
@@ -740,91 +752,47 @@ pw_status pw_get_committed_bits(const pw_ctx* c, int32_t id, int32_t* q_out)
 
 int64_t pw_resident_bytes(const pw_ctx* c) { return c ? c->pool.resident() : 0; }
 
-pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint8_t* q_new, pw_stream compute,
-                                pw_stream copy)
-{
-    if (!c) return fail(PW_ERR_INVALID, "pw_set_committed_bits: null context");
-    if (n < 0) return fail(PW_ERR_INVALID, "pw_set_committed_bits: n < 0");
-    if (n == 0) return ok();
-    if (!ids || !q_new) return fail(PW_ERR_INVALID, "pw_set_committed_bits: null pointer");
-    std::unordered_set<int32_t> seen;
-    for (int i = 0; i < n; ++i) {
-        const int32_t id = ids[i];
-        if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
-            return fail(PW_ERR_INVALID, "pw_set_committed_bits: block id %d not registered", id);
-        if (q_new[i] < PW_QMIN || q_new[i] > PW_QMAX)
-            return fail(PW_ERR_INVALID, "pw_set_committed_bits: q %d not in 3..8", (int)q_new[i]);
-        if (!seen.insert(id).second) return fail(PW_ERR_INVALID, "pw_set_committed_bits: duplicate block id %d", id);
-    }
-    std::vector<int> changed;
-    for (int i = 0; i < n; ++i)
-        if (q_new[i] != c->blocks[ids[i]].q) changed.push_back(i);
-    if (changed.empty()) return ok();
-    if (!c->d.keep_host_masters)
-        return fail(PW_ERR_STATE, "pw_set_committed_bits: the context keeps no host masters (keep_host_masters = 0)");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    hipStream_t cs = (hipStream_t)compute, xs = (hipStream_t)copy;
+// Width changes in two phases.  prepare: new slabs for planes q_old..q_new-1
+// and LUT_{q_new}, their copies from the pinned masters on the copy stream,
+// an event behind them.  apply: the page-table entries on the compute stream
+// (stream-ordered, so work enqueued earlier keeps the old widths), old slabs
+// recycled after that update.
 
-    // 1. allocate everything first so a failure changes nothing
-    struct Plan {
-        int id;
-        int qo, qn;
-        void* planes[8];
-        void* lut;
-    };
-    std::vector<Plan> plans;
-    plans.reserve(changed.size());
-    auto rollback = [&]() {
-        for (auto& p : plans) {
-            const HostBlock& b = c->blocks[p.id];
-            for (int j = p.qo; j < p.qn; ++j) c->pool.release_now(p.planes[j], (size_t)b.pw * 4);
-            c->pool.release_now(p.lut, lut_bytes(b.S, p.qn));
-        }
-    };
-    for (int i : changed) {
-        Plan p;
+static void release_prepared(pw_ctx* c, const std::vector<WidthChange>& plans)
+{
+    for (const auto& p : plans) {
+        const HostBlock& b = c->blocks[p.id];
+        for (int j = p.qo; j < p.qn; ++j) c->pool.release_now(p.planes[j], (size_t)b.pw * 4);
+        c->pool.release_now(p.lut, lut_bytes(b.S, p.qn));
+    }
+}
+
+static pw_status prepare_changes(pw_ctx* c, const char* fn, const std::vector<std::pair<int, int>>& todo,
+                                 hipStream_t xs, std::vector<WidthChange>& plans)
+{
+    hipError_t e = hipSuccess;
+    plans.clear();
+    plans.reserve(todo.size());
+    for (const auto& t : todo) {
+        WidthChange p;
         std::memset(&p, 0, sizeof p);
-        p.id = ids[i];
+        p.id = t.first;
         const HostBlock& b = c->blocks[p.id];
         p.qo = b.q;
-        p.qn = q_new[i];
+        p.qn = t.second;
         plans.push_back(p);
-        Plan& pr = plans.back();
+        WidthChange& pr = plans.back();
         for (int j = pr.qo; j < pr.qn; ++j) {
             if ((e = c->pool.alloc((size_t)b.pw * 4, &pr.planes[j])) != hipSuccess) {
-                rollback();
-                return fail(PW_ERR_OOM, "pw_set_committed_bits: device plane: %s", hipGetErrorString(e));
+                release_prepared(c, plans);
+                return fail(PW_ERR_OOM, "%s: device plane: %s", fn, hipGetErrorString(e));
             }
         }
         if ((e = c->pool.alloc(lut_bytes(b.S, pr.qn), &pr.lut)) != hipSuccess) {
-            rollback();
-            return fail(PW_ERR_OOM, "pw_set_committed_bits: device LUT: %s", hipGetErrorString(e));
+            release_prepared(c, plans);
+            return fail(PW_ERR_OOM, "%s: device LUT: %s", fn, hipGetErrorString(e));
         }
     }
-    // pinned staging for the page-table entries
-    pw_ctx::Staging st{nullptr, plans.size(), nullptr};
-    for (size_t i = 0; i < c->staging.size(); ++i) {
-        if (c->staging[i].n >= plans.size() && hipEventQuery(c->staging[i].ev) == hipSuccess) {
-            st = c->staging[i];
-            c->staging.erase(c->staging.begin() + i);
-            break;
-        }
-    }
-    if (!st.p) {
-        if (hipHostMalloc((void**)&st.p, sizeof(BlockDesc) * plans.size(), hipHostMallocDefault) != hipSuccess) {
-            (void)hipGetLastError();
-            rollback();
-            return fail(PW_ERR_OOM, "pw_set_committed_bits: pinned staging");
-        }
-        st.n = plans.size();
-        if ((e = new_event(c, &st.ev)) != hipSuccess) {
-            (void)hipHostFree(st.p);
-            rollback();
-            return hip_fail(e, "hipEventCreate");
-        }
-    }
-    // 2. copies of raised planes and every new LUT on the copy stream
     for (auto& p : plans) {
         const HostBlock& b = c->blocks[p.id];
         for (int j = p.qo; j < p.qn && e == hipSuccess; ++j)
@@ -837,15 +805,39 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
     hipEvent_t copied = nullptr;
     if (e == hipSuccess) e = new_event(c, &copied);
     if (e == hipSuccess) e = hipEventRecord(copied, xs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(cs, copied, 0);
     if (e != hipSuccess) {
         // copies may be in flight into the new slabs: wait before recycling them
         (void)hipStreamSynchronize(xs);
-        rollback();
-        c->staging.push_back(st);
-        return hip_fail(e, "pw_set_committed_bits: enqueue copies");
+        release_prepared(c, plans);
+        return hip_fail(e, "enqueue plane / LUT copies");
     }
-    // 3. page-table update, stream-ordered on the compute stream
+    for (auto& p : plans) p.copied = copied;
+    return ok();
+}
+
+static pw_status apply_changes(pw_ctx* c, std::vector<WidthChange>& plans, hipStream_t cs)
+{
+    hipError_t e = hipSuccess;
+    // pinned staging for the page-table entries
+    pw_ctx::Staging st{nullptr, plans.size(), nullptr};
+    for (size_t i = 0; i < c->staging.size(); ++i) {
+        if (c->staging[i].n >= plans.size() && hipEventQuery(c->staging[i].ev) == hipSuccess) {
+            st = c->staging[i];
+            c->staging.erase(c->staging.begin() + i);
+            break;
+        }
+    }
+    if (!st.p) {
+        if (hipHostMalloc((void**)&st.p, sizeof(BlockDesc) * plans.size(), hipHostMallocDefault) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(PW_ERR_OOM, "pinned staging");
+        }
+        st.n = plans.size();
+        if ((e = new_event(c, &st.ev)) != hipSuccess) {
+            (void)hipHostFree(st.p);
+            return hip_fail(e, "hipEventCreate");
+        }
+    }
     std::vector<BlockDesc> newdesc(plans.size());
     for (size_t i = 0; i < plans.size(); ++i) {
         HostBlock nb = c->blocks[plans[i].id];
@@ -865,15 +857,13 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
     if (e == hipSuccess) e = hipEventRecord(st.ev, cs);
     if (e != hipSuccess) {
         (void)hipStreamSynchronize(cs);
-        (void)hipStreamSynchronize(xs);
         // the device table may hold some new entries: restore the old ones
         for (auto& p : plans) (void)hipMemcpy(c->d_table + p.id, &c->h_table[p.id], sizeof(BlockDesc), hipMemcpyHostToDevice);
-        rollback();
         c->staging.push_back(st);
-        return hip_fail(e, "pw_set_committed_bits: page-table update");
+        return hip_fail(e, "page-table update");
     }
     c->staging.push_back(st);
-    // 4. commit on the host; old slabs are recycled after `updated`
+    // commit on the host; old slabs are recycled after `updated`
     for (size_t i = 0; i < plans.size(); ++i) {
         HostBlock& b = c->blocks[plans[i].id];
         for (int j = plans[i].qn; j < plans[i].qo; ++j) {
@@ -886,6 +876,109 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
         b.q = plans[i].qn;
         c->h_table[plans[i].id] = newdesc[i];
     }
+    return ok();
+}
+
+// Shared argument checks: registered ids, widths in range, no duplicates, no
+// block with a request in flight.  Collects the blocks whose width changes.
+static pw_status check_changes(pw_ctx* c, const char* fn, int n, const int32_t* ids, const uint8_t* q_new,
+                               std::vector<std::pair<int, int>>& todo)
+{
+    if (n < 0) return fail(PW_ERR_INVALID, "%s: n < 0", fn);
+    if (n > 0 && (!ids || !q_new)) return fail(PW_ERR_INVALID, "%s: null pointer", fn);
+    std::unordered_set<int32_t> seen;
+    for (int i = 0; i < n; ++i) {
+        const int32_t id = ids[i];
+        if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+            return fail(PW_ERR_INVALID, "%s: block id %d not registered", fn, id);
+        if (q_new[i] < PW_QMIN || q_new[i] > PW_QMAX) return fail(PW_ERR_INVALID, "%s: q %d not in 3..8", fn, (int)q_new[i]);
+        if (!seen.insert(id).second) return fail(PW_ERR_INVALID, "%s: duplicate block id %d", fn, id);
+        if (c->pending.count(id)) return fail(PW_ERR_STATE, "%s: block id %d has a width request in flight", fn, id);
+    }
+    todo.clear();
+    for (int i = 0; i < n; ++i)
+        if (q_new[i] != c->blocks[ids[i]].q) todo.push_back({ids[i], (int)q_new[i]});
+    if (!todo.empty() && !c->d.keep_host_masters)
+        return fail(PW_ERR_STATE, "%s: the context keeps no host masters (keep_host_masters = 0)", fn);
+    return ok();
+}
+
+pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint8_t* q_new, pw_stream compute,
+                                pw_stream copy)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_set_committed_bits: null context");
+    std::vector<std::pair<int, int>> todo;
+    pw_status st = check_changes(c, "pw_set_committed_bits", n, ids, q_new, todo);
+    if (st != PW_OK || todo.empty()) return st;
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    hipStream_t cs = (hipStream_t)compute, xs = (hipStream_t)copy;
+    std::vector<WidthChange> plans;
+    if ((st = prepare_changes(c, "pw_set_committed_bits", todo, xs, plans)) != PW_OK) return st;
+    if ((e = hipStreamWaitEvent(cs, plans[0].copied, 0)) != hipSuccess) {
+        (void)hipStreamSynchronize(xs);
+        release_prepared(c, plans);
+        return hip_fail(e, "pw_set_committed_bits: compute waits for the copies");
+    }
+    if ((st = apply_changes(c, plans, cs)) != PW_OK) {
+        (void)hipStreamSynchronize(xs);
+        release_prepared(c, plans);
+    }
+    return st;
+}
+
+pw_status pw_request_widths(pw_ctx* c, int n, const int32_t* ids, const uint8_t* q_desired, pw_stream copy)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_request_widths: null context");
+    std::vector<std::pair<int, int>> todo;
+    pw_status st = check_changes(c, "pw_request_widths", n, ids, q_desired, todo);
+    if (st != PW_OK || todo.empty()) return st;
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    std::vector<WidthChange> plans;
+    if ((st = prepare_changes(c, "pw_request_widths", todo, (hipStream_t)copy, plans)) != PW_OK) return st;
+    for (const auto& p : plans) c->pending[p.id] = p;
+    return ok();
+}
+
+pw_status pw_commit_ready(pw_ctx* c, pw_stream compute, int* n_committed)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_commit_ready: null context");
+    if (n_committed) *n_committed = 0;
+    if (c->pending.empty()) return ok();
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    std::vector<WidthChange> ready;
+    for (const auto& kv : c->pending) {
+        const hipError_t q = hipEventQuery(kv.second.copied);
+        if (q == hipSuccess) ready.push_back(kv.second);
+        else if (q != hipErrorNotReady) return hip_fail(q, "pw_commit_ready: copy event");
+    }
+    if (ready.empty()) return ok();
+    std::sort(ready.begin(), ready.end(), [](const WidthChange& a, const WidthChange& b) { return a.id < b.id; });
+    const pw_status st = apply_changes(c, ready, (hipStream_t)compute);
+    if (st != PW_OK) return st;
+    for (const auto& p : ready) c->pending.erase(p.id);
+    if (n_committed) *n_committed = (int)ready.size();
+    return ok();
+}
+
+pw_status pw_block_state(const pw_ctx* c, int32_t id, int32_t* q_committed, int32_t* q_desired, int32_t* state)
+{
+    if (!c || !q_committed || !q_desired || !state) return fail(PW_ERR_INVALID, "pw_block_state: null pointer");
+    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+        return fail(PW_ERR_INVALID, "pw_block_state: block id %d not registered", id);
+    *q_committed = c->blocks[id].q;
+    const auto it = c->pending.find(id);
+    if (it == c->pending.end()) {
+        *q_desired = c->blocks[id].q;
+        *state = PW_PAGE_RESIDENT;
+        return ok();
+    }
+    *q_desired = it->second.qn;
+    const hipError_t q = hipEventQuery(it->second.copied);
+    if (q != hipSuccess && q != hipErrorNotReady) return hip_fail(q, "pw_block_state: copy event");
+    *state = q == hipSuccess ? PW_PAGE_READY : PW_PAGE_IN_TRANSFER;
     return ok();
 }
 

@@ -122,7 +122,8 @@ int64_t pw_plane_words(int64_t R, int64_t K);
  * LUT_{q_init} to device memory (synchronously) and, if keep_host_masters,
  * keeps a pinned host copy of all planes and LUTs.  Re-registering a block
  * replaces it.  Call only while no work using this layer is in flight.
- * Errors: INVALID (ids, q_init outside 3..8, null pointers), OOM, HIP. */
+ * Errors: INVALID (ids, q_init outside 3..8, null pointers), OOM, HIP, STATE
+ * (the block has a pw_request_widths request in flight). */
 pw_status pw_register_block(pw_ctx *ctx, int layer, int expert, int module,
                             const uint32_t *host_planes, const uint16_t *host_luts, int q_init);
 
@@ -247,10 +248,35 @@ pw_status pw_plan_widths(int L, int E, int H, int I, const uint8_t *q_cur, const
  * masters with asynchronous copies on `copy`; `compute` waits for those
  * copies before the page-table update.  The new widths apply to all work
  * enqueued on `compute` after this call returns and never to earlier work.
- * Errors: INVALID (ids, q outside 3..8, duplicate ids), STATE (raise without
- * host masters), OOM, HIP.  On error nothing changes. */
+ * Errors: INVALID (ids, q outside 3..8, duplicate ids), STATE (a change
+ * without host masters, or a block with a pw_request_widths request in
+ * flight), OOM, HIP.  On error nothing changes. */
 pw_status pw_set_committed_bits(pw_ctx *ctx, int n, const int32_t *block_ids,
                                 const uint8_t *q_new, pw_stream compute, pw_stream copy);
+
+/* Non-blocking width changes (Core components 1 and 3: the page table tracks
+ * a desired width d_i and a committed width q_i; pages move asynchronously
+ * and new widths are committed only at safe boundaries).
+ * pw_request_widths records d_i = q_desired for n blocks and starts the
+ * moves on `copy` right away: new slabs for planes q_i..d_i-1 and LUT_{d_i}
+ * from the pinned host masters (lowering copies only the smaller LUT).  The
+ * committed widths do not change.  Errors as pw_set_committed_bits, plus
+ * STATE for a block that already has a request in flight (one request per
+ * block until it is committed).
+ * pw_commit_ready is the safe-boundary call (between layer steps): every
+ * requested block whose copies have landed is committed, stream-ordered on
+ * `compute` (work enqueued before keeps the old widths); blocks still in
+ * transfer stay pending and nothing on `compute` waits for `copy`.
+ * *n_committed (may be NULL) receives the number of blocks committed.
+ * Slabs a commit drops are recycled after the work enqueued on `compute`
+ * before it.
+ * pw_block_state reports q_i, d_i and the block's page state. */
+enum { PW_PAGE_RESIDENT = 0, PW_PAGE_IN_TRANSFER = 1, PW_PAGE_READY = 2 };
+pw_status pw_request_widths(pw_ctx *ctx, int n, const int32_t *block_ids, const uint8_t *q_desired,
+                            pw_stream copy);
+pw_status pw_commit_ready(pw_ctx *ctx, pw_stream compute, int *n_committed);
+pw_status pw_block_state(const pw_ctx *ctx, int32_t block_id, int32_t *q_committed, int32_t *q_desired,
+                         int32_t *state);
 
 /* Host view of one block's committed width (0 if not registered). */
 pw_status pw_get_committed_bits(const pw_ctx *ctx, int32_t block_id, int32_t *q_out);

@@ -110,6 +110,9 @@ def test_null_context_calls_are_invalid():
     assert L.pw_route_permute(None, None, 1, None, None, None, None, None) == pw.PW_ERR_INVALID
     assert L.pw_moe_ffn_bitplane(None, 0, None, 1, None, None, None, None, None, None, 0, None) == pw.PW_ERR_INVALID
     assert L.pw_moe_layer(None, 0, None, None, 1, None, None, None, None, None, None, 0, None) == pw.PW_ERR_INVALID
+    assert L.pw_request_widths(None, 0, None, None, None) == pw.PW_ERR_INVALID
+    assert L.pw_commit_ready(None, None, None) == pw.PW_ERR_INVALID
+    assert L.pw_block_state(None, 0, None, None, None) == pw.PW_ERR_INVALID
     assert L.pw_routing_mass_enable(None, 1) == pw.PW_ERR_INVALID
     assert L.pw_routing_mass_reset(None, None) == pw.PW_ERR_INVALID
     assert L.pw_routing_mass_read(None, None, None) == pw.PW_ERR_INVALID

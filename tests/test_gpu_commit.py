@@ -163,3 +163,57 @@ def test_no_host_masters_means_no_width_changes():
         ctx.set_committed_bits([bid], [q])  # unchanged width: a no-op, accepted
     finally:
         ctx.close()
+
+
+def test_requested_widths_commit_only_after_their_copies_land():
+    """pw_request_widths starts the moves on a copy stream held back by a
+    spinning kernel: the blocks report IN_TRANSFER, pw_commit_ready commits
+    nothing and a step on the compute stream runs (without waiting for the
+    copy stream) at the old widths.  Once the copy stream has drained the
+    blocks report READY, pw_commit_ready commits all of them and the next step
+    runs at the new widths.  A second request for a pending block, and a
+    pw_set_committed_bits on it, are refused with STATE."""
+    import oracle
+    import torch
+    import any_precision_expert_amd as pw
+    from any_precision_expert_amd.layer import register_layer
+    w, a = _layer(seed=503)
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        torch.cuda.synchronize()
+        q0 = [(b.q, d.q) for b, d in zip(w.gate_up, w.down)]
+        ids = [ctx.block_id(0, e, m) for e in range(w.shape.E) for m in (0, 1)]
+        want = [3 if q0[e][m] > 5 else 8 for e in range(w.shape.E) for m in (0, 1)]
+        from any_precision_expert_amd.layer import Batch
+        compute, copy_stream = torch.cuda.Stream(), torch.cuda.Stream()
+        batches = []
+        for _ in range(2):
+            bb = Batch(ctx, a.x.shape[0])
+            bb.load(a.logits, a.x)
+            batches.append(bb)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(copy_stream):
+            torch.cuda._sleep(200_000_000)  # keeps the copies queued behind it for a while
+        ctx.request_widths(ids, want, copy_stream)
+        states = [ctx.block_state(i) for i in ids]
+        assert all(st == pw.PAGE_IN_TRANSFER for (_, _, st) in states)
+        assert [qd for (_, qd, _) in states] == want
+        assert ctx.commit_ready(compute) == 0
+        with pytest.raises(pw.PwError):
+            ctx.request_widths(ids[:1], [4], copy_stream)
+        with pytest.raises(pw.PwError):
+            ctx.set_committed_bits(ids[:1], [4], compute, copy_stream)
+        batches[0].step(0, compute)
+        compute.synchronize()
+        assert copy_stream.query() is False  # the step did not wait for the moves
+        compare(_fetch(batches[0]), oracle.moe_layer(w, a), label="old widths while moving")
+        copy_stream.synchronize()
+        assert all(ctx.block_state(i)[2] == pw.PAGE_READY for i in ids)
+        assert ctx.commit_ready(compute) == len(ids)
+        assert all(ctx.block_state(i) == (q, q, pw.PAGE_RESIDENT) for i, q in zip(ids, want))
+        batches[1].step(0, compute)
+        pairs = list(zip(want[0::2], want[1::2]))
+        compare(_fetch(batches[1]), oracle.moe_layer(_with_q(w, pairs), a), label="new widths after commit")
+    finally:
+        ctx.close()
