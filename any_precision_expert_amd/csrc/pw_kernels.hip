@@ -450,57 +450,46 @@ __device__ __forceinline__ int route_token(const float* __restrict__ logits, int
         live[i] = e < E;
         v[i] = live[i] ? l[e] : 0.0f;
     }
-    float sv[8];
-    int si[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        sv[j] = 0.0f;
-        si[j] = 0;
-        if (j < k) {
-            float bv = 0.0f;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = lane + 64 * i;
-                if (live[i] && (bi == 0x7fffffff || route_better(v[i], e, bv, bi))) {
-                    bv = v[i];
-                    bi = e;
-                }
-            }
-            // wave-wide best by DPP steps (no LDS round trips): pairs and
-            // quads, mirrored halves of 8, mirrored rows of 16, then rows 0 / 2
-            // into 1 / 3 and row 1 into 2 / 3; lane 63 ends with the best
-            route_dpp_step<0xB1, 0xf>(bv, bi);   // quad_perm [1,0,3,2]
-            route_dpp_step<0x4E, 0xf>(bv, bi);   // quad_perm [2,3,0,1]
-            route_dpp_step<0x141, 0xf>(bv, bi);  // row_half_mirror
-            route_dpp_step<0x140, 0xf>(bv, bi);  // row_mirror
-            route_dpp_step<0x142, 0xa>(bv, bi);  // row_bcast:15
-            route_dpp_step<0x143, 0xc>(bv, bi);  // row_bcast:31
-            bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 63));
-            bi = __builtin_amdgcn_readlane(bi, 63);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (lane + 64 * i == bi) live[i] = false;
-            sv[j] = bv;
-            si[j] = bi;
-        }
-    }
-    const float m = sv[0];
-    float ex[8], s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        ex[j] = j < k ? expf(sv[j] - m) : 0.0f;
-        s += ex[j];
-    }
+    // pick j is kept by lane j; the softmax sums exp(pick - best) in pick
+    // order (a rolled loop keeps the code small: every routing workgroup
+    // runs it once)
     int out = -1;
-    wout = 0.0f;
+    float mine = 0.0f, m = 0.0f, s = 0.0f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+        float bv = 0.0f;
+        int bi = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (j < k && lane == j) {
-            out = si[j];
-            wout = ex[j] / s;
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (live[i] && (bi == 0x7fffffff || route_better(v[i], e, bv, bi))) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+        // wave-wide best by DPP steps (no LDS round trips): pairs and
+        // quads, mirrored halves of 8, mirrored rows of 16, then rows 0 / 2
+        // into 1 / 3 and row 1 into 2 / 3; lane 63 ends with the best
+        route_dpp_step<0xB1, 0xf>(bv, bi);   // quad_perm [1,0,3,2]
+        route_dpp_step<0x4E, 0xf>(bv, bi);   // quad_perm [2,3,0,1]
+        route_dpp_step<0x141, 0xf>(bv, bi);  // row_half_mirror
+        route_dpp_step<0x140, 0xf>(bv, bi);  // row_mirror
+        route_dpp_step<0x142, 0xa>(bv, bi);  // row_bcast:15
+        route_dpp_step<0x143, 0xc>(bv, bi);  // row_bcast:31
+        bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 63));
+        bi = __builtin_amdgcn_readlane(bi, 63);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i == bi) live[i] = false;
+        if (j == 0) m = bv;
+        const float ex = expf(bv - m);
+        s += ex;
+        if (lane == j) {
+            out = bi;
+            mine = ex;
         }
     }
+    wout = lane < k ? mine / s : 0.0f;
     return out;
 }
 
