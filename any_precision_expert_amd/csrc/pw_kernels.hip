@@ -91,6 +91,36 @@ struct Gathered {
     uint32_t r[N];
 };
 
+// Child codes of one plane word set by an 8 x 8 bit transpose per byte: with
+// row r = plane q - 1 - r (rows q..7 zero), byte i of row r holds bit r of the
+// codes of columns 8P + 2i + h at bit 4h + P; three swap stages (4-, 2- and
+// 1-bit blocks between rows 4, 2 and 1 apart) leave in row 4h + P, byte i,
+// the child code of column 8P + 2i + h.  Each swap is two shifts and two
+// bit-selects (v_bitop3); swaps against a row still known to be zero cost
+// less.  X[P] / X[4 + P] are the two code registers of MFMA step P.
+template <int Q>
+__device__ __forceinline__ void transpose_codes(const uint32_t (&W)[Q], uint32_t (&X)[8])
+{
+#pragma unroll
+    for (int r = 0; r < 8; ++r) X[r] = r < Q ? W[Q - 1 - r] : 0u;
+    auto swap = [](uint32_t& a, uint32_t& b, int sh, uint32_t lo) {
+        // a keeps its low bits of each group and takes b's low bits above them;
+        // b keeps its high bits and takes a's high bits below them
+        const uint32_t na = (a & lo) | ((b << sh) & ~lo);
+        const uint32_t nb = (b & ~lo) | ((a >> sh) & lo);
+        a = na;
+        b = nb;
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) swap(X[r], X[r + 4], 4, 0x0F0F0F0Fu);
+    swap(X[0], X[2], 2, 0x33333333u);
+    swap(X[1], X[3], 2, 0x33333333u);
+    swap(X[4], X[6], 2, 0x33333333u);
+    swap(X[5], X[7], 2, 0x33333333u);
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) swap(X[r], X[r + 1], 1, 0x55555555u);
+}
+
 // In the stored word, column 8P + 2i + h is at bit 8i + 4h + P.  Rotating plane
 // p left by (q - 1 - p) moves every bit of that plane by the same amount, so a
 // single and-or per (plane, register) drops its bit of four columns into the
@@ -115,6 +145,14 @@ __device__ __forceinline__ void gather(const uint32_t (&W)[Q], Gathered<Q>& g, c
                 acc = and_or(B[p], M.m[rep_index(P + 2 * Q - 1 - p)], acc);
             }
             g.r[P] = rotr(acc, P);
+        }
+    } else if constexpr (Q == 8) {
+        uint32_t X[8];
+        transpose_codes<Q>(W, X);
+#pragma unroll
+        for (int P = 0; P < 4; ++P) {
+            g.r[2 * P] = X[P];
+            g.r[2 * P + 1] = X[4 + P];
         }
     } else {
 #pragma unroll
@@ -932,32 +970,41 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                     return PAIR && RG == 4 && half ? rotl(0x01010101u << (2 * Q), P) : 0u;
                 };
                 auto b_unit = [&](int s, int row) { return slice_unit(row, te, 4 * (2 * kh + (s >> 2)) + (s & 3)); };
+                // q = 8: all eight code registers of a word pair by one bit
+                // transpose (4 ops per swap, 96 per chunk against 146 for the
+                // and-or gather); narrower codes: rotated planes and one
+                // and-or gather per step (cheaper there: the transpose's
+                // known-zero rows make the compiler split its bit-selects)
+                constexpr bool TRANSPOSE = Q == 8 && !PAIR;
                 Rot<Q, PAIR> rt;
-                {
+                uint32_t X[8];
+                auto prepare = [&](int u) {
                     uint32_t W[Q];
 #pragma unroll
-                    for (int p = 0; p < Q; ++p) W[p] = cur[p][0];
-                    rotate_planes<Q, PAIR>(W, rt);
-                }
+                    for (int p = 0; p < Q; ++p) W[p] = cur[p][u];
+                    if constexpr (TRANSPOSE) transpose_codes<Q>(W, X);
+                    else rotate_planes<Q, PAIR>(W, rt);
+                };
+                auto codes = [&](int P) {
+                    if constexpr (TRANSPOSE) return StepCodes{X[P], X[4 + P]};
+                    else return step_codes<Q, PAIR>(rt, P, masks, acc0(P));
+                };
+                prepare(0);
                 u32x4 bh = slice4[b_unit(0, te)], bl = {0, 0, 0, 0};
                 if (MODE == 1) bl = slice4[b_unit(0, 4 + te)];
                 StepRaw raw;
-                step_lookup<PAIR>(step_codes<Q, PAIR>(rt, 0, masks, acc0(0)), lane_off, lutb, raw);
+                step_lookup<PAIR>(codes(0), lane_off, lutb, raw);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     StepCodes next{0u, 0u};
-                    if (s < 7) {
-                        if (s == 3) {  // word pair 1 (pair 0's rotated words are no longer needed)
-                            uint32_t W[Q];
-#pragma unroll
-                            for (int p = 0; p < Q; ++p) W[p] = cur[p][1];
-                            rotate_planes<Q, PAIR>(W, rt);
-                        }
-                        next = step_codes<Q, PAIR>(rt, (s + 1) & 3, masks, acc0((s + 1) & 3));
-                    }
+                    if (s < 7 && s != 3) next = codes((s + 1) & 3);
                     const half8 A = step_pack<PAIR>(raw);
                     C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bh), C, 0, 0, 0);
                     if (MODE == 1) C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bl), C, 0, 0, 0);
+                    if (s == 3) {  // word pair 1, once step 3's operands are consumed
+                        prepare(1);
+                        next = codes(0);
+                    }
                     if (s < 7) {
                         bh = slice4[b_unit(s + 1, te)];
                         if (MODE == 1) bl = slice4[b_unit(s + 1, 4 + te)];
