@@ -99,10 +99,12 @@ struct Gathered {
 // bit-selects (v_bitop3); swaps against a row still known to be zero cost
 // less.  X[P] / X[4 + P] are the two code registers of MFMA step P.
 template <int Q>
-__device__ __forceinline__ void transpose_codes(const uint32_t (&W)[Q], uint32_t (&X)[8])
+__device__ __forceinline__ void transpose_codes(const uint32_t (&W)[Q], uint32_t (&X)[8], uint32_t zero = 0u)
 {
+    // rows q..7 start as `zero`: a caller that passes a zero the compiler
+    // cannot see keeps every swap a plain bit-select pair
 #pragma unroll
-    for (int r = 0; r < 8; ++r) X[r] = r < Q ? W[Q - 1 - r] : 0u;
+    for (int r = 0; r < 8; ++r) X[r] = r < Q ? W[Q - 1 - r] : zero;
     auto swap = [](uint32_t& a, uint32_t& b, int sh, uint32_t lo) {
         // a keeps its low bits of each group and takes b's low bits above them;
         // b keeps its high bits and takes a's high bits below them
@@ -859,6 +861,9 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     const uint32_t lane_off = lut_lane_off<Q, RG>(lslot, half);
     const char* lutb = (const char*)lds;
     const RepMasks masks = make_masks();
+    // a zero the compiler cannot prove (T >= 1 here): the transpose's empty
+    // rows then stay plain operands of its bit-selects
+    const uint32_t opaque_zero = (uint32_t)__builtin_amdgcn_readfirstlane(a.T >> 30);
 
     // cooperative activation loads: lane = (token xt, 16-byte unit xg)
     const int xt = lane >> 4, xg = lane & 15;
@@ -970,19 +975,21 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                     return PAIR && RG == 4 && half ? rotl(0x01010101u << (2 * Q), P) : 0u;
                 };
                 auto b_unit = [&](int s, int row) { return slice_unit(row, te, 4 * (2 * kh + (s >> 2)) + (s & 3)); };
-                // q = 8: all eight code registers of a word pair by one bit
+                // q >= 5: all eight code registers of a word pair by one bit
                 // transpose (4 ops per swap, 96 per chunk against 146 for the
-                // and-or gather); narrower codes: rotated planes and one
-                // and-or gather per step (cheaper there: the transpose's
-                // known-zero rows make the compiler split its bit-selects)
-                constexpr bool TRANSPOSE = Q == 8 && !PAIR;
+                // and-or gather at q = 8).  Rows q..7 start from a zero the
+                // compiler cannot see through: with a literal zero it splits
+                // the bit-selects of those rows into more, cheaper ops.
+                // Pair tables (q <= 4): rotated planes and one and-or gather
+                // per step.
+                constexpr bool TRANSPOSE = Q >= 5 && !PAIR;
                 Rot<Q, PAIR> rt;
                 uint32_t X[8];
                 auto prepare = [&](int u) {
                     uint32_t W[Q];
 #pragma unroll
                     for (int p = 0; p < Q; ++p) W[p] = cur[p][u];
-                    if constexpr (TRANSPOSE) transpose_codes<Q>(W, X);
+                    if constexpr (TRANSPOSE) transpose_codes<Q>(W, X, opaque_zero);
                     else rotate_planes<Q, PAIR>(W, rt);
                 };
                 auto codes = [&](int P) {
