@@ -4,6 +4,10 @@ Workload: one Qwen1.5-MoE-A2.7B-shaped MoE layer in decode (H=2048, 60 routed
 experts with I=1408, top-4, one shared expert with I=5632 at 8 bits, 4 tokens
 per batch), Zipf(1.1)-biased routing, routed blocks at mixed widths 3..8 tiered
 by routing rank.  All inputs are seeded synthetic arrays (pw_synth).
+`--model-config FILE` replaces the shape by that of a MoE model config
+(pw_synth.shape_from_model_config: hidden_size, moe_intermediate_size,
+num_experts, num_experts_per_tok, shared-expert keys), e.g. for a model whose
+shapes are not built in.
 
 A step is one pass of the whole hot path over one batch: top-k routing ->
 permutation by expert -> gate_up (bit-plane gather, LUT decode, SiLU*mul) ->
@@ -251,9 +255,9 @@ def _graph_ms(run_steps, L, steps, stream):
     return ev0.elapsed_time(ev1) / (reps * L)
 
 
-def baselines_leg(w, packed, steps, L):
+def baselines_leg(spec, seed, w, packed, steps, L):
     """The pages' comparison (mixed widths against uniform quantization, batch
-    1 / 4 / 16) on the same Qwen-shaped layer: the same kernels with every
+    1 / 4 / 16) on the main leg's layer: the same kernels with every
     routed block at one width (4, 5 or 8; the shared expert stays at 8), and an
     fp16 dense expert FFN in torch (batched GEMMs over the active experts'
     fp16 weights, the routing fixed when the graph is captured, so its time
@@ -262,8 +266,7 @@ def baselines_leg(w, packed, steps, L):
     import any_precision_expert_amd as pw
     import pw_synth
     from any_precision_expert_amd.layer import Batch
-    spec = pw_synth.CONFIGS[CFG]
-    shape, seed = spec.shape, pw_synth.config_seed(CFG)
+    shape = spec.shape
     H, I, Is, E, k = shape.H, shape.I, shape.I_shared, shape.E, shape.top_k
     stream = torch.cuda.Stream()
     acts = {T: [pw_synth.make_activations(shape, T, seed, 0, s, spec.logits, w.rank) for s in range(L)]
@@ -321,7 +324,8 @@ def baselines_leg(w, packed, steps, L):
             copies.append(dict(
                 x=torch.from_numpy(acts[T][l].x.astype(np.float16)).cuda(),
                 tok=torch.from_numpy(tok.reshape(-1)).cuda(), wt=torch.from_numpy(wt).cuda()[..., None],
-                wgu=mk(len(act), H, 2 * I), wd=mk(len(act), I, H), sgu=mk(H, 2 * Is), sd=mk(Is, H),
+                wgu=mk(len(act), H, 2 * I), wd=mk(len(act), I, H),
+                sgu=mk(H, 2 * Is) if Is else None, sd=mk(Is, H) if Is else None,
                 y=torch.zeros(T, H, device="cuda", dtype=torch.float32), n=len(act), tm=tm,
                 bytes=(len(act) * 3 * I * H + 3 * Is * H) * 2))
 
@@ -334,6 +338,8 @@ def baselines_leg(w, packed, steps, L):
                 d = torch.bmm(h, c["wd"]).float() * c["wt"]
                 c["y"].zero_()
                 c["y"].index_add_(0, c["tok"], d.view(-1, H))
+                if c["sgu"] is None:
+                    continue
                 hs = c["x"] @ c["sgu"]
                 hs = (torch.nn.functional.silu(hs[:, :Is].float()) * hs[:, Is:].float()).half()
                 c["y"] += (hs @ c["sd"]).float()
@@ -350,7 +356,7 @@ def baselines_leg(w, packed, steps, L):
     return out
 
 
-def cpu_baseline(weights, acts_list, budget_s):
+def cpu_baseline(spec, weights, acts_list, budget_s):
     import oracle
     P = oracle.PreparedLayer(weights)
     n_tok, secs, batches = 0, 0.0, 0
@@ -361,9 +367,10 @@ def cpu_baseline(weights, acts_list, budget_s):
         n_tok += a.x.shape[0]
         batches += 1
     return dict(value=n_tok / secs, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample="%d batches of %d tokens of the same Qwen-shaped layer (route, permute, "
-                       "all routed experts + shared expert, combine) in fp64; %.1f s"
-                       % (batches, acts_list[0].x.shape[0], secs))
+                sample="%d batches of %d tokens of the same layer (%s: route, permute, "
+                       "all routed experts%s, combine) in fp64; %.1f s"
+                       % (batches, acts_list[0].x.shape[0], spec.name,
+                          " + shared expert" if spec.shape.I_shared else "", secs))
 
 
 def main():
@@ -379,6 +386,10 @@ def main():
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the uniform-width and fp16-dense comparison at 1 / 4 / 16 tokens")
     ap.add_argument("--baseline-steps", type=int, default=160)
+    ap.add_argument("--model-config", default=None, metavar="JSON",
+                    help="decode workload from a MoE model config (hidden_size, moe_intermediate_size, "
+                         "num_experts, num_experts_per_tok, ...) instead of the Qwen1.5-MoE-A2.7B shape")
+    ap.add_argument("--tokens", type=int, default=None, help="tokens per batch (default: the workload's)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the bench, copy this many MiB device-to-device (PMC scale reference)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"))
@@ -405,9 +416,12 @@ def main():
     from any_precision_expert_amd.layer import Batch
 
     assert torch.cuda.is_available(), "bench needs a GPU"
-    spec = pw_synth.CONFIGS[CFG]
-    shape, T = spec.shape, spec.tokens[0]
-    seed = pw_synth.config_seed(CFG)
+    if args.model_config:
+        spec, seed = pw_synth.model_config_spec(args.model_config), pw_synth.USER_CONFIG_SEED
+    else:
+        spec, seed = pw_synth.CONFIGS[CFG], pw_synth.config_seed(CFG)
+    shape = spec.shape
+    T = spec.tokens[0] if args.tokens is None else args.tokens
     L = args.layers
     t0 = time.time()
     w = pw_synth.make_weights(shape, seed, 0, spec.q_policy, spec.logits)
@@ -419,9 +433,10 @@ def main():
                      keep_host_masters=False)
     t0 = time.time()
     blocks = [(e, pw.MODULE_GATE_UP, w.gate_up[e]) for e in range(shape.E)] + \
-             [(e, pw.MODULE_DOWN, w.down[e]) for e in range(shape.E)] + \
-             [(pw.EXPERT_SHARED, pw.MODULE_GATE_UP, w.shared_gate_up),
-              (pw.EXPERT_SHARED, pw.MODULE_DOWN, w.shared_down)]
+             [(e, pw.MODULE_DOWN, w.down[e]) for e in range(shape.E)]
+    if shape.I_shared:
+        blocks += [(pw.EXPERT_SHARED, pw.MODULE_GATE_UP, w.shared_gate_up),
+                   (pw.EXPERT_SHARED, pw.MODULE_DOWN, w.shared_down)]
     packed = {}
     for e, m, b in blocks:
         planes, luts = pw.pack_bitplanes(b.code8), pw.concat_luts(b.luts)
@@ -502,7 +517,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, acts, args.cpu_seconds)
+        cpu = cpu_baseline(spec, w, acts, args.cpu_seconds)
         log("cpu oracle: %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
 
     tr = stored_traffic()
@@ -512,7 +527,7 @@ def main():
     if not args.no_baselines:
         ctx.close()
         ctx = None
-        baselines = baselines_leg(w, packed, args.baseline_steps, L)
+        baselines = baselines_leg(spec, seed, w, packed, args.baseline_steps, L)
 
     out = {
         "metric": "routed tokens/s per MoE layer at mixed 3-8 bit + achieved HBM GB/s vs peak",
@@ -529,7 +544,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "H": shape.H, "I": shape.I, "E": shape.E, "top_k": shape.top_k,
                    "I_shared": shape.I_shared, "tokens_per_batch": T, "layer_copies": L,
-                   "q": "routed blocks tiered by Zipf rank (8 / 5-6 / 3-4), shared at 8",
+                   "q": "routed blocks tiered by Zipf rank (8 / 5-6 / 3-4)" + (", shared at 8" if shape.I_shared else ""),
+                   "source": "user model config" if spec.extra.get("user_config") else "built-in shape",
                    "graph": graph is not None},
         "path_gbps": round(mean_b["path"] / (ms_per_step * 1e-3) / 1e9, 1),
         "path_bytes_per_step": int(mean_b["path"]),

@@ -118,6 +118,78 @@ def config_seed(cfg: int) -> int:
     return SEED_BASE + int(cfg)
 
 
+# Seed of every workload built from a user-supplied model config.
+USER_CONFIG_SEED = SEED_BASE + 100
+
+# Model-config keys read for each layer dimension, in order of preference
+# (the names common Hugging Face MoE configs use; H/I/E/top_k/I_shared
+# themselves are accepted too).
+_SHAPE_KEYS = {
+    "H": ("H", "hidden_size", "d_model"),
+    "I": ("I", "moe_intermediate_size", "expert_intermediate_size", "moe_ffn_hidden_size",
+          "intermediate_size"),
+    "E": ("E", "num_experts", "num_local_experts", "n_routed_experts", "moe_num_experts"),
+    "top_k": ("top_k", "num_experts_per_tok", "top_k_experts", "moe_top_k", "num_selected_experts"),
+}
+
+
+def _first(cfg: dict, keys):
+    for key in keys:
+        if cfg.get(key) is not None:
+            return key, cfg[key]
+    return None, None
+
+
+def shape_from_model_config(cfg) -> "tuple[LayerShape, int, str]":
+    """(LayerShape, layers, name) of a MoE model described by a config dict or
+    a JSON file path.  A nested "text_config" dict (multimodal configs) is
+    read first.  The shared expert's width is shared_expert_intermediate_size,
+    else n_shared_experts (or num_shared_experts) times the routed I, else 0.
+    Raises ValueError naming a missing key or a dimension the bit-plane
+    layout cannot hold (H, I and I_shared must be multiples of 32)."""
+    import json
+    import os
+    name = None
+    if not isinstance(cfg, dict):
+        path = os.fspath(cfg)
+        with open(path) as f:
+            cfg = json.load(f)
+        name = os.path.splitext(os.path.basename(path))[0]
+    flat = dict(cfg)
+    if isinstance(cfg.get("text_config"), dict):
+        flat.update({k: v for k, v in cfg["text_config"].items() if v is not None})
+    dims = {}
+    for dim, keys in _SHAPE_KEYS.items():
+        key, val = _first(flat, keys)
+        if key is None:
+            raise ValueError("model config has no %s (looked for %s)" % (dim, ", ".join(keys)))
+        dims[dim] = int(val)
+    _, shared = _first(flat, ("I_shared", "shared_expert_intermediate_size"))
+    if shared is None:
+        _, n_shared = _first(flat, ("n_shared_experts", "num_shared_experts"))
+        shared = int(n_shared or 0) * dims["I"]
+    dims["I_shared"] = int(shared)
+    for dim in ("H", "I", "I_shared"):
+        if dims[dim] < 0 or dims[dim] % 32:
+            raise ValueError("%s = %d: hidden and intermediate sizes must be multiples of 32" % (dim, dims[dim]))
+    if dims["H"] == 0 or dims["I"] == 0:
+        raise ValueError("H and I must be positive")
+    if not 1 <= dims["top_k"] <= dims["E"]:
+        raise ValueError("top_k = %d must lie in 1..E = %d" % (dims["top_k"], dims["E"]))
+    _, layers = _first(flat, ("num_hidden_layers", "n_layers", "num_layers"))
+    name = str(flat.get("name") or flat.get("_name_or_path") or name or flat.get("model_type") or "user-model")
+    return LayerShape(**dims), int(layers or 1), name
+
+
+def model_config_spec(cfg, tokens: Sequence[int] = (4,)) -> ConfigSpec:
+    """Decode workload of one layer of a user-supplied MoE model config
+    (shape_from_model_config): Zipf-biased routing and widths tiered by
+    routing rank, as for the Qwen-shaped layer; seed USER_CONFIG_SEED."""
+    shape, layers, name = shape_from_model_config(cfg)
+    return ConfigSpec("%s-layer-decode" % name, shape, tokens=list(tokens), logits="zipf",
+                      q_policy="zipf_tiers", extra=dict(model_layers=layers, user_config=True))
+
+
 def _rng(seed: int, *key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), *map(int, key)])))
 

@@ -189,6 +189,31 @@ def test_config3_mixtral_prefill_sampled():
     check_layer(w, a, tokens=tokens, label="cfg3 prefill")
 
 
+# ------------------------------------------------------------------ a user-supplied model config
+
+@pytest.fixture(scope="module")
+def user_config():
+    """A MoE shape read from a model-config file (nested text_config, two
+    shared experts, H = 1120 = 8.75 chunks, 24 experts top-6)."""
+    import os
+    from any_precision_expert_amd.layer import register_layer
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "configs", "example_moe_config.json")
+    spec = pw_synth.model_config_spec(path)
+    w = pw_synth.make_weights(spec.shape, pw_synth.USER_CONFIG_SEED, 0, spec.q_policy, spec.logits)
+    ctx = make_ctx(w.shape)
+    register_layer(ctx, 0, w)
+    yield spec, w, ctx
+    ctx.close()
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 300])
+def test_user_model_config_layer(user_config, T):
+    spec, w, ctx = user_config
+    a = pw_synth.make_activations(spec.shape, T, pw_synth.USER_CONFIG_SEED, 0, T, spec.logits, w.rank)
+    tokens = None if T <= 16 else sorted({0, T - 1} | set(range(1, T, 37)))
+    check_layer(w, a, tokens=tokens, label="%s T=%d" % (spec.name, T), ctx=ctx)
+
+
 # ------------------------------------------------------------------ one call per layer
 
 @pytest.fixture(scope="module")
