@@ -454,26 +454,44 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int ww)
 // ---------------------------------------------------------------- routing
 
 // One wave per token: lane l holds the logits of experts l, l+64, l+128,
-// l+192.  Each of the k rounds takes the wave-wide best entry by the key
-// (value descending, expert index ascending) with DPP reduction steps and
-// retires it; the softmax runs over the k selected logits.
-__device__ __forceinline__ bool route_better(float av, int ai, float bv, int bi)
+// l+192.  Each of the k rounds takes the wave-wide best entry by the order
+// (value descending, expert index ascending) and retires it; the softmax runs
+// over the k selected logits.  The order is one unsigned 64-bit key per entry:
+// the logit's bits mapped so that unsigned order is numeric order (high word;
+// -0 is folded into +0 first, so equal logits tie) above 0xffff - expert (low
+// word); 0 marks a retired or absent entry.  Every step is a compare and two
+// selects: no branches, no exec-mask changes.
+struct RouteKey {
+    uint32_t hi, lo;
+};
+
+__device__ __forceinline__ RouteKey route_key(float v, int e)
 {
-    return av > bv || (av == bv && ai < bi);
+    const uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
+    return RouteKey{(u & 0x80000000u) ? ~u : (u | 0x80000000u), 0xffffu - (uint32_t)e};
 }
 
-// One DPP step of the wave-wide best: take the (value, index) the DPP pattern
-// brings in if it is better; lanes whose row is masked off keep their own.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void route_dpp_step(float& bv, int& bi)
+__device__ __forceinline__ float route_key_value(uint32_t hi)
 {
-    const float ov = __int_as_float(
-        __builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), CTRL, ROW_MASK, 0xf, false));
-    const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, ROW_MASK, 0xf, false);
-    if (oi != 0x7fffffff && (bi == 0x7fffffff || route_better(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-    }
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+
+__device__ __forceinline__ void route_key_max(RouteKey& a, uint32_t bh, uint32_t bl)
+{
+    const uint64_t ka = ((uint64_t)a.hi << 32) | a.lo, kb = ((uint64_t)bh << 32) | bl;
+    const bool take = kb > ka;
+    a.hi = take ? bh : a.hi;
+    a.lo = take ? bl : a.lo;
+}
+
+// One DPP step of the wave-wide maximum: lanes take the key the pattern
+// brings in if it is larger; lanes whose row is masked off keep their own.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void route_dpp_step(RouteKey& a)
+{
+    const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp((int)a.hi, (int)a.hi, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp((int)a.lo, (int)a.lo, CTRL, ROW_MASK, 0xf, false);
+    route_key_max(a, oh, ol);
 }
 
 // Top-k of token t's logits by one wave; lanes j < k hold the j-th expert
@@ -482,13 +500,13 @@ __device__ __forceinline__ int route_token(const float* __restrict__ logits, int
 {
     const int lane = threadIdx.x & 63;
     const float* l = logits + (size_t)t * E;
-    float v[4];
-    bool live[4];
+    RouteKey key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        live[i] = e < E;
-        v[i] = live[i] ? l[e] : 0.0f;
+        const float v = l[min(e, E - 1)];  // in bounds on every lane; absent entries drop below
+        const RouteKey kk = route_key(v, e);
+        key[i] = e < E ? kk : RouteKey{0u, 0u};
     }
     // pick j is kept by lane j; the softmax sums exp(pick - best) in pick
     // order (a rolled loop keeps the code small: every routing workgroup
@@ -497,37 +515,33 @@ __device__ __forceinline__ int route_token(const float* __restrict__ logits, int
     float mine = 0.0f, m = 0.0f, s = 0.0f;
 #pragma unroll 1
     for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = 0x7fffffff;
+        RouteKey b = key[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) route_key_max(b, key[i].hi, key[i].lo);
+        // wave-wide maximum by DPP steps (no LDS round trips): pairs and
+        // quads, mirrored halves of 8, mirrored rows of 16, then rows 0 / 2
+        // into 1 / 3 and row 1 into 2 / 3; lane 63 ends with the maximum
+        route_dpp_step<0xB1, 0xf>(b);   // quad_perm [1,0,3,2]
+        route_dpp_step<0x4E, 0xf>(b);   // quad_perm [2,3,0,1]
+        route_dpp_step<0x141, 0xf>(b);  // row_half_mirror
+        route_dpp_step<0x140, 0xf>(b);  // row_mirror
+        route_dpp_step<0x142, 0xa>(b);  // row_bcast:15
+        route_dpp_step<0x143, 0xc>(b);  // row_bcast:31
+        const uint32_t wh = (uint32_t)__builtin_amdgcn_readlane((int)b.hi, 63);
+        const uint32_t wl = (uint32_t)__builtin_amdgcn_readlane((int)b.lo, 63);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            if (live[i] && (bi == 0x7fffffff || route_better(v[i], e, bv, bi))) {
-                bv = v[i];
-                bi = e;
-            }
+            const bool hit = key[i].lo == wl;
+            key[i].hi = hit ? 0u : key[i].hi;
+            key[i].lo = hit ? 0u : key[i].lo;
         }
-        // wave-wide best by DPP steps (no LDS round trips): pairs and
-        // quads, mirrored halves of 8, mirrored rows of 16, then rows 0 / 2
-        // into 1 / 3 and row 1 into 2 / 3; lane 63 ends with the best
-        route_dpp_step<0xB1, 0xf>(bv, bi);   // quad_perm [1,0,3,2]
-        route_dpp_step<0x4E, 0xf>(bv, bi);   // quad_perm [2,3,0,1]
-        route_dpp_step<0x141, 0xf>(bv, bi);  // row_half_mirror
-        route_dpp_step<0x140, 0xf>(bv, bi);  // row_mirror
-        route_dpp_step<0x142, 0xa>(bv, bi);  // row_bcast:15
-        route_dpp_step<0x143, 0xc>(bv, bi);  // row_bcast:31
-        bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 63));
-        bi = __builtin_amdgcn_readlane(bi, 63);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i == bi) live[i] = false;
+        const float bv = route_key_value(wh);
         if (j == 0) m = bv;
         const float ex = expf(bv - m);
         s += ex;
-        if (lane == j) {
-            out = bi;
-            mine = ex;
-        }
+        const bool me = lane == j;
+        out = me ? (int)(0xffffu - wl) : out;
+        mine = me ? ex : mine;
     }
     wout = lane < k ? mine / s : 0.0f;
     return out;
@@ -1096,12 +1110,13 @@ __device__ __forceinline__ void load_widths(const BlockDesc* __restrict__ table,
 
 // Expert of a routed slot: the active experts (offsets[e + 1] > offsets[e])
 // ordered by decreasing width, then by index.  offsets may be global memory
-// or LDS.
+// or LDS.  Each expert's rank in that order is counted branch-free, width by
+// width (one ballot each; groups of 64 experts past E are skipped, a
+// wave-uniform test), then one ballot finds the expert of rank `slot`.
 __device__ __forceinline__ SlotExpert find_slot(const int32_t* offsets, const int (&q)[4], int E, int slot)
 {
     const int lane = threadIdx.x & 63;
-    const uint64_t below = (1ull << lane) - 1ull;
-    int lo[4], hi[4];
+    int lo[4], hi[4], rank[4];
     bool act[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -1110,21 +1125,30 @@ __device__ __forceinline__ SlotExpert find_slot(const int32_t* offsets, const in
         lo[g] = offsets[ec];
         hi[g] = offsets[ec + 1];
         act[g] = e < E && hi[g] > lo[g];
+        rank[g] = -1;
     }
     int base = 0;
 #pragma unroll
     for (int qq = kQMax; qq >= kQMin; --qq) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const bool mine = act[g] && q[g] == qq;
-            const uint64_t m = __ballot(mine);
-            const uint64_t hit = __ballot(mine && base + __popcll(m & below) == slot);
-            if (hit) {
-                const int h = __ffsll((long long)hit) - 1;
-                const int p0 = __builtin_amdgcn_readlane(lo[g], h);
-                return SlotExpert{64 * g + h, p0, __builtin_amdgcn_readlane(hi[g], h) - p0};
+            if (64 * g < E) {
+                const bool mine = act[g] && q[g] == qq;
+                const uint64_t m = __ballot(mine);
+                const int r = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                rank[g] = mine ? r : rank[g];
+                base += __popcll(m);
             }
-            base += __popcll(m);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint64_t hit = __ballot(64 * g < E && rank[g] == slot);
+        if (hit) {
+            const int h = __ffsll((long long)hit) - 1;
+            const int p0 = __builtin_amdgcn_readlane(lo[g], h);
+            return SlotExpert{64 * g + h, p0, __builtin_amdgcn_readlane(hi[g], h) - p0};
         }
     }
     return SlotExpert{-1, 0, 0};
@@ -1569,25 +1593,46 @@ __global__ void __launch_bounds__(kPfThreads, 2) ffn_prefill_kernel(FfnArgs a)
 // y[t][o] = sum_j w[t][j] * (sum over splits of d_(t,j)[o]) (+ shared d), rounded once to fp16.
 __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a)
 {
-    const size_t n = (size_t)a.T * a.H;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int t = (int)(i / a.H), o = (int)(i - (size_t)t * a.H);
+    // grid: (token, 256-column group of H)
+    const int t = blockIdx.x, o = blockIdx.y * 256 + threadIdx.x;
+    if (o >= a.H) return;
     const size_t plane = (size_t)a.drows * a.H;
+    const int SR = a.splits_routed, SS = a.tiles_shared ? a.splits_shared : 0;
+    const float* dr = a.dout + (size_t)t * a.k * a.H + o;                      // token t's routed rows
+    const float* ds = SS ? a.dout + ((size_t)a.T * a.k + t) * a.H + o : dr;  // its shared row
+    // the loads of the first K split (and of up to four shared splits) are all
+    // issued before the first is used (clamped addresses, masked sums): one
+    // memory round trip instead of one per term; sums keep the order of the
+    // definition (splits ascending, then picks ascending)
+    float wj[8], dj[8], sv[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wj[j] = a.topk_w[t * a.k + min(j, a.k - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dj[j] = dr[(size_t)min(j, a.k - 1) * a.H];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sv[u] = ds[(size_t)min(u, max(SS - 1, 0)) * plane];
+    for (int sp0 = 1; sp0 < SR; sp0 += 4) {
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[u][j] = dr[(size_t)min(sp0 + u, SR - 1) * plane + (size_t)min(j, a.k - 1) * a.H];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dj[j] += sp0 + u < SR ? v[u][j] : 0.0f;
+    }
     float s = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-        const float* d = a.dout + ((size_t)t * a.k + j) * a.H + o;
-        float dj = 0.0f;
-        for (int sp = 0; sp < a.splits_routed; ++sp) dj += d[sp * plane];
-        s += a.topk_w[t * a.k + j] * dj;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += j < a.k ? wj[j] * dj[j] : 0.0f;
+    if (SS) {
+        float sh = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sh += u < SS ? sv[u] : 0.0f;
+        for (int sp = 4; sp < SS; ++sp) sh += ds[(size_t)sp * plane];
+        s += sh;
     }
-    if (a.tiles_shared) {
-        const float* d = a.dout + ((size_t)a.T * a.k + t) * a.H + o;
-        float ds = 0.0f;
-        for (int sp = 0; sp < a.splits_shared; ++sp) ds += d[sp * plane];
-        s += ds;
-    }
-    a.y[i] = __builtin_bit_cast(uint16_t, (_Float16)s);
+    a.y[(size_t)t * a.H + o] = __builtin_bit_cast(uint16_t, (_Float16)s);
 }
 
 // ---------------------------------------------------------------- debug export
@@ -1748,9 +1793,8 @@ hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s)
 
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s)
 {
-    const size_t n = (size_t)a.T * a.H;
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    if (a.T <= 0 || a.H <= 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.T, (unsigned)((a.H + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
