@@ -1204,6 +1204,49 @@ __device__ __forceinline__ void route_in_workgroup(const FfnArgs& a, int* rt)
     __syncthreads();
 }
 
+// y[t][o] of the combine (Problem statement: the layer output is the
+// gate-weighted sum of the selected experts' outputs, plus the shared
+// expert): routed partial rows of token t summed over the SR K splits, then
+// weighted and summed over the picks in pick order, plus the shared row
+// summed over its SS K splits.  Every load of the first split (and of up to
+// four shared splits) is issued before the first is used (clamped addresses,
+// masked sums): one memory round trip instead of one per term.
+__device__ __forceinline__ float combine_value(const FfnArgs& a, int t, int o, int SR, int SS)
+{
+    const size_t plane = (size_t)a.drows * a.H;
+    const float* dr = a.dout + (size_t)t * a.k * a.H + o;                      // token t's routed rows
+    const float* ds = SS ? a.dout + ((size_t)a.T * a.k + t) * a.H + o : dr;  // its shared row
+    float wj[8], dj[8], sv[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wj[j] = a.topk_w[t * a.k + min(j, a.k - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dj[j] = dr[(size_t)min(j, a.k - 1) * a.H];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sv[u] = ds[(size_t)min(u, max(SS - 1, 0)) * plane];
+    for (int sp0 = 1; sp0 < SR; sp0 += 4) {
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[u][j] = dr[(size_t)min(sp0 + u, SR - 1) * plane + (size_t)min(j, a.k - 1) * a.H];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dj[j] += sp0 + u < SR ? v[u][j] : 0.0f;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += j < a.k ? wj[j] * dj[j] : 0.0f;
+    if (SS) {
+        float sh = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sh += u < SS ? sv[u] : 0.0f;
+        for (int sp = 4; sp < SS; ++sp) sh += ds[(size_t)sp * plane];
+        s += sh;
+    }
+    return s;
+}
+
 // Workgroup order: work units are (row tile, K split) of the shared expert
 // first (its work is known to exist and is at the widest width), then of the
 // routed slots, slot by slot (slots in decreasing width).  The dispatcher deals
@@ -1596,43 +1639,8 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a)
     // grid: (token, 256-column group of H)
     const int t = blockIdx.x, o = blockIdx.y * 256 + threadIdx.x;
     if (o >= a.H) return;
-    const size_t plane = (size_t)a.drows * a.H;
-    const int SR = a.splits_routed, SS = a.tiles_shared ? a.splits_shared : 0;
-    const float* dr = a.dout + (size_t)t * a.k * a.H + o;                      // token t's routed rows
-    const float* ds = SS ? a.dout + ((size_t)a.T * a.k + t) * a.H + o : dr;  // its shared row
-    // the loads of the first K split (and of up to four shared splits) are all
-    // issued before the first is used (clamped addresses, masked sums): one
-    // memory round trip instead of one per term; sums keep the order of the
-    // definition (splits ascending, then picks ascending)
-    float wj[8], dj[8], sv[4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wj[j] = a.topk_w[t * a.k + min(j, a.k - 1)];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dj[j] = dr[(size_t)min(j, a.k - 1) * a.H];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sv[u] = ds[(size_t)min(u, max(SS - 1, 0)) * plane];
-    for (int sp0 = 1; sp0 < SR; sp0 += 4) {
-        float v[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[u][j] = dr[(size_t)min(sp0 + u, SR - 1) * plane + (size_t)min(j, a.k - 1) * a.H];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dj[j] += sp0 + u < SR ? v[u][j] : 0.0f;
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s += j < a.k ? wj[j] * dj[j] : 0.0f;
-    if (SS) {
-        float sh = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sh += u < SS ? sv[u] : 0.0f;
-        for (int sp = 4; sp < SS; ++sp) sh += ds[(size_t)sp * plane];
-        s += sh;
-    }
-    a.y[(size_t)t * a.H + o] = __builtin_bit_cast(uint16_t, (_Float16)s);
+    const float v = combine_value(a, t, o, a.splits_routed, a.tiles_shared ? a.splits_shared : 0);
+    a.y[(size_t)t * a.H + o] = __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
 // ---------------------------------------------------------------- debug export

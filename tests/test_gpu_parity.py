@@ -244,6 +244,41 @@ def test_layer_call_equals_separate_calls_qwen(qwen, T):
     compare(one, oracle.moe_layer(w, a), label="layer call T=%d" % T)
 
 
+@pytest.mark.parametrize("T", [4, 16])
+def test_decode_calls_repeatable(qwen, T):
+    """Two batches run alternately 40 times each (every fourth call with the
+    separate routing launches), y poisoned before every call: every y equals
+    the first bit for bit, and the first matches the oracle."""
+    import torch
+    import oracle
+    from any_precision_expert_amd.layer import Batch
+    w, ctx = qwen
+    spec = pw_synth.CONFIGS[1]
+    acts = [pw_synth.make_activations(spec.shape, T, pw_synth.config_seed(1), 0, 20 + i, spec.logits, w.rank)
+            for i in range(2)]
+    batches = []
+    for a in acts:
+        b = Batch(ctx, T)
+        b.load(a.logits, a.x)
+        batches.append(b)
+    outs = [[], []]
+    for rep in range(40):
+        for i, b in enumerate(batches):
+            b.y.fill_(-7.0)
+            b.step(0, separate=(rep % 4 == 3))
+            outs[i].append(b.y.clone())
+    torch.cuda.synchronize()
+    for i in range(2):
+        first = outs[i][0].cpu().numpy()
+        for rep, y in enumerate(outs[i][1:], 1):
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), first.view(np.uint16)), \
+                "batch %d, call %d: y differs from the first call" % (i, rep)
+        b = batches[i]
+        gpu = dict(idx=b.idx.cpu().numpy(), w=b.w.cpu().numpy(), offsets=b.offsets.cpu().numpy(),
+                   sorted=b.sorted.cpu().numpy()[:T * ctx.desc.top_k], y=first.astype(np.float64))
+        compare(gpu, oracle.moe_layer(w, acts[i]), label="repeated T=%d batch %d" % (T, i))
+
+
 @pytest.mark.parametrize("T", [16, 300])
 def test_layer_call_equals_separate_calls_toy(T):
     from any_precision_expert_amd.layer import register_layer
