@@ -579,8 +579,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     a.offsets = offsets;
     a.sorted = sorted;
     a.topk_w = w;
-    a.h_hi = (uint16_t*)(ws + L.h_hi);
-    a.h_lo = (uint16_t*)(ws + L.h_lo);
+    a.h = (uint16_t*)(ws + L.h);
     a.dout = (float*)(ws + L.dout);
     a.y = y;
     a.T = T;
@@ -1056,9 +1055,8 @@ WsLayout ws_layout(int T, int k, int H, int I, int Is)
     const size_t hs = (size_t)std::max(I, Is);
     const size_t splits = (size_t)std::max(down_splits(I), Is ? down_splits(Is) : 1);
     WsLayout L;
-    L.h_hi = 0;
-    L.h_lo = up(L.h_hi + rows * hs * 2);
-    L.dout = up(L.h_lo + rows * hs * 2);
+    L.h = 0;
+    L.dout = up(L.h + rows * hs * 2);
     L.total = up(L.dout + splits * rows * (size_t)H * 4);
     return L;
 }

@@ -36,8 +36,7 @@ struct FfnArgs {
     const int32_t* offsets;   // [E + 1]
     const int32_t* sorted;    // [T * k]
     const float* topk_w;      // [T * k]
-    uint16_t* h_hi;           // fp16 [T * k + T][hstride]
-    uint16_t* h_lo;           // fp16 [T * k + T][hstride]
+    uint16_t* h;              // fp16 [T * k + T][hstride]: silu(g) * u rounded to fp16
     float* dout;              // fp32 [T * k + T][H]
     uint16_t* y;              // fp16 [T][H]
     int32_t T, H, I, Is, E, k;
@@ -92,7 +91,7 @@ inline int down_splits(int K)
 // and lo [T*k (+T)][max(I, Is)], then the per-split down outputs
 // [splits][T*k (+T)][H] fp32.
 struct WsLayout {
-    size_t h_hi, h_lo, dout, total;
+    size_t h, dout, total;
 };
 WsLayout ws_layout(int T, int k, int H, int I, int Is);
 

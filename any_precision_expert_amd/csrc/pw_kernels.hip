@@ -749,12 +749,12 @@ __global__ void __launch_bounds__(1024) route_permute_kernel(const float* __rest
 // Contraction of one 64-row tile on the matrix cores (v_mfma_f32_32x32x16_f16).
 //
 // MODE 0: gate_up. Row group 0 = 32 gate rows, row group 1 = the matching 32
-//         up rows; input x (fp16); epilogue h = silu(g) * u stored as fp16 hi
-//         + fp16 lo (hi + lo carries h to about 2^-22 relative).
-// MODE 1: down. Row groups 0 / 1 = 64 consecutive output rows; input h = hi +
-//         lo (two MFMAs per step); the K range may be split over several
-//         workgroups, each writing the fp32 partial expert output of its split
-//         (summed in split order by the combine).
+//         up rows; input x (fp16); epilogue h = silu(g) * u rounded to fp16
+//         (the MFMA operand of down; accumulation stays fp32).
+// MODE 1: down. Row groups 0 / 1 = 64 consecutive output rows; input h
+//         (fp16); the K range may be split over several workgroups, each
+//         writing the fp32 partial expert output of its split (summed in
+//         split order by the combine).
 //
 // Waves 0-3 own row group 0 and waves 4-7 row group 1; the four waves of a
 // group split K by 128-column chunks.  Lane l = (rho = l % 32, kh = l / 32)
@@ -762,8 +762,8 @@ __global__ void __launch_bounds__(1024) route_permute_kernel(const float* __rest
 // (8-byte loads: a wave reads 32 rows x 16 B = 512 B contiguous per plane).
 // Word pair u pairs word u (kh = 0) with word 2 + u (kh = 1) in one 16-deep
 // MFMA step set: step P takes columns 8P..8P+7 of each word, which is exactly
-// what the gather produces for register P.  The tokens of a pass (up to
-// 8 for gate_up, 4 for down) are the MFMA's N columns; a weight is decoded once per pass.
+// what the gather produces for register P.  The tokens of a pass (up to 8)
+// are the MFMA's N columns; a weight is decoded once per pass.
 //
 // Memory pipeline.  Each wave keeps D chunks of plane loads in flight (a
 // static ring, so no in-flight register is ever moved) and loads the next
@@ -781,7 +781,7 @@ typedef __attribute__((address_space(1))) const u32x2* gu32x2p;
 typedef __attribute__((address_space(1))) const u32x4* gcu32x4p;
 typedef __attribute__((address_space(4))) const int32_t* ci32p;
 
-constexpr int kTokPass = 8;               // most tokens per pass (gate_up; down: 4)
+constexpr int kTokPass = 8;               // most tokens per pass
 constexpr int kKWaves = kWaves / 2;       // waves per row group (K split)
 constexpr int kSliceWords = 512;          // per-wave slice: 8 rows x 16 units of 16 B
 static_assert(kWaves * kSliceWords >= kStageWords, "pair staging lives in the slice region");
@@ -805,16 +805,18 @@ template <int Q>
 __device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const BlockDesc* __restrict__ bd, int c, int R,
                                                 int row, int kh)
 {
-    const size_t at = ((size_t)c * R + row) * 2 + kh;
+    // byte offset in 32 bits (a plane is below 4 GB): the loads take the
+    // plane pointer as a scalar base and one shared vector offset
+    const uint32_t at = (((uint32_t)c * (uint32_t)R + (uint32_t)row) * 2u + (uint32_t)kh) * 8u;
     const __attribute__((address_space(4))) BlockDesc* cbd = (const __attribute__((address_space(4))) BlockDesc*)(uintptr_t)bd;
 #pragma unroll
-    for (int p = 0; p < Q; ++p) pg[p] = __builtin_nontemporal_load((gu32x2p)(uintptr_t)cbd->planes[p] + at);
+    for (int p = 0; p < Q; ++p) pg[p] = __builtin_nontemporal_load((gu32x2p)((uintptr_t)cbd->planes[p] + at));
 }
 
-// 16-byte unit g (8 fp16 columns) of row j of a wave's slice: gate_up rows
-// are the pass's tokens (up to 8), down rows are the tokens' h hi (0-3) and h
-// lo (4-7).  The unit index is XOR-swizzled with the token so the B reads of
-// different tokens in one instruction fall in different banks.
+// 16-byte unit g (8 fp16 columns) of row j of a wave's slice: the rows are
+// the pass's tokens (up to 8; x for gate_up, h for down).  The unit index is
+// XOR-swizzled with the token so the B reads of different tokens in one
+// instruction fall in different banks.
 __device__ __forceinline__ int slice_unit(int j, int t, int g)
 {
     return j * 16 + (g ^ t);
@@ -828,7 +830,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
 {
     constexpr int D = Q <= 4 ? 2 : 1;      // chunks of plane loads in flight
     constexpr int NPART = 2;               // activation loads per lane and chunk
-    constexpr int TP = MODE == 0 ? 8 : 4;  // tokens per pass
+    constexpr int TP = 8;                  // tokens per pass
     constexpr int KW = kWaves / RG;        // waves per row group (K split)
     constexpr bool PAIR = LutLoad<Q, RG>::PAIR;
     constexpr int HR = 16 * RG;            // gate_up: h rows per tile (gate and up rows each)
@@ -887,9 +889,9 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     const uint16_t* xsrc[NPART];
     int nt = 0;
 
-    // Activation rows of the pass starting at t0: gate_up tokens xt and
-    // xt + 4, down token xt's h hi and lo (tokens past the pass repeat its
-    // last token, whose slots are never read).
+    // Activation rows of the pass starting at t0: tokens xt and xt + 4 (x for
+    // gate_up, h for down; tokens past the pass repeat its last token, whose
+    // slots are never read).
     auto set_sources = [&](int t0) {
         nt = min(TP, ntok - t0);
         if (MODE == 0) {
@@ -921,10 +923,12 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
             xsrc[0] = a.x + (size_t)tok[0] * a.H;
             xsrc[1] = a.x + (size_t)tok[1] * a.H;
         } else {
-            const int te = min(xt, nt - 1);
-            const int hrow = shared ? TK + t0 + te : p0 + t0 + te;
-            xsrc[0] = a.h_hi + (size_t)hrow * a.hstride;
-            xsrc[1] = a.h_lo + (size_t)hrow * a.hstride;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int te = min(xt + 4 * h, nt - 1);
+                const int hrow = shared ? TK + t0 + te : p0 + t0 + te;
+                xsrc[h] = a.h + (size_t)hrow * a.hstride;
+            }
         }
     };
     // activation unit of chunk c (column clamped into the row; the store zeroes it)
@@ -972,7 +976,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 const bool ok = live && c * kChunkCols + 8 * xg < K;
 #pragma unroll
                 for (int pp = 0; pp < NPART; ++pp)
-                    slice4[slice_unit(4 * pp + xt, MODE == 0 ? 4 * pp + xt : xt, xg)] = ok ? xv[pp] : u32x4{0, 0, 0, 0};
+                    slice4[slice_unit(4 * pp + xt, 4 * pp + xt, xg)] = ok ? xv[pp] : u32x4{0, 0, 0, 0};
                 // prefetch: next chunk's activations, then the planes D chunks on
                 u32x2 cur[Q];
 #pragma unroll
@@ -1011,8 +1015,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                     else return step_codes<Q, PAIR>(rt, P, masks, acc0(P));
                 };
                 prepare(0);
-                u32x4 bh = slice4[b_unit(0, te)], bl = {0, 0, 0, 0};
-                if (MODE == 1) bl = slice4[b_unit(0, 4 + te)];
+                u32x4 bh = slice4[b_unit(0, te)];
                 StepRaw raw;
                 step_lookup<PAIR>(codes(0), lane_off, lutb, raw);
 #pragma unroll
@@ -1021,14 +1024,12 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                     if (s < 7 && s != 3) next = codes((s + 1) & 3);
                     const half8 A = step_pack<PAIR>(raw);
                     C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bh), C, 0, 0, 0);
-                    if (MODE == 1) C = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bl), C, 0, 0, 0);
                     if (s == 3) {  // word pair 1, once step 3's operands are consumed
                         prepare(1);
                         next = codes(0);
                     }
                     if (s < 7) {
                         bh = slice4[b_unit(s + 1, te)];
-                        if (MODE == 1) bl = slice4[b_unit(s + 1, 4 + te)];
                         step_lookup<PAIR>(next, lane_off, lutb, raw);
                     }
                 }
@@ -1059,12 +1060,8 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 const int i = tile * HR + hr;
                 if (i < Iblk) {
                     const float h = g / (1.0f + __expf(-g)) * u;
-                    const _Float16 hi = (_Float16)h;
-                    const _Float16 lo = (_Float16)(h - (float)hi);
                     const int hrow = shared ? TK + t0 + n : p0 + t0 + n;
-                    const size_t o = (size_t)hrow * a.hstride + i;
-                    a.h_hi[o] = __builtin_bit_cast(uint16_t, hi);
-                    a.h_lo[o] = __builtin_bit_cast(uint16_t, lo);
+                    a.h[(size_t)hrow * a.hstride + i] = __builtin_bit_cast(uint16_t, (_Float16)h);
                 }
             }
         } else {
@@ -1422,7 +1419,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
         xsrc = a.x + (size_t)tok * a.H;
     } else {
         const int hrow = shared ? TK + te : p0 + te;
-        xsrc = a.h_hi + (size_t)hrow * a.hstride;
+        xsrc = a.h + (size_t)hrow * a.hstride;
     }
 
     u32x4* wt = (u32x4*)(lds + kPfW);  // [buffer][128 rows x 4 units]
@@ -1543,7 +1540,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
                             const float g = C[i][j][e], u = up[r * kPfTok + t];
                             const float h = g / (1.0f + __expf(-g)) * u;
                             const int hrow = shared ? TK + n0 + t : p0 + n0 + t;
-                            a.h_hi[(size_t)hrow * a.hstride + hi] = __builtin_bit_cast(uint16_t, (_Float16)h);
+                            a.h[(size_t)hrow * a.hstride + hi] = __builtin_bit_cast(uint16_t, (_Float16)h);
                         }
                     }
         }

@@ -58,8 +58,8 @@ def step_bytes(shape, wq, offsets, T):
         dn += block_bytes(H, Is, 8)
     rows_h = T * k * I + (T * Is if Is else 0)
     rows_d = (T * k + (T if Is else 0)) * H
-    gate_up = gu + T * H * 2 + rows_h * 4          # planes+LUT, x in, h (hi+lo fp16) out
-    down = dn + rows_h * 4 + rows_d * 4            # planes+LUT, h in, per-assignment d out
+    gate_up = gu + T * H * 2 + rows_h * 2          # planes+LUT, x in, h (fp16) out
+    down = dn + rows_h * 2 + rows_d * 4            # planes+LUT, h in, per-assignment d out
     path = gu + dn + T * H * 2 + T * H * 2 + T * E * 4  # weights + x + y + logits
     return dict(gate_up=gate_up, down=down, path=path, weights=gu + dn, active=len(active))
 
