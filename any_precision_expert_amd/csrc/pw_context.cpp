@@ -274,24 +274,25 @@ void free_block_now(pw_ctx* c, HostBlock& b)
 // is enabled, so recording adds no allocation to the launch path.
 constexpr size_t kProfEvents = 1 << 14;
 
+// The first kernel launched inside the scope records a pair of pool events
+// from its own dispatch (start and end of the kernel itself).
 struct ProfScope {
     pw_ctx* c;
     const char* name;
-    hipStream_t s;
-    hipEvent_t a = nullptr;
-    ProfScope(pw_ctx* c_, const char* n, hipStream_t s_) : c(c_), name(n), s(s_)
+    LaunchEvents ev;
+    ProfScope(pw_ctx* c_, const char* n, hipStream_t) : c(c_), name(n)
     {
         if (c->profiling && c->prof_next + 2 <= c->prof_pool.size()) {
-            a = c->prof_pool[c->prof_next++];
-            (void)hipEventRecord(a, s);
+            ev.start = c->prof_pool[c->prof_next++];
+            ev.stop = c->prof_pool[c->prof_next++];
+            launch_events = &ev;
         }
     }
     ~ProfScope()
     {
-        if (!a) return;
-        hipEvent_t b = c->prof_pool[c->prof_next++];
-        (void)hipEventRecord(b, s);
-        c->prof[name].push_back({a, b});
+        if (!ev.start) return;
+        launch_events = nullptr;
+        if (ev.used) c->prof[name].push_back({ev.start, ev.stop});
     }
 };
 

@@ -96,6 +96,16 @@ struct WsLayout {
 WsLayout ws_layout(int T, int k, int H, int I, int Is);
 
 // Launchers (return the launch's hipError_t).
+// Timing of one launch by its own dispatch (hipExtLaunchKernelGGL start /
+// stop events): while launch_events points at an unused pair, the next kernel
+// launched on this thread records it and sets `used`.  The events then bracket
+// the kernel alone, not the queue packets around it.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool used = false;
+};
+extern thread_local LaunchEvents* launch_events;
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                              hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,

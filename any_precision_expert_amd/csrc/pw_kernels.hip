@@ -23,6 +23,7 @@
 // packed half2) per look-up.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include "pw_internal.h"
 
@@ -1729,24 +1730,38 @@ __global__ void __launch_bounds__(64) debug_decode_kernel(const BlockDesc* __res
 
 // ---------------------------------------------------------------- launchers
 
+thread_local LaunchEvents* launch_events = nullptr;
+
+template <typename Kern, typename... Args>
+static void launch(Kern kernel, dim3 grid, dim3 block, hipStream_t s, Args... args)
+{
+    LaunchEvents* ev = launch_events;
+    if (ev && !ev->used) {
+        ev->used = true;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev->start, ev->stop, 0, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    }
+}
+
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s)
 {
-    hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+    launch(route_topk_kernel, dim3((T + 3) / 4), dim3(256), s, logits, T, E, k, idx, w);
     return hipGetLastError();
 }
 
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* offsets,
                                 int32_t* sorted, hipStream_t s)
 {
-    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(1024), 0, s, logits, T, E, k, idx, w, offsets, sorted);
+    launch(route_permute_kernel, dim3(1), dim3(1024), s, logits, T, E, k, idx, w, offsets, sorted);
     return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* sorted,
                           hipStream_t s)
 {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, idx, T * k, E, offsets, sorted);
+    launch(permute_kernel, dim3(1), dim3(1024), s, idx, T * k, E, offsets, sorted);
     return hipGetLastError();
 }
 
@@ -1765,11 +1780,11 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
     if (grid == 0) return hipSuccess;
     if (a.logits) {
         if (a.rg != 4 || a.T * a.k > kLayerRouteMaxAssign || a.E > 256) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((ffn_gemv_kernel<0, 4, true>), dim3(grid), dim3(kThreads), 0, s, a);
+        launch((ffn_gemv_kernel<0, 4, true>), dim3(grid), dim3(kThreads), s, a);
     } else if (a.rg == 4) {
-        hipLaunchKernelGGL((ffn_gemv_kernel<0, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+        launch((ffn_gemv_kernel<0, 4>), dim3(grid), dim3(kThreads), s, a);
     } else {
-        hipLaunchKernelGGL((ffn_gemv_kernel<0, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+        launch((ffn_gemv_kernel<0, 2>), dim3(grid), dim3(kThreads), s, a);
     }
     return hipGetLastError();
 }
@@ -1779,9 +1794,9 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s)
     const int grid = gemv_grid(a);
     if (grid == 0) return hipSuccess;
     if (a.rg == 4)
-        hipLaunchKernelGGL((ffn_gemv_kernel<1, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+        launch((ffn_gemv_kernel<1, 4>), dim3(grid), dim3(kThreads), s, a);
     else
-        hipLaunchKernelGGL((ffn_gemv_kernel<1, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+        launch((ffn_gemv_kernel<1, 2>), dim3(grid), dim3(kThreads), s, a);
     return hipGetLastError();
 }
 
@@ -1790,30 +1805,30 @@ hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s)
     const int grid = a.tiles_shared * a.tok_tiles_shared + a.tiles_routed * a.tok_tiles_routed;
     if (grid == 0) return hipSuccess;
     if (module == 0)
-        hipLaunchKernelGGL(ffn_prefill_kernel<0>, dim3(grid), dim3(kPfThreads), 0, s, a);
+        launch(ffn_prefill_kernel<0>, dim3(grid), dim3(kPfThreads), s, a);
     else
-        hipLaunchKernelGGL(ffn_prefill_kernel<1>, dim3(grid), dim3(kPfThreads), 0, s, a);
+        launch(ffn_prefill_kernel<1>, dim3(grid), dim3(kPfThreads), s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s)
 {
     if (a.T <= 0 || a.H <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.T, (unsigned)((a.H + 255) / 256)), dim3(256), 0, s, a);
+    launch(combine_kernel, dim3((unsigned)a.T, (unsigned)((a.H + 255) / 256)), dim3(256), s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_routing_mass(const int32_t* offsets, const int32_t* sorted, const float* w, int E, double* mass,
                                hipStream_t s)
 {
-    hipLaunchKernelGGL(routing_mass_kernel, dim3(1), dim3(256), 0, s, offsets, sorted, w, E, mass);
+    launch(routing_mass_kernel, dim3(1), dim3(256), s, offsets, sorted, w, E, mass);
     return hipGetLastError();
 }
 
 hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s)
 {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_f64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    launch(fill_f64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, p, n);
     return hipGetLastError();
 }
 
@@ -1821,7 +1836,7 @@ hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int K,
                                uint16_t* w_out, hipStream_t s)
 {
     const int tiles = lut_slots(R, module) / 32;
-    hipLaunchKernelGGL(debug_decode_kernel, dim3(tiles), dim3(64), 0, s, entry, module, R, K, codes_out, w_out);
+    launch(debug_decode_kernel, dim3(tiles), dim3(64), s, entry, module, R, K, codes_out, w_out);
     return hipGetLastError();
 }
 

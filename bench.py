@@ -17,8 +17,10 @@ region replays a HIP graph of those steps (no host launch overhead), with the
 inputs already resident in HBM.
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (gate_up):
-algorithmic bytes per launch / its mean duration from HIP events recorded
-around every launch on the launch stream.  `cpu_baseline` times the fp64 CPU
+algorithmic bytes per launch / its mean duration from the HIP start / stop
+events that each launch records from its own dispatch (hipExtLaunchKernelGGL
+on the launch stream), over a pass of the same steps right after the timed
+region.  `cpu_baseline` times the fp64 CPU
 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -497,7 +499,8 @@ def main():
     log("timed %d steps: %.4f ms/step (wall %.4f ms/step), %.0f tokens/s/layer, path %.1f GB/s"
         % (n, ms_per_step, wall_s / n * 1e3, tok_s, mean_b["path"] / (ms_per_step * 1e-3) / 1e9))
 
-    # per-kernel durations: HIP events around every launch, on the launch stream
+    # per-kernel durations: start / stop events recorded by each launch's own
+    # dispatch on the launch stream (the kernel alone, no queue packets)
     ctx.profile_enable(True)
     with torch.cuda.stream(stream):
         run_steps(min(args.steps, 1600))
