@@ -783,7 +783,6 @@ typedef __attribute__((address_space(1))) const u32x4* gcu32x4p;
 typedef __attribute__((address_space(4))) const int32_t* ci32p;
 
 constexpr int kTokPass = 8;               // most tokens per pass
-constexpr int kKWaves = kWaves / 2;       // waves per row group (K split)
 constexpr int kSliceWords = 512;          // per-wave slice: 8 rows x 16 units of 16 B
 static_assert(kWaves * kSliceWords >= kStageWords, "pair staging lives in the slice region");
 static_assert(kWaves * 32 * kTokPass <= kWaves * kSliceWords, "reduction lives in the slice region");
@@ -1385,7 +1384,6 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int R = bd->R;
     const int kwords = bd->kwords;
-    const int K = kwords * 32;
     const int nsteps = kwords;
     const int Iblk = R >> 1;
     const int TK = a.T * a.k;
