@@ -169,6 +169,46 @@ def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, copy_
     print("\n".join(lines))
 
 
+def summarize_counters(dirs, out, commands, title):
+    """Per-kernel means of every counter in one or more rocprofv3 --pmc runs
+    (each pass in a directory of its own) -> markdown.  Wait / active counters
+    are also given as a share of SQ_WAVE_CYCLES when that counter was taken."""
+    from collections import defaultdict
+    agg = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        for r in _csv_rows(_find(d, "counter_collection.csv")):
+            name = r["Kernel_Name"].split("(")[0]
+            if "pw::" not in name:
+                continue
+            agg[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = ["# " + title, ""] + ["Command: `%s`" % c for c in commands] + [""]
+    counters = sorted({c for k in agg.values() for c in k})
+    lines += ["| kernel | dispatches | " + " | ".join(counters) + " |",
+              "|---|---|" + "---|" * len(counters)]
+    for name, cs in agg.items():
+        n = max(len(v) for v in cs.values())
+        vals = []
+        for c in counters:
+            v = cs.get(c)
+            vals.append("%.4g" % (sum(v) / len(v)) if v else "")
+        lines.append("| %s | %d | %s |" % (name, n, " | ".join(vals)))
+    share = [c for c in counters if c.startswith(("SQ_WAIT", "SQ_ACTIVE"))]
+    if "SQ_WAVE_CYCLES" in counters and share:
+        lines += ["", "Share of wave cycles (counter / SQ_WAVE_CYCLES, per kernel):", "",
+                  "| kernel | " + " | ".join(share) + " |", "|---|" + "---|" * len(share)]
+        for name, cs in agg.items():
+            if "SQ_WAVE_CYCLES" not in cs:
+                continue
+            wc = sum(cs["SQ_WAVE_CYCLES"]) / len(cs["SQ_WAVE_CYCLES"])
+            if wc <= 0:
+                continue
+            lines.append("| %s | %s |" % (name, " | ".join(
+                "%.1f%%" % (100.0 * sum(cs[c]) / len(cs[c]) / wc) if c in cs else "" for c in share)))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 MFMA_F16_PEAK_TFLOPS = 2500.0
 PREFILL_CFG = 3
 
@@ -396,6 +436,9 @@ def main():
                     help="after the bench, copy this many MiB device-to-device (PMC scale reference)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"))
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_MD"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR_OR_OUT_MD",
+                    help="PMC_DIR [PMC_DIR ...] OUT_MD: per-kernel counter means of rocprofv3 --pmc runs")
+    ap.add_argument("--title", default="PMC counters per kernel")
     ap.add_argument("--command", default="", help="command line recorded in the summary")
     ap.add_argument("--command2", default="", help="second command line (WRITE_SIZE pass)")
     ap.add_argument("--alg-bytes", type=float, default=0.0, help="gate_up algorithmic bytes per launch")
@@ -406,6 +449,10 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2], args.command,
                       args.command2, args.copy_calibration_mib, args.alg_bytes)
+        return
+    if args.summarize_counters:
+        cmds = [c for c in (args.command, args.command2) if c]
+        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], cmds, args.title)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",
