@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "pw_internal.h"
 
 namespace pw {
@@ -1340,25 +1342,32 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 // ---------------------------------------------------------------- prefill GEMM
 //
 // Large token counts per expert (prefill): an expert's contraction is a GEMM
-// [tokens x K] x [rows x K]^T on the matrix cores.  One 8-wave workgroup per
+// [tokens x K] x [rows x K]^T on the matrix cores.  One 16-wave workgroup per
 // CU owns 128 weight rows (gate_up: 64 gate rows and their 64 up rows; down:
 // 128 output rows) x 512 tokens and walks K in 32-column steps (one plane
 // word).  The weight and activation tiles of a step live in LDS, double
-// buffered: while the waves run the MFMAs of step s they decode step s + 1's
-// weights (each thread: one row, 8 columns, with the same gather and LUT
-// look-up as the decode path) and store the activations of step s + 1 (each
-// thread: one token row, gathered through the expert's assignment list), so
-// decode and matrix work overlap and one barrier ends a step.  Global loads
-// run two steps ahead.  Tiles are XOR-swizzled by row so the fragment reads
-// and the stores are conflict-free.  Each wave owns 64 rows x 128 tokens (2 x
-// 4 blocks of v_mfma_f32_32x32x16_f16); a weight is decoded once per 512
-// tokens.  gate_up writes h = silu(g) * u rounded to fp16 (the MFMA operand of
+// buffered: while the waves run the MFMAs of step s, waves 0-7 decode step
+// s + 1's weights (each thread: one row, 8 columns, with the same gather and
+// LUT look-up as the decode path) and waves 8-15 store the activations of
+// step s + 1 (each thread: one token row, gathered through the expert's
+// assignment list), so decode and matrix work overlap and one barrier ends a
+// step.  Global loads run two steps ahead.  Tiles are XOR-swizzled by row so
+// the fragment reads and the stores are conflict-free.  Each wave owns 64
+// rows x 64 tokens (2 x 2 blocks of v_mfma_f32_32x32x16_f16); a weight is
+// decoded once per 512 tokens.  gate_up writes h = silu(g) * u rounded to fp16 (the MFMA operand of
 // the down GEMM); down writes the fp32 expert outputs that the combine
 // weights and sums.
 
 constexpr int kPfRows = 128;   // weight rows per tile
 constexpr int kPfTok = 512;    // tokens per tile
-constexpr int kPfThreads = 512;
+// 16 waves per prefill workgroup (four per SIMD; 8 is the two-per-SIMD form
+// in which every thread both decodes and gathers: 5% slower on the
+// Mixtral-shaped prefill layer)
+#ifndef PW_PF_WAVES
+#define PW_PF_WAVES 16
+#endif
+constexpr int kPfWaves = PW_PF_WAVES;
+constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfStepCols = 32;  // columns per K step (one plane word)
 // LDS words: LUT (64 KB) | weight tiles 2 x [128 rows][4 units] | activation tiles 2 x [512 tokens][4 units]
 constexpr int kPfW = kLutBytes / 4;
@@ -1375,13 +1384,21 @@ static_assert(64 * kPfTok <= kPfLdsWords, "gate_up epilogue exchange fits in LDS
 // LDS banks
 __device__ __forceinline__ int pf_unit(int r, int u) { return r * 4 + (u ^ (((r >> 1) ^ (r >> 3)) & 3)); }
 
-template <int MODE, int Q>
+template <int MODE, int Q, int W>
 __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
                                               int ntok, int mtile, int ntile, uint32_t* lds)
 {
     constexpr bool PAIR = LutLoad<Q, 4>::PAIR;
+    constexpr int NTH = 64 * W;
+    // W = 8: every thread decodes one unit and gathers one token row per
+    // step.  W = 16: waves 0-7 decode, waves 8-15 gather; every wave does
+    // matrix work, so each SIMD runs four waves.
+    constexpr bool SPLIT = W == 16;
+    constexpr int TB = W == 8 ? 4 : 2;  // 32-token blocks per wave
+    constexpr int TS = 32 * TB;         // tokens per wave
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool decoder = !SPLIT || wave < 8;
     const int R = bd->R;
     const int kwords = bd->kwords;
     const int nsteps = kwords;
@@ -1399,7 +1416,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
         }
     };
     // decoder: thread = (tile row dr, 8-column unit dP of the step's word)
-    const int dr = tid & (kPfRows - 1), dP = wave >> 1;  // dP is wave-uniform
+    const int dr = tid & (kPfRows - 1), dP = (wave >> 1) & 3;  // dP is wave-uniform
     bool dvalid;
     const int drow = tile_row(dr, dvalid);
     const int dlrow = dvalid ? drow : 0;
@@ -1409,9 +1426,10 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     const int lslot = MODE == 0 ? dr & 63 : 32 * (dr >> 6) + (dr & 31);
     const uint32_t lane_off = lut_lane_off<Q, 4>(lslot, half);
     const uint32_t acc0 = PAIR && half ? rotl(0x01010101u << (2 * Q), dP) : 0u;
-    // activation loader: thread = token row tid of the tile
+    // activation loader: thread = token row xr_t of the tile
+    const int xt_row = SPLIT ? (tid & 511) : tid;
     const int n0 = ntile * kPfTok;
-    const int te = n0 + tid < ntok ? n0 + tid : n0;
+    const int te = n0 + xt_row < ntok ? n0 + xt_row : n0;
     const uint16_t* xsrc;
     if (MODE == 0) {
         const int tok = shared ? te : a.sorted[p0 + te] / a.k;
@@ -1426,102 +1444,118 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     const char* lutb = (const char*)lds;
     const __attribute__((address_space(4))) BlockDesc* cbd =
         (const __attribute__((address_space(4))) BlockDesc*)(uintptr_t)bd;
-
-    // loads of step s (columns 32 s .. 32 s + 31); two steps are in flight
-    u32x4 xr[2][4];
-    uint32_t pw[2][Q];
-    auto issue = [&](int st, int slot) {
-        const int s = min(st, nsteps - 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xr[slot][j] = *(gcu32x4p)(uintptr_t)(xsrc + s * kPfStepCols + 8 * j);
-        const size_t at = ((size_t)(s >> 2) * R + dlrow) * 4 + (s & 3);
-#pragma unroll
-        for (int p = 0; p < Q; ++p)
-            pw[slot][p] = __builtin_nontemporal_load((__attribute__((address_space(1))) const uint32_t*)(uintptr_t)cbd->planes[p] + at);
-    };
-    // step s (loaded in `slot`) -> LDS buffer s & 1
-    auto stage = [&](int s, int slot) {
-        const int buf = s & 1;
-        Rot<Q, PAIR> rt;
-        rotate_planes<Q, PAIR>(pw[slot], rt);
-        const half8 A = step_weights_u<Q, PAIR>(rt, dP, lane_off, lutb, acc0);
-        wt[buf * (kPfWWords / 4) + pf_unit(dr, dP)] = __builtin_bit_cast(u32x4, A);
-        // steps past K (padding to an even count) multiply by zero activations
-        const bool live = s < nsteps;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xt[buf * (kPfXWords / 4) + pf_unit(tid, j)] = live ? xr[slot][j] : u32x4{0, 0, 0, 0};
-    };
-
-    {
-        LutLoad<Q, 4> ls;
-        ls.issue(bd->lut, bd->slots, mtile * LutLoad<Q, 4>::NSLOT, lane, wave);
-        issue(0, 0);
-        issue(1, 1);
-        ls.commit(lds, lds + kPfW, lane, wave);  // pair staging in the (idle) weight tiles
-        __syncthreads();
-    }
-    stage(0, 0);
-    issue(2, 0);
-    __syncthreads();
-
-    const int rb = wave & 1, tb = wave >> 1;  // this wave: 64 rows x 128 tokens
-    f32x16 C[2][4];
+    const int rb = wave & 1, tb = wave >> 1;  // this wave: 64 rows x TS tokens
+    f32x16 C[2][TB];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) C[i][j] = f32x16{};
+        for (int j = 0; j < TB; ++j) C[i][j] = f32x16{};
 
-    // K steps in pairs so the register slots of the loads stay static; the
-    // body is branch-free (a branch would make the compiler wait for every
-    // load in flight at its join)
-    for (int s = 0; s < nsteps; s += 2) {
+    // The K loop of one role (DW: decode weights, DX: gather activations),
+    // so that a thread's registers hold only its own role's loads.  Loads of
+    // step s (columns 32 s .. 32 s + 31); two steps are in flight.
+    auto run = [&](auto dw_tag, auto dx_tag) {
+        constexpr bool DW = decltype(dw_tag)::value, DX = decltype(dx_tag)::value;
+        u32x4 xr[2][DX ? 4 : 1];
+        uint32_t pw[2][DW ? Q : 1];
+        auto issue = [&](int st, int slot) {
+            const int s = min(st, nsteps - 1);
+            if constexpr (DX) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int st = s + h;
-            {
+                for (int j = 0; j < 4; ++j) xr[slot][j] = *(gcu32x4p)(uintptr_t)(xsrc + s * kPfStepCols + 8 * j);
+            }
+            if constexpr (DW) {
+                const size_t at = ((size_t)(s >> 2) * R + dlrow) * 4 + (s & 3);
+#pragma unroll
+                for (int p = 0; p < Q; ++p)
+                    pw[slot][p] = __builtin_nontemporal_load(
+                        (__attribute__((address_space(1))) const uint32_t*)(uintptr_t)cbd->planes[p] + at);
+            }
+        };
+        // step s (loaded in `slot`) -> LDS buffer s & 1
+        auto stage = [&](int s, int slot) {
+            const int buf = s & 1;
+            if constexpr (DW) {
+                Rot<Q, PAIR> rt;
+                rotate_planes<Q, PAIR>(pw[slot], rt);
+                const half8 A = step_weights_u<Q, PAIR>(rt, dP, lane_off, lutb, acc0);
+                wt[buf * (kPfWWords / 4) + pf_unit(dr, dP)] = __builtin_bit_cast(u32x4, A);
+            }
+            if constexpr (DX) {
+                // steps past K (padding to an even count) multiply by zero activations
+                const bool live = s < nsteps;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xt[buf * (kPfXWords / 4) + pf_unit(xt_row, j)] = live ? xr[slot][j] : u32x4{0, 0, 0, 0};
+            }
+        };
+        {
+            LutLoad<Q, 4, NTH> ls;
+            ls.issue(bd->lut, bd->slots, mtile * LutLoad<Q, 4, NTH>::NSLOT, lane, wave);
+            issue(0, 0);
+            issue(1, 1);
+            ls.commit(lds, lds + kPfW, lane, wave);  // pair staging in the (idle) weight tiles
+            __syncthreads();
+        }
+        stage(0, 0);
+        issue(2, 0);
+        __syncthreads();
+        // K steps in pairs so the register slots of the loads stay static;
+        // the body is branch-free (a branch would make the compiler wait for
+        // every load in flight at its join).  After the matrix work of step
+        // st: step st + 1 into the other buffer, then the loads of st + 3
+        // into the registers just consumed (kept in this order: a load
+        // hoisted above the stores would force register copies and a wait
+        // for every load in flight).
+        for (int s = 0; s < nsteps; s += 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int st = s + h;
                 const int buf = st & 1;
-                // matrix work of step st
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const int u = 2 * kk + (lane >> 5);
-                    half8 Af[2], Bf[4];
+                    half8 Af[2], Bf[TB];
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
                         Af[i] = __builtin_bit_cast(half8, wt[buf * (kPfWWords / 4) + pf_unit(64 * rb + 32 * i + (lane & 31), u)]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        Bf[j] = __builtin_bit_cast(half8, xt[buf * (kPfXWords / 4) + pf_unit(128 * tb + 32 * j + (lane & 31), u)]);
+                    for (int j = 0; j < TB; ++j)
+                        Bf[j] = __builtin_bit_cast(half8, xt[buf * (kPfXWords / 4) + pf_unit(TS * tb + 32 * j + (lane & 31), u)]);
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
+                        for (int j = 0; j < TB; ++j)
                             C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i], Bf[j], C[i][j], 0, 0, 0);
                 }
-                // step st + 1 into the other buffer, then the loads of st + 3
-                // into the registers just consumed (kept in this order: a
-                // load hoisted above the stores would force register copies
-                // and a wait for every load in flight)
                 stage(st + 1, 1 - h);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(st + 3, 1 - h);
+                __syncthreads();
             }
-            __syncthreads();
         }
+    };
+    // both roles pass the same barriers
+    if constexpr (SPLIT) {
+        if (decoder) run(std::true_type{}, std::false_type{});
+        else run(std::false_type{}, std::true_type{});
+    } else {
+        run(std::true_type{}, std::true_type{});
     }
 
     // epilogue; C[i][j][e]: tile row 64 rb + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
-    // token n0 + 128 tb + 32 j + lane % 32
+    // token n0 + TS tb + 32 j + lane % 32
     if (MODE == 0) {
         float* up = (float*)lds;  // [64 rows][512 tokens]
         if (rb == 1) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < TB; ++j)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                        up[r * kPfTok + 128 * tb + 32 * j + (lane & 31)] = C[i][j][e];
+                        up[r * kPfTok + TS * tb + 32 * j + (lane & 31)] = C[i][j][e];
                     }
         }
         __syncthreads();
@@ -1529,11 +1563,11 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < TB; ++j)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                        const int t = 128 * tb + 32 * j + (lane & 31);
+                        const int t = TS * tb + 32 * j + (lane & 31);
                         const int hi = mtile * 64 + r;
                         if (n0 + t < ntok && hi < Iblk) {
                             const float g = C[i][j][e], u = up[r * kPfTok + t];
@@ -1545,8 +1579,8 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = 128 * tb + 32 * j + (lane & 31);
+        for (int j = 0; j < TB; ++j) {
+            const int t = TS * tb + 32 * j + (lane & 31);
             if (n0 + t >= ntok) continue;
             const int orow = shared ? TK + n0 + t : a.sorted[p0 + n0 + t];
             float* dst = a.dout + (size_t)orow * a.H + mtile * kPfRows;
@@ -1567,7 +1601,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
 // tile return at once.  Row tiles are fastest so neighbouring workgroups share
 // an activation tile.
 template <int MODE>
-__global__ void __launch_bounds__(kPfThreads, 2) ffn_prefill_kernel(FfnArgs a)
+__global__ void __launch_bounds__(kPfThreads, kPfWaves / 4) ffn_prefill_kernel(FfnArgs a)
 {
     __shared__ __align__(16) uint32_t lds[kPfLdsWords];
     KArgs& ka = kernel_args();
@@ -1619,12 +1653,12 @@ __global__ void __launch_bounds__(kPfThreads, 2) ffn_prefill_kernel(FfnArgs a)
     }
     const BlockDesc* bd = a.table + (e * 2 + MODE);
     switch (bd->q) {
-        case 3: prefill_block<MODE, 3>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 4: prefill_block<MODE, 4>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 5: prefill_block<MODE, 5>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 6: prefill_block<MODE, 6>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 7: prefill_block<MODE, 7>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 8: prefill_block<MODE, 8>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 3: prefill_block<MODE, 3, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 4: prefill_block<MODE, 4, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 5: prefill_block<MODE, 5, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 6: prefill_block<MODE, 6, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 7: prefill_block<MODE, 7, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 8: prefill_block<MODE, 8, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
         default: break;
     }
 }
