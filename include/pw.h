@@ -176,10 +176,10 @@ pw_status pw_moe_ffn_bitplane(pw_ctx *ctx, int layer, const uint16_t *x, int T,
  * all of them run at once: at most two per compute unit, counting the
  * shared expert's 64-row tiles and min(E, T*k) routed blocks' 64-row tiles)
  * the routing runs inside the gate_up launch:
- * every workgroup with routed work routes and sorts the batch in LDS (a
- * fraction of a microsecond of its start-up) instead of waiting for a separate
- * routing launch, and one of them writes the routing outputs for the caller
- * and for the down and combine launches.  Larger batches run the separate
+ * every workgroup with routed work routes and sorts the batch in LDS (3-5 us
+ * of its start-up, while the shared expert's workgroups already stream)
+ * instead of waiting for a separate routing launch, and one of them writes
+ * the routing outputs for the caller and for the down and combine launches.  Larger batches run the separate
  * launches.  logits: dev fp32 [T][E]; the other arguments, the errors and the
  * workspace rule are those of the two calls.  T = 0 sets expert_offsets to
  * zero and enqueues nothing else. */
