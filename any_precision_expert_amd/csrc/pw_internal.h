@@ -78,17 +78,21 @@ constexpr int kPrefillMinT = 256;
 constexpr int kGateUpRowGroups = 4;
 constexpr int kDownRowGroups = 2;
 
-// K splits of a down-projection row tile: about kChunksPerSplit 128-column
-// chunks per workgroup (two per wave), so long K ranges spread over the chip.
-constexpr int kChunksPerSplit = 16;
+// K splits of a down-projection row tile, so long K ranges spread over the
+// chip: at most 16 128-column chunks per workgroup (four per wave) up to 64
+// chunks, at most 32 beyond.  Each split stages the tile's whole LUT again,
+// so for long K (Mixtral-shaped, 112 chunks) fewer, longer splits win (down
+// -10..-18% at batch 1-16), while a short K (the Qwen-shaped shared expert,
+// 44 chunks) needs the parallelism of 16-chunk splits.
 inline int down_splits(int K)
 {
     const int nchunks = (K + kChunkCols - 1) / kChunkCols;
-    return nchunks <= kChunksPerSplit ? 1 : (nchunks + kChunksPerSplit - 1) / kChunksPerSplit;
+    const int per = nchunks > 64 ? 32 : 16;
+    return nchunks <= per ? 1 : (nchunks + per - 1) / per;
 }
 
-// Workspace carve-up for T tokens (byte offsets, 256-aligned): h as fp16 hi
-// and lo [T*k (+T)][max(I, Is)], then the per-split down outputs
+// Workspace carve-up for T tokens (byte offsets, 256-aligned): h as fp16
+// [T*k (+T)][max(I, Is)], then the per-split down outputs
 // [splits][T*k (+T)][H] fp32.
 struct WsLayout {
     size_t h, dout, total;

@@ -270,6 +270,66 @@ def prefill_leg(steps):
                          "frac": round(gu_tf / MFMA_F16_PEAK_TFLOPS, 4), "down_achieved": round(dn_tf, 1)}}
 
 
+MIXTRAL_DECODE_CFG = 2
+
+
+def mixtral_decode_leg(steps, L=2):
+    """The decode path on the Mixtral-8x7B-shaped layer (8 experts, top-2,
+    widths 3..8 drawn per block) at batch 1 / 4 / 16 / 64: step time of one
+    pw_moe_layer call (graph replay over L weight copies), tokens/s, the
+    layer's algorithmic bytes per second, and gate_up / down GB/s from the
+    dispatch-event kernel times."""
+    import torch
+    import any_precision_expert_amd as pw
+    import pw_synth
+    from any_precision_expert_amd.layer import Batch, register_layer
+    spec = pw_synth.CONFIGS[MIXTRAL_DECODE_CFG]
+    shape, seed = spec.shape, pw_synth.config_seed(MIXTRAL_DECODE_CFG)
+    t0 = time.time()
+    w = pw_synth.make_weights(shape, seed, 0, spec.q_policy, spec.logits)
+    wq = np.array([[g.q, d.q] for g, d in zip(w.gate_up, w.down)])
+    ctx = pw.Context(0, L, shape.E, shape.H, shape.I, shape.top_k, shape.I_shared, keep_host_masters=False)
+    for l in range(L):
+        register_layer(ctx, l, w)
+    log("mixtral decode: set up %s (%d copies) in %.1fs" % (spec.name, L, time.time() - t0))
+    stream = torch.cuda.Stream()
+    out = {"workload": spec.name, "H": shape.H, "I": shape.I, "E": shape.E, "top_k": shape.top_k,
+           "q": "uniform 3..8 per block", "layer_copies": L}
+    for T in spec.tokens:
+        batches = []
+        for l in range(L):
+            a = pw_synth.make_activations(shape, T, seed, 0, l, spec.logits, w.rank)
+            b = Batch(ctx, T)
+            b.load(a.logits, a.x)
+            batches.append(b)
+
+        def run_steps(n):
+            for i in range(n):
+                batches[i % L].step(i % L, stream)
+        ms = _graph_ms(run_steps, L, steps, stream)
+        ctx.profile_enable(True)
+        with torch.cuda.stream(stream):
+            run_steps(max(L, steps // 4))
+        torch.cuda.synchronize()
+        kern = {}
+        for name in ("route", "gate_up", "down", "combine"):
+            kms, cnt = ctx.profile_read(name)
+            kern[name] = kms / max(cnt, 1) * 1e3
+        ctx.profile_enable(False)
+        sb = [step_bytes(shape, wq, b.offsets.cpu().numpy(), T) for b in batches]
+        mb = {k: float(np.mean([x[k] for x in sb])) for k in sb[0]}
+        out["T=%d" % T] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                           "path_gbps": round(mb["path"] / (ms * 1e-3) / 1e9, 1),
+                           "path_bytes_per_step": int(mb["path"]),
+                           "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+                           "gate_up_gbps": round(mb["gate_up"] / (kern["gate_up"] * 1e-6) / 1e9, 1),
+                           "down_gbps": round(mb["down"] / (kern["down"] * 1e-6) / 1e9, 1)}
+        log("mixtral decode T=%d: %.4f ms/step, path %.0f GB/s, gate_up %.1f us, down %.1f us"
+            % (T, ms, mb["path"] / (ms * 1e-3) / 1e9, kern["gate_up"], kern["down"]))
+    ctx.close()
+    return out
+
+
 BASELINE_TOKENS = (1, 4, 16)
 UNIFORM_WIDTHS = (4, 5, 8)
 
@@ -425,6 +485,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the Mixtral-shaped prefill leg")
     ap.add_argument("--prefill-steps", type=int, default=8)
+    ap.add_argument("--no-mixtral-decode", action="store_true",
+                    help="skip the Mixtral-shaped decode leg (batch 1 / 4 / 16 / 64)")
+    ap.add_argument("--mixtral-decode-steps", type=int, default=64)
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the uniform-width and fp16-dense comparison at 1 / 4 / 16 tokens")
     ap.add_argument("--baseline-steps", type=int, default=160)
@@ -573,6 +636,7 @@ def main():
     tr = stored_traffic()
     traffic = int(tr["traffic_bytes"]) if tr else None  # HBM bytes per launch (PMC, scaled)
     prefill = None if args.no_prefill else prefill_leg(args.prefill_steps)
+    mixtral_decode = None if args.no_mixtral_decode else mixtral_decode_leg(args.mixtral_decode_steps)
     baselines = None
     if not args.no_baselines:
         ctx.close()
@@ -607,6 +671,7 @@ def main():
                      "down_achieved": round(dn_gbps, 1)},
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "mixtral_decode": mixtral_decode,
         "baselines": baselines,
     }
     print(json.dumps(out), flush=True)
