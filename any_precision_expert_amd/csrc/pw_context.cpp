@@ -540,6 +540,13 @@ static pw_status ffn_check(const pw_ctx* c, const char* fn, int layer, const uin
     const pw_model_desc& d = c->d;
     const WsLayout L = ws_layout(T, d.top_k, d.hidden, d.inter, d.inter_shared);
     if (ws_bytes < L.total) return fail(PW_ERR_INVALID, "%s: workspace %zu B < %zu B needed", fn, ws_bytes, L.total);
+    if (T >= kPrefillMinT) {
+        // the prefill kernels address x and h by 32-bit byte offsets
+        const uint64_t xb = (uint64_t)T * d.hidden * 2;
+        const uint64_t hb = (uint64_t)T * (d.top_k + 1) * std::max(d.inter, d.inter_shared) * 2;
+        if (std::max(xb, hb) > 0xffffffffull)
+            return fail(PW_ERR_INVALID, "%s: T=%d: x or h of the prefill path exceeds 4 GiB; split the batch", fn, T);
+    }
     const int E = d.num_experts;
     for (int s = 0; s <= E; ++s) {
         if (s == E && d.inter_shared == 0) break;

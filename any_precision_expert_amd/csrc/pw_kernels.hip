@@ -317,14 +317,28 @@ __device__ __forceinline__ half8_t step_pack(const StepRaw& raw)
     return __builtin_bit_cast(half8_t, w);
 }
 
-// step_weights for a wave-uniform unit index P known only at run time: the
-// masks 0x01010101 << s are formed with scalar shifts of P, so no register
-// array is indexed dynamically.
+// Form of rotate_planes / step_weights for a unit index P that differs
+// between the lanes of a wave: rotating every plane word right by P as well
+// turns the masks of unit P into those of unit 0, so the bit selects keep
+// fixed (scalar) masks and the final rotate by P disappears; the rotate
+// amounts are per lane (v_alignbit takes them from a register).  acc0 is the
+// pair-table seed of unit 0.
 template <int Q, bool PAIR>
-__device__ __forceinline__ half8_t step_weights_u(const Rot<Q, PAIR>& r, int P, uint32_t lane_off,
-                                                 const char* lutb, uint32_t acc0)
+__device__ __forceinline__ void rotate_planes_lane(const uint32_t (&W)[Q], int P, Rot<Q, PAIR>& r)
 {
-    auto mask = [&](int k) { return 0x01010101u << ((P + k) & 7); };
+#pragma unroll
+    for (int p = 0; p < Q; ++p) r.A[p] = rotr(W[p], P + p + 1 - Q);
+    if constexpr (PAIR) {
+#pragma unroll
+        for (int p = 0; p < Q; ++p) r.B[p] = rotr(W[p], P + p + 5 - 2 * Q);
+    }
+}
+
+template <int Q, bool PAIR>
+__device__ __forceinline__ half8_t step_weights_lane(const Rot<Q, PAIR>& r, uint32_t lane_off, const char* lutb,
+                                                    uint32_t acc0)
+{
+    auto mask = [](int k) { return 0x01010101u << (k & 7); };
     half8_t f;
     if constexpr (PAIR) {
         uint32_t acc = acc0;
@@ -333,10 +347,9 @@ __device__ __forceinline__ half8_t step_weights_u(const Rot<Q, PAIR>& r, int P, 
             acc = and_or(r.A[p], mask(Q - 1 - p), acc);
             acc = and_or(r.B[p], mask(2 * Q - 1 - p), acc);
         }
-        const uint32_t pr = rotr(acc, P);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const h2 v = *(const h2*)(lutb + lut_addr(pr, lane_off, i));
+            const h2 v = *(const h2*)(lutb + lut_addr(acc, lane_off, i));
             f[2 * i] = v.x;
             f[2 * i + 1] = v.y;
         }
@@ -347,8 +360,7 @@ __device__ __forceinline__ half8_t step_weights_u(const Rot<Q, PAIR>& r, int P, 
             c0 = and_or(r.A[p], mask(Q - 1 - p), c0);
             c1 = and_or(r.A[p], mask(4 + Q - 1 - p), c1);
         }
-        c0 = rotr(c0, P);
-        c1 = rotr(c1, 4 + P);
+        c1 = rotr(c1, 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f[2 * i] = *(const _Float16*)(lutb + lut_addr(c0, lane_off, i));
@@ -1349,9 +1361,12 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 // buffered: while the waves run the MFMAs of step s, waves 0-7 decode step
 // s + 1's weights (each thread: one row, 8 columns, with the same gather and
 // LUT look-up as the decode path) and waves 8-15 store the activations of
-// step s + 1 (each thread: one token row, gathered through the expert's
-// assignment list), so decode and matrix work overlap and one barrier ends a
-// step.  Global loads run two steps ahead.  Tiles are XOR-swizzled by row so
+// step s + 1 (gathered through the expert's assignment list), so decode and
+// matrix work overlap and one barrier ends a step.  Global loads run two
+// steps ahead.  Both roles put four lanes on one row (a weight row's plane
+// word, a token's 64 bytes), so a wave's load touches 2 (planes) or 16
+// (activations) cache lines instead of 8 or 64: the vector memory pipeline's
+// per-line cost, not the bytes, limited these loads.  Tiles are XOR-swizzled by row so
 // the fragment reads and the stores are conflict-free.  Each wave owns 64
 // rows x 64 tokens (2 x 2 blocks of v_mfma_f32_32x32x16_f16); a weight is
 // decoded once per 512 tokens.  gate_up writes h = silu(g) * u rounded to fp16 (the MFMA operand of
@@ -1415,8 +1430,10 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
             return row;
         }
     };
-    // decoder: thread = (tile row dr, 8-column unit dP of the step's word)
-    const int dr = tid & (kPfRows - 1), dP = (wave >> 1) & 3;  // dP is wave-uniform
+    // decoder: thread = (tile row dr, 8-column unit dP of the step's word);
+    // a wave decodes 16 rows, four lanes per row, so its loads of a plane word
+    // touch 256 contiguous bytes (two cache lines) and its tile store is 1 KB
+    const int dr = 16 * (wave & 7) + (lane >> 2), dP = lane & 3;
     bool dvalid;
     const int drow = tile_row(dr, dvalid);
     const int dlrow = dvalid ? drow : 0;
@@ -1425,18 +1442,28 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     const int half = MODE == 0 ? dr >> 6 : (dr >> 5) & 1;
     const int lslot = MODE == 0 ? dr & 63 : 32 * (dr >> 6) + (dr & 31);
     const uint32_t lane_off = lut_lane_off<Q, 4>(lslot, half);
-    const uint32_t acc0 = PAIR && half ? rotl(0x01010101u << (2 * Q), dP) : 0u;
-    // activation loader: thread = token row xr_t of the tile
-    const int xt_row = SPLIT ? (tid & 511) : tid;
+    const uint32_t acc0 = PAIR && half ? 0x01010101u << (2 * Q) : 0u;
+    // activation loader: thread g loads 16-byte unit g % 4 of tile token rows
+    // g / 4 + 128 j (j = 0..3), so four neighbouring lanes read one token's 64
+    // bytes of a step and a wave's load touches 16 rows instead of 64.  Byte
+    // offsets from the x / h base are 32-bit (the launcher checks the bound).
+    const int g = tid & 511, gu = g & 3;
     const int n0 = ntile * kPfTok;
-    const int te = n0 + xt_row < ntok ? n0 + xt_row : n0;
-    const uint16_t* xsrc;
-    if (MODE == 0) {
-        const int tok = shared ? te : a.sorted[p0 + te] / a.k;
-        xsrc = a.x + (size_t)tok * a.H;
-    } else {
-        const int hrow = shared ? TK + te : p0 + te;
-        xsrc = a.h + (size_t)hrow * a.hstride;
+    const uintptr_t xbase = MODE == 0 ? (uintptr_t)a.x : (uintptr_t)a.h;
+    uint32_t xoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = 128 * j + (g >> 2);
+        const int te = n0 + t < ntok ? n0 + t : n0;
+        uint32_t row, stride;
+        if (MODE == 0) {
+            row = shared ? te : a.sorted[p0 + te] / a.k;
+            stride = a.H;
+        } else {
+            row = shared ? TK + te : p0 + te;
+            stride = a.hstride;
+        }
+        xoff[j] = (row * stride + 8u * gu) * 2u;
     }
 
     u32x4* wt = (u32x4*)(lds + kPfW);  // [buffer][128 rows x 4 units]
@@ -1462,7 +1489,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
             const int s = min(st, nsteps - 1);
             if constexpr (DX) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) xr[slot][j] = *(gcu32x4p)(uintptr_t)(xsrc + s * kPfStepCols + 8 * j);
+                for (int j = 0; j < 4; ++j) xr[slot][j] = *(gcu32x4p)(xbase + (xoff[j] + (uint32_t)s * (2 * kPfStepCols)));
             }
             if constexpr (DW) {
                 const size_t at = ((size_t)(s >> 2) * R + dlrow) * 4 + (s & 3);
@@ -1477,8 +1504,8 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
             const int buf = s & 1;
             if constexpr (DW) {
                 Rot<Q, PAIR> rt;
-                rotate_planes<Q, PAIR>(pw[slot], rt);
-                const half8 A = step_weights_u<Q, PAIR>(rt, dP, lane_off, lutb, acc0);
+                rotate_planes_lane<Q, PAIR>(pw[slot], dP, rt);
+                const half8 A = step_weights_lane<Q, PAIR>(rt, lane_off, lutb, acc0);
                 wt[buf * (kPfWWords / 4) + pf_unit(dr, dP)] = __builtin_bit_cast(u32x4, A);
             }
             if constexpr (DX) {
@@ -1486,7 +1513,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
                 const bool live = s < nsteps;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    xt[buf * (kPfXWords / 4) + pf_unit(xt_row, j)] = live ? xr[slot][j] : u32x4{0, 0, 0, 0};
+                    xt[buf * (kPfXWords / 4) + pf_unit(128 * j + (g >> 2), gu)] = live ? xr[slot][j] : u32x4{0, 0, 0, 0};
             }
         };
         {

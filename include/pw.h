@@ -163,7 +163,10 @@ pw_status pw_route_permute(pw_ctx *ctx, const float *logits, int T, int32_t *top
  * y: dev fp16 [T][H] output (fp32 accumulation, rounded once to fp16);
  * workspace: dev, >= pw_workspace_size(ctx, T) bytes, 256-byte aligned,
  * contents undefined on entry and exit.  Every routed block of `layer` (and
- * the shared expert's, if the model has one) must be registered, else STATE. */
+ * the shared expert's, if the model has one) must be registered, else STATE.
+ * From T = 256 on (the prefill GEMM path) x and the workspace's fp16 h
+ * (T * (k + 1) rows of max(I, I_shared)) must each span at most 4 GiB, else
+ * INVALID: split such a batch into several calls. */
 pw_status pw_moe_ffn_bitplane(pw_ctx *ctx, int layer, const uint16_t *x, int T,
                               const int32_t *topk_idx, const float *topk_w,
                               const int32_t *expert_offsets, const int32_t *sorted_assign,
