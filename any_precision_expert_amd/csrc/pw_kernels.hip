@@ -1477,6 +1477,10 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < TB; ++j) C[i][j] = f32x16{};
+    // a wave whose token range holds no token of the tile (the ragged last
+    // tile of an expert may hold a few dozen) skips its matrix work (its
+    // outputs are never stored); the test is wave-uniform
+    const bool nlive = __builtin_amdgcn_readfirstlane(n0 + TS * tb < ntok ? 1 : 0) != 0;
 
     // The K loop of one role (DW: decode weights, DX: gather activations),
     // so that a thread's registers hold only its own role's loads.  Loads of
@@ -1542,18 +1546,20 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const int u = 2 * kk + (lane >> 5);
-                    half8 Af[2], Bf[TB];
+                    if (nlive > 0) {
+                        half8 Af[2], Bf[TB];
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        Af[i] = __builtin_bit_cast(half8, wt[buf * (kPfWWords / 4) + pf_unit(64 * rb + 32 * i + (lane & 31), u)]);
-#pragma unroll
-                    for (int j = 0; j < TB; ++j)
-                        Bf[j] = __builtin_bit_cast(half8, xt[buf * (kPfXWords / 4) + pf_unit(TS * tb + 32 * j + (lane & 31), u)]);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                        for (int i = 0; i < 2; ++i)
+                            Af[i] = __builtin_bit_cast(half8, wt[buf * (kPfWWords / 4) + pf_unit(64 * rb + 32 * i + (lane & 31), u)]);
 #pragma unroll
                         for (int j = 0; j < TB; ++j)
-                            C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i], Bf[j], C[i][j], 0, 0, 0);
+                            Bf[j] = __builtin_bit_cast(half8, xt[buf * (kPfXWords / 4) + pf_unit(TS * tb + 32 * j + (lane & 31), u)]);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+#pragma unroll
+                            for (int j = 0; j < TB; ++j)
+                                C[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Af[i], Bf[j], C[i][j], 0, 0, 0);
+                    }
                 }
                 stage(st + 1, 1 - h);
                 __builtin_amdgcn_sched_barrier(0);
