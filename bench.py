@@ -106,10 +106,10 @@ def _find(d, suffix):
     raise FileNotFoundError("%s under %s" % (suffix, d))
 
 
-def summarize_trace(trace_dir, out, command):
+def summarize_trace(trace_dir, out, command, title=None):
     """Kernel-trace statistics (rocprofv3 --kernel-trace --stats) -> markdown."""
     rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
-    lines = ["# Kernel time of bench.py: Qwen-shaped decode layer steps and the Mixtral-shaped prefill leg", "",
+    lines = ["# " + (title or "Kernel time of bench.py"), "",
              "Command: `%s`" % command, "",
              "| kernel | calls | average us | total ms | share % |", "|---|---|---|---|---|"]
     for r in rows:
@@ -501,13 +501,13 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_MD"))
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR_OR_OUT_MD",
                     help="PMC_DIR [PMC_DIR ...] OUT_MD: per-kernel counter means of rocprofv3 --pmc runs")
-    ap.add_argument("--title", default="PMC counters per kernel")
+    ap.add_argument("--title", default=None, help="heading of a --summarize-* markdown file")
     ap.add_argument("--command", default="", help="command line recorded in the summary")
     ap.add_argument("--command2", default="", help="second command line (WRITE_SIZE pass)")
     ap.add_argument("--alg-bytes", type=float, default=0.0, help="gate_up algorithmic bytes per launch")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command)
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command, args.title)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2], args.command,
@@ -515,7 +515,8 @@ def main():
         return
     if args.summarize_counters:
         cmds = [c for c in (args.command, args.command2) if c]
-        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], cmds, args.title)
+        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], cmds,
+                           args.title or "PMC counters per kernel")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",

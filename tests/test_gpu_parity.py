@@ -118,18 +118,32 @@ def test_ffn_k_equals_E_and_large_tiles():
 
 @pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
 def test_prefill_each_width(q):
-    """128-row x 256-token MFMA tiles over weights decoded into LDS; ragged
+    """128-row x 512-token MFMA tiles over weights decoded into LDS; ragged
     rows (I = 352 is not a multiple of 64), ragged K and partial token tiles."""
     w, a = pw_synth.make_small(H=416, I=352, E=4, top_k=2, T=300, I_shared=160, seed=700 + q, q_fixed=q)
     check_layer(w, a, label="prefill q=%d" % q)
 
 
 def test_prefill_mixed_widths_hot_expert():
-    """Mixed widths and one expert with every token: 600 tokens -> three
-    token tiles for that expert, empty experts skipped."""
+    """Mixed widths and one expert with every token: 600 tokens -> two token
+    tiles for that expert (the second holds 88), empty experts skipped."""
     w, a = pw_synth.make_small(H=256, I=192, E=6, top_k=2, T=600, seed=710)
     a.logits[:, 4] += 100.0
     check_layer(w, a, label="prefill hot expert")
+
+
+def test_prefill_ragged_token_tiles():
+    """Token counts per expert just past a 512-token tile and at the 64-token
+    boundary of a wave's range: last tiles holding 1, 64 and 65 tokens (the
+    waves past them skip their matrix work), an expert with none, and a
+    shared expert whose third tile holds 130 tokens."""
+    counts = [513, 576, 65, 0]
+    T = sum(counts)
+    w, a = pw_synth.make_small(H=256, I=192, E=4, top_k=1, T=T, I_shared=96, seed=720)
+    target = np.repeat(np.arange(4), counts)
+    np.random.default_rng(720).shuffle(target)
+    a.logits[np.arange(T), target] += 100.0
+    check_layer(w, a, label="prefill ragged tiles")
 
 
 def test_zero_tokens_enqueues_nothing():
