@@ -597,6 +597,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     a.E = E;
     a.k = d.top_k;
     a.n_slots = std::min(E, T * d.top_k);
+    a.keep_planes = (int64_t)T * d.top_k >= (int64_t)kKeepPlanesPerExpert * E ? 1 : 0;
     a.hstride = std::max(d.inter, d.inter_shared);
     a.drows = T * d.top_k + (d.inter_shared ? T : 0);
     hipStream_t s = (hipStream_t)stream;

@@ -49,6 +49,7 @@ struct FfnArgs {
     int32_t drows;            // rows of one dout split plane: T * k (+ T with a shared expert)
     int32_t rg;               // 32-row groups per workgroup tile: 2 or 4
     int32_t big_wgs;          // rg 4: workgroups taking whole tiles before tiles split in halves (0: all whole)
+    int32_t keep_planes;      // decode: ordinary (not nontemporal) plane loads, set when tiles take several passes
     // prefill launches: token tiles of the shared block, and an upper bound
     // on the routed token tiles (sum over experts of ceil(tokens / 512))
     int32_t tok_tiles_shared;
@@ -68,6 +69,12 @@ struct FfnArgs {
 
 // Most assignments (T * k) a gate_up launch routes by itself.
 constexpr int kLayerRouteMaxAssign = 64;
+
+// Decode launches load planes with ordinary loads (which the MALL keeps)
+// instead of nontemporal ones once the batch averages this many assignments
+// per expert: nearly every tile then takes two or more 8-token passes and
+// re-reads its planes.  Below it, nontemporal loads are faster (one pass).
+constexpr int kKeepPlanesPerExpert = 16;
 
 // Tokens per call from which the prefill GEMM path runs.
 constexpr int kPrefillMinT = 256;

@@ -814,8 +814,11 @@ __device__ __forceinline__ KArgs& kernel_args()
 // The loads are unconditional (callers pass an in-range row even for lanes
 // whose row is past the block; those lanes' outputs are never stored): a
 // lane-divergent load makes the compiler wait for every outstanding load
-// (vmcnt(0)), which would serialise the prefetch ring.
-template <int Q>
+// (vmcnt(0)), which would serialise the prefetch ring.  KEEP: ordinary loads
+// instead of nontemporal ones, for launches whose tiles are streamed more
+// than once (more than one pass of tokens), so the later passes can hit the
+// MALL.
+template <int Q, bool KEEP = false>
 __device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const BlockDesc* __restrict__ bd, int c, int R,
                                                 int row, int kh)
 {
@@ -824,7 +827,10 @@ __device__ __forceinline__ void load_pair_words(u32x2 (&pg)[Q], const BlockDesc*
     const uint32_t at = (((uint32_t)c * (uint32_t)R + (uint32_t)row) * 2u + (uint32_t)kh) * 8u;
     const __attribute__((address_space(4))) BlockDesc* cbd = (const __attribute__((address_space(4))) BlockDesc*)(uintptr_t)bd;
 #pragma unroll
-    for (int p = 0; p < Q; ++p) pg[p] = __builtin_nontemporal_load((gu32x2p)((uintptr_t)cbd->planes[p] + at));
+    for (int p = 0; p < Q; ++p) {
+        if constexpr (KEEP) pg[p] = *((gu32x2p)((uintptr_t)cbd->planes[p] + at));
+        else pg[p] = __builtin_nontemporal_load((gu32x2p)((uintptr_t)cbd->planes[p] + at));
+    }
 }
 
 // 16-byte unit g (8 fp16 columns) of row j of a wave's slice: the rows are
@@ -838,7 +844,7 @@ __device__ __forceinline__ int slice_unit(int j, int t, int g)
 
 // FUSED (gate_up of a launch that routed the batch itself): lane i of tokreg
 // holds the slot's i-th sorted assignment instead of a.sorted in memory.
-template <int MODE, int Q, int RG, bool FUSED = false>
+template <int MODE, int Q, int RG, bool FUSED = false, bool KEEP = false>
 __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
                                            int ntok, int tile, int split, int nsplit, uint32_t* lds, int tokreg = 0)
 {
@@ -954,7 +960,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     auto issue_ring = [&]() {
         issue_x(first);
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_pair_words<Q>(pg[d], bd, min(first + d * KW, lastc), R, lrow, kh);
+        for (int d = 0; d < D; ++d) load_pair_words<Q, KEEP>(pg[d], bd, min(first + d * KW, lastc), R, lrow, kh);
     };
 
     // pass 0: LUT loads first, then the ring's first loads, then LUT -> LDS
@@ -996,7 +1002,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
 #pragma unroll
                 for (int p = 0; p < Q; ++p) cur[p] = pg[d][p];
                 issue_x(min(c + KW, lastc));
-                load_pair_words<Q>(pg[d], bd, min(c + D * KW, lastc), R, lrow, kh);
+                load_pair_words<Q, KEEP>(pg[d], bd, min(c + D * KW, lastc), R, lrow, kh);
                 // the 8 MFMA steps s = 4u + P of the chunk (word pair u,
                 // columns 8P..8P+7), pipelined by one step: the B read and the
                 // LUT look-ups of step s + 1 are issued before step s's MFMA
@@ -1270,7 +1276,7 @@ __device__ __forceinline__ float combine_value(const FfnArgs& a, int t, int o, i
 // FUSED (gate_up only): the launch routes the batch itself (a.logits); the
 // workgroup of the first routed unit writes the routing results for the caller
 // and for the down and combine launches.
-template <int MODE, int RG, bool FUSED = false>
+template <int MODE, int RG, bool FUSED = false, bool KEEP = false>
 __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 {
     __shared__ __align__(16) uint32_t lds[kGemvLdsWords];
@@ -1332,12 +1338,12 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
     KArgs& ka = kernel_args();
 #define PW_GEMV_CASES(RGX, TILE)                                                                                  \
     switch (bd->q) {                                                                                             \
-        case 3: mfma_block<MODE, 3, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 4: mfma_block<MODE, 4, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 5: mfma_block<MODE, 5, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 6: mfma_block<MODE, 6, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 7: mfma_block<MODE, 7, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 8: mfma_block<MODE, 8, RGX, FUSED>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 3: mfma_block<MODE, 3, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 4: mfma_block<MODE, 4, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 5: mfma_block<MODE, 5, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 6: mfma_block<MODE, 6, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 7: mfma_block<MODE, 7, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 8: mfma_block<MODE, 8, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
         default: break;                                                                                          \
     }
     if constexpr (RG == 4) {
@@ -1497,10 +1503,12 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
             }
             if constexpr (DW) {
                 const size_t at = ((size_t)(s >> 2) * R + dlrow) * 4 + (s & 3);
+                // ordinary (temporal) loads: every token tile of an expert
+                // re-reads its planes, and with the plain tile order the next
+                // token tile's reads hit the MALL (nontemporal loads: +7%)
 #pragma unroll
                 for (int p = 0; p < Q; ++p)
-                    pw[slot][p] = __builtin_nontemporal_load(
-                        (__attribute__((address_space(1))) const uint32_t*)(uintptr_t)cbd->planes[p] + at);
+                    pw[slot][p] = *((__attribute__((address_space(1))) const uint32_t*)(uintptr_t)cbd->planes[p] + at);
             }
         };
         // step s (loaded in `slot`) -> LDS buffer s & 1
@@ -1847,7 +1855,10 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
         if (a.rg != 4 || a.T * a.k > kLayerRouteMaxAssign || a.E > 256) return hipErrorInvalidValue;
         launch((ffn_gemv_kernel<0, 4, true>), dim3(grid), dim3(kThreads), s, a);
     } else if (a.rg == 4) {
-        launch((ffn_gemv_kernel<0, 4>), dim3(grid), dim3(kThreads), s, a);
+        if (a.keep_planes)
+            launch((ffn_gemv_kernel<0, 4, false, true>), dim3(grid), dim3(kThreads), s, a);
+        else
+            launch((ffn_gemv_kernel<0, 4>), dim3(grid), dim3(kThreads), s, a);
     } else {
         launch((ffn_gemv_kernel<0, 2>), dim3(grid), dim3(kThreads), s, a);
     }
@@ -1860,6 +1871,8 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s)
     if (grid == 0) return hipSuccess;
     if (a.rg == 4)
         launch((ffn_gemv_kernel<1, 4>), dim3(grid), dim3(kThreads), s, a);
+    else if (a.keep_planes)
+        launch((ffn_gemv_kernel<1, 2, false, true>), dim3(grid), dim3(kThreads), s, a);
     else
         launch((ffn_gemv_kernel<1, 2>), dim3(grid), dim3(kThreads), s, a);
     return hipGetLastError();

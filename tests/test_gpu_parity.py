@@ -92,7 +92,7 @@ def test_ffn_each_width(q):
     check_layer(w, a, label="q=%d" % q)
 
 
-@pytest.mark.parametrize("T", [1, 2, 5, 9, 33])
+@pytest.mark.parametrize("T", [1, 2, 5, 9, 33, 45])  # 45: ~18 tokens per expert, three passes, kept plane loads
 def test_ffn_mixed_widths_ragged(T):
     w, a = pw_synth.make_small(H=352, I=224, E=5, top_k=2, T=T, seed=300 + T)
     check_layer(w, a, label="mixed T=%d" % T)
