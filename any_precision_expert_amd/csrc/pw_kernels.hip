@@ -1638,9 +1638,12 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
 
 // Workgroups: the shared block's (token tile, row tile) pairs first, then the
 // routed ones.  Routed token tiles are numbered over the experts in index
-// order (expert e has ceil(ntok_e / 256) of them); workgroups past the last
-// tile return at once.  Row tiles are fastest so neighbouring workgroups share
-// an activation tile.
+// order (expert e has ceil(ntok_e / 512) of them); workgroups past the last
+// tile return at once.  Row tiles are fastest: the chip sweeps the row tiles
+// of one token tile together (its activation tile stays in the L2s and the
+// MALL), and the next token tile of the same expert re-reads the expert's
+// planes from the MALL.  Giving each XCD a contiguous run of this order
+// instead was 14% slower.
 template <int MODE>
 __global__ void __launch_bounds__(kPfThreads, kPfWaves / 4) ffn_prefill_kernel(FfnArgs a)
 {
