@@ -1397,7 +1397,7 @@ constexpr int kPfX = kPfW + 2 * kPfWWords;
 constexpr int kPfXWords = kPfTok * kPfStepCols / 2;
 constexpr int kPfLdsWords = kPfX + 2 * kPfXWords;
 static_assert(kPfLdsWords * 4 == 144 * 1024, "prefill LDS: 144 KB");
-static_assert(64 * kPfTok <= kPfLdsWords, "gate_up epilogue exchange fits in LDS");
+static_assert(64 * kPfTok <= kPfLdsWords, "epilogue exchanges (64 rows x 512 tokens fp32) fit in LDS");
 
 // swizzled 16-byte unit u (columns 8u..8u+7 of the step) of tile row r: any
 // 8 (16) consecutive rows put a given unit in 8 (16) distinct 16-byte bank
@@ -1600,6 +1600,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
                     }
         }
         __syncthreads();
+        // h = silu(g) * u of every entry, in place of g
         if (rb == 0) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -1608,30 +1609,76 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                        const int t = TS * tb + 32 * j + (lane & 31);
-                        const int hi = mtile * 64 + r;
-                        if (n0 + t < ntok && hi < Iblk) {
-                            const float g = C[i][j][e], u = up[r * kPfTok + t];
-                            const float h = g / (1.0f + __expf(-g)) * u;
-                            const int hrow = shared ? TK + n0 + t : p0 + n0 + t;
-                            a.h[(size_t)hrow * a.hstride + hi] = __builtin_bit_cast(uint16_t, (_Float16)h);
-                        }
+                        const float g = C[i][j][e], u = up[r * kPfTok + TS * tb + 32 * j + (lane & 31)];
+                        C[i][j][e] = g / (1.0f + __expf(-g)) * u;
                     }
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < TB; ++j) {
-            const int t = TS * tb + 32 * j + (lane & 31);
-            if (n0 + t >= ntok) continue;
-            const int orow = shared ? TK + n0 + t : a.sorted[p0 + n0 + t];
-            float* dst = a.dout + (size_t)orow * a.H + mtile * kPfRows;
+        __syncthreads();  // `up` is consumed: its LDS holds the fp16 h tile next
+        // h tile [512 tokens][32 words], word w = rows 2w (low half) and 2w + 1;
+        // the word index is XORed with (t & 7) << 2 so the pair stores of a
+        // half-wave (32 tokens) spread over 8 banks and each 8-row group stays
+        // 16 contiguous bytes
+        uint32_t* hw = lds;
+        if (rb == 0) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int r = 64 * rb + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if (mtile * kPfRows + r < R) dst[r] = C[i][j][e];
+                for (int j = 0; j < TB; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; e += 2) {
+                        const int w = (32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) >> 1;
+                        const int t = TS * tb + 32 * j + (lane & 31);
+                        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)C[i][j][e]);
+                        const uint32_t hi16 = __builtin_bit_cast(uint16_t, (_Float16)C[i][j][e + 1]);
+                        hw[t * 32 + (w ^ ((t & 7) << 2))] = lo | (hi16 << 16);
+                    }
+        }
+        __syncthreads();
+        // stores of whole rows: eight lanes write a token's 64 h entries (128
+        // contiguous bytes); I and I_shared are multiples of 32, so an 8-row
+        // group is wholly inside or outside the block
+#pragma unroll
+        for (int k = tid; k < kPfTok * 8; k += kPfThreads) {
+            const int t = k >> 3, g8 = k & 7;
+            const int hi = mtile * 64 + 8 * g8;
+            if (n0 + t < ntok && hi < Iblk) {
+                const u32x4 v = *(const u32x4*)&hw[t * 32 + ((4 * g8) ^ ((t & 7) << 2))];
+                const int hrow = shared ? TK + n0 + t : p0 + n0 + t;
+                *(u32x4*)(a.h + (size_t)hrow * a.hstride + hi) = v;
+            }
+        }
+    } else {
+        // two halves of 64 rows: the half's waves stage it in LDS as [512 tokens]
+        // [64 rows] fp32 (row index XORed with (t & 15) << 2, which keeps 4-row
+        // groups contiguous), then sixteen lanes write each token's 256
+        // contiguous bytes of its expert-output row
+        float* sto = (float*)lds;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            __syncthreads();  // LDS free: the K loop's (hh 0) or the first half's (hh 1) reads are done
+            if (rb == hh) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < TB; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                            const int t = TS * tb + 32 * j + (lane & 31);
+                            sto[t * 64 + (r ^ ((t & 15) << 2))] = C[i][j][e];
+                        }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = tid; k < kPfTok * 16; k += kPfThreads) {
+                const int t = k >> 4, g4 = k & 15;
+                const int row = mtile * kPfRows + 64 * hh + 4 * g4;
+                if (n0 + t < ntok && row < R) {
+                    const int orow = shared ? TK + n0 + t : a.sorted[p0 + n0 + t];
+                    const u32x4 v = *(const u32x4*)&sto[t * 64 + ((4 * g4) ^ ((t & 15) << 2))];
+                    *(u32x4*)(a.dout + (size_t)orow * a.H + row) = v;
                 }
+            }
         }
     }
 }
