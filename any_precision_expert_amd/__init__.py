@@ -31,12 +31,13 @@ EXPORTS = (
     "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_routing_mass_enable", "pw_routing_mass_reset",
     "pw_routing_mass_read", "pw_plan_widths", "pw_request_widths", "pw_commit_ready", "pw_block_state",
     "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
-    "pw_resident_bytes", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
+    "pw_resident_bytes", "pw_debug_decode", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
     "pw_profile_read",
 )
 
 
 PAGE_RESIDENT, PAGE_IN_TRANSFER, PAGE_READY = 0, 1, 2
+DECODE_PATH_TILE128, DECODE_PATH_TILE64, DECODE_PATH_PREFILL = 0, 1, 2
 
 
 class PlanParams(ctypes.Structure):
@@ -97,6 +98,7 @@ def lib() -> ctypes.CDLL:
         L.pw_block_id.restype = i32
         L.pw_resident_bytes.argtypes = [vp]
         L.pw_resident_bytes.restype = i64
+        L.pw_debug_decode.argtypes = [vp, i32, ctypes.c_int, vp, vp, vp]
         L.pw_debug_decode_codes.argtypes = [vp, i32, vp, vp]
         L.pw_debug_dequant.argtypes = [vp, i32, vp, vp]
         L.pw_profile_enable.argtypes = [vp, ctypes.c_int]
@@ -285,6 +287,9 @@ class Context:
         return out
 
     # test exports and profiling ----------------------------------------
+    def debug_decode(self, block_id: int, path: int, codes_out=None, w_out=None, stream=None) -> None:
+        _check(lib().pw_debug_decode(self.h, block_id, int(path), _ptr(codes_out), _ptr(w_out), _stream(stream)))
+
     def debug_decode_codes(self, block_id: int, out, stream=None) -> None:
         _check(lib().pw_debug_decode_codes(self.h, block_id, _ptr(out), _stream(stream)))
 

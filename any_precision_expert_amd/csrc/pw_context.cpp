@@ -990,28 +990,33 @@ pw_status pw_block_state(const pw_ctx* c, int32_t id, int32_t* q_committed, int3
     return ok();
 }
 
-pw_status pw_debug_decode_codes(pw_ctx* c, int32_t id, uint8_t* out, pw_stream stream)
+pw_status pw_debug_decode(pw_ctx* c, int32_t id, int path, uint8_t* codes_out, uint16_t* w_out, pw_stream stream)
 {
-    if (!c || !out) return fail(PW_ERR_INVALID, "pw_debug_decode_codes: null pointer");
+    if (!c || (!codes_out && !w_out)) return fail(PW_ERR_INVALID, "pw_debug_decode: null pointer");
     if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
-        return fail(PW_ERR_INVALID, "pw_debug_decode_codes: block id %d not registered", id);
+        return fail(PW_ERR_INVALID, "pw_debug_decode: block id %d not registered", id);
+    if (path < PW_DECODE_PATH_TILE128 || path > PW_DECODE_PATH_PREFILL)
+        return fail(PW_ERR_INVALID, "pw_debug_decode: path %d not in 0..2", path);
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    const HostBlock& b = c->blocks[id];
-    e = launch_debug_decode(c->d_table + id, id & 1, b.R, b.K, out, nullptr, (hipStream_t)stream);
+    e = launch_debug_decode(c->d_table + id, id & 1, c->blocks[id].R, path, codes_out, w_out, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "debug decode launch");
+}
+
+// The decode contraction's tile of each module: gate_up 128-row tiles, down
+// 64-row tiles.
+static int default_decode_path(int32_t id) { return (id & 1) ? PW_DECODE_PATH_TILE64 : PW_DECODE_PATH_TILE128; }
+
+pw_status pw_debug_decode_codes(pw_ctx* c, int32_t id, uint8_t* out, pw_stream stream)
+{
+    if (!out) return fail(PW_ERR_INVALID, "pw_debug_decode_codes: null pointer");
+    return pw_debug_decode(c, id, default_decode_path(id), out, nullptr, stream);
 }
 
 pw_status pw_debug_dequant(pw_ctx* c, int32_t id, uint16_t* out, pw_stream stream)
 {
-    if (!c || !out) return fail(PW_ERR_INVALID, "pw_debug_dequant: null pointer");
-    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
-        return fail(PW_ERR_INVALID, "pw_debug_dequant: block id %d not registered", id);
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    const HostBlock& b = c->blocks[id];
-    e = launch_debug_decode(c->d_table + id, id & 1, b.R, b.K, nullptr, out, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "debug dequant launch");
+    if (!out) return fail(PW_ERR_INVALID, "pw_debug_dequant: null pointer");
+    return pw_debug_decode(c, id, default_decode_path(id), nullptr, out, stream);
 }
 
 pw_status pw_profile_enable(pw_ctx* c, int on)

@@ -134,7 +134,10 @@ hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
 hipError_t launch_routing_mass(const int32_t* offsets, const int32_t* sorted, const float* w, int E, double* mass,
                                hipStream_t s);
 hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s);
-hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int K, uint8_t* codes_out,
+// Decode of one block as an FFN path runs it (path: 0 decode contraction
+// with 128-row gate_up / down tiles (RG = 4), 1 with 64-row tiles (RG = 2),
+// 2 prefill decoder); codes_out uint8 [R][K] and / or w_out fp16 [R][K].
+hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int path, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s);
 
 // Host packer (pw_pack.cpp).

@@ -44,7 +44,6 @@ constexpr int kStageWords = 16 * 64;  // pair-table staging (single LUT of q <= 
 // LUT + eight 2 KB per-wave activation slices (which also hold the pair-table
 // staging and the cross-wave reduction): 80 KB, two 8-wave workgroups per CU.
 constexpr int kGemvLdsWords = kLutBytes / 4 + kWaves * 512;
-constexpr int kDebugLdsWords = kLutBytes / 4 + 16 * 64;        // LUT + pair staging
 
 // ---------------------------------------------------------------- bit gather
 
@@ -85,15 +84,6 @@ __device__ __forceinline__ RepMasks make_masks()
 }
 #undef PW_SMASK
 
-// Gathered child codes of one 32-column plane word set (W[p] = word of plane p).
-//  single (q >= 5): r[2P + h] byte i = code of column 8P + 2i + h
-//  pair   (q <= 4): r[P]      byte i = code(8P + 2i) | code(8P + 2i + 1) << q
-template <int Q>
-struct Gathered {
-    static constexpr int N = Q <= 4 ? 4 : 8;
-    uint32_t r[N];
-};
-
 // Child codes of one plane word set by an 8 x 8 bit transpose per byte: with
 // row r = plane q - 1 - r (rows q..7 zero), byte i of row r holds bit r of the
 // codes of columns 8P + 2i + h at bit 4h + P; three swap stages (4-, 2- and
@@ -126,83 +116,21 @@ __device__ __forceinline__ void transpose_codes(const uint32_t (&W)[Q], uint32_t
     for (int r = 0; r < 8; r += 2) swap(X[r], X[r + 1], 1, 0x55555555u);
 }
 
-// In the stored word, column 8P + 2i + h is at bit 8i + 4h + P.  Rotating plane
-// p left by (q - 1 - p) moves every bit of that plane by the same amount, so a
-// single and-or per (plane, register) drops its bit of four columns into the
-// right position of four bytes at once; one final rotate per register aligns
-// the bytes.
-template <int Q>
-__device__ __forceinline__ void gather(const uint32_t (&W)[Q], Gathered<Q>& g, const RepMasks& M)
-{
-    uint32_t A[Q];
-#pragma unroll
-    for (int p = 0; p < Q; ++p) A[p] = rotl(W[p], Q - 1 - p);
-    if constexpr (Q <= 4) {
-        uint32_t B[Q];
-#pragma unroll
-        for (int p = 0; p < Q; ++p) B[p] = rotl(W[p], 2 * Q - 5 - p);
-#pragma unroll
-        for (int P = 0; P < 4; ++P) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int p = 0; p < Q; ++p) {
-                acc = and_or(A[p], M.m[rep_index(P + Q - 1 - p)], acc);
-                acc = and_or(B[p], M.m[rep_index(P + 2 * Q - 1 - p)], acc);
-            }
-            g.r[P] = rotr(acc, P);
-        }
-    } else if constexpr (Q == 8) {
-        uint32_t X[8];
-        transpose_codes<Q>(W, X);
-#pragma unroll
-        for (int P = 0; P < 4; ++P) {
-            g.r[2 * P] = X[P];
-            g.r[2 * P + 1] = X[4 + P];
-        }
-    } else {
-#pragma unroll
-        for (int P = 0; P < 4; ++P) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t acc = 0;
-#pragma unroll
-                for (int p = 0; p < Q; ++p) acc = and_or(A[p], M.m[rep_index(4 * h + P + Q - 1 - p)], acc);
-                g.r[2 * P + h] = rotr(acc, 4 * h + P);
-            }
-        }
-    }
-}
-
 // LDS byte address of byte i of `codes`: (code << 8) | lane_off.
 __device__ __forceinline__ uint32_t lut_addr(uint32_t codes, uint32_t lane_off, int i)
 {
     return __builtin_amdgcn_perm(codes, lane_off, 0x0c0c0000u | ((4u + (uint32_t)i) << 8));
 }
 
-// Weights of the 32 columns as 16 half2 pairs: w2[4P + i] = (W[8P+2i], W[8P+2i+1]).
-template <int Q>
-__device__ __forceinline__ void lookup(const Gathered<Q>& g, uint32_t lane_off, const char* lutb,
-                                       h2 (&w2)[16])
-{
-#pragma unroll
-    for (int P = 0; P < 4; ++P) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (Q <= 4) {
-                w2[4 * P + i] = *(const h2*)(lutb + lut_addr(g.r[P], lane_off, i));
-            } else {
-                h2 v;
-                v.x = *(const _Float16*)(lutb + lut_addr(g.r[2 * P], lane_off, i));
-                v.y = *(const _Float16*)(lutb + lut_addr(g.r[2 * P + 1], lane_off, i));
-                w2[4 * P + i] = v;
-            }
-        }
-    }
-}
-
-// Step-wise form of gather + lookup used by the contraction: the planes are
-// rotated once (Rot), then each MFMA step P assembles only its own code
-// register(s) and looks up its 8 weights, which keeps few registers live.
+// Code gather of one plane word set W[p] (word of plane p), step by step.
+// In the stored word, column 8P + 2i + h is at bit 8i + 4h + P.  Rotating
+// plane p left by (q - 1 - p) moves every bit of that plane by the same
+// amount, so one and-or per (plane, code register) drops its bit of four
+// columns into the right position of four bytes at once, and one final rotate
+// per register aligns the bytes.  The planes are rotated once (Rot); each
+// MFMA step P then assembles only its own code register(s) and looks up its
+// 8 weights, which keeps few registers live.  Pair tables (two weights per
+// look-up) gather code(8P + 2i) | code(8P + 2i + 1) << q into byte i.
 template <int Q, bool PAIR>
 struct Rot {
     uint32_t A[Q];
@@ -220,52 +148,16 @@ __device__ __forceinline__ void rotate_planes(const uint32_t (&W)[Q], Rot<Q, PAI
     }
 }
 
-// Weights of columns 8P..8P+7 of the word as an MFMA A fragment (8 x fp16).
-// Pair tables: acc0 seeds the code bytes (the LUT set bit of a two-set pair
-// table, pre-rotated so the final rotate puts it above the pair code).
-template <int Q, bool PAIR>
-__device__ __forceinline__ half8_t step_weights(const Rot<Q, PAIR>& r, int P, const RepMasks& M, uint32_t lane_off,
-                                               const char* lutb, uint32_t acc0)
-{
-    half8_t f;
-    if constexpr (PAIR) {
-        uint32_t acc = acc0;
-#pragma unroll
-        for (int p = 0; p < Q; ++p) {
-            acc = and_or(r.A[p], M.m[rep_index(P + Q - 1 - p)], acc);
-            acc = and_or(r.B[p], M.m[rep_index(P + 2 * Q - 1 - p)], acc);
-        }
-        const uint32_t pr = rotr(acc, P);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const h2 v = *(const h2*)(lutb + lut_addr(pr, lane_off, i));
-            f[2 * i] = v.x;
-            f[2 * i + 1] = v.y;
-        }
-    } else {
-        uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-        for (int p = 0; p < Q; ++p) {
-            c0 = and_or(r.A[p], M.m[rep_index(P + Q - 1 - p)], c0);
-            c1 = and_or(r.A[p], M.m[rep_index(4 + P + Q - 1 - p)], c1);
-        }
-        c0 = rotr(c0, P);
-        c1 = rotr(c1, 4 + P);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = *(const _Float16*)(lutb + lut_addr(c0, lane_off, i));
-            f[2 * i + 1] = *(const _Float16*)(lutb + lut_addr(c1, lane_off, i));
-        }
-    }
-    return f;
-}
-
-// step_weights split in three so that a step's look-ups can be in flight
-// while the previous step waits and multiplies: step_codes assembles the
-// code register(s) of step P, step_lookup issues the LDS reads, step_pack
-// forms the A fragment once they have arrived.
+// One MFMA step's weights in three parts, so that a step's look-ups can be in
+// flight while the previous step waits and multiplies: step_codes assembles
+// the code register(s) of step P, step_lookup issues the LDS reads, step_pack
+// forms the A fragment (8 x fp16, element e = column 8P + e of the word) once
+// they have arrived.
 struct StepCodes {
-    uint32_t c0, c1;  // pair tables: c0 = the four pair codes; single: codes of registers P and 4 + P
+    // single tables: byte i of c0 / c1 = child code of column 8P + 2i / 8P + 2i + 1;
+    // pair tables: byte i of c0 = code(8P + 2i) | code(8P + 2i + 1) << q, with
+    // the LUT set of a two-set table above them (bit 2q); c1 unused
+    uint32_t c0, c1;
 };
 
 struct StepRaw {
@@ -317,7 +209,7 @@ __device__ __forceinline__ half8_t step_pack(const StepRaw& raw)
     return __builtin_bit_cast(half8_t, w);
 }
 
-// Form of rotate_planes / step_weights for a unit index P that differs
+// Form of rotate_planes / step_codes for a unit index P that differs
 // between the lanes of a wave: rotating every plane word right by P as well
 // turns the masks of unit P into those of unit 0, so the bit selects keep
 // fixed (scalar) masks and the final rotate by P disappears; the rotate
@@ -335,11 +227,9 @@ __device__ __forceinline__ void rotate_planes_lane(const uint32_t (&W)[Q], int P
 }
 
 template <int Q, bool PAIR>
-__device__ __forceinline__ half8_t step_weights_lane(const Rot<Q, PAIR>& r, uint32_t lane_off, const char* lutb,
-                                                    uint32_t acc0)
+__device__ __forceinline__ StepCodes step_codes_lane(const Rot<Q, PAIR>& r, uint32_t acc0)
 {
     auto mask = [](int k) { return 0x01010101u << (k & 7); };
-    half8_t f;
     if constexpr (PAIR) {
         uint32_t acc = acc0;
 #pragma unroll
@@ -347,12 +237,7 @@ __device__ __forceinline__ half8_t step_weights_lane(const Rot<Q, PAIR>& r, uint
             acc = and_or(r.A[p], mask(Q - 1 - p), acc);
             acc = and_or(r.B[p], mask(2 * Q - 1 - p), acc);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const h2 v = *(const h2*)(lutb + lut_addr(acc, lane_off, i));
-            f[2 * i] = v.x;
-            f[2 * i + 1] = v.y;
-        }
+        return StepCodes{acc, 0u};
     } else {
         uint32_t c0 = 0, c1 = 0;
 #pragma unroll
@@ -360,14 +245,8 @@ __device__ __forceinline__ half8_t step_weights_lane(const Rot<Q, PAIR>& r, uint
             c0 = and_or(r.A[p], mask(Q - 1 - p), c0);
             c1 = and_or(r.A[p], mask(4 + Q - 1 - p), c1);
         }
-        c1 = rotr(c1, 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = *(const _Float16*)(lutb + lut_addr(c0, lane_off, i));
-            f[2 * i + 1] = *(const _Float16*)(lutb + lut_addr(c1, lane_off, i));
-        }
+        return StepCodes{c0, rotr(c1, 4)};
     }
-    return f;
 }
 
 // LUT staging of a decode tile.  The block's LUT_q is stored in the slot
@@ -454,17 +333,71 @@ __device__ __forceinline__ uint32_t lut_lane_off(int sl, int h)
     return (uint32_t)sl * 4u + 2u * (uint32_t)h;
 }
 
-__device__ __forceinline__ uint4 load_planes_chunk(const uint32_t* plane, int c, int R, int row, bool valid)
+// A lane's row in a decode tile of RG 32-row groups (row group grp, lane row
+// rho) and the LUT column that holds it.  gate_up tiles hold 16 * RG h-rows:
+// groups [0, RG/2) are gate rows i, groups [RG/2, RG) the matching up rows
+// I + i (LUT slot = h-row, gate in the low half, up in the high half).  down
+// tiles hold 32 * RG consecutive rows (slot 32 m + r holds rows 64 m + r and
+// 64 m + 32 + r).  Rows past the block are not valid: their loads use row 0
+// and their outputs are never stored.
+struct TileLane {
+    int row, lrow;      // the row; the row the loads use
+    bool valid;
+    uint32_t lane_off;  // LDS byte offset of the row's LUT column
+    bool set1;          // two-set pair tables: the row's table is the second set
+};
+
+template <int MODE, int Q, int RG>
+__device__ __forceinline__ TileLane tile_lane(int tile, int grp, int rho, int R)
 {
-    if (!valid) return make_uint4(0, 0, 0, 0);
-    const u32x4 v = __builtin_nontemporal_load((gu32x4p)(uintptr_t)plane + ((size_t)c * R + row));
-    return make_uint4(v.x, v.y, v.z, v.w);
+    TileLane t;
+    if (MODE == 0) {
+        const int Iblk = R >> 1;
+        const int sub = grp % (RG / 2), up = grp / (RG / 2);
+        const int i = tile * (16 * RG) + 32 * sub + rho;
+        t.valid = i < Iblk;
+        t.row = up ? Iblk + i : i;
+    } else {
+        t.row = tile * (32 * RG) + 32 * grp + rho;
+        t.valid = t.row < R;
+    }
+    t.lrow = t.valid ? t.row : 0;
+    const int half = (MODE == 0 && RG == 4) ? grp / 2 : grp % 2;
+    const int lslot = (MODE == 0 && RG == 4) ? 32 * (grp % 2) + rho : (RG == 4 ? 32 * (grp / 2) + rho : rho);
+    t.lane_off = lut_lane_off<Q, RG>(lslot, half);
+    t.set1 = LutLoad<Q, RG>::PAIR && RG == 4 && half;
+    return t;
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int ww)
-{
-    return ww == 0 ? v.x : ww == 1 ? v.y : ww == 2 ? v.z : v.w;
-}
+// Code gather of one lane of a decode tile at width Q.  Single tables from
+// q = 5 on take all eight code registers of a word by the bit transpose (4
+// ops per swap: 96 per 128-column chunk against 146 for the and-or gather at
+// q = 8); otherwise the planes are rotated once and each MFMA step gathers its
+// own register (pair tables: two weights per look-up, the LUT set bit of a
+// two-set table seeded above the 2q-bit pair code).  `zero` must be a zero the
+// compiler cannot see through: with a literal zero it splits the bit-selects
+// of the transpose's rows q..7 into more, cheaper ops.
+template <int Q, int RG>
+struct WordDecoder {
+    static constexpr bool PAIR = LutLoad<Q, RG>::PAIR;
+    static constexpr bool TRANSPOSE = Q >= 5 && !PAIR;
+    RepMasks masks;
+    uint32_t zero;
+    bool set1;
+    Rot<Q, PAIR> rt;
+    uint32_t X[8];
+
+    __device__ __forceinline__ void prepare(const uint32_t (&W)[Q])
+    {
+        if constexpr (TRANSPOSE) transpose_codes<Q>(W, X, zero);
+        else rotate_planes<Q, PAIR>(W, rt);
+    }
+    __device__ __forceinline__ StepCodes codes(int P) const
+    {
+        if constexpr (TRANSPOSE) return StepCodes{X[P], X[4 + P]};
+        else return step_codes<Q, PAIR>(rt, P, masks, set1 ? rotl(0x01010101u << (2 * Q), P) : 0u);
+    }
+};
 
 // ---------------------------------------------------------------- routing
 
@@ -862,28 +795,8 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     const int nchunks = bd->nchunks, kwords = bd->kwords;
     const int K = kwords * 32;
     const int Iblk = R >> 1;
-    // row of row group g, lane row r; gate_up: groups [0, RG/2) gate rows,
-    // [RG/2, RG) the matching up rows
-    auto group_row = [&](int g, int r, bool& valid) {
-        if (MODE == 0) {
-            const int sub = g % (RG / 2), up = g / (RG / 2);
-            const int i = tile * HR + 32 * sub + r;
-            valid = i < Iblk;
-            return up ? Iblk + i : i;
-        } else {
-            const int row = tile * TR + 32 * g + r;
-            valid = row < R;
-            return row;
-        }
-    };
-    bool rvalid;
-    const int row = group_row(grp, rho, rvalid);
-    const int lrow = rvalid ? row : 0;  // in-range load row
-    // LUT slot and half of this lane's row (slot layout: gate_up slot = h-row
-    // with gate / up in the halves; down slot 32 m + r holds rows 64 m + r and
-    // 64 m + 32 + r)
-    const int half = (MODE == 0 && RG == 4) ? grp / 2 : grp % 2;
-    const int lslot = (MODE == 0 && RG == 4) ? 32 * (grp % 2) + rho : (RG == 4 ? 32 * (grp / 2) + rho : rho);
+    const TileLane tl = tile_lane<MODE, Q, RG>(tile, grp, rho, R);
+    const int lrow = tl.lrow;  // in-range load row
     const int cps = (nchunks + nsplit - 1) / nsplit;
     const int c_begin = split * cps;
     const int c_end = min(nchunks, c_begin + cps);
@@ -894,12 +807,13 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
 
     uint32_t* slice = lds + kLutBytes / 4 + wave * kSliceWords;
     u32x4* slice4 = (u32x4*)slice;
-    const uint32_t lane_off = lut_lane_off<Q, RG>(lslot, half);
+    const uint32_t lane_off = tl.lane_off;
     const char* lutb = (const char*)lds;
-    const RepMasks masks = make_masks();
-    // a zero the compiler cannot prove (T >= 1 here): the transpose's empty
-    // rows then stay plain operands of its bit-selects
-    const uint32_t opaque_zero = (uint32_t)__builtin_amdgcn_readfirstlane(a.T >> 30);
+    WordDecoder<Q, RG> dec;
+    dec.masks = make_masks();
+    // a zero the compiler cannot prove (T >= 1 here)
+    dec.zero = (uint32_t)__builtin_amdgcn_readfirstlane(a.T >> 30);
+    dec.set1 = tl.set1;
 
     // cooperative activation loads: lane = (token xt, 16-byte unit xg)
     const int xt = lane >> 4, xg = lane & 15;
@@ -1007,33 +921,15 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 // columns 8P..8P+7), pipelined by one step: the B read and the
                 // LUT look-ups of step s + 1 are issued before step s's MFMA
                 // finishes, and step s + 1's code gather runs while step s's
-                // reads are in flight.  Two-set pair tables carry the set bit
-                // above the 2q-bit pair code (acc0).
-                auto acc0 = [&](int P) {
-                    return PAIR && RG == 4 && half ? rotl(0x01010101u << (2 * Q), P) : 0u;
-                };
+                // reads are in flight.
                 auto b_unit = [&](int s, int row) { return slice_unit(row, te, 4 * (2 * kh + (s >> 2)) + (s & 3)); };
-                // q >= 5: all eight code registers of a word pair by one bit
-                // transpose (4 ops per swap, 96 per chunk against 146 for the
-                // and-or gather at q = 8).  Rows q..7 start from a zero the
-                // compiler cannot see through: with a literal zero it splits
-                // the bit-selects of those rows into more, cheaper ops.
-                // Pair tables (q <= 4): rotated planes and one and-or gather
-                // per step.
-                constexpr bool TRANSPOSE = Q >= 5 && !PAIR;
-                Rot<Q, PAIR> rt;
-                uint32_t X[8];
                 auto prepare = [&](int u) {
                     uint32_t W[Q];
 #pragma unroll
                     for (int p = 0; p < Q; ++p) W[p] = cur[p][u];
-                    if constexpr (TRANSPOSE) transpose_codes<Q>(W, X, opaque_zero);
-                    else rotate_planes<Q, PAIR>(W, rt);
+                    dec.prepare(W);
                 };
-                auto codes = [&](int P) {
-                    if constexpr (TRANSPOSE) return StepCodes{X[P], X[4 + P]};
-                    else return step_codes<Q, PAIR>(rt, P, masks, acc0(P));
-                };
+                auto codes = [&](int P) { return dec.codes(P); };
                 prepare(0);
                 u32x4 bh = slice4[b_unit(0, te)];
                 StepRaw raw;
@@ -1405,6 +1301,66 @@ static_assert(64 * kPfTok <= kPfLdsWords, "epilogue exchanges (64 rows x 512 tok
 // LDS banks
 __device__ __forceinline__ int pf_unit(int r, int u) { return r * 4 + (u ^ (((r >> 1) ^ (r >> 3)) & 3)); }
 
+// A prefill decoder thread: tile row dr = 16 * (wave % 8) + lane / 4 of a
+// 128-row tile (gate_up: rows 0..63 are gate rows i of the tile's 64 h-rows,
+// rows 64..127 the matching up rows; down: 128 consecutive rows) and 8-column
+// unit dP = lane % 4 of each 32-column step.  Four lanes share a row, so a
+// wave's load of a plane word spans 256 contiguous bytes (two cache lines).
+// LUT slot / half of the row as in the slot layout (gate_up: slot = h-row, up
+// rows in the high half; down: slot 32 m + r holds tile rows 64 m + r and
+// 64 m + 32 + r); two-set pair tables seed the set bit above the pair code.
+struct PfLane {
+    int dr, dP, lrow;
+    bool valid;
+    uint32_t lane_off, acc0;
+};
+
+template <int MODE, int Q>
+__device__ __forceinline__ PfLane pf_lane(int mtile, int wave, int lane, int R)
+{
+    PfLane L;
+    L.dr = 16 * (wave & 7) + (lane >> 2);
+    L.dP = lane & 3;
+    int row;
+    if (MODE == 0) {
+        const int Iblk = R >> 1;
+        const int i = mtile * 64 + (L.dr & 63);
+        L.valid = i < Iblk;
+        row = L.dr < 64 ? i : Iblk + i;
+    } else {
+        row = mtile * kPfRows + L.dr;
+        L.valid = row < R;
+    }
+    L.lrow = L.valid ? row : 0;
+    const int half = MODE == 0 ? L.dr >> 6 : (L.dr >> 5) & 1;
+    const int lslot = MODE == 0 ? L.dr & 63 : 32 * (L.dr >> 6) + (L.dr & 31);
+    L.lane_off = lut_lane_off<Q, 4>(lslot, half);
+    L.acc0 = LutLoad<Q, 4>::PAIR && half ? 0x01010101u << (2 * Q) : 0u;
+    return L;
+}
+
+// Word index (uint32, within a plane) of step s's word of row `lrow`.
+__device__ __forceinline__ size_t pf_word_at(int s, int R, int lrow)
+{
+    return ((size_t)(s >> 2) * R + lrow) * 4 + (s & 3);
+}
+
+// Weights of the lane's unit dP of one plane word set W[p] (an MFMA A
+// fragment: element e = column 8 dP + e of the word); *codes receives the
+// gathered codes when non-null.
+template <int Q, bool PAIR>
+__device__ __forceinline__ half8_t pf_decode(const uint32_t (&W)[Q], const PfLane& L, const char* lutb,
+                                             StepCodes* codes = nullptr)
+{
+    Rot<Q, PAIR> rt;
+    rotate_planes_lane<Q, PAIR>(W, L.dP, rt);
+    const StepCodes c = step_codes_lane<Q, PAIR>(rt, L.acc0);
+    StepRaw raw;
+    step_lookup<PAIR>(c, L.lane_off, lutb, raw);
+    if (codes) *codes = c;
+    return step_pack<PAIR>(raw);
+}
+
 template <int MODE, int Q, int W>
 __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
                                               int ntok, int mtile, int ntile, uint32_t* lds)
@@ -1425,30 +1381,8 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     const int nsteps = kwords;
     const int Iblk = R >> 1;
     const int TK = a.T * a.k;
-    auto tile_row = [&](int r, bool& valid) {
-        if (MODE == 0) {
-            const int i = mtile * 64 + (r & 63);
-            valid = i < Iblk;
-            return r < 64 ? i : Iblk + i;
-        } else {
-            const int row = mtile * kPfRows + r;
-            valid = row < R;
-            return row;
-        }
-    };
-    // decoder: thread = (tile row dr, 8-column unit dP of the step's word);
-    // a wave decodes 16 rows, four lanes per row, so its loads of a plane word
-    // touch 256 contiguous bytes (two cache lines) and its tile store is 1 KB
-    const int dr = 16 * (wave & 7) + (lane >> 2), dP = lane & 3;
-    bool dvalid;
-    const int drow = tile_row(dr, dvalid);
-    const int dlrow = dvalid ? drow : 0;
-    // LUT slot / half of the row (gate_up: slot = h-row, up rows in the high
-    // half; down: slot 32 m + r holds tile rows 64 m + r and 64 m + 32 + r)
-    const int half = MODE == 0 ? dr >> 6 : (dr >> 5) & 1;
-    const int lslot = MODE == 0 ? dr & 63 : 32 * (dr >> 6) + (dr & 31);
-    const uint32_t lane_off = lut_lane_off<Q, 4>(lslot, half);
-    const uint32_t acc0 = PAIR && half ? 0x01010101u << (2 * Q) : 0u;
+    // decoder: a wave decodes 16 rows of the tile, four lanes per row (PfLane)
+    const PfLane dl = pf_lane<MODE, Q>(mtile, wave, lane, R);
     // activation loader: thread g loads 16-byte unit g % 4 of tile token rows
     // g / 4 + 128 j (j = 0..3), so four neighbouring lanes read one token's 64
     // bytes of a step and a wave's load touches 16 rows instead of 64.  Byte
@@ -1502,7 +1436,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
                 for (int j = 0; j < 4; ++j) xr[slot][j] = *(gcu32x4p)(xbase + (xoff[j] + (uint32_t)s * (2 * kPfStepCols)));
             }
             if constexpr (DW) {
-                const size_t at = ((size_t)(s >> 2) * R + dlrow) * 4 + (s & 3);
+                const size_t at = pf_word_at(s, R, dl.lrow);
                 // ordinary (temporal) loads: every token tile of an expert
                 // re-reads its planes, and with the plain tile order the next
                 // token tile's reads hit the MALL (nontemporal loads: +7%)
@@ -1515,10 +1449,8 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
         auto stage = [&](int s, int slot) {
             const int buf = s & 1;
             if constexpr (DW) {
-                Rot<Q, PAIR> rt;
-                rotate_planes_lane<Q, PAIR>(pw[slot], dP, rt);
-                const half8 A = step_weights_lane<Q, PAIR>(rt, lane_off, lutb, acc0);
-                wt[buf * (kPfWWords / 4) + pf_unit(dr, dP)] = __builtin_bit_cast(u32x4, A);
+                const half8 A = pf_decode<Q, PAIR>(pw[slot], dl, lutb);
+                wt[buf * (kPfWWords / 4) + pf_unit(dl.dr, dl.dP)] = __builtin_bit_cast(u32x4, A);
             }
             if constexpr (DX) {
                 // steps past K (padding to an even count) multiply by zero activations
@@ -1765,90 +1697,144 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a)
 }
 
 // ---------------------------------------------------------------- debug export
+//
+// The decode of one block exactly as the FFN kernels run it, with the codes
+// and weights written out instead of multiplied: the same LUT staging
+// (LutLoad), lane geometry (tile_lane / pf_lane), plane loads
+// (load_pair_words / pf_word_at) and code gather and look-up (WordDecoder,
+// step_lookup, step_pack / pf_decode).  Outputs are row-major [R][K] (codes
+// uint8, weights fp16 bits); either may be null.
 
-// Same LUT staging, gather and look-up as the FFN: one wave per tile of 32
-// LUT slots (RG = 2 geometry: lane = half * 32 + slot, the rows of
-// lut_slot_rows), writing each row's child codes and/or decoded weights.
-template <int Q>
-__device__ void debug_block(const BlockDesc* __restrict__ bd, int module, int R, int K, uint8_t* codes_out,
-                            uint16_t* w_out, uint32_t* lds)
+// The 8 codes and weights of one MFMA step of row `row` (columns col..col+7;
+// columns past K -- the zero words of a partial last chunk -- are skipped).
+template <int Q, bool PAIR>
+__device__ __forceinline__ void debug_store_step(const StepCodes& c, const half8_t& A, int row, int col, int K,
+                                                 uint8_t* codes_out, uint16_t* w_out)
 {
-    const int lane = threadIdx.x;
-    const int sl = lane & 31, h = lane >> 5;
-    const int j = blockIdx.x * 32 + sl;
-    int row;
-    if (module == 0) {
-        row = j < R / 2 ? j + h * (R / 2) : -1;
-    } else {
-        row = 64 * (j / 32) + 32 * h + j % 32;
-        if (row >= R) row = -1;
-    }
-    const bool valid = row >= 0;
-    {
-        LutLoad<Q, 2, 64> ls;
-        ls.issue(bd->lut, bd->slots, blockIdx.x * 32, lane, 0);
-        ls.commit(lds, lds + kLutBytes / 4, lane, 0);
-    }
-    __syncthreads();
-    const char* lutb = (const char*)lds;
-    const uint32_t lane_off = lut_lane_off<Q, 2>(sl, h);
-    const RepMasks masks = make_masks();
-    for (int c = 0; c < bd->nchunks; ++c) {
-        uint4 pv[Q];
+    if (col >= K) return;
+    const size_t base = (size_t)row * K + col;
+    const u32x4 wv = __builtin_bit_cast(u32x4, A);
 #pragma unroll
-        for (int p = 0; p < Q; ++p) pv[p] = load_planes_chunk(bd->planes[p], c, R, row, valid);
-        for (int ww = 0; ww < 4 && 4 * c + ww < bd->kwords; ++ww) {
+    for (int i = 0; i < 4; ++i) {
+        uint32_t ca, cb;
+        if constexpr (PAIR) {
+            const uint32_t pr = (c.c0 >> (8 * i)) & 0xffu;
+            ca = pr & ((1u << Q) - 1u);
+            cb = (pr >> Q) & ((1u << Q) - 1u);
+        } else {
+            ca = (c.c0 >> (8 * i)) & 0xffu;
+            cb = (c.c1 >> (8 * i)) & 0xffu;
+        }
+        if (codes_out) {
+            codes_out[base + 2 * i] = (uint8_t)ca;
+            codes_out[base + 2 * i + 1] = (uint8_t)cb;
+        }
+        if (w_out) {
+            w_out[base + 2 * i] = (uint16_t)(wv[i] & 0xffffu);
+            w_out[base + 2 * i + 1] = (uint16_t)(wv[i] >> 16);
+        }
+    }
+}
+
+// One decode-contraction tile (8 waves, RG row groups, as mfma_block).
+template <int MODE, int Q, int RG>
+__device__ void debug_gemv_tile(const BlockDesc* __restrict__ bd, int tile, uint8_t* codes_out, uint16_t* w_out,
+                                uint32_t* lds)
+{
+    constexpr int KW = kWaves / RG;
+    constexpr bool PAIR = LutLoad<Q, RG>::PAIR;
+    const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave / KW, kw = wave % KW;
+    const int R = bd->R, K = bd->kwords * 32, nchunks = bd->nchunks;
+    const TileLane tl = tile_lane<MODE, Q, RG>(tile, grp, rho, R);
+    {
+        LutLoad<Q, RG> ls;
+        ls.issue(bd->lut, bd->slots, tile * LutLoad<Q, RG>::NSLOT, lane, wave);
+        ls.commit(lds, lds + kLutBytes / 4, lane, wave);
+        __syncthreads();
+    }
+    WordDecoder<Q, RG> dec;
+    dec.masks = make_masks();
+    dec.zero = (uint32_t)__builtin_amdgcn_readfirstlane(R >> 30);  // R < 2^30
+    dec.set1 = tl.set1;
+    const char* lutb = (const char*)lds;
+    for (int c = kw; c < nchunks; c += KW) {
+        u32x2 pg[Q];
+        load_pair_words<Q>(pg, bd, c, R, tl.lrow, kh);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
             uint32_t W[Q];
 #pragma unroll
-            for (int p = 0; p < Q; ++p) W[p] = word_of(pv[p], ww);
-            Gathered<Q> g;
-            gather<Q>(W, g, masks);
-            h2 w2[16];
-            lookup<Q>(g, lane_off, lutb, w2);
-            if (!valid) continue;
-            const size_t base = (size_t)row * K + 32 * (4 * c + ww);
+            for (int p = 0; p < Q; ++p) W[p] = pg[p][u];
+            dec.prepare(W);
 #pragma unroll
             for (int P = 0; P < 4; ++P) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint32_t ca, cb;
-                    if constexpr (Q <= 4) {
-                        const uint32_t pr = (g.r[P] >> (8 * i)) & 0xffu;
-                        ca = pr & ((1u << Q) - 1u);
-                        cb = pr >> Q;
-                    } else {
-                        ca = (g.r[2 * P] >> (8 * i)) & 0xffu;
-                        cb = (g.r[2 * P + 1] >> (8 * i)) & 0xffu;
-                    }
-                    const int col = 8 * P + 2 * i;
-                    if (codes_out) {
-                        codes_out[base + col] = (uint8_t)ca;
-                        codes_out[base + col + 1] = (uint8_t)cb;
-                    }
-                    if (w_out) {
-                        const uint32_t pr = __builtin_bit_cast(uint32_t, w2[4 * P + i]);
-                        w_out[base + col] = (uint16_t)(pr & 0xffffu);
-                        w_out[base + col + 1] = (uint16_t)(pr >> 16);
-                    }
-                }
+                const StepCodes sc = dec.codes(P);
+                StepRaw raw;
+                step_lookup<PAIR>(sc, tl.lane_off, lutb, raw);
+                const half8_t A = step_pack<PAIR>(raw);
+                if (tl.valid)
+                    debug_store_step<Q, PAIR>(sc, A, tl.row, c * kChunkCols + 32 * (2 * kh + u) + 8 * P, K, codes_out,
+                                              w_out);
             }
         }
     }
 }
 
-__global__ void __launch_bounds__(64) debug_decode_kernel(const BlockDesc* __restrict__ bd, int module, int R,
-                                                          int K, uint8_t* codes_out, uint16_t* w_out)
+// One prefill tile's decoder waves (16-wave workgroup, as prefill_block).
+template <int MODE, int Q>
+__device__ void debug_prefill_tile(const BlockDesc* __restrict__ bd, int mtile, uint8_t* codes_out, uint16_t* w_out,
+                                   uint32_t* lds)
 {
-    __shared__ __align__(16) uint32_t lds[kDebugLdsWords];
-    switch (bd->q) {
-        case 3: debug_block<3>(bd, module, R, K, codes_out, w_out, lds); break;
-        case 4: debug_block<4>(bd, module, R, K, codes_out, w_out, lds); break;
-        case 5: debug_block<5>(bd, module, R, K, codes_out, w_out, lds); break;
-        case 6: debug_block<6>(bd, module, R, K, codes_out, w_out, lds); break;
-        case 7: debug_block<7>(bd, module, R, K, codes_out, w_out, lds); break;
-        case 8: debug_block<8>(bd, module, R, K, codes_out, w_out, lds); break;
+    constexpr bool PAIR = LutLoad<Q, 4>::PAIR;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int R = bd->R, K = bd->kwords * 32;
+    {
+        LutLoad<Q, 4, kPfThreads> ls;
+        ls.issue(bd->lut, bd->slots, mtile * LutLoad<Q, 4, kPfThreads>::NSLOT, lane, wave);
+        ls.commit(lds, lds + kPfW, lane, wave);
+        __syncthreads();
+    }
+    if (wave >= 8) return;  // the gatherer waves
+    const PfLane dl = pf_lane<MODE, Q>(mtile, wave, lane, R);
+    const __attribute__((address_space(4))) BlockDesc* cbd =
+        (const __attribute__((address_space(4))) BlockDesc*)(uintptr_t)bd;
+    const char* lutb = (const char*)lds;
+    for (int s = 0; s < bd->kwords; ++s) {
+        const size_t at = pf_word_at(s, R, dl.lrow);
+        uint32_t W[Q];
+#pragma unroll
+        for (int p = 0; p < Q; ++p) W[p] = *((__attribute__((address_space(1))) const uint32_t*)(uintptr_t)cbd->planes[p] + at);
+        StepCodes sc;
+        const half8_t A = pf_decode<Q, PAIR>(W, dl, lutb, &sc);
+        if (dl.valid) debug_store_step<Q, PAIR>(sc, A, dl.lrow, 32 * s + 8 * dl.dP, K, codes_out, w_out);
+    }
+}
+
+constexpr int kDebugPfLdsWords = kPfX;  // LUT + the weight tiles (pair-table staging)
+
+// PATH 0 / 1: decode contraction with RG = 4 / RG = 2 tiles; PATH 2: prefill
+// decoder.  One workgroup per tile of that path.
+template <int PATH>
+__global__ void __launch_bounds__(PATH == 2 ? kPfThreads : kThreads)
+    debug_decode_kernel(const BlockDesc* __restrict__ bd, int module, uint8_t* codes_out, uint16_t* w_out)
+{
+    __shared__ __align__(16) uint32_t lds[PATH == 2 ? kDebugPfLdsWords : kGemvLdsWords];
+    const int tile = blockIdx.x;
+#define PW_DEBUG_CASE(M, QQ)                                                                        \
+    case 2 * (QQ) + (M):                                                                            \
+        if constexpr (PATH == 2) debug_prefill_tile<M, QQ>(bd, tile, codes_out, w_out, lds);        \
+        else debug_gemv_tile<M, QQ, PATH == 0 ? 4 : 2>(bd, tile, codes_out, w_out, lds);           \
+        break;
+    switch (2 * bd->q + module) {
+        PW_DEBUG_CASE(0, 3) PW_DEBUG_CASE(1, 3) PW_DEBUG_CASE(0, 4) PW_DEBUG_CASE(1, 4)
+        PW_DEBUG_CASE(0, 5) PW_DEBUG_CASE(1, 5) PW_DEBUG_CASE(0, 6) PW_DEBUG_CASE(1, 6)
+        PW_DEBUG_CASE(0, 7) PW_DEBUG_CASE(1, 7) PW_DEBUG_CASE(0, 8) PW_DEBUG_CASE(1, 8)
         default: break;
     }
+#undef PW_DEBUG_CASE
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1960,11 +1946,24 @@ hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int K, uint8_t* codes_out,
+hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int path, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s)
 {
-    const int tiles = lut_slots(R, module) / 32;
-    launch(debug_decode_kernel, dim3(tiles), dim3(64), s, entry, module, R, K, codes_out, w_out);
+    const int rows = module == 0 ? R / 2 : R;  // gate_up tiles count h-rows
+    if (path == 2) {
+        const int per = module == 0 ? kPfRows / 2 : kPfRows;
+        launch(debug_decode_kernel<2>, dim3((rows + per - 1) / per), dim3(kPfThreads), s, entry, module, codes_out,
+               w_out);
+    } else {
+        const int rg = path == 0 ? 4 : 2;
+        const int per = module == 0 ? 16 * rg : 32 * rg;
+        if (path == 0)
+            launch(debug_decode_kernel<0>, dim3((rows + per - 1) / per), dim3(kThreads), s, entry, module, codes_out,
+                   w_out);
+        else
+            launch(debug_decode_kernel<1>, dim3((rows + per - 1) / per), dim3(kThreads), s, entry, module, codes_out,
+                   w_out);
+    }
     return hipGetLastError();
 }
 

@@ -21,13 +21,14 @@ pw_status plan_fail(const char* msg);
 namespace {
 
 struct Block {
-    int64_t plane_b;  // bytes of one plane
-    int S;            // LUT slots
+    int64_t plane_b;  // bytes of one plane: R * K / 8
+    int64_t R;
     double weight;    // sensitivity x (routing share + eps) x multiplier
     int floor;
 };
 
-int64_t block_bytes(const Block& b, int q) { return (int64_t)q * b.plane_b + (int64_t)b.S * (4LL << q); }
+// q bit-planes plus LUT_q (R rows of 2^q fp16 entries)
+int64_t block_bytes(const Block& b, int q) { return (int64_t)q * b.plane_b + b.R * (2LL << q); }
 
 // damage added by lowering from q to q - 1 (quantisation error power grows
 // about 4x per dropped bit: 3 * 4^(8 - q) in units of the 8-bit error)
@@ -57,8 +58,8 @@ extern "C" pw_status pw_plan_widths(int L, int E, int H, int I, const uint8_t* q
                 const int b = (l * E + e) * 2 + m;
                 const int R = m == 0 ? 2 * I : H, K = m == 0 ? H : I;
                 Block& x = bl[b];
-                x.plane_b = plane_words(R, K) * 4;
-                x.S = lut_slots(R, m);
+                x.plane_b = (int64_t)R * K / 8;
+                x.R = R;
                 x.weight = (double)sens[b] * (share + p->mass_eps) * (hot ? p->hot_mult : 1.0);
                 x.floor = hot ? std::max(p->q_min, p->hot_floor) : p->q_min;
                 q[b] = std::min(std::max((int)q_cur[b], x.floor), p->q_max);

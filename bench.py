@@ -67,8 +67,10 @@ def step_bytes(shape, wq, offsets, T):
 
 
 KERNEL_SRC = os.path.join(ROOT, "any_precision_expert_amd", "csrc", "pw_kernels.hip")
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "gate_up_qwen_decode_traffic.md")
-GATE_UP_NAME = "ffn_gemv_kernel<0,"  # demangled prefix of the gate_up decode kernel
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "decode_qwen_gate_up_down_traffic.md")
+TRACE_MD = os.path.join(ROOT, "profiles", "decode_qwen_kernel_trace.md")
+# demangled prefixes of the decode kernels
+KERNEL_PREFIX = {"gate_up": "ffn_gemv_kernel<0,", "down": "ffn_gemv_kernel<1,"}
 COPY_NAME = "copyBuffer"
 
 
@@ -78,18 +80,28 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per gate_up launch from the committed PMC summary, or None if
-    the kernel source changed since the counters were taken."""
+def _stored_json(path, tag):
+    """The JSON object on the `tag:` line of a committed profile summary, or
+    None if the kernel source changed since the profile was taken."""
     try:
-        with open(TRAFFIC_MD) as f:
+        with open(path) as f:
             for line in f:
-                if line.startswith("TRAFFIC_JSON:"):
+                if line.startswith(tag + ":"):
                     t = json.loads(line.split(":", 1)[1])
                     return t if t.get("kernel_sha") == kernel_sha() else None
     except OSError:
         pass
     return None
+
+
+def stored_traffic():
+    """HBM bytes per gate_up / down launch from the committed PMC summary."""
+    return _stored_json(TRAFFIC_MD, "TRAFFIC_JSON")
+
+
+def stored_trace():
+    """Average rocprofv3 kernel-trace durations (us) of the decode kernels."""
+    return _stored_json(TRACE_MD, "TRACE_JSON")
 
 
 def _csv_rows(path):
@@ -107,17 +119,22 @@ def _find(d, suffix):
 
 
 def summarize_trace(trace_dir, out, command, title=None):
-    """Kernel-trace statistics (rocprofv3 --kernel-trace --stats) -> markdown."""
+    """Kernel-trace statistics (rocprofv3 --kernel-trace --stats) -> markdown,
+    with a TRACE_JSON line of the decode kernels' average durations."""
     rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
     lines = ["# " + (title or "Kernel time of bench.py"), "",
              "Command: `%s`" % command, "",
              "| kernel | calls | average us | total ms | share % |", "|---|---|---|---|---|"]
+    avg = {}
     for r in rows:
         name = r["Name"]
         if not name.startswith("void pw::") and not name.startswith("pw::"):
             continue
-        lines.append("| %s | %s | %.2f | %.2f | %.1f |" % (name.split("(")[0], r["Calls"], float(r["AverageNs"]) / 1e3,
+        short = name.split("(")[0]
+        lines.append("| %s | %s | %.2f | %.2f | %.1f |" % (short, r["Calls"], float(r["AverageNs"]) / 1e3,
                                                        float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+        avg[short.replace("void ", "").replace("pw::", "")] = float(r["AverageNs"]) / 1e3
+    lines += ["", "TRACE_JSON: " + json.dumps(dict(kernel_sha=kernel_sha(), average_us=avg))]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -138,32 +155,33 @@ def _pmc_mean(d, counter, kname, largest_only=False):
 
 
 def summarize_pmc(fetch_dir, write_dir, out, command_fetch, command_write, copy_mib, alg_bytes):
-    """FETCH_SIZE / WRITE_SIZE per gate_up launch, scaled by the same counters
-    on a device copy of known size (copy reads and writes copy_mib MiB)."""
-    gu_f, n_f = _pmc_mean(fetch_dir, "FETCH_SIZE", GATE_UP_NAME)
-    gu_w, n_w = _pmc_mean(write_dir, "WRITE_SIZE", GATE_UP_NAME)
+    """FETCH_SIZE / WRITE_SIZE per gate_up and per down launch, scaled by the
+    same counters on a device copy of known size (the copy reads and writes
+    copy_mib MiB).  alg_bytes: {"gate_up": B, "down": B} algorithmic bytes
+    per launch."""
     cp_f, _ = _pmc_mean(fetch_dir, "FETCH_SIZE", COPY_NAME, largest_only=True)
     cp_w, _ = _pmc_mean(write_dir, "WRITE_SIZE", COPY_NAME, largest_only=True)
     known_kib = copy_mib * 1024.0
     sf, sw = known_kib / cp_f, known_kib / cp_w
-    fetch_b = gu_f * sf * 1024.0
-    write_b = gu_w * sw * 1024.0
-    t = dict(kernel_sha=kernel_sha(), fetch_bytes=fetch_b, write_bytes=write_b,
-             traffic_bytes=fetch_b + write_b, scale_fetch=sf, scale_write=sw,
-             algorithmic_bytes=alg_bytes)
-    lines = ["# HBM traffic of the gate_up kernel, Qwen-shaped decode layer", "",
+    t = dict(kernel_sha=kernel_sha(), scale_fetch=sf, scale_write=sw)
+    lines = ["# HBM traffic of the decode kernels, Qwen-shaped decode layer", "",
              "FETCH_SIZE command: `%s`" % command_fetch, "",
              "WRITE_SIZE command: `%s`" % command_write, "",
              "| quantity | value |", "|---|---|",
-             "| gate_up FETCH_SIZE per launch (raw KiB, %d launches) | %.1f |" % (n_f, gu_f),
-             "| gate_up WRITE_SIZE per launch (raw KiB, %d launches) | %.1f |" % (n_w, gu_w),
              "| copy kernel FETCH_SIZE / WRITE_SIZE (raw KiB, %d MiB copied) | %.1f / %.1f |" % (copy_mib, cp_f, cp_w),
-             "| scale factor fetch / write (known KiB / counted KiB) | %.3f / %.3f |" % (sf, sw),
-             "| gate_up HBM read per launch (scaled, MB) | %.2f |" % (fetch_b / 1e6),
-             "| gate_up HBM write per launch (scaled, MB) | %.2f |" % (write_b / 1e6),
-             "| gate_up algorithmic bytes per launch (MB) | %.2f |" % (alg_bytes / 1e6),
-             "| traffic / algorithmic | %.3f |" % ((fetch_b + write_b) / alg_bytes), "",
-             "TRAFFIC_JSON: " + json.dumps(t)]
+             "| scale factor fetch / write (known KiB / counted KiB) | %.3f / %.3f |" % (sf, sw)]
+    for k, prefix in KERNEL_PREFIX.items():
+        f_kib, n_f = _pmc_mean(fetch_dir, "FETCH_SIZE", prefix)
+        w_kib, n_w = _pmc_mean(write_dir, "WRITE_SIZE", prefix)
+        fetch_b, write_b = f_kib * sf * 1024.0, w_kib * sw * 1024.0
+        ab = float(alg_bytes[k])
+        t[k] = dict(fetch_bytes=fetch_b, write_bytes=write_b, traffic_bytes=fetch_b + write_b, algorithmic_bytes=ab)
+        lines += ["| %s FETCH_SIZE per launch (raw KiB, %d launches) | %.1f |" % (k, n_f, f_kib),
+                  "| %s WRITE_SIZE per launch (raw KiB, %d launches) | %.1f |" % (k, n_w, w_kib),
+                  "| %s HBM read / write per launch (scaled, MB) | %.2f / %.2f |" % (k, fetch_b / 1e6, write_b / 1e6),
+                  "| %s algorithmic bytes per launch (MB) | %.2f |" % (k, ab / 1e6),
+                  "| %s traffic / algorithmic | %.3f |" % (k, (fetch_b + write_b) / ab)]
+    lines += ["", "TRAFFIC_JSON: " + json.dumps(t)]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -458,21 +476,52 @@ def baselines_leg(spec, seed, w, packed, steps, L):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec, weights, acts_list, budget_s):
+    """The fp64 oracle on the host: batches of the timed workload for about
+    budget_s seconds on all its threads, then about a quarter of that on one
+    thread."""
     import oracle
     P = oracle.PreparedLayer(weights)
-    n_tok, secs, batches = 0, 0.0, 0
-    while secs < budget_s:
-        a = acts_list[batches % len(acts_list)]
-        dt, _ = oracle.timed_layer(P, a)
-        secs += dt
-        n_tok += a.x.shape[0]
-        batches += 1
-    return dict(value=n_tok / secs, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+
+    def run(budget):
+        n_tok, secs, batches = 0, 0.0, 0
+        while secs < budget:
+            a = acts_list[batches % len(acts_list)]
+            dt, _ = oracle.timed_layer(P, a)
+            secs += dt
+            n_tok += a.x.shape[0]
+            batches += 1
+        return n_tok, secs, batches
+
+    threads = oracle.num_threads()
+    n_tok, secs, batches = run(budget_s)
+    oracle.set_threads(1)
+    try:
+        n1, s1, b1 = run(budget_s / 4)
+    finally:
+        oracle.set_threads(threads)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return dict(value=n_tok / secs, unit="tokens/s", cores=threads, kind="oracle",
+                value_1thread=n1 / s1, nproc=os.cpu_count(), affinity_cpus=affinity, cpu_model=cpu_model(),
                 sample="%d batches of %d tokens of the same layer (%s: route, permute, "
-                       "all routed experts%s, combine) in fp64; %.1f s"
+                       "all routed experts%s, combine) in fp64; %.1f s on %d threads, then %d batches in %.1f s "
+                       "on 1 thread"
                        % (batches, acts_list[0].x.shape[0], spec.name,
-                          " + shared expert" if spec.shape.I_shared else "", secs))
+                          " + shared expert" if spec.shape.I_shared else "", secs, threads, b1, s1))
 
 
 def main():
@@ -504,14 +553,16 @@ def main():
     ap.add_argument("--title", default=None, help="heading of a --summarize-* markdown file")
     ap.add_argument("--command", default="", help="command line recorded in the summary")
     ap.add_argument("--command2", default="", help="second command line (WRITE_SIZE pass)")
-    ap.add_argument("--alg-bytes", type=float, default=0.0, help="gate_up algorithmic bytes per launch")
+    ap.add_argument("--alg-bytes", type=float, nargs=2, default=(0.0, 0.0), metavar=("GATE_UP", "DOWN"),
+                    help="algorithmic bytes per gate_up and per down launch")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command, args.title)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2], args.command,
-                      args.command2, args.copy_calibration_mib, args.alg_bytes)
+                      args.command2, args.copy_calibration_mib,
+                      {"gate_up": args.alg_bytes[0], "down": args.alg_bytes[1]})
         return
     if args.summarize_counters:
         cmds = [c for c in (args.command, args.command2) if c]
@@ -577,32 +628,51 @@ def main():
     offsets = [b.offsets.cpu().numpy() for b in batches]
     sb = [step_bytes(shape, wq, o, T) for o in offsets]
 
-    # graph of L consecutive steps (one per layer copy)
-    graph = None
+    # graphs of L consecutive steps (one per layer copy) and of the r < L
+    # steps that complete a requested count, so exactly the requested number
+    # of steps runs
+    graphs = {}
+
+    def graph_of(n):
+        if n not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                run_steps(n)
+            torch.cuda.synchronize()
+            graphs[n] = g
+        return graphs[n]
+
+    def replay(n_steps):
+        full, rem = divmod(n_steps, L)
+        if args.no_graph:
+            run_steps(n_steps)
+            return
+        for _ in range(full):
+            graph_of(L).replay()
+        if rem:
+            graph_of(rem).replay()
+
     if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            run_steps(L)
-        torch.cuda.synchronize()
+        graph_of(L)
+        if args.steps % L:
+            graph_of(args.steps % L)
+        if args.warmup % L:
+            graph_of(args.warmup % L)
 
     def timed(n_steps):
-        reps = max(1, n_steps // L)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         ev0.record(stream)
         w0 = time.perf_counter()
-        for _ in range(reps):
-            if graph is not None:
-                graph.replay()
-            else:
-                run_steps(L)
+        replay(n_steps)
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        return reps * L, ev0.elapsed_time(ev1) / 1e3, wall
+        return n_steps, ev0.elapsed_time(ev1) / 1e3, wall
 
     with torch.cuda.stream(stream):
-        timed(args.warmup)
+        if args.warmup > 0:
+            timed(args.warmup)
         n, gpu_s, wall_s = timed(args.steps)
     ms_per_step = gpu_s / n * 1e3
     tok_s = T * n / gpu_s
@@ -634,8 +704,17 @@ def main():
         cpu = cpu_baseline(spec, w, acts, args.cpu_seconds)
         log("cpu oracle: %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
 
-    tr = stored_traffic()
-    traffic = int(tr["traffic_bytes"]) if tr else None  # HBM bytes per launch (PMC, scaled)
+    tr = stored_traffic()  # HBM bytes per launch (PMC, scaled), if taken for this kernel source
+    trc = stored_trace()   # rocprofv3 average kernel durations, if taken for this kernel source
+
+    def rocprof_us(kernel):
+        if not trc:
+            return None
+        hits = [v for k, v in trc["average_us"].items() if k.startswith(KERNEL_PREFIX[kernel])]
+        return hits[0] if len(hits) == 1 else None
+
+    def rate(nbytes, us):
+        return None if not us else round(nbytes / (us * 1e-6) / 1e9, 1)
     prefill = None if args.no_prefill else prefill_leg(args.prefill_steps)
     mixtral_decode = None if args.no_mixtral_decode else mixtral_decode_leg(args.mixtral_decode_steps)
     baselines = None
@@ -661,15 +740,27 @@ def main():
                    "I_shared": shape.I_shared, "tokens_per_batch": T, "layer_copies": L,
                    "q": "routed blocks tiered by Zipf rank (8 / 5-6 / 3-4)" + (", shared at 8" if shape.I_shared else ""),
                    "source": "user model config" if spec.extra.get("user_config") else "built-in shape",
-                   "graph": graph is not None},
+                   "graph": not args.no_graph},
         "path_gbps": round(mean_b["path"] / (ms_per_step * 1e-3) / 1e9, 1),
         "path_bytes_per_step": int(mean_b["path"]),
         "active_experts_per_step": mean_b["active"],
         "kernels_us": {k: round(v["mean_us"], 3) for k, v in kern.items()},
+        # dominant kernel: gate_up (event-timed; the rocprofv3 kernel-trace
+        # figure beside it), then down, then the whole decode path: plane + LUT
+        # bytes of the active blocks over the three kernels' time and over the
+        # graph-replayed step
         "roofline": {"bound": "hbm", "kernel": "gate_up", "achieved": round(gu_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "bytes_per_launch": int(mean_b["gate_up"]),
-                     "down_achieved": round(dn_gbps, 1)},
+                     "traffic": int(tr["gate_up"]["traffic_bytes"]) if tr else None,
+                     "bytes_per_launch": int(mean_b["gate_up"]),
+                     "achieved_rocprof": rate(mean_b["gate_up"], rocprof_us("gate_up")),
+                     "down_achieved": round(dn_gbps, 1),
+                     "down_achieved_rocprof": rate(mean_b["down"], rocprof_us("down")),
+                     "down_traffic": int(tr["down"]["traffic_bytes"]) if tr else None,
+                     "down_bytes_per_launch": int(mean_b["down"]),
+                     "path_weight_bytes": int(mean_b["weights"]),
+                     "path_weights_achieved": rate(mean_b["weights"], gu_us + dn_us + kern["combine"]["mean_us"]),
+                     "step_weights_achieved": rate(mean_b["weights"], ms_per_step * 1e3)},
         "cpu_baseline": cpu,
         "prefill": prefill,
         "mixtral_decode": mixtral_decode,

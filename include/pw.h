@@ -139,6 +139,10 @@ pw_status pw_route_topk(pw_ctx *ctx, const float *logits, int T, int32_t *topk_i
                         float *topk_w, pw_stream stream);
 
 /* Group the T*k assignments a = t*k + j by expert: a stable counting sort.
+ * ("Technical summary: PagedWeight", Problem statement: each token activates
+ * only a few experts; Core components 3: the fused operation reads each
+ * expert's linear blocks at their own widths.  Grouping the tokens routed to
+ * an expert lets its planes and LUT be read once for all of them.)
  * expert_offsets: dev int32 [E+1] (offsets[0] = 0, offsets[E] = T*k);
  * sorted_assign: dev int32 [T*k], the assignments routed to expert e, in
  * ascending a, at [offsets[e], offsets[e+1]).  topk_idx entries must be in
@@ -222,9 +226,10 @@ typedef struct {
  * byte under a memory target; hot experts protected by a higher width floor
  * and a damage multiplier).  Pure host function, no context or device.
  * Routed blocks b = (layer * E + expert) * 2 + module (gate_up R = 2I x K = H,
- * down R = H x K = I) at width q hold q planes plus LUT_q as the library
- * stores them (q * 4 * ceil(K/128) * R * 4 bytes of planes, S * 2^q * 4 of LUT
- * with S the LUT slots of the block).  With share = mass[l][e] / sum over the
+ * down R = H x K = I) at width q count their q bit-planes plus LUT_q:
+ * R * K * q / 8 + R * 2^q * 2 bytes (the device storage adds only the padding
+ * of K to a multiple of 128 columns and of the LUT to whole 64-slot groups,
+ * none when 128 divides both R and K).  With share = mass[l][e] / sum over the
  * layer (0 if the layer has none) and hot = share >= hot_share, block b's
  * weight is sensitivity[b] * (share + mass_eps) * (hot ? hot_mult : 1), its
  * floor max(q_min, hot_floor) if hot else q_min, and lowering it from q to
@@ -290,14 +295,30 @@ int32_t pw_block_id(const pw_ctx *ctx, int layer, int expert, int module);
 /* Device bytes held for planes and LUTs of committed widths. */
 int64_t pw_resident_bytes(const pw_ctx *ctx);
 
-/* Test export: the child codes (code8 >> (8 - q)) of one block at its
- * committed width, produced by the same device gather routine the FFN uses.
- * out: dev uint8 [R][K].  Asynchronous on `stream`. */
-pw_status pw_debug_decode_codes(pw_ctx *ctx, int32_t block_id, uint8_t *out, pw_stream stream);
+/* Test exports: one block's decode at its committed width, run by the very
+ * routines an FFN path uses (the same LUT staging into LDS, lane-to-row
+ * mapping, plane loads, code gather and LDS look-up), with the codes and
+ * weights written out instead of multiplied.  The decode is defined in
+ * "Technical summary: PagedWeight", Core components 1 (overlaid bit-planes
+ * read at a block's own width, weights from its LUT): the child code is
+ * code8 >> (8 - q) and the weight LUT_q[row][child code].
+ * path selects the FFN path whose decode runs:
+ *   PW_DECODE_PATH_TILE128: the decode contraction with 128-row tiles (the
+ *     decode gate_up's whole tiles: 64 gate rows with their 64 up rows);
+ *   PW_DECODE_PATH_TILE64: the decode contraction with 64-row tiles (the
+ *     decode down tiles and the gate_up half tiles);
+ *   PW_DECODE_PATH_PREFILL: the prefill GEMM's weight-tile decoder.
+ * codes_out: dev uint8 [R][K] child codes; w_out: dev fp16 [R][K] weights
+ * (bit patterns); either may be NULL, not both.  Asynchronous on `stream`.
+ * Errors: INVALID (null outputs, unregistered block, path out of range), HIP. */
+enum { PW_DECODE_PATH_TILE128 = 0, PW_DECODE_PATH_TILE64 = 1, PW_DECODE_PATH_PREFILL = 2 };
+pw_status pw_debug_decode(pw_ctx *ctx, int32_t block_id, int path, uint8_t *codes_out, uint16_t *w_out,
+                          pw_stream stream);
 
-/* Test export: the decoded fp16 weights LUT_q[r][code] of one block, produced
- * by the same device gather and LDS look-up the FFN uses.  out: dev fp16
- * [R][K].  Asynchronous on `stream`. */
+/* pw_debug_decode on the decode contraction's tile of the block's module
+ * (gate_up: PW_DECODE_PATH_TILE128; down: PW_DECODE_PATH_TILE64), codes only
+ * (pw_debug_decode_codes) or weights only (pw_debug_dequant). */
+pw_status pw_debug_decode_codes(pw_ctx *ctx, int32_t block_id, uint8_t *out, pw_stream stream);
 pw_status pw_debug_dequant(pw_ctx *ctx, int32_t block_id, uint16_t *out, pw_stream stream);
 
 /* Optional per-kernel timing with HIP events on the launch stream.  While

@@ -11,24 +11,19 @@ counts how often and how strongly it is selected.  The pages' Hessian
 sensitivity is an input here and their prompt residuals are left out (both
 need trained models).  Readings (stated in the library header too):
 routing mass = sum of gate weights, per call summed in ascending assignment
-order; damage of lowering q -> q - 1 = weight * 3 * 4^(8 - q); the block
-byte model is the library's storage (q planes + LUT_q in the slot layout).
+order; damage of lowering q -> q - 1 = weight * 3 * 4^(8 - q); a block's
+bytes at width q are its q bit-planes plus LUT_q: R * K * q / 8 + R * 2^q * 2.
 """
 from __future__ import annotations
 
 from typing import List, Sequence, Tuple
 
 
-def lut_slots(R: int, module: int) -> int:
-    """Slots of a block's slot-layout LUT: gate_up pairs row i with row R/2 + i,
-    down pairs rows 64m + r and 64m + 32 + r; rounded up to 64."""
-    s = R // 2 if module == 0 else (R + 63) // 64 * 32
-    return (s + 63) // 64 * 64
-
-
-def block_bytes(R: int, K: int, module: int, q: int) -> int:
-    plane = ((K + 127) // 128) * R * 4 * 4          # ceil(K/128) chunks x R rows x 4 words x 4 bytes
-    return q * plane + lut_slots(R, module) * (1 << q) * 4
+def block_bytes(R: int, K: int, q: int) -> int:
+    """Bytes of one R x K linear block at width q: its q bit-planes, one bit
+    per weight each (R * K * q / 8), plus LUT_q, 2^q fp16 entries per row
+    (R * 2^q * 2)."""
+    return R * K * q // 8 + R * (1 << q) * 2
 
 
 def block_shape(module: int, H: int, I: int) -> Tuple[int, int]:
@@ -72,7 +67,7 @@ def plan_widths(L: int, E: int, H: int, I: int, q_cur, mass, sens, q_min: int, q
 
     def nbytes(b, qq):
         R, K = block_shape(blocks[b][2], H, I)
-        return block_bytes(R, K, blocks[b][2], qq)
+        return block_bytes(R, K, qq)
 
     def drop(b, qq):  # damage added by lowering from qq to qq - 1
         return blocks[b][3] * (3.0 * float(4 ** (8 - qq)))

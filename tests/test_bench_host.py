@@ -69,27 +69,37 @@ def _write_csv(path, rows):
 def test_pmc_summary_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
     gu = "void pw::ffn_gemv_kernel<0, 4, true>(pw::FfnArgs)"
+    dn = "void pw::ffn_gemv_kernel<1, 2, false, false>(pw::FfnArgs)"
     cp = "__amd_rocclr_copyBuffer"
     # the counters see half the copied bytes on fetch and all of them on write
     _write_csv(os.path.join(fetch, "run_counter_collection.csv"), [
         {"Kernel_Name": gu, "Counter_Name": "FETCH_SIZE", "Counter_Value": "1000"},
         {"Kernel_Name": gu, "Counter_Name": "FETCH_SIZE", "Counter_Value": "1200"},
+        {"Kernel_Name": dn, "Counter_Name": "FETCH_SIZE", "Counter_Value": "300"},
         {"Kernel_Name": cp, "Counter_Name": "FETCH_SIZE", "Counter_Value": str(512 * 1024)},
         {"Kernel_Name": cp, "Counter_Name": "FETCH_SIZE", "Counter_Value": "10"},  # small staging copy, ignored
     ])
     _write_csv(os.path.join(write, "run_counter_collection.csv"), [
         {"Kernel_Name": gu, "Counter_Name": "WRITE_SIZE", "Counter_Value": "50"},
+        {"Kernel_Name": dn, "Counter_Name": "WRITE_SIZE", "Counter_Value": "20"},
         {"Kernel_Name": cp, "Counter_Name": "WRITE_SIZE", "Counter_Value": str(1024 * 1024)},
     ])
     out = str(tmp_path / "traffic.md")
     monkeypatch.setattr(bench, "kernel_sha", lambda: "abc")
-    bench.summarize_pmc(fetch, write, out, "cmd f", "cmd w", 1024, 2.0e6)
+    bench.summarize_pmc(fetch, write, out, "cmd f", "cmd w", 1024, {"gate_up": 2.0e6, "down": 1.0e6})
     line = [l for l in open(out) if l.startswith("TRAFFIC_JSON:")][0]
     t = json.loads(line.split(":", 1)[1])
     assert abs(t["scale_fetch"] - 2.0) < 1e-12 and abs(t["scale_write"] - 1.0) < 1e-12
-    assert abs(t["fetch_bytes"] - 1100 * 2.0 * 1024) < 1e-6
-    assert abs(t["write_bytes"] - 50 * 1024) < 1e-6
+    assert abs(t["gate_up"]["fetch_bytes"] - 1100 * 2.0 * 1024) < 1e-6
+    assert abs(t["gate_up"]["write_bytes"] - 50 * 1024) < 1e-6
+    assert abs(t["down"]["traffic_bytes"] - (300 * 2.0 + 20) * 1024) < 1e-6
+    assert t["down"]["algorithmic_bytes"] == 1.0e6
     assert t["kernel_sha"] == "abc"
+    # read back only while the kernel source is the one profiled
+    monkeypatch.setattr(bench, "TRAFFIC_MD", out)
+    assert bench.stored_traffic()["gate_up"]["write_bytes"] == t["gate_up"]["write_bytes"]
+    monkeypatch.setattr(bench, "kernel_sha", lambda: "changed")
+    assert bench.stored_traffic() is None
 
 
 def test_trace_and_counter_summaries(tmp_path):
@@ -105,6 +115,8 @@ def test_trace_and_counter_summaries(tmp_path):
     text = open(out).read()
     assert "| void pw::ffn_gemv_kernel<0, 4, true> | 10 | 21.00 | 0.21 | 60.0 |" in text
     assert "fillBuffer" not in text
+    t = json.loads([l for l in text.splitlines() if l.startswith("TRACE_JSON:")][0].split(":", 1)[1])
+    assert t["average_us"] == {"ffn_gemv_kernel<0, 4, true>": 21.0}
 
     pmc = str(tmp_path / "c")
     k = "void pw::ffn_prefill_kernel<0>(pw::FfnArgs)"

@@ -21,27 +21,55 @@ def _gpu(require_gpu):
 
 # ------------------------------------------------------------------ decode
 
+# Every decode path an FFN kernel runs, pinned bit for bit: the codes and the
+# fp16 weights produced by the FFN's own decode routines (pw_debug_decode) must
+# equal the oracle's code8 >> (8 - q) and LUT_q[row][code] ("Technical summary:
+# PagedWeight", Core components 1).  Paths: the decode contraction's 128-row
+# tiles (gate_up whole tiles; q = 3 two-set pair tables, q = 4 single tables,
+# q >= 5 bit transpose) and 64-row tiles (gate_up half tiles, down; q <= 4 pair
+# tables), and the prefill decoder (per-lane rotate form).  Shapes: ragged row
+# tiles, ragged K (a last chunk of 1 or 3 words) and several chunks per K-wave.
+DECODE_SHAPES = {"ragged": (352, 224), "multi_chunk": (1056, 608)}
+
+
+@pytest.mark.parametrize("shape", sorted(DECODE_SHAPES))
 @pytest.mark.parametrize("q", [3, 4, 5, 6, 7, 8])
-def test_debug_decode_codes_and_weights_bit_exact(q):
+def test_ffn_decode_paths_bit_exact(q, shape):
     import torch
     import any_precision_expert_amd as pw
-    # down block R = H = 352 (ragged 64-row tile), K = I = 224 (one chunk + 3 words)
-    w, _ = pw_synth.make_small(H=352, I=224, E=2, top_k=1, T=1, seed=100 + q, q_fixed=q)
+    import oracle
+    H, I = DECODE_SHAPES[shape]
+    w, _ = pw_synth.make_small(H=H, I=I, E=2, top_k=1, T=1, seed=100 + q + 10 * H, q_fixed=q)
     ctx = make_ctx(w.shape)
+    paths = {"tile128": pw.DECODE_PATH_TILE128, "tile64": pw.DECODE_PATH_TILE64,
+             "prefill": pw.DECODE_PATH_PREFILL}
     try:
         for e in range(2):
             for m, blk in ((pw.MODULE_GATE_UP, w.gate_up[e]), (pw.MODULE_DOWN, w.down[e])):
                 ctx.register_code_block(0, e, m, blk.code8, blk.luts, blk.q)
                 bid = ctx.block_id(0, e, m)
+                want_codes = oracle.decode_codes(blk.code8, q)
+                want_w = oracle.decode_block(blk)
+                for name, path in paths.items():
+                    say("decode q=%d %s expert %d module %d path %s" % (q, shape, e, m, name))
+                    codes = torch.full(blk.code8.shape, 255, dtype=torch.uint8, device="cuda")
+                    wts = torch.full(blk.code8.shape, -7.0, dtype=torch.float16, device="cuda")
+                    ctx.debug_decode(bid, path, codes, wts)
+                    torch.cuda.synchronize()
+                    got_c = codes.cpu().numpy()
+                    got_w = wts.cpu().numpy().astype(np.float64)
+                    bad = np.argwhere(got_c != want_codes)
+                    assert bad.size == 0, "%s: %d codes differ, first at %s" % (name, len(bad), bad[0])
+                    bad = np.argwhere(got_w != want_w)
+                    assert bad.size == 0, "%s: %d weights differ, first at %s" % (name, len(bad), bad[0])
+                # the two single-output exports run the decode contraction's tile
                 out = torch.zeros(blk.code8.shape, dtype=torch.uint8, device="cuda")
                 ctx.debug_decode_codes(bid, out)
                 wout = torch.zeros(blk.code8.shape, dtype=torch.float16, device="cuda")
                 ctx.debug_dequant(bid, wout)
                 torch.cuda.synchronize()
-                expect = blk.code8 >> (8 - q)
-                assert np.array_equal(out.cpu().numpy(), expect)
-                direct = np.take_along_axis(blk.luts[q], expect.astype(np.int64), axis=1)
-                assert np.array_equal(wout.cpu().numpy().view(np.uint16), direct.view(np.uint16))
+                assert np.array_equal(out.cpu().numpy(), want_codes)
+                assert np.array_equal(wout.cpu().numpy().astype(np.float64), want_w)
     finally:
         ctx.close()
 
@@ -192,14 +220,37 @@ def test_config2_mixtral_decode(mixtral, T):
     w, ctx = mixtral
     spec = pw_synth.CONFIGS[2]
     a = pw_synth.make_activations(spec.shape, T, pw_synth.config_seed(2), 0, 0, spec.logits)
-    tokens = None if T <= 16 else list(range(0, T, 4))
-    check_layer(w, a, tokens=tokens, label="cfg2 T=%d" % T, ctx=ctx)
+    check_layer(w, a, label="cfg2 T=%d" % T, ctx=ctx)  # every token of the batch
 
 
-def test_config3_mixtral_prefill_sampled():
+def stratified_tokens(idx, offsets, sorted_assign, k, seed, tile=512, wave_range=64):
+    """Tokens that cover every cell of the prefill GEMM: for each expert, one
+    random assignment in each (512-token tile, 64-token wave range) of its
+    sorted assignment list, plus the expert's first and last assignment; the
+    token of each chosen assignment."""
+    rng = np.random.default_rng(seed)
+    picks = set()
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo:
+            continue
+        picks.update((lo, hi - 1))
+        for start in range(lo, hi, wave_range):
+            end = min(hi, start + wave_range)
+            picks.add(int(rng.integers(start, end)))
+    return sorted({int(sorted_assign[p]) // k for p in picks})
+
+
+def test_config3_mixtral_prefill_stratified():
+    """Every (expert, 512-token tile, 64-token wave range) cell of the
+    Mixtral-shaped prefill layer (4096 tokens) holds a compared token, and so do
+    each expert's first and last assignments (the ragged last tiles)."""
+    import oracle
     w, a = pw_synth.make_config(3)
-    rng = np.random.default_rng(3)
-    tokens = sorted(set(rng.choice(4096, size=8, replace=False).tolist()) | {0, 4095})
+    idx, _ = oracle.route_topk(a.logits, w.shape.top_k)
+    offsets, srt = oracle.permute(idx, w.shape.E)
+    tokens = stratified_tokens(idx, offsets, srt, w.shape.top_k, seed=3)
+    say("cfg3: %d stratified tokens" % len(tokens))
     check_layer(w, a, tokens=tokens, label="cfg3 prefill")
 
 
@@ -331,7 +382,7 @@ def test_routing_mass_accumulates_like_the_oracle():
     try:
         for l in range(2):
             register_layer(ctx, l, w)
-        want_bytes = 2 * sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), m, int(b.q))
+        want_bytes = 2 * sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), int(b.q))
                              for m, blocks in ((0, w.gate_up), (1, w.down)) for b in blocks)
         assert ctx.resident_bytes() == want_bytes
         calls = [(0, 16), (1, 16), (0, 300), (1, 5), (0, 16)]

@@ -133,8 +133,8 @@ def test_budget_planner_stack():
         sens = np.random.default_rng(seed).uniform(0.5, 1.5, size=(L, shape.E, 2)).astype(np.float32)
         params = dict(q_min=3, q_max=8, hot_floor=6, hot_share=0.15, hot_mult=4.0, mass_eps=1e-3)
         def uniform_bytes(qq):
-            return L * shape.E * sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), m, qq) for m in (0, 1))
-        assert init == sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), m, int(q0[l, e, m]))
+            return L * shape.E * sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), qq) for m in (0, 1))
+        assert init == sum(op.block_bytes(*op.block_shape(m, shape.H, shape.I), int(q0[l, e, m]))
                            for l in range(L) for e in range(shape.E) for m in (0, 1))
         targets = [uniform_bytes(4), uniform_bytes(7), uniform_bytes(5)]
         drv = StackDriver(ctx, q0, logits, x, commit_every=4, byte_targets=targets, sensitivity=sens,

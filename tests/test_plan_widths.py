@@ -31,8 +31,21 @@ def total_bytes(H, I, q):
         for e in range(E):
             for m in range(2):
                 R, K = op.block_shape(m, H, I)
-                s += op.block_bytes(R, K, m, int(q[l, e, m]))
+                s += op.block_bytes(R, K, int(q[l, e, m]))
     return s
+
+
+def test_block_bytes_hand_computed():
+    # 64 x 256 block at q = 3: 3 planes of 64 * 256 bits = 3 * 2048 bytes, plus
+    # 64 rows x 8 fp16 entries = 1024 bytes
+    assert op.block_bytes(64, 256, 3) == 6144 + 1024
+    # q = 8: one byte per weight (16384) plus 64 rows x 256 entries x 2 bytes (32768)
+    assert op.block_bytes(64, 256, 8) == 16384 + 32768
+    # a Qwen1.5-MoE-shaped gate_up block (2 x 1408 rows, K = 2048) at q = 5:
+    # 2816 * 2048 * 5 / 8 = 3604480 plus 2816 * 32 * 2 = 180224
+    assert op.block_bytes(*op.block_shape(0, 2048, 1408), 5) == 3604480 + 180224
+    # down block of the same expert (2048 x 1408) at q = 4
+    assert op.block_bytes(*op.block_shape(1, 2048, 1408), 4) == 1441792 + 65536
 
 
 def test_target_that_fits_everything_raises_all_to_q_max():
@@ -88,7 +101,7 @@ def test_raise_takes_the_block_with_most_damage_removed_per_byte():
     sens[0, 2, 1] = 1e4  # block 5 dominates
     base = total_bytes(H, I, q)
     R, K = op.block_shape(1, H, I)
-    step = op.block_bytes(R, K, 1, 4) - op.block_bytes(R, K, 1, 3)
+    step = op.block_bytes(R, K, 4) - op.block_bytes(R, K, 3)
     out, total = run_oracle(H, I, q.tolist(), mass.tolist(), sens.tolist(), base + step, hot_share=0.0)
     assert np.argwhere(out != q).tolist() == [[0, 2, 1]] and out[0, 2, 1] == 4
     assert total == base + step
