@@ -30,13 +30,15 @@ EXPORTS = (
     "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
     "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_routing_mass_enable", "pw_routing_mass_reset",
     "pw_routing_mass_read", "pw_plan_widths", "pw_request_widths", "pw_commit_ready", "pw_block_state",
-    "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id",
+    "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id", "pw_plane_states", "pw_committed_widths",
+    "pw_routing_mass_copy", "pw_plan_event", "pw_retarget", "pw_trim", "pw_pool_stats",
     "pw_resident_bytes", "pw_debug_decode", "pw_debug_decode_codes", "pw_debug_dequant", "pw_profile_enable",
     "pw_profile_read",
 )
 
 
 PAGE_RESIDENT, PAGE_IN_TRANSFER, PAGE_READY = 0, 1, 2
+PLANE_GPU, PLANE_IN_TRANSFER, PLANE_READY, PLANE_CPU, PLANE_ABSENT = 0, 1, 2, 3, 4
 DECODE_PATH_TILE128, DECODE_PATH_TILE64, DECODE_PATH_PREFILL = 0, 1, 2
 
 
@@ -93,6 +95,16 @@ def lib() -> ctypes.CDLL:
         L.pw_plan_widths.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp,
                                      ctypes.POINTER(PlanParams), i64, vp, ctypes.POINTER(i64)]
         L.pw_set_committed_bits.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
+        L.pw_plane_states.argtypes = [vp, i32, vp]
+        L.pw_committed_widths.argtypes = [vp, vp]
+        L.pw_routing_mass_copy.argtypes = [vp, vp, vp]
+        L.pw_plan_event.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
+                                    ctypes.POINTER(ctypes.c_int)]
+        L.pw_retarget.argtypes = [vp, i64, vp, vp, ctypes.POINTER(PlanParams), vp, ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(i64)]
+        L.pw_trim.argtypes = [vp, ctypes.POINTER(i64)]
+        L.pw_pool_stats.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                    ctypes.POINTER(i64)]
         L.pw_get_committed_bits.argtypes = [vp, i32, ctypes.POINTER(i32)]
         L.pw_block_id.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.pw_block_id.restype = i32
@@ -273,6 +285,47 @@ class Context:
         _check(lib().pw_block_state(self.h, block_id, ctypes.byref(qc), ctypes.byref(qd), ctypes.byref(st)))
         return qc.value, qd.value, st.value
 
+    def plane_states(self, block_id: int) -> np.ndarray:
+        """int32 [9]: state of bit-planes 0..7 and of the desired width's LUT (PLANE_*)."""
+        out = np.zeros(9, dtype=np.int32)
+        _check(lib().pw_plane_states(self.h, block_id, out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def committed_widths(self) -> np.ndarray:
+        """uint8 [L][E + 1][2]: committed width of every block (slot E = shared expert; 0 = not registered)."""
+        d = self.desc
+        out = np.zeros((d.num_layers, d.num_experts + 1, 2), dtype=np.uint8)
+        _check(lib().pw_committed_widths(self.h, out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def routing_mass_copy(self, dst, stream=None) -> None:
+        """Enqueue a copy of the routing mass into dst (device tensor or pinned host tensor of L*E fp64)."""
+        _check(lib().pw_routing_mass_copy(self.h, _ptr(dst), _stream(stream)))
+
+    def retarget(self, byte_target: int, mass: np.ndarray, sensitivity: np.ndarray, copy_stream=None,
+                 q_min: int = 3, q_max: int = 8, hot_floor: int = 6, hot_share: float = 0.1,
+                 hot_mult: float = 4.0, mass_eps: float = 1e-3):
+        """pw_retarget: (blocks requested, planned routed bytes)."""
+        d = self.desc
+        m = np.ascontiguousarray(mass, dtype=np.float64).reshape(d.num_layers, d.num_experts)
+        s = np.ascontiguousarray(sensitivity, dtype=np.float32).reshape(d.num_layers, d.num_experts, 2)
+        p = PlanParams(q_min, q_max, hot_floor, hot_share, hot_mult, mass_eps)
+        n, total = ctypes.c_int(0), ctypes.c_int64(0)
+        _check(lib().pw_retarget(self.h, int(byte_target), m.ctypes.data_as(ctypes.c_void_p),
+                                 s.ctypes.data_as(ctypes.c_void_p), ctypes.byref(p), _stream(copy_stream),
+                                 ctypes.byref(n), ctypes.byref(total)))
+        return n.value, total.value
+
+    def trim(self) -> int:
+        freed = ctypes.c_int64(0)
+        _check(lib().pw_trim(self.h, ctypes.byref(freed)))
+        return freed.value
+
+    def pool_stats(self) -> dict:
+        v = [ctypes.c_int64(0) for _ in range(4)]
+        _check(lib().pw_pool_stats(self.h, *[ctypes.byref(x) for x in v]))
+        return dict(resident=v[0].value, cached=v[1].value, waiting=v[2].value, events=v[3].value)
+
     def routing_mass_enable(self, on: bool = True) -> None:
         _check(lib().pw_routing_mass_enable(self.h, 1 if on else 0))
 
@@ -304,6 +357,23 @@ class Context:
         n = ctypes.c_int64()
         _check(lib().pw_profile_read(self.h, kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
         return float(ms.value), int(n.value)
+
+
+def plan_event(q_cur: np.ndarray, mass: np.ndarray, lower: bool, n_change: int, skip: Optional[np.ndarray] = None):
+    """pw_plan_event: (block ids int32, new widths uint8) of one fixed-fraction
+    commit event.  q_cur: [L][E][2]; mass: [L][E]; skip: [L][E][2] or None."""
+    q = np.ascontiguousarray(q_cur, dtype=np.uint8)
+    L, E = q.shape[0], q.shape[1]
+    m = np.ascontiguousarray(mass, dtype=np.float64).reshape(L, E)
+    sk = None if skip is None else np.ascontiguousarray(skip, dtype=np.uint8).reshape(L, E, 2)
+    ids = np.zeros(max(n_change, 1), dtype=np.int32)
+    qs = np.zeros(max(n_change, 1), dtype=np.uint8)
+    n = ctypes.c_int(0)
+    _check(lib().pw_plan_event(L, E, q.ctypes.data_as(ctypes.c_void_p), m.ctypes.data_as(ctypes.c_void_p),
+                               None if sk is None else sk.ctypes.data_as(ctypes.c_void_p), 1 if lower else 0,
+                               int(n_change), ids.ctypes.data_as(ctypes.c_void_p), qs.ctypes.data_as(ctypes.c_void_p),
+                               ctypes.byref(n)))
+    return ids[:n.value].copy(), qs[:n.value].copy()
 
 
 def plan_widths(H: int, I: int, q_cur: np.ndarray, mass: np.ndarray, sensitivity: np.ndarray,

@@ -55,10 +55,67 @@ pw_status ok()
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
+// Events recorded behind library work (copies of a width change, page-table
+// updates), recycled once no one needs them any more: each holder takes a
+// reference, and an event whose last reference is dropped goes back to the
+// free list (a later hipEventRecord re-arms it; waits already enqueued on its
+// earlier record are not affected).
+class EventPool {
+public:
+    ~EventPool() { clear(); }
+
+    hipError_t acquire(hipEvent_t* ev)
+    {
+        if (!free_.empty()) {
+            *ev = free_.back();
+            free_.pop_back();
+        } else {
+            hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+            ++created_;
+        }
+        refs_[*ev] = 0;
+        return hipSuccess;
+    }
+
+    void hold(hipEvent_t ev) { ++refs_[ev]; }
+
+    // drops one reference; an event with none left is free again
+    void drop(hipEvent_t ev)
+    {
+        auto it = refs_.find(ev);
+        if (it == refs_.end()) return;
+        if (--it->second <= 0) {
+            refs_.erase(it);
+            free_.push_back(ev);
+        }
+    }
+
+    size_t created() const { return created_; }
+    size_t in_use() const { return refs_.size(); }
+
+    void clear()
+    {
+        for (auto ev : free_) (void)hipEventDestroy(ev);
+        for (auto& kv : refs_) (void)hipEventDestroy(kv.first);
+        free_.clear();
+        refs_.clear();
+        created_ = 0;
+    }
+
+private:
+    std::vector<hipEvent_t> free_;
+    std::unordered_map<hipEvent_t, int> refs_;
+    size_t created_ = 0;
+};
+
 // Device slabs for planes and LUTs, recycled by size.  A released slab is only
-// reused after an event recorded behind the last work that may read it.
+// reused after an event recorded behind the last work that may read it (the
+// pool holds a reference on that event until then).  trim() returns the free
+// slabs to the device.
 class SlabPool {
 public:
+    explicit SlabPool(EventPool* evs) : evs_(evs) {}
     ~SlabPool() { clear(); }
 
     hipError_t alloc(size_t bytes, void** out)
@@ -69,6 +126,7 @@ public:
         if (it != free_.end() && !it->second.empty()) {
             *out = it->second.back();
             it->second.pop_back();
+            free_bytes_ -= bytes;
             resident_ += bytes;
             return hipSuccess;
         }
@@ -89,6 +147,7 @@ public:
         if (!p) return;
         bytes = round(bytes);
         free_[bytes].push_back(p);
+        free_bytes_ += bytes;
         resident_ -= bytes;
     }
 
@@ -96,6 +155,7 @@ public:
     {
         if (!p) return;
         bytes = round(bytes);
+        evs_->hold(ev);
         pending_.push_back({p, bytes, ev});
         resident_ -= bytes;
     }
@@ -106,6 +166,8 @@ public:
         for (size_t i = 0; i < pending_.size(); ++i) {
             if (hipEventQuery(pending_[i].ev) == hipSuccess) {
                 free_[pending_[i].bytes].push_back(pending_[i].p);
+                free_bytes_ += pending_[i].bytes;
+                evs_->drop(pending_[i].ev);
             } else {
                 pending_[w++] = pending_[i];
             }
@@ -113,7 +175,32 @@ public:
         pending_.resize(w);
     }
 
+    // hipFree every free slab (those still waiting for their event stay);
+    // returns the bytes given back
+    size_t trim()
+    {
+        reclaim();
+        size_t freed = 0;
+        for (auto& kv : free_) {
+            for (void* p : kv.second) {
+                (void)hipFree(p);
+                all_.erase(p);
+                freed += kv.first;
+            }
+        }
+        free_.clear();
+        free_bytes_ = 0;
+        return freed;
+    }
+
     int64_t resident() const { return (int64_t)resident_; }
+    int64_t free_bytes() const { return (int64_t)free_bytes_; }
+    int64_t waiting_bytes() const
+    {
+        size_t b = 0;
+        for (const auto& p : pending_) b += p.bytes;
+        return (int64_t)b;
+    }
 
     void clear()
     {
@@ -122,6 +209,7 @@ public:
         free_.clear();
         pending_.clear();
         resident_ = 0;
+        free_bytes_ = 0;
     }
 
 private:
@@ -131,10 +219,12 @@ private:
         size_t bytes;
         hipEvent_t ev;
     };
+    EventPool* evs_;
     std::unordered_map<size_t, std::vector<void*>> free_;
     std::vector<Pending> pending_;
     std::unordered_map<void*, size_t> all_;
     size_t resident_ = 0;
+    size_t free_bytes_ = 0;
 };
 
 struct HostBlock {
@@ -180,7 +270,8 @@ struct pw_ctx {
     BlockDesc* d_table = nullptr;
     std::vector<BlockDesc> h_table;
     std::vector<HostBlock> blocks;
-    SlabPool pool;
+    EventPool evs;  // declared before the slab pool, which holds references on its events
+    SlabPool pool{&evs};
     // pinned staging for page-table updates, recycled after their event
     struct Staging {
         BlockDesc* p;
@@ -188,7 +279,6 @@ struct pw_ctx {
         hipEvent_t ev;
     };
     std::vector<Staging> staging;
-    std::vector<hipEvent_t> events;  // owned events (released at destroy)
     int num_cus = 256;  // compute units of the device (decode tile schedule)
     std::map<int, WidthChange> pending;  // width requests whose commit has not happened
     double* d_mass = nullptr;  // routing-mass accumulator [L][E] fp64 (pw_routing_mass_enable)
@@ -201,10 +291,11 @@ struct pw_ctx {
 
 namespace {
 
+// An event from the context's pool with one reference held by the caller.
 hipError_t new_event(pw_ctx* c, hipEvent_t* ev)
 {
-    hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
-    if (e == hipSuccess) c->events.push_back(*ev);
+    hipError_t e = c->evs.acquire(ev);
+    if (e == hipSuccess) c->evs.hold(*ev);
     return e;
 }
 
@@ -377,8 +468,8 @@ pw_status pw_destroy(pw_ctx* c)
     for (auto& b : c->blocks)
         if (b.registered) free_block_now(c, b);
     for (auto& s : c->staging) (void)hipHostFree(s.p);
-    for (auto ev : c->events) (void)hipEventDestroy(ev);
     c->pool.clear();
+    c->evs.clear();
     (void)hipFree(c->d_table);
     if (c->d_mass) (void)hipFree(c->d_mass);
     delete c;
@@ -766,13 +857,22 @@ int64_t pw_resident_bytes(const pw_ctx* c) { return c ? c->pool.resident() : 0; 
 // (stream-ordered, so work enqueued earlier keeps the old widths), old slabs
 // recycled after that update.
 
+// Undo prepared changes that will not be committed: their new slabs go back
+// to the pool and each plan's reference on the copy event is dropped.
 static void release_prepared(pw_ctx* c, const std::vector<WidthChange>& plans)
 {
     for (const auto& p : plans) {
         const HostBlock& b = c->blocks[p.id];
         for (int j = p.qo; j < p.qn; ++j) c->pool.release_now(p.planes[j], (size_t)b.pw * 4);
         c->pool.release_now(p.lut, lut_bytes(b.S, p.qn));
+        c->evs.drop(p.copied);
     }
+}
+
+// After a commit: the plans' references on their copy event.
+static void drop_copy_events(pw_ctx* c, const std::vector<WidthChange>& plans)
+{
+    for (const auto& p : plans) c->evs.drop(p.copied);
 }
 
 static pw_status prepare_changes(pw_ctx* c, const char* fn, const std::vector<std::pair<int, int>>& todo,
@@ -817,9 +917,15 @@ static pw_status prepare_changes(pw_ctx* c, const char* fn, const std::vector<st
         // copies may be in flight into the new slabs: wait before recycling them
         (void)hipStreamSynchronize(xs);
         release_prepared(c, plans);
+        if (copied) c->evs.drop(copied);
         return hip_fail(e, "enqueue plane / LUT copies");
     }
-    for (auto& p : plans) p.copied = copied;
+    // every plan holds a reference on the copy event until it is committed
+    for (auto& p : plans) {
+        p.copied = copied;
+        c->evs.hold(copied);
+    }
+    c->evs.drop(copied);
     return ok();
 }
 
@@ -868,6 +974,7 @@ static pw_status apply_changes(pw_ctx* c, std::vector<WidthChange>& plans, hipSt
         // the device table may hold some new entries: restore the old ones
         for (auto& p : plans) (void)hipMemcpy(c->d_table + p.id, &c->h_table[p.id], sizeof(BlockDesc), hipMemcpyHostToDevice);
         c->staging.push_back(st);
+        if (updated) c->evs.drop(updated);
         return hip_fail(e, "page-table update");
     }
     c->staging.push_back(st);
@@ -884,6 +991,7 @@ static pw_status apply_changes(pw_ctx* c, std::vector<WidthChange>& plans, hipSt
         b.q = plans[i].qn;
         c->h_table[plans[i].id] = newdesc[i];
     }
+    c->evs.drop(updated);  // the released slabs hold it until they are reclaimed
     return ok();
 }
 
@@ -931,7 +1039,9 @@ pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint
     if ((st = apply_changes(c, plans, cs)) != PW_OK) {
         (void)hipStreamSynchronize(xs);
         release_prepared(c, plans);
+        return st;
     }
+    drop_copy_events(c, plans);
     return st;
 }
 
@@ -966,6 +1076,7 @@ pw_status pw_commit_ready(pw_ctx* c, pw_stream compute, int* n_committed)
     std::sort(ready.begin(), ready.end(), [](const WidthChange& a, const WidthChange& b) { return a.id < b.id; });
     const pw_status st = apply_changes(c, ready, (hipStream_t)compute);
     if (st != PW_OK) return st;
+    drop_copy_events(c, ready);
     for (const auto& p : ready) c->pending.erase(p.id);
     if (n_committed) *n_committed = (int)ready.size();
     return ok();
@@ -987,6 +1098,111 @@ pw_status pw_block_state(const pw_ctx* c, int32_t id, int32_t* q_committed, int3
     const hipError_t q = hipEventQuery(it->second.copied);
     if (q != hipSuccess && q != hipErrorNotReady) return hip_fail(q, "pw_block_state: copy event");
     *state = q == hipSuccess ? PW_PAGE_READY : PW_PAGE_IN_TRANSFER;
+    return ok();
+}
+
+pw_status pw_committed_widths(const pw_ctx* c, uint8_t* q_out)
+{
+    if (!c || !q_out) return fail(PW_ERR_INVALID, "pw_committed_widths: null pointer");
+    for (int id = 0; id < c->nblocks; ++id) q_out[id] = c->blocks[id].registered ? (uint8_t)c->blocks[id].q : 0;
+    return ok();
+}
+
+pw_status pw_routing_mass_copy(pw_ctx* c, double* dst, pw_stream stream)
+{
+    if (!c || !dst) return fail(PW_ERR_INVALID, "pw_routing_mass_copy: null pointer");
+    if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_copy: routing mass was never enabled");
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
+    e = hipMemcpyAsync(dst, c->d_mass, bytes, hipMemcpyDefault, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "pw_routing_mass_copy");
+}
+
+pw_status pw_plane_states(const pw_ctx* c, int32_t id, int32_t* states)
+{
+    if (!c || !states) return fail(PW_ERR_INVALID, "pw_plane_states: null pointer");
+    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+        return fail(PW_ERR_INVALID, "pw_plane_states: block id %d not registered", id);
+    const HostBlock& b = c->blocks[id];
+    const int off_gpu = c->d.keep_host_masters ? PW_PLANE_CPU : PW_PLANE_ABSENT;
+    const auto it = c->pending.find(id);
+    if (it == c->pending.end()) {
+        for (int p = 0; p < 8; ++p) states[p] = p < b.q ? PW_PLANE_GPU : off_gpu;
+        states[8] = PW_PLANE_GPU;
+        return ok();
+    }
+    const hipError_t q = hipEventQuery(it->second.copied);
+    if (q != hipSuccess && q != hipErrorNotReady) return hip_fail(q, "pw_plane_states: copy event");
+    const int moving = q == hipSuccess ? PW_PLANE_READY : PW_PLANE_IN_TRANSFER;
+    const int qo = it->second.qo, qn = it->second.qn;
+    for (int p = 0; p < 8; ++p) {
+        if (p < qo) states[p] = PW_PLANE_GPU;  // lowering: planes qn..qo-1 stay in use until the commit
+        else if (p < qn) states[p] = moving;
+        else states[p] = off_gpu;
+    }
+    states[8] = moving;  // LUT_{d_i}
+    return ok();
+}
+
+pw_status pw_trim(pw_ctx* c, int64_t* freed_bytes)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_trim: null context");
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    const size_t freed = c->pool.trim();
+    if (freed_bytes) *freed_bytes = (int64_t)freed;
+    return ok();
+}
+
+pw_status pw_pool_stats(const pw_ctx* c, int64_t* resident, int64_t* cached, int64_t* waiting, int64_t* events)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_pool_stats: null context");
+    if (resident) *resident = c->pool.resident();
+    if (cached) *cached = c->pool.free_bytes();
+    if (waiting) *waiting = c->pool.waiting_bytes();
+    if (events) *events = (int64_t)c->evs.created();
+    return ok();
+}
+
+pw_status pw_retarget(pw_ctx* c, int64_t byte_target, const double* mass, const float* sens,
+                      const pw_plan_params* params, pw_stream copy, int* n_requested, int64_t* planned_bytes)
+{
+    if (!c || !mass || !sens || !params) return fail(PW_ERR_INVALID, "pw_retarget: null pointer");
+    if (n_requested) *n_requested = 0;
+    const int L = c->d.num_layers, E = c->d.num_experts;
+    std::vector<uint8_t> q_cur((size_t)L * E * 2), q_plan(q_cur.size());
+    for (int l = 0; l < L; ++l)
+        for (int e = 0; e < E; ++e)
+            for (int m = 0; m < 2; ++m) {
+                const int id = (l * (E + 1) + e) * 2 + m;
+                if (!c->blocks[id].registered)
+                    return fail(PW_ERR_STATE, "pw_retarget: block (layer %d, expert %d, module %d) not registered", l, e, m);
+                const auto it = c->pending.find(id);
+                q_cur[((size_t)l * E + e) * 2 + m] = (uint8_t)(it == c->pending.end() ? c->blocks[id].q : it->second.qn);
+            }
+    int64_t total = 0;
+    pw_status st = pw_plan_widths(L, E, c->d.hidden, c->d.inter, q_cur.data(), mass, sens, params, byte_target,
+                                  q_plan.data(), &total);
+    if (st != PW_OK) return st;
+    std::vector<int32_t> ids;
+    std::vector<uint8_t> qs;
+    for (int l = 0; l < L; ++l)
+        for (int e = 0; e < E; ++e)
+            for (int m = 0; m < 2; ++m) {
+                const size_t b = ((size_t)l * E + e) * 2 + m;
+                const int id = (l * (E + 1) + e) * 2 + m;
+                if (q_plan[b] != q_cur[b] && !c->pending.count(id)) {
+                    ids.push_back(id);
+                    qs.push_back(q_plan[b]);
+                }
+            }
+    if (!ids.empty()) {
+        st = pw_request_widths(c, (int)ids.size(), ids.data(), qs.data(), copy);
+        if (st != PW_OK) return st;
+    }
+    if (n_requested) *n_requested = (int)ids.size();
+    if (planned_bytes) *planned_bytes = total;
     return ok();
 }
 

@@ -110,3 +110,41 @@ extern "C" pw_status pw_plan_widths(int L, int E, int H, int I, const uint8_t* q
     if (bytes_out) *bytes_out = total;
     return PW_OK;
 }
+
+// One commit event of the fixed-fraction schedule: among the routed blocks
+// not skipped and not at the bound (q > 3 when lowering, q < 8 when
+// raising), the n_change with the least routing mass of their expert (both
+// modules of an expert share it; ties: lower block id) move one bit.
+extern "C" pw_status pw_plan_event(int L, int E, const uint8_t* q_cur, const double* mass, const uint8_t* skip,
+                                   int lower, int n_change, int32_t* ids_out, uint8_t* q_out, int* n_out)
+{
+    using namespace pw;
+    if (!q_cur || !mass || !n_out || (n_change > 0 && (!ids_out || !q_out)))
+        return plan_fail("pw_plan_event: null pointer");
+    if (L < 1 || E < 1 || n_change < 0) return plan_fail("pw_plan_event: size out of range");
+    struct Cand {
+        double m;
+        int32_t id;
+        int b;
+    };
+    std::vector<Cand> cand;
+    for (int l = 0; l < L; ++l)
+        for (int e = 0; e < E; ++e)
+            for (int m = 0; m < 2; ++m) {
+                const int b = (l * E + e) * 2 + m;
+                const int q = q_cur[b];
+                if (q < PW_QMIN || q > PW_QMAX) return plan_fail("pw_plan_event: width out of range");
+                if ((skip && skip[b]) || (lower ? q <= PW_QMIN : q >= PW_QMAX)) continue;
+                cand.push_back({mass[(size_t)l * E + e], (l * (E + 1) + e) * 2 + m, b});
+            }
+    std::sort(cand.begin(), cand.end(), [](const Cand& x, const Cand& y) {
+        return x.m < y.m || (x.m == y.m && x.id < y.id);
+    });
+    const int n = std::min<int>(n_change, (int)cand.size());
+    for (int i = 0; i < n; ++i) {
+        ids_out[i] = cand[i].id;
+        q_out[i] = (uint8_t)(q_cur[cand[i].b] + (lower ? -1 : 1));
+    }
+    *n_out = n;
+    return PW_OK;
+}

@@ -286,6 +286,67 @@ pw_status pw_commit_ready(pw_ctx *ctx, pw_stream compute, int *n_committed);
 pw_status pw_block_state(const pw_ctx *ctx, int32_t block_id, int32_t *q_committed, int32_t *q_desired,
                          int32_t *state);
 
+/* Per-plane page states of one block ("Technical summary: PagedWeight", Core
+ * components 1: pages reside on the GPU, on the CPU, or are in transfer).
+ * states: host int32 [9]; states[p] for bit-plane p = 0..7, states[8] for
+ * the LUT of the desired width d_i.  A plane is PW_PLANE_GPU while a device
+ * copy is in use (planes q_i..d_i-1 of a lowering request stay in use until
+ * its commit); IN_TRANSFER / READY while a raise request's copy is in flight /
+ * has landed and awaits the commit; PW_PLANE_CPU when only the pinned host
+ * master holds it; PW_PLANE_ABSENT when no copy is kept (a context without
+ * host masters).  Errors: INVALID (null pointer, unregistered block), HIP. */
+enum { PW_PLANE_GPU = 0, PW_PLANE_IN_TRANSFER = 1, PW_PLANE_READY = 2, PW_PLANE_CPU = 3, PW_PLANE_ABSENT = 4 };
+pw_status pw_plane_states(const pw_ctx *ctx, int32_t block_id, int32_t *states);
+
+/* Committed width of every block, by block id (host uint8 [num_layers *
+ * (num_experts + 1) * 2]; 0 for a block not registered). */
+pw_status pw_committed_widths(const pw_ctx *ctx, uint8_t *q_out);
+
+/* Copy the routing-mass accumulator [L][E] fp64 to `dst` (device memory or
+ * pinned host memory) after the work enqueued on `stream`, without waiting:
+ * the caller synchronises on the stream (or an event recorded after this
+ * call) before reading.  Errors: INVALID, STATE (never enabled), HIP. */
+pw_status pw_routing_mass_copy(pw_ctx *ctx, double *dst, pw_stream stream);
+
+/* One commit event of a fixed-fraction schedule (Core components 2 and 3:
+ * the lowest-mass blocks change first, widths change by whole planes).
+ * Pure host function.  Among the routed blocks b = (l * E + e) * 2 + m with
+ * skip[b] == 0 (skip may be NULL) and not at the bound (q_cur[b] > 3 when
+ * `lower`, < 8 otherwise), the n_change blocks with the least mass[l][e]
+ * (ties: lower block id) move one bit down (lower) or up.  ids_out receives
+ * their library block ids (l * (E + 1) + e) * 2 + m in that order, q_out
+ * their new widths, *n_out how many (fewer than n_change if fewer qualify).
+ * q_cur, skip: uint8 [L][E][2]; mass: fp64 [L][E].  Errors: INVALID. */
+pw_status pw_plan_event(int L, int E, const uint8_t *q_cur, const double *mass, const uint8_t *skip, int lower,
+                        int n_change, int32_t *ids_out, uint8_t *q_out, int *n_out);
+
+/* Memory-target trigger (Core components 2: the planner runs when memory
+ * pressure, e.g. a growing KV cache, sets a new budget for the weights).
+ * Plans the routed blocks' widths with pw_plan_widths against byte_target,
+ * starting from each block's desired width d_i, and issues pw_request_widths
+ * (on `copy`) for every block whose planned width differs and that has no
+ * request in flight; the new widths are committed later by pw_commit_ready
+ * at a safe boundary.  mass, sens, params: as pw_plan_widths.
+ * *n_requested (may be NULL): blocks requested; *planned_bytes (may be NULL):
+ * the plan's routed bytes.  Errors: INVALID, STATE (a routed block not
+ * registered, or no host masters), OOM, HIP. */
+pw_status pw_retarget(pw_ctx *ctx, int64_t byte_target, const double *mass, const float *sens,
+                      const pw_plan_params *params, pw_stream copy, int *n_requested, int64_t *planned_bytes);
+
+/* Return device slabs that no block uses any more (planes dropped by
+ * lowered widths, replaced LUTs) to the device with hipFree.  Slabs whose
+ * last reader may still be running are kept until a later call.  Not for the
+ * hot path: hipFree may synchronise the device.  *freed_bytes (may be NULL)
+ * receives the bytes returned.  Errors: INVALID, HIP. */
+pw_status pw_trim(pw_ctx *ctx, int64_t *freed_bytes);
+
+/* Device-slab accounting: bytes held by committed widths (as
+ * pw_resident_bytes), bytes of free slabs kept for reuse, bytes of released
+ * slabs still waiting for their last reader, and HIP events created so far
+ * (events are recycled once no pending work refers to them).  Any output may
+ * be NULL. */
+pw_status pw_pool_stats(const pw_ctx *ctx, int64_t *resident, int64_t *cached, int64_t *waiting, int64_t *events);
+
 /* Host view of one block's committed width (0 if not registered). */
 pw_status pw_get_committed_bits(const pw_ctx *ctx, int32_t block_id, int32_t *q_out);
 
