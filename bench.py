@@ -348,6 +348,110 @@ def mixtral_decode_leg(steps, L=2):
     return out
 
 
+STACK_CFG = 4
+
+
+def stack_leg():
+    """The 24-layer Qwen-shaped decode stack (batch 4, 64 steps, a commit event
+    every 8 steps moving 20% of the routed blocks one bit, lowest routing mass
+    first; odd events lower, even events raise), one HIP graph per step of 24
+    pw_moe_layer calls.  Three runs from the same initial widths: no events,
+    the asynchronous events (pw_request_widths at the event, pw_commit_ready at
+    every step boundary) and the blocking events (pw_set_committed_bits before
+    the event's step).  Reports per-layer tokens/s of each run, the stall the
+    events add over the no-event run, the host-to-device bytes and rate of the
+    plane / LUT reloads (copy-stream events around each request), and the
+    overlap fraction 1 - stall / copy time of the asynchronous run.  For set-up
+    time the 24 layers share layer 0's codes and LUTs; each layer keeps its own
+    Zipf ranks, routed widths, logits and activations."""
+    import torch
+    import any_precision_expert_amd as pw
+    import pw_synth
+    from any_precision_expert_amd.stack import StackDriver
+    spec = pw_synth.CONFIGS[STACK_CFG]
+    shape, T, L, S = spec.shape, spec.tokens[0], spec.layers, spec.steps
+    seed = pw_synth.config_seed(STACK_CFG)
+    t0 = time.time()
+    w0 = pw_synth.make_weights(shape, seed, 0, spec.q_policy, spec.logits)
+    packed = {}
+    for e in range(shape.E):
+        packed[(e, 0)] = (pw.pack_bitplanes(w0.gate_up[e].code8), pw.concat_luts(w0.gate_up[e].luts))
+        packed[(e, 1)] = (pw.pack_bitplanes(w0.down[e].code8), pw.concat_luts(w0.down[e].luts))
+    shared = [(pw.pack_bitplanes(b.code8), pw.concat_luts(b.luts)) for b in (w0.shared_gate_up, w0.shared_down)]
+    ctx = pw.Context(0, L, shape.E, shape.H, shape.I, shape.top_k, shape.I_shared, keep_host_masters=True)
+    q0 = np.zeros((L, shape.E, 2), np.int64)
+    ranks = []
+    for l in range(L):
+        rank = pw_synth.zipf_rank(seed, l, shape.E)
+        q0[l] = pw_synth.draw_q(seed, l, shape.E, spec.q_policy, rank)
+        ranks.append(rank)
+        for (e, m), (planes, luts) in packed.items():
+            ctx.register_block(l, e, m, planes, luts, int(q0[l, e, m]))
+        for m in (0, 1):
+            ctx.register_block(l, pw.EXPERT_SHARED, m, shared[m][0], shared[m][1], 8)
+    logits = np.zeros((S, L, T, shape.E), np.float32)
+    x = np.zeros((S, L, T, shape.H), np.float16)
+    for s_ in range(S):
+        for l in range(L):
+            a = pw_synth.make_activations(shape, T, seed, l, s_, spec.logits, ranks[l])
+            logits[s_, l], x[s_, l] = a.logits, a.x
+    log("stack: set up %d layers in %.1fs, resident %.2f GB" % (L, time.time() - t0, ctx.resident_bytes() / 1e9))
+    ids_all = np.array([ctx.block_id(l, e, m) for l in range(L) for e in range(shape.E) for m in (0, 1)], np.int32)
+
+    def reset_widths():
+        torch.cuda.synchronize()
+        cur = ctx.committed_widths()[:, :shape.E, :].reshape(-1)
+        ctx.set_committed_bits(ids_all, q0.reshape(-1).astype(np.uint8))
+        torch.cuda.synchronize()
+        return int(np.sum(cur != q0.reshape(-1)))
+
+    out = {"workload": spec.name, "layers": L, "steps": S, "tokens_per_batch": T,
+           "events": "every %d steps, %d%% of routed blocks by one bit" % (spec.extra["commit_every"],
+                                                                          round(100 * spec.extra["commit_fraction"])),
+           "weights": "layer-0 codes and LUTs registered for every layer; per-layer Zipf ranks and widths"}
+    times = {}
+    for mode in ("none", "async", "blocking"):
+        reset_widths()
+        drv = StackDriver(ctx, q0, logits, x, commit_every=spec.extra["commit_every"],
+                          fraction=spec.extra["commit_fraction"], mode=mode)
+        drv.capture_graphs()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w_0 = time.perf_counter()
+        ev0.record(drv.compute)
+        drv.run()
+        ev1.record(drv.compute)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w_0
+        gpu_ms = ev0.elapsed_time(ev1)
+        total_s = max(wall, gpu_ms * 1e-3)
+        r = {"ms_total": round(total_s * 1e3, 3), "ms_per_step": round(total_s * 1e3 / S, 4),
+             "tokens_per_s_per_layer": round(T * S * L / total_s, 1), "gpu_stream_ms": round(gpu_ms, 3),
+             "events": [(e[0], "lower" if e[1] else "raise", e[2]) for e in drv.events]}
+        if mode == "async":
+            copy_ms = [a.elapsed_time(b) for (_, _, _, a, b) in drv.requests]
+            h2d = sum(req[2] for req in drv.requests)
+            r["commits"] = drv.commits
+            r["h2d_bytes"] = int(h2d)
+            r["copy_ms"] = round(sum(copy_ms), 3)
+            r["h2d_gbps"] = round(h2d / (sum(copy_ms) * 1e-3) / 1e9, 1) if sum(copy_ms) > 0 else None
+            drv.drain()
+        times[mode] = total_s
+        out[mode] = r
+        log("stack %s: %.3f ms total, %.4f ms/step" % (mode, total_s * 1e3, total_s * 1e3 / S))
+        del drv
+    base = times["none"]
+    for mode in ("async", "blocking"):
+        stall = times[mode] - base
+        out[mode]["stall_ms_total"] = round(stall * 1e3, 3)
+        out[mode]["stall_us_per_event"] = round(stall * 1e6 / max(1, len(out[mode]["events"])), 1)
+    cm = out["async"]["copy_ms"]
+    out["async"]["overlap_fraction"] = round(max(0.0, 1.0 - max(0.0, times["async"] - base) * 1e3 / cm), 3) if cm else None
+    reset_widths()
+    ctx.close()
+    return out
+
+
 BASELINE_TOKENS = (1, 4, 16)
 UNIFORM_WIDTHS = (4, 5, 8)
 
@@ -540,6 +644,8 @@ def main():
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the uniform-width and fp16-dense comparison at 1 / 4 / 16 tokens")
     ap.add_argument("--baseline-steps", type=int, default=160)
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 24-layer stack leg with asynchronous width commits")
     ap.add_argument("--model-config", default=None, metavar="JSON",
                     help="decode workload from a MoE model config (hidden_size, moe_intermediate_size, "
                          "num_experts, num_experts_per_tok, ...) instead of the Qwen1.5-MoE-A2.7B shape")
@@ -717,9 +823,15 @@ def main():
         return None if not us else round(nbytes / (us * 1e-6) / 1e9, 1)
     prefill = None if args.no_prefill else prefill_leg(args.prefill_steps)
     mixtral_decode = None if args.no_mixtral_decode else mixtral_decode_leg(args.mixtral_decode_steps)
+    stack = None
+    if not args.no_stack:
+        ctx.close()
+        ctx = None
+        stack = stack_leg()
     baselines = None
     if not args.no_baselines:
-        ctx.close()
+        if ctx is not None:
+            ctx.close()
         ctx = None
         baselines = baselines_leg(spec, seed, w, packed, args.baseline_steps, L)
 
@@ -765,6 +877,7 @@ def main():
         "prefill": prefill,
         "mixtral_decode": mixtral_decode,
         "baselines": baselines,
+        "stack": stack,
     }
     print(json.dumps(out), flush=True)
     if args.copy_calibration_mib > 0:

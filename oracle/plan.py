@@ -1,4 +1,4 @@
-"""Oracle of the width planner and the routing-mass accumulator.
+"""Oracle of the width planners and the routing-mass accumulator.
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py): plain Python loops over
 Python floats (IEEE fp64), written from the description of the
@@ -104,3 +104,27 @@ def plan_widths(L: int, E: int, H: int, I: int, q_cur, mass, sens, q_min: int, q
     for b, (l, e, m, _, _) in enumerate(blocks):
         out[l][e][m] = q[b]
     return out, total
+
+
+def plan_event(mass, q, lower: bool, n_change: int, skip=None):
+    """One commit event of the fixed-fraction schedule: every routed block
+    (layer l, expert e, module m) not skipped and not at the bound (q > 3 when
+    lowering, q < 8 when raising) is a candidate; candidates are taken in
+    order of their expert's routing mass, then of their block id
+    (l * (E + 1) + e) * 2 + m, and the first n_change move one bit.  Returns
+    (block ids, new widths) in that order."""
+    L = len(q)
+    E = len(q[0]) if L else 0
+    cands = []
+    for l in range(L):
+        for e in range(E):
+            for m in range(2):
+                if skip is not None and skip[l][e][m]:
+                    continue
+                qq = int(q[l][e][m])
+                if (lower and qq <= 3) or (not lower and qq >= 8):
+                    continue
+                cands.append((float(mass[l][e]), (l * (E + 1) + e) * 2 + m, qq))
+    cands.sort()
+    chosen = cands[:max(0, n_change)]
+    return [c[1] for c in chosen], [c[2] + (-1 if lower else 1) for c in chosen]

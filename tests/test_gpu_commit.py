@@ -206,8 +206,14 @@ def test_requested_widths_commit_only_after_their_copies_land():
             ctx.set_committed_bits(ids[:1], [4], compute, copy_stream)
         batches[0].step(0, compute)
         compute.synchronize()
-        assert copy_stream.query() is False  # the step did not wait for the moves
+        # the library adds no wait of the compute stream on the copy stream;
+        # whether the step finished while the copies were still held back also
+        # depends on the two streams landing on different hardware queues
+        # (4 per process), which the library does not control: logged only
+        say("copy stream still busy after the step: %s" % (not copy_stream.query()))
         compare(_fetch(batches[0]), oracle.moe_layer(w, a), label="old widths while moving")
+        assert all(ctx.block_state(i)[0] == q for i, q in zip(ids, [q0[e][m] for e in range(w.shape.E)
+                                                                    for m in (0, 1)]))
         copy_stream.synchronize()
         assert all(ctx.block_state(i)[2] == pw.PAGE_READY for i in ids)
         assert ctx.commit_ready(compute) == len(ids)
@@ -215,5 +221,36 @@ def test_requested_widths_commit_only_after_their_copies_land():
         batches[1].step(0, compute)
         pairs = list(zip(want[0::2], want[1::2]))
         compare(_fetch(batches[1]), oracle.moe_layer(_with_q(w, pairs), a), label="new widths after commit")
+    finally:
+        ctx.close()
+
+
+def test_copy_and_update_events_are_recycled():
+    """60 request / commit cycles on two blocks: the HIP events behind the
+    copies and the page-table updates are reused once nothing waits on them,
+    so the context creates a handful, not one or two per cycle; widths and
+    resident bytes follow the last commit."""
+    import torch
+    import any_precision_expert_amd as pw
+    from any_precision_expert_amd.layer import register_layer
+    w, a = _layer(seed=507)
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        ids = [ctx.block_id(0, 0, 0), ctx.block_id(0, 1, 1)]
+        compute, copy_stream = torch.cuda.Stream(), torch.cuda.Stream()
+        ctx.set_committed_bits(ids, [8, 3], compute, copy_stream)
+        torch.cuda.synchronize()
+        ev0 = ctx.pool_stats()["events"]
+        for i in range(60):
+            q = [4, 7] if i % 2 == 0 else [5, 6]  # always differs from the committed pair
+            ctx.request_widths(ids, q, copy_stream)
+            copy_stream.synchronize()
+            assert ctx.commit_ready(compute) == 2
+            compute.synchronize()
+            assert [ctx.committed_bits(b) for b in ids] == q
+        created = ctx.pool_stats()["events"] - ev0
+        say("events created over 60 cycles: %d" % created)
+        assert created <= 8
     finally:
         ctx.close()
