@@ -22,13 +22,14 @@ QMIN, QMAX = 3, 8
 MODULE_GATE_UP, MODULE_DOWN = 0, 1
 EXPERT_SHARED = -1
 MAX_TOKENS = 65536
+STATIC_SCRATCH_BYTES = 16 << 20
 LUT_HALVES_PER_ROW = sum(1 << k for k in range(QMIN, QMAX + 1))
 
 # every function declared in include/pw.h
 EXPORTS = (
     "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
     "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
-    "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_routing_mass_enable", "pw_routing_mass_reset",
+    "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_moe_layer_noalloc", "pw_routing_mass_enable", "pw_routing_mass_reset",
     "pw_routing_mass_read", "pw_plan_widths", "pw_request_widths", "pw_commit_ready", "pw_block_state",
     "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id", "pw_plane_states", "pw_committed_widths",
     "pw_routing_mass_copy", "pw_plan_event", "pw_retarget", "pw_trim", "pw_pool_stats",
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
         L.pw_route_permute.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
         L.pw_moe_ffn_bitplane.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pw_moe_layer.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pw_moe_layer_noalloc.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp]
         L.pw_request_widths.argtypes = [vp, ctypes.c_int, vp, vp, vp]
         L.pw_commit_ready.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int)]
         L.pw_block_state.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -266,6 +268,11 @@ class Context:
         _check(lib().pw_moe_layer(self.h, layer, _ptr(logits), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
                                   _ptr(offsets), _ptr(sorted_assign), _ptr(y), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
+
+    def moe_layer_noalloc(self, layer: int, logits, x, T: int, topk_idx, topk_w, offsets, sorted_assign, y,
+                          stream=None) -> None:
+        _check(lib().pw_moe_layer_noalloc(self.h, layer, _ptr(logits), _ptr(x), T, _ptr(topk_idx), _ptr(topk_w),
+                                          _ptr(offsets), _ptr(sorted_assign), _ptr(y), _stream(stream)))
 
     def request_widths(self, block_ids, q_desired, copy_stream=None) -> None:
         ids = np.ascontiguousarray(block_ids, dtype=np.int32)

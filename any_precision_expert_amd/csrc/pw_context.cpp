@@ -280,6 +280,7 @@ struct pw_ctx {
     };
     std::vector<Staging> staging;
     int num_cus = 256;  // compute units of the device (decode tile schedule)
+    void* scratch = nullptr;  // this device's library-held workspace (pw_moe_layer_noalloc)
     std::map<int, WidthChange> pending;  // width requests whose commit has not happened
     double* d_mass = nullptr;  // routing-mass accumulator [L][E] fp64 (pw_routing_mass_enable)
     bool mass_on = false;
@@ -455,6 +456,13 @@ pw_status pw_create(pw_ctx** out, int hip_device, const pw_model_desc* d)
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess && cus > 0)
         c->num_cus = cus;
+    // device address of the library-held workspace, with this device current
+    e = static_scratch(hip_device, &c->scratch);
+    if (e != hipSuccess) {
+        (void)hipFree(c->d_table);
+        delete c;
+        return hip_fail(e, "pw_create: static scratch address");
+    }
     *out = c;
     return ok();
 }
@@ -798,6 +806,18 @@ pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t
     }
     const LayerRoute r{logits, idx, w, offsets, sorted, mass};
     return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, &r);
+}
+
+pw_status pw_moe_layer_noalloc(pw_ctx* c, int layer, const float* logits, const uint16_t* x, int T, int32_t* idx,
+                               float* w, int32_t* offsets, int32_t* sorted, uint16_t* y, pw_stream stream)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: null context");
+    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: T=%d out of range", T);
+    const size_t need = pw_workspace_size(c, T);
+    if (need > kStaticScratchBytes)
+        return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: T=%d needs %zu B of workspace, above the %zu B the library "
+                    "holds; use pw_moe_layer with a caller workspace", T, need, kStaticScratchBytes);
+    return pw_moe_layer(c, layer, logits, x, T, idx, w, offsets, sorted, y, c->scratch, kStaticScratchBytes, stream);
 }
 
 pw_status pw_routing_mass_enable(pw_ctx* c, int on)

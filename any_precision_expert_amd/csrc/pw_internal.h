@@ -140,6 +140,13 @@ hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s);
 hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int path, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s);
 
+// Library-held workspace of pw_moe_layer_noalloc (pw_kernels.hip): its size,
+// and its device address on `device`, looked up once per device (call with
+// that device current).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(int device, void** out);
+
 // Host packer (pw_pack.cpp).
 void pack_bitplanes(const uint8_t* codes, int64_t R, int64_t K, uint32_t* planes);
 int64_t plane_words(int64_t R, int64_t K);

@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pw_internal.h"
@@ -1835,6 +1836,31 @@ __global__ void __launch_bounds__(PATH == 2 ? kPfThreads : kThreads)
         default: break;
     }
 #undef PW_DEBUG_CASE
+}
+
+// ---------------------------------------------------------------- static scratch
+//
+// Workspace of the allocation-free layer entry point: file-scope device
+// memory, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (in host code it is a stand-in, not a
+// device address): static_scratch() looks up each device's address once,
+// with that device current, and every later use goes through it.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(int device, void** out)
+{
+    static std::mutex mu;
+    static void* ptrs[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptrs[device] = p;
+    }
+    *out = ptrs[device];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------- launchers

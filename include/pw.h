@@ -195,6 +195,22 @@ pw_status pw_moe_layer(pw_ctx *ctx, int layer, const float *logits, const uint16
                        int32_t *sorted_assign, uint16_t *y, void *workspace, size_t ws_bytes,
                        pw_stream stream);
 
+/* Allocation-free form of pw_moe_layer, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same work and outputs, with the workspace taken from a
+ * device buffer the library holds for each GPU (PW_STATIC_SCRATCH_BYTES,
+ * 16 MiB, kept until the process ends) instead of from the caller.  It
+ * enqueues no allocation and no free.  T with pw_workspace_size(ctx, T)
+ * above PW_STATIC_SCRATCH_BYTES is refused with INVALID (the decode sizes fit:
+ * e.g. 64 tokens of a 4096 x 14336 top-2 layer need 12.1 MB).  Every call on
+ * one GPU uses the same buffer, whatever the context or stream: calls that
+ * overlap on a GPU race, so the caller serialises them (one stream, or an
+ * event between streams).  Errors: as pw_moe_layer. */
+#define PW_STATIC_SCRATCH_BYTES (16u << 20)
+pw_status pw_moe_layer_noalloc(pw_ctx *ctx, int layer, const float *logits, const uint16_t *x, int T,
+                               int32_t *topk_idx, float *topk_w, int32_t *expert_offsets, int32_t *sorted_assign,
+                               uint16_t *y, pw_stream stream);
+
 /* Routing-mass accumulator (Core components 2: online routing statistics,
  * the routing mass of an expert = how often and how strongly it is chosen).
  * pw_routing_mass_enable(ctx, 1) allocates a device array mass [L][E] fp64,
