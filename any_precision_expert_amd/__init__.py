@@ -40,7 +40,7 @@ EXPORTS = (
 
 PAGE_RESIDENT, PAGE_IN_TRANSFER, PAGE_READY = 0, 1, 2
 PLANE_GPU, PLANE_IN_TRANSFER, PLANE_READY, PLANE_CPU, PLANE_ABSENT = 0, 1, 2, 3, 4
-DECODE_PATH_TILE128, DECODE_PATH_TILE64, DECODE_PATH_PREFILL = 0, 1, 2
+DECODE_PATH_TILE128, DECODE_PATH_TILE64, DECODE_PATH_PREFILL, DECODE_PATH_TILE64_WIDE = 0, 1, 2, 3
 
 
 class PlanParams(ctypes.Structure):

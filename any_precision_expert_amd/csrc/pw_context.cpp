@@ -236,6 +236,9 @@ struct HostBlock {
     void* dlut = nullptr;
     uint32_t* hplanes = nullptr;  // pinned master: 8 planes
     uint32_t* hluts = nullptr;    // pinned master: LUT_3..LUT_8, each in the device slot layout
+    // the masters' device-side addresses (read by the copy kernel), or null
+    const uint32_t* dv_hplanes = nullptr;
+    const uint32_t* dv_hluts = nullptr;
 };
 
 // A width change of one block: its new slabs (planes q_old..q_new-1 and
@@ -272,10 +275,13 @@ struct pw_ctx {
     std::vector<HostBlock> blocks;
     EventPool evs;  // declared before the slab pool, which holds references on its events
     SlabPool pool{&evs};
-    // pinned staging for page-table updates, recycled after their event
+    // pinned staging (copy lists, page-table entries) read by kernels through
+    // its device-side address, reused once the event behind its last reader
+    // has completed
     struct Staging {
-        BlockDesc* p;
-        size_t n;
+        void* p;
+        void* dp;
+        size_t bytes;
         hipEvent_t ev;
     };
     std::vector<Staging> staging;
@@ -299,6 +305,34 @@ hipError_t new_event(pw_ctx* c, hipEvent_t* ev)
     if (e == hipSuccess) c->evs.hold(*ev);
     return e;
 }
+
+// A free pinned staging buffer of at least `bytes` (one whose event has
+// completed), or a new one.  The caller records st.ev behind the work that
+// reads it and hands it back with put_staging.
+pw_status take_staging(pw_ctx* c, size_t bytes, pw_ctx::Staging& st)
+{
+    for (size_t i = 0; i < c->staging.size(); ++i) {
+        if (c->staging[i].bytes >= bytes && hipEventQuery(c->staging[i].ev) == hipSuccess) {
+            st = c->staging[i];
+            c->staging.erase(c->staging.begin() + i);
+            return PW_OK;
+        }
+    }
+    st = pw_ctx::Staging{nullptr, nullptr, (bytes + 4095) & ~size_t(4095), nullptr};
+    if (hipHostMalloc(&st.p, st.bytes, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PW_ERR_OOM, "pinned staging of %zu B", st.bytes);
+    }
+    hipError_t e = hipHostGetDevicePointer(&st.dp, st.p, 0);
+    if (e == hipSuccess) e = new_event(c, &st.ev);
+    if (e != hipSuccess) {
+        (void)hipHostFree(st.p);
+        return hip_fail(e, "pinned staging");
+    }
+    return PW_OK;
+}
+
+void put_staging(pw_ctx* c, const pw_ctx::Staging& st) { c->staging.push_back(st); }
 
 int block_id(const pw_ctx* c, int layer, int expert, int module)
 {
@@ -359,6 +393,8 @@ void free_block_now(pw_ctx* c, HostBlock& b)
     if (b.hluts) (void)hipHostFree(b.hluts);
     b.hplanes = nullptr;
     b.hluts = nullptr;
+    b.dv_hplanes = nullptr;
+    b.dv_hluts = nullptr;
     b.registered = false;
 }
 
@@ -534,6 +570,13 @@ pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const 
             undo();
             return fail(PW_ERR_OOM, "pw_register_block: pinned host master");
         }
+        void *dvp = nullptr, *dvl = nullptr;
+        if (hipHostGetDevicePointer(&dvp, nb.hplanes, 0) == hipSuccess &&
+            hipHostGetDevicePointer(&dvl, nb.hluts, 0) == hipSuccess) {
+            nb.dv_hplanes = (const uint32_t*)dvp;
+            nb.dv_hluts = (const uint32_t*)dvl;
+        }
+        (void)hipGetLastError();
         std::memcpy(nb.hplanes, host_planes, plane_b * 8);
         for (int q = PW_QMIN; q <= PW_QMAX; ++q)
             convert_lut(host_luts, R, module, q, nb.hluts + lut_offset_words(nb.S, q));
@@ -696,7 +739,8 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     a.E = E;
     a.k = d.top_k;
     a.n_slots = std::min(E, T * d.top_k);
-    a.keep_planes = (int64_t)T * d.top_k >= (int64_t)kKeepPlanesPerExpert * E ? 1 : 0;
+    a.tok_pass = decode_tok_pass(T, d.top_k, E, d.inter_shared);
+    a.keep_planes = (int64_t)T * d.top_k >= (int64_t)kKeepPlanesPasses * a.tok_pass * E ? 1 : 0;
     a.hstride = std::max(d.inter, d.inter_shared);
     a.drows = T * d.top_k + (d.inter_shared ? T : 0);
     hipStream_t s = (hipStream_t)stream;
@@ -728,7 +772,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     }
     {
         ProfScope ps(c, "gate_up", s);
-        a.rg = kGateUpRowGroups;
+        a.rg = a.tok_pass == 16 ? 2 : kGateUpRowGroups;
         a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         a.tiles_routed = (d.inter + 16 * a.rg - 1) / (16 * a.rg);
         a.tiles_shared = (d.inter_shared + 16 * a.rg - 1) / (16 * a.rg);
@@ -794,7 +838,8 @@ pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t
     const long long gu_units = (d.inter_shared + gu_rows - 1) / gu_rows +
                                std::min<long long>(d.num_experts, n) * ((d.inter + gu_rows - 1) / gu_rows);
     double* mass = c->mass_on ? c->d_mass + (size_t)layer * d.num_experts : nullptr;
-    if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus) {
+    if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus ||
+        decode_tok_pass(T, d.top_k, d.num_experts, d.inter_shared) != 8) {
         // the separate routing launch, then the FFN (identical results)
         st = pw_route_permute(c, logits, T, idx, w, offsets, sorted, stream);
         if (st != PW_OK || T == 0) return st;
@@ -921,14 +966,44 @@ static pw_status prepare_changes(pw_ctx* c, const char* fn, const std::vector<st
             return fail(PW_ERR_OOM, "%s: device LUT: %s", fn, hipGetErrorString(e));
         }
     }
-    for (auto& p : plans) {
+    // the copies: one kernel over a copy list in pinned staging when every
+    // master has a device-side address, else one hipMemcpyAsync per plane / LUT
+    bool by_kernel = true;
+    size_t ncopy = 0;
+    for (const auto& p : plans) {
         const HostBlock& b = c->blocks[p.id];
-        for (int j = p.qo; j < p.qn && e == hipSuccess; ++j)
-            e = hipMemcpyAsync(p.planes[j], b.hplanes + (size_t)j * b.pw, (size_t)b.pw * 4, hipMemcpyHostToDevice, xs);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(p.lut, b.hluts + lut_offset_words(b.S, p.qn), lut_bytes(b.S, p.qn),
-                               hipMemcpyHostToDevice, xs);
-        if (e != hipSuccess) break;
+        by_kernel = by_kernel && b.dv_hplanes && b.dv_hluts;
+        ncopy += (size_t)std::max(0, p.qn - p.qo) + 1;
+    }
+    pw_ctx::Staging st{};
+    if (by_kernel) {
+        const pw_status sst = take_staging(c, ncopy * sizeof(CopyDesc), st);
+        if (sst != PW_OK) {
+            release_prepared(c, plans);
+            return sst;
+        }
+        CopyDesc* list = (CopyDesc*)st.p;
+        size_t n = 0;
+        for (const auto& p : plans) {
+            const HostBlock& b = c->blocks[p.id];
+            for (int j = p.qo; j < p.qn; ++j)
+                list[n++] = CopyDesc{b.dv_hplanes + (size_t)j * b.pw, p.planes[j], (uint64_t)b.pw * 4};
+            list[n++] = CopyDesc{b.dv_hluts + lut_offset_words(b.S, p.qn), p.lut, (uint64_t)lut_bytes(b.S, p.qn)};
+        }
+        e = launch_pull_copy((const CopyDesc*)st.dp, (int)n, xs);
+        if (e == hipSuccess) e = hipEventRecord(st.ev, xs);
+        put_staging(c, st);
+    } else {
+        for (auto& p : plans) {
+            const HostBlock& b = c->blocks[p.id];
+            for (int j = p.qo; j < p.qn && e == hipSuccess; ++j)
+                e = hipMemcpyAsync(p.planes[j], b.hplanes + (size_t)j * b.pw, (size_t)b.pw * 4, hipMemcpyHostToDevice,
+                                   xs);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(p.lut, b.hluts + lut_offset_words(b.S, p.qn), lut_bytes(b.S, p.qn),
+                                   hipMemcpyHostToDevice, xs);
+            if (e != hipSuccess) break;
+        }
     }
     hipEvent_t copied = nullptr;
     if (e == hipSuccess) e = new_event(c, &copied);
@@ -952,28 +1027,18 @@ static pw_status prepare_changes(pw_ctx* c, const char* fn, const std::vector<st
 static pw_status apply_changes(pw_ctx* c, std::vector<WidthChange>& plans, hipStream_t cs)
 {
     hipError_t e = hipSuccess;
-    // pinned staging for the page-table entries
-    pw_ctx::Staging st{nullptr, plans.size(), nullptr};
-    for (size_t i = 0; i < c->staging.size(); ++i) {
-        if (c->staging[i].n >= plans.size() && hipEventQuery(c->staging[i].ev) == hipSuccess) {
-            st = c->staging[i];
-            c->staging.erase(c->staging.begin() + i);
-            break;
-        }
+    // the new entries and their ids in pinned staging, scattered into the
+    // device table by one kernel on the compute stream
+    const size_t n = plans.size();
+    pw_ctx::Staging st{};
+    {
+        const pw_status sst = take_staging(c, n * (sizeof(BlockDesc) + sizeof(int32_t)), st);
+        if (sst != PW_OK) return sst;
     }
-    if (!st.p) {
-        if (hipHostMalloc((void**)&st.p, sizeof(BlockDesc) * plans.size(), hipHostMallocDefault) != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(PW_ERR_OOM, "pinned staging");
-        }
-        st.n = plans.size();
-        if ((e = new_event(c, &st.ev)) != hipSuccess) {
-            (void)hipHostFree(st.p);
-            return hip_fail(e, "hipEventCreate");
-        }
-    }
-    std::vector<BlockDesc> newdesc(plans.size());
-    for (size_t i = 0; i < plans.size(); ++i) {
+    BlockDesc* descs = (BlockDesc*)st.p;
+    int32_t* sids = (int32_t*)(descs + n);
+    std::vector<BlockDesc> newdesc(n);
+    for (size_t i = 0; i < n; ++i) {
         HostBlock nb = c->blocks[plans[i].id];
         for (int j = 0; j < 8; ++j)
             if (j >= plans[i].qo && j < plans[i].qn) nb.dplanes[j] = plans[i].planes[j];
@@ -981,10 +1046,10 @@ static pw_status apply_changes(pw_ctx* c, std::vector<WidthChange>& plans, hipSt
         nb.q = plans[i].qn;
         nb.dlut = plans[i].lut;
         newdesc[i] = make_desc(nb);
-        st.p[i] = newdesc[i];
+        descs[i] = newdesc[i];
+        sids[i] = plans[i].id;
     }
-    for (size_t i = 0; i < plans.size() && e == hipSuccess; ++i)
-        e = hipMemcpyAsync(c->d_table + plans[i].id, st.p + i, sizeof(BlockDesc), hipMemcpyHostToDevice, cs);
+    e = launch_scatter_desc(c->d_table, (const int32_t*)((BlockDesc*)st.dp + n), (const BlockDesc*)st.dp, (int)n, cs);
     hipEvent_t updated = nullptr;
     if (e == hipSuccess) e = new_event(c, &updated);
     if (e == hipSuccess) e = hipEventRecord(updated, cs);
@@ -993,11 +1058,11 @@ static pw_status apply_changes(pw_ctx* c, std::vector<WidthChange>& plans, hipSt
         (void)hipStreamSynchronize(cs);
         // the device table may hold some new entries: restore the old ones
         for (auto& p : plans) (void)hipMemcpy(c->d_table + p.id, &c->h_table[p.id], sizeof(BlockDesc), hipMemcpyHostToDevice);
-        c->staging.push_back(st);
+        put_staging(c, st);
         if (updated) c->evs.drop(updated);
         return hip_fail(e, "page-table update");
     }
-    c->staging.push_back(st);
+    put_staging(c, st);
     // commit on the host; old slabs are recycled after `updated`
     for (size_t i = 0; i < plans.size(); ++i) {
         HostBlock& b = c->blocks[plans[i].id];
@@ -1231,8 +1296,8 @@ pw_status pw_debug_decode(pw_ctx* c, int32_t id, int path, uint8_t* codes_out, u
     if (!c || (!codes_out && !w_out)) return fail(PW_ERR_INVALID, "pw_debug_decode: null pointer");
     if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
         return fail(PW_ERR_INVALID, "pw_debug_decode: block id %d not registered", id);
-    if (path < PW_DECODE_PATH_TILE128 || path > PW_DECODE_PATH_PREFILL)
-        return fail(PW_ERR_INVALID, "pw_debug_decode: path %d not in 0..2", path);
+    if (path < PW_DECODE_PATH_TILE128 || path > PW_DECODE_PATH_TILE64_WIDE)
+        return fail(PW_ERR_INVALID, "pw_debug_decode: path %d not in 0..3", path);
     hipError_t e = hipSetDevice(c->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
     e = launch_debug_decode(c->d_table + id, id & 1, c->blocks[id].R, path, codes_out, w_out, (hipStream_t)stream);

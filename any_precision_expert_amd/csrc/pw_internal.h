@@ -50,6 +50,7 @@ struct FfnArgs {
     int32_t rg;               // 32-row groups per workgroup tile: 2 or 4
     int32_t big_wgs;          // rg 4: workgroups taking whole tiles before tiles split in halves (0: all whole)
     int32_t keep_planes;      // decode: ordinary (not nontemporal) plane loads, set when tiles take several passes
+    int32_t tok_pass;         // decode: tokens per pass, 8 or 16 (16: 64-row tiles only, routing outside)
     // prefill launches: token tiles of the shared block, and an upper bound
     // on the routed token tiles (sum over experts of ceil(tokens / 512))
     int32_t tok_tiles_shared;
@@ -71,10 +72,18 @@ struct FfnArgs {
 constexpr int kLayerRouteMaxAssign = 64;
 
 // Decode launches load planes with ordinary loads (which the MALL keeps)
-// instead of nontemporal ones once the batch averages this many assignments
-// per expert: nearly every tile then takes two or more 8-token passes and
-// re-reads its planes.  Below it, nontemporal loads are faster (one pass).
-constexpr int kKeepPlanesPerExpert = 16;
+// instead of nontemporal ones once the batch averages two passes per expert:
+// nearly every tile then re-reads its planes.  Below it, nontemporal loads
+// are faster (one pass).
+constexpr int kKeepPlanesPasses = 2;
+
+// Tokens per decode pass: 16 (each weight decoded once per 16 tokens, 64-row
+// tiles) when some work unit surely holds more than 8 tokens -- the shared
+// expert with T > 8, or routed experts averaging more than 8 -- else 8.
+inline int decode_tok_pass(int T, int k, int E, int I_shared)
+{
+    return T > 8 && (I_shared > 0 || (long long)T * k > 8LL * E) ? 16 : 8;
+}
 
 // Tokens per call from which the prefill GEMM path runs.
 constexpr int kPrefillMinT = 256;
@@ -136,9 +145,22 @@ hipError_t launch_routing_mass(const int32_t* offsets, const int32_t* sorted, co
 hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s);
 // Decode of one block as an FFN path runs it (path: 0 decode contraction
 // with 128-row gate_up / down tiles (RG = 4), 1 with 64-row tiles (RG = 2),
-// 2 prefill decoder); codes_out uint8 [R][K] and / or w_out fp16 [R][K].
+// 2 prefill decoder, 3 64-row tiles of 16-token passes); codes_out uint8
+// [R][K] and / or w_out fp16 [R][K].
 hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int path, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s);
+
+// One host-to-device copy of a width change (device-side addresses; src in
+// pinned host memory, bytes a multiple of 16).
+struct CopyDesc {
+    const void* src;
+    void* dst;
+    uint64_t bytes;
+};
+// The copies of list[0..n) (the list itself in pinned host memory), one launch.
+hipError_t launch_pull_copy(const CopyDesc* list, int n, hipStream_t s);
+// table[ids[i]] = descs[i] for i < n (ids and descs in pinned host memory).
+hipError_t launch_scatter_desc(BlockDesc* table, const int32_t* ids, const BlockDesc* descs, int n, hipStream_t s);
 
 // Library-held workspace of pw_moe_layer_noalloc (pw_kernels.hip): its size,
 // and its device address on `device`, looked up once per device (call with

@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -267,10 +268,12 @@ __device__ __forceinline__ StepCodes step_codes_lane(const Rot<Q, PAIR>& r, uint
 // use: issue() starts every load of the wave, commit() writes LDS (pair
 // tables: with a barrier between staging and building; the caller's barrier
 // follows).
-template <int Q, int RG, int NT = kThreads>
+template <int Q, int RG, int NT = kThreads, bool WIDE = false>
 struct LutLoad {
     static constexpr int NSLOT = 16 * RG;
-    static constexpr bool PAIR = RG == 2 ? Q <= 4 : Q <= 3;
+    // WIDE (16-token passes): no q = 4 pair table for 64-row tiles, whose 64 KB
+    // would leave no room for the wider activation slices
+    static constexpr bool PAIR = RG == 2 ? Q <= (WIDE ? 3 : 4) : Q <= 3;
     static constexpr int NC = 1 << Q;
     static constexpr int PPE = NSLOT / 4;         // 16-byte pieces per entry
     static constexpr int BLOCKS = NC * PPE / 64;  // 64-piece blocks, one per wave load
@@ -327,10 +330,10 @@ struct LutLoad {
 // LDS byte offset of a look-up for the row held in half `h` of tile slot
 // `sl` (pair tables: RG = 2 uses pair slot 32 h + sl, RG = 4 the slot with h
 // carried in the code byte).
-template <int Q, int RG>
+template <int Q, int RG, bool WIDE = false>
 __device__ __forceinline__ uint32_t lut_lane_off(int sl, int h)
 {
-    if constexpr (LutLoad<Q, RG>::PAIR) return (uint32_t)(RG == 2 ? 32 * h + sl : sl) * 4u;
+    if constexpr (LutLoad<Q, RG, kThreads, WIDE>::PAIR) return (uint32_t)(RG == 2 ? 32 * h + sl : sl) * 4u;
     return (uint32_t)sl * 4u + 2u * (uint32_t)h;
 }
 
@@ -348,7 +351,7 @@ struct TileLane {
     bool set1;          // two-set pair tables: the row's table is the second set
 };
 
-template <int MODE, int Q, int RG>
+template <int MODE, int Q, int RG, bool WIDE = false>
 __device__ __forceinline__ TileLane tile_lane(int tile, int grp, int rho, int R)
 {
     TileLane t;
@@ -365,8 +368,8 @@ __device__ __forceinline__ TileLane tile_lane(int tile, int grp, int rho, int R)
     t.lrow = t.valid ? t.row : 0;
     const int half = (MODE == 0 && RG == 4) ? grp / 2 : grp % 2;
     const int lslot = (MODE == 0 && RG == 4) ? 32 * (grp % 2) + rho : (RG == 4 ? 32 * (grp / 2) + rho : rho);
-    t.lane_off = lut_lane_off<Q, RG>(lslot, half);
-    t.set1 = LutLoad<Q, RG>::PAIR && RG == 4 && half;
+    t.lane_off = lut_lane_off<Q, RG, WIDE>(lslot, half);
+    t.set1 = LutLoad<Q, RG, kThreads, WIDE>::PAIR && RG == 4 && half;
     return t;
 }
 
@@ -378,9 +381,9 @@ __device__ __forceinline__ TileLane tile_lane(int tile, int grp, int rho, int R)
 // two-set table seeded above the 2q-bit pair code).  `zero` must be a zero the
 // compiler cannot see through: with a literal zero it splits the bit-selects
 // of the transpose's rows q..7 into more, cheaper ops.
-template <int Q, int RG>
+template <int Q, int RG, bool WIDE = false>
 struct WordDecoder {
-    static constexpr bool PAIR = LutLoad<Q, RG>::PAIR;
+    static constexpr bool PAIR = LutLoad<Q, RG, kThreads, WIDE>::PAIR;
     static constexpr bool TRANSPOSE = Q >= 5 && !PAIR;
     RepMasks masks;
     uint32_t zero;
@@ -778,15 +781,18 @@ __device__ __forceinline__ int slice_unit(int j, int t, int g)
 
 // FUSED (gate_up of a launch that routed the batch itself): lane i of tokreg
 // holds the slot's i-th sorted assignment instead of a.sorted in memory.
-template <int MODE, int Q, int RG, bool FUSED = false, bool KEEP = false>
+template <int MODE, int Q, int RG, bool FUSED = false, bool KEEP = false, int TP = 8>
 __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
                                            int ntok, int tile, int split, int nsplit, uint32_t* lds, int tokreg = 0)
 {
+    // TP tokens per pass: 8, or 16 (WIDE) for launches where experts hold more
+    // than 8 tokens, so each weight is decoded once per 16 tokens
+    constexpr bool WIDE = TP == 16;
+    static_assert(TP == 8 || (WIDE && RG == 2 && !FUSED), "16-token passes: 64-row tiles, routing outside");
     constexpr int D = Q <= 4 ? 2 : 1;      // chunks of plane loads in flight
-    constexpr int NPART = 2;               // activation loads per lane and chunk
-    constexpr int TP = 8;                  // tokens per pass
+    constexpr int NPART = TP / 4;          // activation loads per lane and chunk
     constexpr int KW = kWaves / RG;        // waves per row group (K split)
-    constexpr bool PAIR = LutLoad<Q, RG>::PAIR;
+    constexpr bool PAIR = LutLoad<Q, RG, kThreads, WIDE>::PAIR;
     constexpr int HR = 16 * RG;            // gate_up: h rows per tile (gate and up rows each)
     constexpr int TR = 32 * RG;            // down: output rows per tile
     const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
@@ -796,7 +802,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     const int nchunks = bd->nchunks, kwords = bd->kwords;
     const int K = kwords * 32;
     const int Iblk = R >> 1;
-    const TileLane tl = tile_lane<MODE, Q, RG>(tile, grp, rho, R);
+    const TileLane tl = tile_lane<MODE, Q, RG, WIDE>(tile, grp, rho, R);
     const int lrow = tl.lrow;  // in-range load row
     const int cps = (nchunks + nsplit - 1) / nsplit;
     const int c_begin = split * cps;
@@ -806,11 +812,21 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     const int lastc = nch > 0 ? first + (nch - 1) * KW : 0;  // chunk 0 always exists
     const int TK = a.T * a.k;
 
-    uint32_t* slice = lds + kLutBytes / 4 + wave * kSliceWords;
-    u32x4* slice4 = (u32x4*)slice;
+    // byte b of wave w's activation slice (TP token rows x 16 units of 16 B).
+    // 8-token passes: 2 KB per wave after the LUT.  16-token passes (64-row
+    // tiles): 4 KB per wave inside the 64 KB LUT area, in space the tile's
+    // table never uses: the upper half of every 256-byte entry row at q = 8
+    // (a 64-row tile fills slots 0..31), else rows 128..255 (2^q <= 128 single
+    // entries, or 64 rows of the q = 3 pair table).
+    char* const ldsb = (char*)lds;
+    auto slice_at = [&](int w, int b) -> char* {
+        if constexpr (!WIDE) return ldsb + kLutBytes + w * (kSliceWords * 4) + b;
+        else if constexpr (Q == 8) return ldsb + ((((32 * w + (b >> 7)) << 8) | 128) | (b & 127));
+        else return ldsb + 32768 + w * 4096 + b;
+    };
     const uint32_t lane_off = tl.lane_off;
     const char* lutb = (const char*)lds;
-    WordDecoder<Q, RG> dec;
+    WordDecoder<Q, RG, WIDE> dec;
     dec.masks = make_masks();
     // a zero the compiler cannot prove (T >= 1 here)
     dec.zero = (uint32_t)__builtin_amdgcn_readfirstlane(a.T >> 30);
@@ -824,16 +840,16 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     const uint16_t* xsrc[NPART];
     int nt = 0;
 
-    // Activation rows of the pass starting at t0: tokens xt and xt + 4 (x for
+    // Activation rows of the pass starting at t0: tokens xt + 4 pp (x for
     // gate_up, h for down; tokens past the pass repeat its last token, whose
     // slots are never read).
     auto set_sources = [&](int t0) {
         nt = min(TP, ntok - t0);
         if (MODE == 0) {
-            int tok[2];
+            int tok[NPART];
             if (shared) {
-                tok[0] = t0 + min(xt, nt - 1);
-                tok[1] = t0 + min(xt + 4, nt - 1);
+#pragma unroll
+                for (int pp = 0; pp < NPART; ++pp) tok[pp] = t0 + min(xt + 4 * pp, nt - 1);
             } else {
                 int sa[TP];
                 if constexpr (FUSED) {
@@ -847,7 +863,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                     for (int j = 0; j < TP; ++j) sa[j] = srt[base + min(j, nt - 1)];
                 }
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < NPART; ++h) {
                     const int te = xt + 4 * h;
                     int v = sa[0];
 #pragma unroll
@@ -855,11 +871,11 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                     tok[h] = v / a.k;
                 }
             }
-            xsrc[0] = a.x + (size_t)tok[0] * a.H;
-            xsrc[1] = a.x + (size_t)tok[1] * a.H;
+#pragma unroll
+            for (int pp = 0; pp < NPART; ++pp) xsrc[pp] = a.x + (size_t)tok[pp] * a.H;
         } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < NPART; ++h) {
                 const int te = min(xt + 4 * h, nt - 1);
                 const int hrow = shared ? TK + t0 + te : p0 + t0 + te;
                 xsrc[h] = a.h + (size_t)hrow * a.hstride;
@@ -880,8 +896,8 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
 
     // pass 0: LUT loads first, then the ring's first loads, then LUT -> LDS
     {
-        LutLoad<Q, RG> ls;
-        ls.issue(bd->lut, bd->slots, tile * LutLoad<Q, RG>::NSLOT, lane, wave);
+        LutLoad<Q, RG, kThreads, WIDE> ls;
+        ls.issue(bd->lut, bd->slots, tile * LutLoad<Q, RG, kThreads, WIDE>::NSLOT, lane, wave);
         set_sources(0);
         if (ntok > 0) issue_ring();
         ls.commit(lds, lds + kLutBytes / 4, lane, wave);
@@ -911,7 +927,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 const bool ok = live && c * kChunkCols + 8 * xg < K;
 #pragma unroll
                 for (int pp = 0; pp < NPART; ++pp)
-                    slice4[slice_unit(4 * pp + xt, 4 * pp + xt, xg)] = ok ? xv[pp] : u32x4{0, 0, 0, 0};
+                    *(u32x4*)slice_at(wave, 16 * slice_unit(4 * pp + xt, 4 * pp + xt, xg)) = ok ? xv[pp] : u32x4{0, 0, 0, 0};
                 // prefetch: next chunk's activations, then the planes D chunks on
                 u32x2 cur[Q];
 #pragma unroll
@@ -931,8 +947,9 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                     dec.prepare(W);
                 };
                 auto codes = [&](int P) { return dec.codes(P); };
+                auto b_read = [&](int s) { return *(const u32x4*)slice_at(wave, 16 * b_unit(s, te)); };
                 prepare(0);
-                u32x4 bh = slice4[b_unit(0, te)];
+                u32x4 bh = b_read(0);
                 StepRaw raw;
                 step_lookup<PAIR>(codes(0), lane_off, lutb, raw);
 #pragma unroll
@@ -946,21 +963,22 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                         next = codes(0);
                     }
                     if (s < 7) {
-                        bh = slice4[b_unit(s + 1, te)];
+                        bh = b_read(s + 1);
                         step_lookup<PAIR>(next, lane_off, lutb, raw);
                     }
                 }
             }
         }
 
-        // cross-wave reduction through the slice region
+        // cross-wave reduction through the slices: wave w's partial of (row r,
+        // token n) at byte 4 (r TP + n) of its slice
         __syncthreads();
-        float* red = (float*)(lds + kLutBytes / 4);  // [wave][row 32][token TP]
+        auto red = [&](int w, int r, int n) -> float* { return (float*)slice_at(w, 4 * (r * TP + n)); };
         if (nvalid) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = 8 * (i >> 2) + 4 * kh + (i & 3);
-                red[(wave * 32 + r) * TP + rho] = C[i];
+                *red(wave, r, rho) = C[i];
             }
         }
         __syncthreads();
@@ -971,8 +989,8 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 float g = 0.0f, u = 0.0f;
 #pragma unroll
                 for (int w = 0; w < KW; ++w) {
-                    g += red[((sub * KW + w) * 32 + r) * TP + n];
-                    u += red[(((RG / 2 + sub) * KW + w) * 32 + r) * TP + n];
+                    g += *red(sub * KW + w, r, n);
+                    u += *red((RG / 2 + sub) * KW + w, r, n);
                 }
                 const int i = tile * HR + hr;
                 if (i < Iblk) {
@@ -987,7 +1005,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 const int g = rt >> 5, r = rt & 31;
                 float d = 0.0f;
 #pragma unroll
-                for (int w = 0; w < KW; ++w) d += red[((g * KW + w) * 32 + r) * TP + n];
+                for (int w = 0; w < KW; ++w) d += *red(g * KW + w, r, n);
                 const int orow_r = tile * TR + rt;
                 if (orow_r < R) {
                     const int orow = shared ? TK + t0 + n : a.sorted[p0 + t0 + n];
@@ -1173,7 +1191,7 @@ __device__ __forceinline__ float combine_value(const FfnArgs& a, int t, int o, i
 // FUSED (gate_up only): the launch routes the batch itself (a.logits); the
 // workgroup of the first routed unit writes the routing results for the caller
 // and for the down and combine launches.
-template <int MODE, int RG, bool FUSED = false, bool KEEP = false>
+template <int MODE, int RG, bool FUSED = false, bool KEEP = false, int TP = 8>
 __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 {
     __shared__ __align__(16) uint32_t lds[kGemvLdsWords];
@@ -1235,15 +1253,15 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
     KArgs& ka = kernel_args();
 #define PW_GEMV_CASES(RGX, TILE)                                                                                  \
     switch (bd->q) {                                                                                             \
-        case 3: mfma_block<MODE, 3, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 4: mfma_block<MODE, 4, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 5: mfma_block<MODE, 5, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 6: mfma_block<MODE, 6, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 7: mfma_block<MODE, 7, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
-        case 8: mfma_block<MODE, 8, RGX, FUSED, KEEP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 3: mfma_block<MODE, 3, RGX, FUSED, KEEP, TP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 4: mfma_block<MODE, 4, RGX, FUSED, KEEP, TP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 5: mfma_block<MODE, 5, RGX, FUSED, KEEP, TP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 6: mfma_block<MODE, 6, RGX, FUSED, KEEP, TP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 7: mfma_block<MODE, 7, RGX, FUSED, KEEP, TP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
+        case 8: mfma_block<MODE, 8, RGX, FUSED, KEEP, TP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
         default: break;                                                                                          \
     }
-    if constexpr (RG == 4) {
+    if constexpr (RG == 4 && TP == 8) {
         if (half >= 0) {
             const int t2 = 2 * tile + half;
             PW_GEMV_CASES(2, t2)
@@ -1737,25 +1755,26 @@ __device__ __forceinline__ void debug_store_step(const StepCodes& c, const half8
     }
 }
 
-// One decode-contraction tile (8 waves, RG row groups, as mfma_block).
-template <int MODE, int Q, int RG>
+// One decode-contraction tile (8 waves, RG row groups, as mfma_block; WIDE:
+// the tables of 16-token passes).
+template <int MODE, int Q, int RG, bool WIDE = false>
 __device__ void debug_gemv_tile(const BlockDesc* __restrict__ bd, int tile, uint8_t* codes_out, uint16_t* w_out,
                                 uint32_t* lds)
 {
     constexpr int KW = kWaves / RG;
-    constexpr bool PAIR = LutLoad<Q, RG>::PAIR;
+    constexpr bool PAIR = LutLoad<Q, RG, kThreads, WIDE>::PAIR;
     const int tid = threadIdx.x, lane = tid & 63, rho = lane & 31, kh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave / KW, kw = wave % KW;
     const int R = bd->R, K = bd->kwords * 32, nchunks = bd->nchunks;
-    const TileLane tl = tile_lane<MODE, Q, RG>(tile, grp, rho, R);
+    const TileLane tl = tile_lane<MODE, Q, RG, WIDE>(tile, grp, rho, R);
     {
-        LutLoad<Q, RG> ls;
-        ls.issue(bd->lut, bd->slots, tile * LutLoad<Q, RG>::NSLOT, lane, wave);
+        LutLoad<Q, RG, kThreads, WIDE> ls;
+        ls.issue(bd->lut, bd->slots, tile * LutLoad<Q, RG, kThreads, WIDE>::NSLOT, lane, wave);
         ls.commit(lds, lds + kLutBytes / 4, lane, wave);
         __syncthreads();
     }
-    WordDecoder<Q, RG> dec;
+    WordDecoder<Q, RG, WIDE> dec;
     dec.masks = make_masks();
     dec.zero = (uint32_t)__builtin_amdgcn_readfirstlane(R >> 30);  // R < 2^30
     dec.set1 = tl.set1;
@@ -1817,7 +1836,8 @@ __device__ void debug_prefill_tile(const BlockDesc* __restrict__ bd, int mtile, 
 constexpr int kDebugPfLdsWords = kPfX;  // LUT + the weight tiles (pair-table staging)
 
 // PATH 0 / 1: decode contraction with RG = 4 / RG = 2 tiles; PATH 2: prefill
-// decoder.  One workgroup per tile of that path.
+// decoder; PATH 3: RG = 2 tiles of 16-token passes.  One workgroup per tile
+// of that path.
 template <int PATH>
 __global__ void __launch_bounds__(PATH == 2 ? kPfThreads : kThreads)
     debug_decode_kernel(const BlockDesc* __restrict__ bd, int module, uint8_t* codes_out, uint16_t* w_out)
@@ -1827,7 +1847,7 @@ __global__ void __launch_bounds__(PATH == 2 ? kPfThreads : kThreads)
 #define PW_DEBUG_CASE(M, QQ)                                                                        \
     case 2 * (QQ) + (M):                                                                            \
         if constexpr (PATH == 2) debug_prefill_tile<M, QQ>(bd, tile, codes_out, w_out, lds);        \
-        else debug_gemv_tile<M, QQ, PATH == 0 ? 4 : 2>(bd, tile, codes_out, w_out, lds);           \
+        else debug_gemv_tile<M, QQ, PATH == 0 ? 4 : 2, PATH == 3>(bd, tile, codes_out, w_out, lds); \
         break;
     switch (2 * bd->q + module) {
         PW_DEBUG_CASE(0, 3) PW_DEBUG_CASE(1, 3) PW_DEBUG_CASE(0, 4) PW_DEBUG_CASE(1, 4)
@@ -1836,6 +1856,53 @@ __global__ void __launch_bounds__(PATH == 2 ? kPfThreads : kThreads)
         default: break;
     }
 #undef PW_DEBUG_CASE
+}
+
+// ---------------------------------------------------------------- width changes
+//
+// Page movement of a width change in one launch each (Core components 3:
+// pages move asynchronously, widths are committed at safe boundaries), so a
+// change of hundreds of blocks costs the host a few calls instead of one
+// copy per plane and per page-table entry.
+
+// Host-to-device copies of the new planes and LUTs: the copy list and the
+// sources are pinned host memory, read by the kernel over the host link
+// (device-side addresses); every size is a multiple of 16 bytes.  The copy is
+// bound by the host link, not by the CUs, so a few workgroups (kPullWgs)
+// take the copies round-robin with 8 x 16 bytes per thread in flight, and the
+// compute kernels running meanwhile keep nearly every CU.
+constexpr int kPullWgs = 16;
+__global__ void __launch_bounds__(256) pull_copy_kernel(const CopyDesc* __restrict__ list, int n)
+{
+    constexpr int U = 8;
+    for (int j = blockIdx.x; j < n; j += gridDim.x) {
+        const CopyDesc d = list[j];
+        const u32x4* src = (const u32x4*)d.src;
+        u32x4* dst = (u32x4*)d.dst;
+        const uint64_t n16 = d.bytes / 16;
+        for (uint64_t i = threadIdx.x; i < n16; i += U * 256) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t at = i + (uint64_t)u * 256;
+                v[u] = at < n16 ? src[at] : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t at = i + (uint64_t)u * 256;
+                if (at < n16) dst[at] = v[u];
+            }
+        }
+    }
+}
+
+// Commit of new page-table entries: descs[i] (pinned host memory) ->
+// table[ids[i]], eight threads per 128-byte entry.
+__global__ void __launch_bounds__(256) scatter_desc_kernel(BlockDesc* __restrict__ table, const int32_t* __restrict__ ids,
+                                                           const BlockDesc* __restrict__ descs, int n)
+{
+    const int i = blockIdx.x * 32 + (threadIdx.x >> 3), part = threadIdx.x & 7;
+    if (i < n) ((u32x4*)(table + ids[i]))[part] = ((const u32x4*)(descs + i))[part];
 }
 
 // ---------------------------------------------------------------- static scratch
@@ -1913,7 +1980,13 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
 {
     const int grid = gemv_grid(a);
     if (grid == 0) return hipSuccess;
-    if (a.logits) {
+    if (a.tok_pass == 16) {
+        if (a.rg != 2 || a.logits) return hipErrorInvalidValue;
+        if (a.keep_planes)
+            launch((ffn_gemv_kernel<0, 2, false, true, 16>), dim3(grid), dim3(kThreads), s, a);
+        else
+            launch((ffn_gemv_kernel<0, 2, false, false, 16>), dim3(grid), dim3(kThreads), s, a);
+    } else if (a.logits) {
         if (a.rg != 4 || a.T * a.k > kLayerRouteMaxAssign || a.E > 256) return hipErrorInvalidValue;
         launch((ffn_gemv_kernel<0, 4, true>), dim3(grid), dim3(kThreads), s, a);
     } else if (a.rg == 4) {
@@ -1931,7 +2004,13 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s)
 {
     const int grid = gemv_grid(a);
     if (grid == 0) return hipSuccess;
-    if (a.rg == 4)
+    if (a.tok_pass == 16) {
+        if (a.rg != 2) return hipErrorInvalidValue;
+        if (a.keep_planes)
+            launch((ffn_gemv_kernel<1, 2, false, true, 16>), dim3(grid), dim3(kThreads), s, a);
+        else
+            launch((ffn_gemv_kernel<1, 2, false, false, 16>), dim3(grid), dim3(kThreads), s, a);
+    } else if (a.rg == 4)
         launch((ffn_gemv_kernel<1, 4>), dim3(grid), dim3(kThreads), s, a);
     else if (a.keep_planes)
         launch((ffn_gemv_kernel<1, 2, false, true>), dim3(grid), dim3(kThreads), s, a);
@@ -1972,6 +2051,20 @@ hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_pull_copy(const CopyDesc* list, int n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    launch(pull_copy_kernel, dim3((unsigned)std::min(n, kPullWgs)), dim3(256), s, list, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_desc(BlockDesc* table, const int32_t* ids, const BlockDesc* descs, int n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    launch(scatter_desc_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), s, table, ids, descs, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int path, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s)
 {
@@ -1983,12 +2076,13 @@ hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int pa
     } else {
         const int rg = path == 0 ? 4 : 2;
         const int per = module == 0 ? 16 * rg : 32 * rg;
+        const dim3 grid((rows + per - 1) / per);
         if (path == 0)
-            launch(debug_decode_kernel<0>, dim3((rows + per - 1) / per), dim3(kThreads), s, entry, module, codes_out,
-                   w_out);
+            launch(debug_decode_kernel<0>, grid, dim3(kThreads), s, entry, module, codes_out, w_out);
+        else if (path == 1)
+            launch(debug_decode_kernel<1>, grid, dim3(kThreads), s, entry, module, codes_out, w_out);
         else
-            launch(debug_decode_kernel<1>, dim3((rows + per - 1) / per), dim3(kThreads), s, entry, module, codes_out,
-                   w_out);
+            launch(debug_decode_kernel<3>, grid, dim3(kThreads), s, entry, module, codes_out, w_out);
     }
     return hipGetLastError();
 }

@@ -25,6 +25,7 @@ this module only marshals buffers and holds the schedule.
 """
 from __future__ import annotations
 
+import time
 from typing import Callable, Optional, Sequence
 
 import numpy as np
@@ -84,6 +85,7 @@ class StackDriver:
         self.commits = []     # (step boundary, blocks committed there)
         self.requests = []    # async: (step, n blocks, H2D bytes, start / end events on the copy stream)
         self.last_target = None
+        self.host_s = {"request": 0.0, "commit": 0.0, "plan": 0.0}  # host time in library calls
         ctx.routing_mass_enable(True)
         ctx.routing_mass_reset(self.compute)
         self.graphs = None
@@ -181,8 +183,10 @@ class StackDriver:
         import torch
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(self.copy)
+        t0 = time.perf_counter()
         if ids.size:
             self.ctx.request_widths(ids, newq, self.copy)
+        self.host_s["request"] += time.perf_counter() - t0
         end.record(self.copy)
         h2d = 0
         for b, qn in zip(ids.tolist(), newq.tolist()):
@@ -225,7 +229,9 @@ class StackDriver:
     def boundary(self, s: int) -> None:
         """Safe boundary before step s: commit the requests whose copies landed."""
         if self.mode == "async":
+            t0 = time.perf_counter()
             n = self.ctx.commit_ready(self.compute)
+            self.host_s["commit"] += time.perf_counter() - t0
             if n:
                 self._refresh_committed()
                 self.commits.append((s, n))
@@ -252,7 +258,9 @@ class StackDriver:
                 target = self.byte_targets[(s // self.commit_every - 1) % len(self.byte_targets)]
                 self._budget_event(s, mass, target)
             else:
+                t0 = time.perf_counter()
                 ids, newq, lowered = self._choose(s, mass)
+                self.host_s["plan"] += time.perf_counter() - t0
                 self._request(s, ids, newq, lowered)
 
     def drain(self) -> None:

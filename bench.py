@@ -435,6 +435,7 @@ def stack_leg():
             r["h2d_bytes"] = int(h2d)
             r["copy_ms"] = round(sum(copy_ms), 3)
             r["h2d_gbps"] = round(h2d / (sum(copy_ms) * 1e-3) / 1e9, 1) if sum(copy_ms) > 0 else None
+            r["host_ms"] = {k: round(v * 1e3, 3) for k, v in drv.host_s.items()}
             drv.drain()
         times[mode] = total_s
         out[mode] = r

@@ -384,11 +384,14 @@ int64_t pw_resident_bytes(const pw_ctx *ctx);
  *     decode gate_up's whole tiles: 64 gate rows with their 64 up rows);
  *   PW_DECODE_PATH_TILE64: the decode contraction with 64-row tiles (the
  *     decode down tiles and the gate_up half tiles);
- *   PW_DECODE_PATH_PREFILL: the prefill GEMM's weight-tile decoder.
+ *   PW_DECODE_PATH_PREFILL: the prefill GEMM's weight-tile decoder;
+ *   PW_DECODE_PATH_TILE64_WIDE: 64-row tiles of the 16-token passes (single
+ *     tables at q = 4) that decode batches holding more than 8 tokens per
+ *     expert use.
  * codes_out: dev uint8 [R][K] child codes; w_out: dev fp16 [R][K] weights
  * (bit patterns); either may be NULL, not both.  Asynchronous on `stream`.
  * Errors: INVALID (null outputs, unregistered block, path out of range), HIP. */
-enum { PW_DECODE_PATH_TILE128 = 0, PW_DECODE_PATH_TILE64 = 1, PW_DECODE_PATH_PREFILL = 2 };
+enum { PW_DECODE_PATH_TILE128 = 0, PW_DECODE_PATH_TILE64 = 1, PW_DECODE_PATH_PREFILL = 2, PW_DECODE_PATH_TILE64_WIDE = 3 };
 pw_status pw_debug_decode(pw_ctx *ctx, int32_t block_id, int path, uint8_t *codes_out, uint16_t *w_out,
                           pw_stream stream);
 

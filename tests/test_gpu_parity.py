@@ -27,7 +27,8 @@ def _gpu(require_gpu):
 # PagedWeight", Core components 1).  Paths: the decode contraction's 128-row
 # tiles (gate_up whole tiles; q = 3 two-set pair tables, q = 4 single tables,
 # q >= 5 bit transpose) and 64-row tiles (gate_up half tiles, down; q <= 4 pair
-# tables), and the prefill decoder (per-lane rotate form).  Shapes: ragged row
+# tables), 64-row tiles of 16-token passes (single tables at q = 4), and the
+# prefill decoder (per-lane rotate form).  Shapes: ragged row
 # tiles, ragged K (a last chunk of 1 or 3 words) and several chunks per K-wave.
 DECODE_SHAPES = {"ragged": (352, 224), "multi_chunk": (1056, 608)}
 
@@ -42,7 +43,7 @@ def test_ffn_decode_paths_bit_exact(q, shape):
     w, _ = pw_synth.make_small(H=H, I=I, E=2, top_k=1, T=1, seed=100 + q + 10 * H, q_fixed=q)
     ctx = make_ctx(w.shape)
     paths = {"tile128": pw.DECODE_PATH_TILE128, "tile64": pw.DECODE_PATH_TILE64,
-             "prefill": pw.DECODE_PATH_PREFILL}
+             "prefill": pw.DECODE_PATH_PREFILL, "tile64_wide": pw.DECODE_PATH_TILE64_WIDE}
     try:
         for e in range(2):
             for m, blk in ((pw.MODULE_GATE_UP, w.gate_up[e]), (pw.MODULE_DOWN, w.down[e])):
