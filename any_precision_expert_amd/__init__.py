@@ -105,8 +105,7 @@ def lib() -> ctypes.CDLL:
         L.pw_retarget.argtypes = [vp, i64, vp, vp, ctypes.POINTER(PlanParams), vp, ctypes.POINTER(ctypes.c_int),
                                   ctypes.POINTER(i64)]
         L.pw_trim.argtypes = [vp, ctypes.POINTER(i64)]
-        L.pw_pool_stats.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64),
-                                    ctypes.POINTER(i64)]
+        L.pw_pool_stats.argtypes = [vp] + [ctypes.POINTER(i64)] * 6
         L.pw_get_committed_bits.argtypes = [vp, i32, ctypes.POINTER(i32)]
         L.pw_block_id.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.pw_block_id.restype = i32
@@ -329,9 +328,10 @@ class Context:
         return freed.value
 
     def pool_stats(self) -> dict:
-        v = [ctypes.c_int64(0) for _ in range(4)]
+        v = [ctypes.c_int64(0) for _ in range(6)]
         _check(lib().pw_pool_stats(self.h, *[ctypes.byref(x) for x in v]))
-        return dict(resident=v[0].value, cached=v[1].value, waiting=v[2].value, events=v[3].value)
+        keys = ("resident", "cached", "waiting", "held", "device_allocs", "events")
+        return {k: x.value for k, x in zip(keys, v)}
 
     def routing_mass_enable(self, on: bool = True) -> None:
         _check(lib().pw_routing_mass_enable(self.h, 1 if on else 0))

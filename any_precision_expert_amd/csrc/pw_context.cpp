@@ -109,54 +109,81 @@ private:
     size_t created_ = 0;
 };
 
-// Device slabs for planes and LUTs, recycled by size.  A released slab is only
-// reused after an event recorded behind the last work that may read it (the
-// pool holds a reference on that event until then).  trim() returns the free
-// slabs to the device.
+// Device slabs for planes and LUTs.  Slabs are carved from chunks of about
+// kChunkBytes, one chunk per class (slab size, plane index or LUT): a device
+// allocation (hipMalloc) stalls the kernels running on the device for tens
+// of microseconds, so a width change of hundreds of blocks must not make one
+// per slab.  A released slab goes back to its class's free list, but only
+// after an event recorded behind the last work that may read it (the pool
+// holds a reference on that event until then).  trim() returns the chunks
+// whose slabs are all free to the device (dropping plane p of many blocks
+// frees whole plane-p chunks).
 class SlabPool {
 public:
+    static constexpr size_t kChunkBytes = (size_t)32 << 20;
+    static constexpr int kLutTag = 8;  // class tag of LUT slabs (planes use their index 0..7)
+
     explicit SlabPool(EventPool* evs) : evs_(evs) {}
     ~SlabPool() { clear(); }
 
-    hipError_t alloc(size_t bytes, void** out)
+    hipError_t alloc(size_t bytes, int tag, void** out)
     {
         bytes = round(bytes);
         reclaim();
-        auto it = free_.find(bytes);
+        const uint64_t key = cls(bytes, tag);
+        auto it = free_.find(key);
         if (it != free_.end() && !it->second.empty()) {
             *out = it->second.back();
             it->second.pop_back();
+            chunk_of(*out).live++;
             free_bytes_ -= bytes;
             resident_ += bytes;
             return hipSuccess;
         }
-        void* p = nullptr;
-        hipError_t e = hipMalloc(&p, bytes);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return e;
+        auto op = open_.find(key);
+        if (op == open_.end()) {
+            int n = (int)std::max<size_t>(1, std::min<size_t>(64, kChunkBytes / bytes));
+            void* base = nullptr;
+            hipError_t e = hipMalloc(&base, (size_t)n * bytes);
+            if (e != hipSuccess && n > 1) {
+                (void)hipGetLastError();
+                n = 1;
+                e = hipMalloc(&base, bytes);
+            }
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return e;
+            }
+            ++device_allocs_;
+            held_ += (size_t)n * bytes;
+            chunks_[(char*)base] = Chunk{key, bytes, n, 0, 0};
+            op = open_.emplace(key, (char*)base).first;
         }
-        all_[p] = bytes;
+        Chunk& ch = chunks_[op->second];
+        *out = op->second + (size_t)ch.carved * bytes;
+        ch.carved++;
+        ch.live++;
+        if (ch.carved == ch.n) open_.erase(op);
         resident_ += bytes;
-        *out = p;
         return hipSuccess;
     }
 
-    void release_now(void* p, size_t bytes)
+    void release_now(void* p, size_t bytes, int tag)
     {
         if (!p) return;
         bytes = round(bytes);
-        free_[bytes].push_back(p);
+        free_[cls(bytes, tag)].push_back(p);
+        chunk_of(p).live--;
         free_bytes_ += bytes;
         resident_ -= bytes;
     }
 
-    void release_after(void* p, size_t bytes, hipEvent_t ev)
+    void release_after(void* p, size_t bytes, int tag, hipEvent_t ev)
     {
         if (!p) return;
         bytes = round(bytes);
         evs_->hold(ev);
-        pending_.push_back({p, bytes, ev});
+        pending_.push_back({p, bytes, cls(bytes, tag), ev});
         resident_ -= bytes;
     }
 
@@ -165,7 +192,8 @@ public:
         size_t w = 0;
         for (size_t i = 0; i < pending_.size(); ++i) {
             if (hipEventQuery(pending_[i].ev) == hipSuccess) {
-                free_[pending_[i].bytes].push_back(pending_[i].p);
+                free_[pending_[i].key].push_back(pending_[i].p);
+                chunk_of(pending_[i].p).live--;
                 free_bytes_ += pending_[i].bytes;
                 evs_->drop(pending_[i].ev);
             } else {
@@ -175,26 +203,39 @@ public:
         pending_.resize(w);
     }
 
-    // hipFree every free slab (those still waiting for their event stay);
-    // returns the bytes given back
+    // hipFree every chunk none of whose slabs is in use or waiting; returns
+    // the bytes given back to the device
     size_t trim()
     {
         reclaim();
         size_t freed = 0;
-        for (auto& kv : free_) {
-            for (void* p : kv.second) {
-                (void)hipFree(p);
-                all_.erase(p);
-                freed += kv.first;
+        for (auto it = chunks_.begin(); it != chunks_.end();) {
+            Chunk& ch = it->second;
+            if (ch.live != 0) {
+                ++it;
+                continue;
             }
+            char* base = it->first;
+            char* end = base + (size_t)ch.n * ch.slab;
+            auto& fl = free_[ch.key];
+            const size_t before = fl.size();
+            fl.erase(std::remove_if(fl.begin(), fl.end(), [&](void* q) { return (char*)q >= base && (char*)q < end; }),
+                     fl.end());
+            free_bytes_ -= (before - fl.size()) * ch.slab;
+            auto op = open_.find(ch.key);
+            if (op != open_.end() && op->second == base) open_.erase(op);
+            (void)hipFree(base);
+            held_ -= (size_t)ch.n * ch.slab;
+            freed += (size_t)ch.n * ch.slab;
+            it = chunks_.erase(it);
         }
-        free_.clear();
-        free_bytes_ = 0;
         return freed;
     }
 
     int64_t resident() const { return (int64_t)resident_; }
     int64_t free_bytes() const { return (int64_t)free_bytes_; }
+    int64_t held() const { return (int64_t)held_; }
+    int64_t device_allocs() const { return (int64_t)device_allocs_; }
     int64_t waiting_bytes() const
     {
         size_t b = 0;
@@ -204,27 +245,42 @@ public:
 
     void clear()
     {
-        for (auto& kv : all_) (void)hipFree(kv.first);
-        all_.clear();
+        for (auto& kv : chunks_) (void)hipFree(kv.first);
+        chunks_.clear();
+        open_.clear();
         free_.clear();
         pending_.clear();
         resident_ = 0;
         free_bytes_ = 0;
+        held_ = 0;
     }
 
 private:
     static size_t round(size_t b) { return (b + 255) & ~size_t(255); }
+    static uint64_t cls(size_t bytes, int tag) { return ((uint64_t)bytes << 4) | (uint64_t)tag; }
+    struct Chunk {
+        uint64_t key;
+        size_t slab;
+        int n, carved, live;  // slabs in the chunk, carved so far, in use or waiting
+    };
     struct Pending {
         void* p;
         size_t bytes;
+        uint64_t key;
         hipEvent_t ev;
     };
+    Chunk& chunk_of(void* p)
+    {
+        auto it = chunks_.upper_bound((char*)p);
+        --it;  // every slab lies in a chunk
+        return it->second;
+    }
     EventPool* evs_;
-    std::unordered_map<size_t, std::vector<void*>> free_;
+    std::map<char*, Chunk> chunks_;                           // by base address
+    std::unordered_map<uint64_t, char*> open_;                // class -> chunk with uncarved slabs
+    std::unordered_map<uint64_t, std::vector<void*>> free_;   // class -> free slabs
     std::vector<Pending> pending_;
-    std::unordered_map<void*, size_t> all_;
-    size_t resident_ = 0;
-    size_t free_bytes_ = 0;
+    size_t resident_ = 0, free_bytes_ = 0, held_ = 0, device_allocs_ = 0;
 };
 
 struct HostBlock {
@@ -384,10 +440,10 @@ BlockDesc make_desc(const HostBlock& b)
 void free_block_now(pw_ctx* c, HostBlock& b)
 {
     for (int p = 0; p < 8; ++p) {
-        c->pool.release_now(b.dplanes[p], (size_t)b.pw * 4);
+        c->pool.release_now(b.dplanes[p], (size_t)b.pw * 4, p);
         b.dplanes[p] = nullptr;
     }
-    c->pool.release_now(b.dlut, lut_bytes(b.S, b.q));
+    c->pool.release_now(b.dlut, lut_bytes(b.S, b.q), SlabPool::kLutTag);
     b.dlut = nullptr;
     if (b.hplanes) (void)hipHostFree(b.hplanes);
     if (b.hluts) (void)hipHostFree(b.hluts);
@@ -548,18 +604,18 @@ pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const 
     const size_t plane_b = (size_t)nb.pw * 4;
     const size_t luts_b = lut_offset_words(nb.S, PW_QMAX + 1) * 4;  // LUT_3..LUT_8, slot layout
     auto undo = [&]() {
-        for (int p = 0; p < 8; ++p) c->pool.release_now(nb.dplanes[p], plane_b);
-        c->pool.release_now(nb.dlut, lut_bytes(nb.S, q_init));
+        for (int p = 0; p < 8; ++p) c->pool.release_now(nb.dplanes[p], plane_b, p);
+        c->pool.release_now(nb.dlut, lut_bytes(nb.S, q_init), SlabPool::kLutTag);
         if (nb.hplanes) (void)hipHostFree(nb.hplanes);
         if (nb.hluts) (void)hipHostFree(nb.hluts);
     };
     for (int p = 0; p < q_init; ++p) {
-        if ((e = c->pool.alloc(plane_b, &nb.dplanes[p])) != hipSuccess) {
+        if ((e = c->pool.alloc(plane_b, p, &nb.dplanes[p])) != hipSuccess) {
             undo();
             return fail(PW_ERR_OOM, "pw_register_block: device plane: %s", hipGetErrorString(e));
         }
     }
-    if ((e = c->pool.alloc(lut_bytes(nb.S, q_init), &nb.dlut)) != hipSuccess) {
+    if ((e = c->pool.alloc(lut_bytes(nb.S, q_init), SlabPool::kLutTag, &nb.dlut)) != hipSuccess) {
         undo();
         return fail(PW_ERR_OOM, "pw_register_block: device LUT: %s", hipGetErrorString(e));
     }
@@ -740,7 +796,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     a.k = d.top_k;
     a.n_slots = std::min(E, T * d.top_k);
     a.tok_pass = decode_tok_pass(T, d.top_k, E, d.inter_shared);
-    a.keep_planes = (int64_t)T * d.top_k >= (int64_t)kKeepPlanesPasses * a.tok_pass * E ? 1 : 0;
+    a.keep_planes = keep_planes(T, d.top_k, E, a.tok_pass) ? 1 : 0;
     a.hstride = std::max(d.inter, d.inter_shared);
     a.drows = T * d.top_k + (d.inter_shared ? T : 0);
     hipStream_t s = (hipStream_t)stream;
@@ -928,8 +984,8 @@ static void release_prepared(pw_ctx* c, const std::vector<WidthChange>& plans)
 {
     for (const auto& p : plans) {
         const HostBlock& b = c->blocks[p.id];
-        for (int j = p.qo; j < p.qn; ++j) c->pool.release_now(p.planes[j], (size_t)b.pw * 4);
-        c->pool.release_now(p.lut, lut_bytes(b.S, p.qn));
+        for (int j = p.qo; j < p.qn; ++j) c->pool.release_now(p.planes[j], (size_t)b.pw * 4, j);
+        c->pool.release_now(p.lut, lut_bytes(b.S, p.qn), SlabPool::kLutTag);
         c->evs.drop(p.copied);
     }
 }
@@ -956,12 +1012,12 @@ static pw_status prepare_changes(pw_ctx* c, const char* fn, const std::vector<st
         plans.push_back(p);
         WidthChange& pr = plans.back();
         for (int j = pr.qo; j < pr.qn; ++j) {
-            if ((e = c->pool.alloc((size_t)b.pw * 4, &pr.planes[j])) != hipSuccess) {
+            if ((e = c->pool.alloc((size_t)b.pw * 4, j, &pr.planes[j])) != hipSuccess) {
                 release_prepared(c, plans);
                 return fail(PW_ERR_OOM, "%s: device plane: %s", fn, hipGetErrorString(e));
             }
         }
-        if ((e = c->pool.alloc(lut_bytes(b.S, pr.qn), &pr.lut)) != hipSuccess) {
+        if ((e = c->pool.alloc(lut_bytes(b.S, pr.qn), SlabPool::kLutTag, &pr.lut)) != hipSuccess) {
             release_prepared(c, plans);
             return fail(PW_ERR_OOM, "%s: device LUT: %s", fn, hipGetErrorString(e));
         }
@@ -1067,11 +1123,11 @@ static pw_status apply_changes(pw_ctx* c, std::vector<WidthChange>& plans, hipSt
     for (size_t i = 0; i < plans.size(); ++i) {
         HostBlock& b = c->blocks[plans[i].id];
         for (int j = plans[i].qn; j < plans[i].qo; ++j) {
-            c->pool.release_after(b.dplanes[j], (size_t)b.pw * 4, updated);
+            c->pool.release_after(b.dplanes[j], (size_t)b.pw * 4, j, updated);
             b.dplanes[j] = nullptr;
         }
         for (int j = plans[i].qo; j < plans[i].qn; ++j) b.dplanes[j] = plans[i].planes[j];
-        c->pool.release_after(b.dlut, lut_bytes(b.S, b.q), updated);
+        c->pool.release_after(b.dlut, lut_bytes(b.S, b.q), SlabPool::kLutTag, updated);
         b.dlut = plans[i].lut;
         b.q = plans[i].qn;
         c->h_table[plans[i].id] = newdesc[i];
@@ -1240,12 +1296,15 @@ pw_status pw_trim(pw_ctx* c, int64_t* freed_bytes)
     return ok();
 }
 
-pw_status pw_pool_stats(const pw_ctx* c, int64_t* resident, int64_t* cached, int64_t* waiting, int64_t* events)
+pw_status pw_pool_stats(const pw_ctx* c, int64_t* resident, int64_t* cached, int64_t* waiting, int64_t* held,
+                        int64_t* device_allocs, int64_t* events)
 {
     if (!c) return fail(PW_ERR_INVALID, "pw_pool_stats: null context");
     if (resident) *resident = c->pool.resident();
     if (cached) *cached = c->pool.free_bytes();
     if (waiting) *waiting = c->pool.waiting_bytes();
+    if (held) *held = c->pool.held();
+    if (device_allocs) *device_allocs = c->pool.device_allocs();
     if (events) *events = (int64_t)c->evs.created();
     return ok();
 }

@@ -71,11 +71,6 @@ struct FfnArgs {
 // Most assignments (T * k) a gate_up launch routes by itself.
 constexpr int kLayerRouteMaxAssign = 64;
 
-// Decode launches load planes with ordinary loads (which the MALL keeps)
-// instead of nontemporal ones once the batch averages two passes per expert:
-// nearly every tile then re-reads its planes.  Below it, nontemporal loads
-// are faster (one pass).
-constexpr int kKeepPlanesPasses = 2;
 
 // Tokens per decode pass: 16 (each weight decoded once per 16 tokens, 64-row
 // tiles) when some work unit surely holds more than 8 tokens -- the shared
@@ -83,6 +78,18 @@ constexpr int kKeepPlanesPasses = 2;
 inline int decode_tok_pass(int T, int k, int E, int I_shared)
 {
     return T > 8 && (I_shared > 0 || (long long)T * k > 8LL * E) ? 16 : 8;
+}
+
+// Decode launches load planes with ordinary loads (which the MALL keeps)
+// instead of nontemporal ones when many tiles take a second pass and re-read
+// their planes: 8-token passes from 16 assignments per expert on average,
+// 16-token passes from 8 (Mixtral-shaped layer, 16-token passes: batch 32
+// 0.386 -> 0.371 ms, batch 64 0.452 -> 0.395 ms).  Below, nontemporal loads
+// are faster (one pass: ordinary loads made the Qwen-shaped step 4% and
+// Mixtral-shaped batches of 1-16 1-3% slower).
+inline bool keep_planes(int T, int k, int E, int tok_pass)
+{
+    return (long long)T * k >= (tok_pass == 16 ? 8LL : 16LL) * E;
 }
 
 // Tokens per call from which the prefill GEMM path runs.

@@ -38,7 +38,7 @@ class StackDriver:
                  commit_every: int = 8, fraction: float = 0.2, device="cuda:0",
                  byte_targets: Optional[Sequence[int]] = None, sensitivity: Optional[np.ndarray] = None,
                  plan_params: Optional[dict] = None, mode: str = "async",
-                 target_fn: Optional[Callable[[int], int]] = None):
+                 target_fn: Optional[Callable[[int], int]] = None, request_lead: int = 0):
         """q_init: int [L][E][2] routed widths as registered; logits: fp32
         [S][L][T][E]; x: fp16 [S][L][T][H] (staged to the device once).
 
@@ -50,7 +50,12 @@ class StackDriver:
         routing mass with the per-block `sensitivity` [L][E][2] and
         plan_params).  target_fn(step) -> routed-byte target replaces the
         event schedule by a memory-target trigger: whenever the target
-        changes, the widths are re-planned for it (async mode only)."""
+        changes, the widths are re-planned for it (async mode only).
+        request_lead (async mode): the host enqueues this many further steps
+        before it plans and issues an event's request, so the host time of
+        the request overlaps work already queued on the GPU (the widths the
+        steps use are unaffected: commits happen only at step boundaries
+        after the request's copies land)."""
         import torch
         d = ctx.desc
         S, L, T, E = logits.shape
@@ -67,6 +72,7 @@ class StackDriver:
         self.sensitivity = None if sensitivity is None else np.asarray(sensitivity, np.float32)
         self.plan_params = dict(plan_params or {})
         self.target_fn = target_fn
+        self.request_lead = max(0, int(request_lead))
         self.logits = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).to(device)
         self.x = torch.from_numpy(np.ascontiguousarray(x, np.float16)).to(device)
         self.idx = torch.zeros((S, L, T, self.k), dtype=torch.int32, device=device)
@@ -236,32 +242,41 @@ class StackDriver:
                 self._refresh_committed()
                 self.commits.append((s, n))
 
+    def _async_event(self, s: int, snap, target) -> None:
+        mass = self._mass(snap)  # the GPU runs the steps enqueued since meanwhile
+        if target is not None:
+            self.last_target = target
+            self._budget_event(s, mass, target)
+        elif self.byte_targets is not None:
+            tgt = self.byte_targets[(s // self.commit_every - 1) % len(self.byte_targets)]
+            self._budget_event(s, mass, tgt)
+        else:
+            t0 = time.perf_counter()
+            ids, newq, lowered = self._choose(s, mass)
+            self.host_s["plan"] += time.perf_counter() - t0
+            self._request(s, ids, newq, lowered)
+
     def run(self, steps: Optional[int] = None, on_layer=None) -> None:
         """All steps; on_layer(s, l) (if given) is called after each layer's
         work is enqueued (for checks; it may synchronise)."""
-        for s in range(self.S if steps is None else steps):
+        n_steps = self.S if steps is None else steps
+        deferred = []  # async events (step, snapshot event, trigger target or None) not yet requested
+        for s in range(n_steps):
             self.boundary(s)
             if self.mode == "blocking" and self.is_event(s):
                 self._blocking_event(s)
             target = self.target_fn(s) if self.target_fn is not None else None
             trigger = target is not None and target != self.last_target
-            snap = self._snapshot() if (self.mode == "async" and (self.is_event(s) or trigger)) else None
-            self.q_log.append(self.q.copy())
-            self.enqueue_step(s, on_layer)
-            if snap is None:
-                continue
-            mass = self._mass(snap)  # the GPU runs step s meanwhile
             if trigger:
                 self.last_target = target
-                self._budget_event(s, mass, target)
-            elif self.byte_targets is not None:
-                target = self.byte_targets[(s // self.commit_every - 1) % len(self.byte_targets)]
-                self._budget_event(s, mass, target)
-            else:
-                t0 = time.perf_counter()
-                ids, newq, lowered = self._choose(s, mass)
-                self.host_s["plan"] += time.perf_counter() - t0
-                self._request(s, ids, newq, lowered)
+            if self.mode == "async" and (self.is_event(s) or trigger):
+                deferred.append((s, self._snapshot(), target if trigger else None))
+            self.q_log.append(self.q.copy())
+            self.enqueue_step(s, on_layer)
+            while deferred and s >= deferred[0][0] + self.request_lead:
+                self._async_event(*deferred.pop(0))
+        while deferred:
+            self._async_event(*deferred.pop(0))
 
     def drain(self) -> None:
         """Wait for outstanding copies and commit them (end of a run)."""

@@ -417,6 +417,7 @@ def stack_leg():
         drv.capture_graphs()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        allocs0 = ctx.pool_stats()["device_allocs"]
         w_0 = time.perf_counter()
         ev0.record(drv.compute)
         drv.run()
@@ -427,7 +428,8 @@ def stack_leg():
         total_s = max(wall, gpu_ms * 1e-3)
         r = {"ms_total": round(total_s * 1e3, 3), "ms_per_step": round(total_s * 1e3 / S, 4),
              "tokens_per_s_per_layer": round(T * S * L / total_s, 1), "gpu_stream_ms": round(gpu_ms, 3),
-             "events": [(e[0], "lower" if e[1] else "raise", e[2]) for e in drv.events]}
+             "events": [(e[0], "lower" if e[1] else "raise", e[2]) for e in drv.events],
+             "device_allocs": ctx.pool_stats()["device_allocs"] - allocs0}
         if mode == "async":
             copy_ms = [a.elapsed_time(b) for (_, _, _, a, b) in drv.requests]
             h2d = sum(req[2] for req in drv.requests)

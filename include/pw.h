@@ -349,19 +349,25 @@ pw_status pw_plan_event(int L, int E, const uint8_t *q_cur, const double *mass, 
 pw_status pw_retarget(pw_ctx *ctx, int64_t byte_target, const double *mass, const float *sens,
                       const pw_plan_params *params, pw_stream copy, int *n_requested, int64_t *planned_bytes);
 
-/* Return device slabs that no block uses any more (planes dropped by
- * lowered widths, replaced LUTs) to the device with hipFree.  Slabs whose
+/* Return to the device (hipFree) every slab chunk none of whose slabs is
+ * used by a block any more (planes dropped by lowered widths, replaced LUTs):
+ * dropping plane p of many blocks frees whole plane-p chunks.  Slabs whose
  * last reader may still be running are kept until a later call.  Not for the
  * hot path: hipFree may synchronise the device.  *freed_bytes (may be NULL)
  * receives the bytes returned.  Errors: INVALID, HIP. */
 pw_status pw_trim(pw_ctx *ctx, int64_t *freed_bytes);
 
-/* Device-slab accounting: bytes held by committed widths (as
- * pw_resident_bytes), bytes of free slabs kept for reuse, bytes of released
- * slabs still waiting for their last reader, and HIP events created so far
- * (events are recycled once no pending work refers to them).  Any output may
- * be NULL. */
-pw_status pw_pool_stats(const pw_ctx *ctx, int64_t *resident, int64_t *cached, int64_t *waiting, int64_t *events);
+/* Device-slab accounting.  Plane and LUT slabs are carved from chunks of
+ * about 32 MiB, one chunk per class (slab size, plane index or LUT), so that
+ * width changes rarely allocate device memory (each hipMalloc stalls the
+ * kernels running on the device).  Outputs (any may be NULL): bytes of slabs
+ * in use by committed widths (as pw_resident_bytes), bytes of free slabs kept
+ * for reuse, bytes of released slabs still waiting for their last reader,
+ * bytes of device memory the chunks hold, the number of device allocations
+ * made so far, and HIP events created so far (events are recycled once no
+ * pending work refers to them). */
+pw_status pw_pool_stats(const pw_ctx *ctx, int64_t *resident, int64_t *cached, int64_t *waiting, int64_t *held,
+                        int64_t *device_allocs, int64_t *events);
 
 /* Host view of one block's committed width (0 if not registered). */
 pw_status pw_get_committed_bits(const pw_ctx *ctx, int32_t block_id, int32_t *q_out);
