@@ -660,22 +660,23 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR_OR_OUT_MD",
                     help="PMC_DIR [PMC_DIR ...] OUT_MD: per-kernel counter means of rocprofv3 --pmc runs")
     ap.add_argument("--title", default=None, help="heading of a --summarize-* markdown file")
-    ap.add_argument("--command", default="", help="command line recorded in the summary")
-    ap.add_argument("--command2", default="", help="second command line (WRITE_SIZE pass)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line recorded in a --summarize-* file (repeat: one per profiler pass, "
+                         "FETCH_SIZE pass first for --summarize-pmc)")
     ap.add_argument("--alg-bytes", type=float, nargs=2, default=(0.0, 0.0), metavar=("GATE_UP", "DOWN"),
                     help="algorithmic bytes per gate_up and per down launch")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command, args.title)
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], " ; ".join(args.command), args.title)
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2], args.command,
-                      args.command2, args.copy_calibration_mib,
+        cmds = args.command + ["", ""]
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2], cmds[0],
+                      cmds[1], args.copy_calibration_mib,
                       {"gate_up": args.alg_bytes[0], "down": args.alg_bytes[1]})
         return
     if args.summarize_counters:
-        cmds = [c for c in (args.command, args.command2) if c]
-        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], cmds,
+        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], args.command,
                            args.title or "PMC counters per kernel")
         return
     if args.gpus != 1:
