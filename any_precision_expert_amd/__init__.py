@@ -28,7 +28,7 @@ LUT_HALVES_PER_ROW = sum(1 << k for k in range(QMIN, QMAX + 1))
 # every function declared in include/pw.h
 EXPORTS = (
     "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
-    "pw_register_block", "pw_workspace_size", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
+    "pw_register_block", "pw_workspace_size", "pw_decode_tokens_per_pass", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
     "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_moe_layer_noalloc", "pw_routing_mass_enable", "pw_routing_mass_reset",
     "pw_routing_mass_read", "pw_plan_widths", "pw_request_widths", "pw_commit_ready", "pw_block_state",
     "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id", "pw_plane_states", "pw_committed_widths",
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.pw_register_block.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int]
         L.pw_workspace_size.argtypes = [vp, ctypes.c_int]
         L.pw_workspace_size.restype = sz
+        L.pw_decode_tokens_per_pass.argtypes = [ctypes.c_int] * 4
+        L.pw_decode_tokens_per_pass.restype = i32
         L.pw_route_topk.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
         L.pw_permute_by_expert.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
         L.pw_route_permute.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
@@ -119,7 +121,7 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(i64)]
         for name in EXPORTS:
             if name not in ("pw_last_error", "pw_plane_words", "pw_workspace_size", "pw_block_id",
-                            "pw_resident_bytes"):
+                            "pw_resident_bytes", "pw_decode_tokens_per_pass"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -364,6 +366,12 @@ class Context:
         n = ctypes.c_int64()
         _check(lib().pw_profile_read(self.h, kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
         return float(ms.value), int(n.value)
+
+
+def decode_tokens_per_pass(T: int, top_k: int, E: int, I_shared: int = 0) -> int:
+    """pw_decode_tokens_per_pass: 8, 16 or 32 tokens per decode pass for a
+    call of T tokens (0: no decode call, or the prefill path)."""
+    return int(lib().pw_decode_tokens_per_pass(T, top_k, E, I_shared))
 
 
 def plan_event(q_cur: np.ndarray, mass: np.ndarray, lower: bool, n_change: int, skip: Optional[np.ndarray] = None):

@@ -670,6 +670,12 @@ size_t pw_workspace_size(const pw_ctx* c, int T)
     return ws_layout(T, c->d.top_k, c->d.hidden, c->d.inter, c->d.inter_shared).total;
 }
 
+int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared)
+{
+    if (T <= 0 || T >= kPrefillMinT || top_k <= 0 || E <= 0) return 0;
+    return decode_tok_pass(T, top_k, E, I_shared);
+}
+
 pw_status pw_route_topk(pw_ctx* c, const float* logits, int T, int32_t* idx, float* w, pw_stream stream)
 {
     if (!c) return fail(PW_ERR_INVALID, "pw_route_topk: null context");
@@ -796,7 +802,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     a.k = d.top_k;
     a.n_slots = std::min(E, T * d.top_k);
     a.tok_pass = decode_tok_pass(T, d.top_k, E, d.inter_shared);
-    a.keep_planes = keep_planes(T, d.top_k, E, a.tok_pass) ? 1 : 0;
+    a.keep_planes = keep_planes(T, d.top_k, E, d.inter_shared, a.tok_pass) ? 1 : 0;
     a.hstride = std::max(d.inter, d.inter_shared);
     a.drows = T * d.top_k + (d.inter_shared ? T : 0);
     hipStream_t s = (hipStream_t)stream;
@@ -828,7 +834,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     }
     {
         ProfScope ps(c, "gate_up", s);
-        a.rg = a.tok_pass == 16 ? 2 : kGateUpRowGroups;
+        a.rg = a.tok_pass >= 16 ? 2 : kGateUpRowGroups;
         a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         a.tiles_routed = (d.inter + 16 * a.rg - 1) / (16 * a.rg);
         a.tiles_shared = (d.inter_shared + 16 * a.rg - 1) / (16 * a.rg);

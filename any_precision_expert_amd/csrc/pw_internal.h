@@ -50,7 +50,7 @@ struct FfnArgs {
     int32_t rg;               // 32-row groups per workgroup tile: 2 or 4
     int32_t big_wgs;          // rg 4: workgroups taking whole tiles before tiles split in halves (0: all whole)
     int32_t keep_planes;      // decode: ordinary (not nontemporal) plane loads, set when tiles take several passes
-    int32_t tok_pass;         // decode: tokens per pass, 8 or 16 (16: 64-row tiles only, routing outside)
+    int32_t tok_pass;         // decode: tokens per pass, 8, 16 or 32 (16, 32: 64-row tiles only, routing outside)
     // prefill launches: token tiles of the shared block, and an upper bound
     // on the routed token tiles (sum over experts of ceil(tokens / 512))
     int32_t tok_tiles_shared;
@@ -72,24 +72,39 @@ struct FfnArgs {
 constexpr int kLayerRouteMaxAssign = 64;
 
 
-// Tokens per decode pass: 16 (each weight decoded once per 16 tokens, 64-row
-// tiles) when some work unit surely holds more than 8 tokens -- the shared
-// expert with T > 8, or routed experts averaging more than 8 -- else 8.
+// Tokens per decode pass: the smallest of 8, 16 and 32 that covers the
+// largest token count a work unit is expected to hold -- the shared expert's
+// T, or for routed experts the mean T k / E plus two standard deviations of a
+// Poisson count.  Wider passes decode each weight once for more tokens (the
+// MFMA's B operand has 32 token columns either way) but cost more per pass:
+// on a Mixtral-shaped layer with all units in one pass, 16-token passes were
+// 5% and 32-token passes 14% slower than 8-token ones; batch 32 (12 tokens on
+// the fullest expert) 0.40 -> 0.30 ms with 16-token passes, batch 64 0.41 ->
+// 0.33 ms and batch 128 0.66 -> 0.45 ms with 32-token passes; a
+// Qwen-shaped layer (shared expert) 0.068 -> 0.062 ms at batch 12 with 16,
+// 0.21 -> 0.12 ms at batch 64 with 32.
+inline double decode_unit_tokens(int T, int k, int E, int I_shared)
+{
+    const double a = (double)T * k / E;
+    const double m = a + 2.0 * __builtin_sqrt(a);
+    return I_shared > 0 && T > m ? (double)T : m;
+}
+
 inline int decode_tok_pass(int T, int k, int E, int I_shared)
 {
-    return T > 8 && (I_shared > 0 || (long long)T * k > 8LL * E) ? 16 : 8;
+    const double m = decode_unit_tokens(T, k, E, I_shared);
+    return m <= 8.0 ? 8 : m <= 16.0 ? 16 : 32;
 }
 
 // Decode launches load planes with ordinary loads (which the MALL keeps)
-// instead of nontemporal ones when many tiles take a second pass and re-read
-// their planes: 8-token passes from 16 assignments per expert on average,
-// 16-token passes from 8 (Mixtral-shaped layer, 16-token passes: batch 32
-// 0.386 -> 0.371 ms, batch 64 0.452 -> 0.395 ms).  Below, nontemporal loads
-// are faster (one pass: ordinary loads made the Qwen-shaped step 4% and
-// Mixtral-shaped batches of 1-16 1-3% slower).
-inline bool keep_planes(int T, int k, int E, int tok_pass)
+// instead of nontemporal ones when the fullest units are expected to take a
+// second pass and re-read their planes (Mixtral-shaped batch 128 0.469 ->
+// 0.443 ms).  With one pass, nontemporal loads are faster (ordinary loads
+// made the Qwen-shaped step 4% and Mixtral-shaped batches of 1-48 1-3%
+// slower).
+inline bool keep_planes(int T, int k, int E, int I_shared, int tok_pass)
 {
-    return (long long)T * k >= (tok_pass == 16 ? 8LL : 16LL) * E;
+    return decode_unit_tokens(T, k, E, I_shared) > (double)tok_pass;
 }
 
 // Tokens per call from which the prefill GEMM path runs.

@@ -130,6 +130,15 @@ pw_status pw_register_block(pw_ctx *ctx, int layer, int expert, int module,
 /* Bytes of workspace pw_moe_ffn_bitplane needs for T tokens (0 if T <= 0). */
 size_t pw_workspace_size(const pw_ctx *ctx, int T);
 
+/* Tokens per pass the decode contraction uses for a call of T tokens on a
+ * layer of E experts, top_k, shared-expert width I_shared (0: none): 8, 16 or
+ * 32, the smallest that covers the largest token count a work unit is
+ * expected to hold (the shared expert's T; routed experts: T top_k / E plus
+ * two standard deviations of a Poisson count).  A unit holding more tokens
+ * takes several passes, each decoding its weights again.  0 when T <= 0 or
+ * the call takes the prefill GEMM path (T >= 256).  Pure function; no GPU. */
+int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared);
+
 /* Top-k routing (Problem statement: each token activates a subset of the
  * experts).  logits: dev fp32 [T][E]; topk_idx: dev int32 [T][k]; topk_w: dev
  * fp32 [T][k].  Per token the k largest logits are chosen in the order
@@ -391,9 +400,9 @@ int64_t pw_resident_bytes(const pw_ctx *ctx);
  *   PW_DECODE_PATH_TILE64: the decode contraction with 64-row tiles (the
  *     decode down tiles and the gate_up half tiles);
  *   PW_DECODE_PATH_PREFILL: the prefill GEMM's weight-tile decoder;
- *   PW_DECODE_PATH_TILE64_WIDE: 64-row tiles of the 16-token passes (single
- *     tables at q = 4) that decode batches holding more than 8 tokens per
- *     expert use.
+ *   PW_DECODE_PATH_TILE64_WIDE: 64-row tiles of the 16- and 32-token passes
+ *     (single tables at q = 4) that decode batches whose fullest unit is
+ *     expected to hold more than 8 tokens use.
  * codes_out: dev uint8 [R][K] child codes; w_out: dev fp16 [R][K] weights
  * (bit patterns); either may be NULL, not both.  Asynchronous on `stream`.
  * Errors: INVALID (null outputs, unregistered block, path out of range), HIP. */

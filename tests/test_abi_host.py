@@ -121,3 +121,27 @@ def test_null_context_calls_are_invalid():
     assert L.pw_destroy(None) == pw.PW_OK
     assert L.pw_workspace_size(None, 4) == 0
     assert L.pw_block_id(None, 0, 0, 0) == -1
+
+
+# (T, top_k, E, I_shared) -> tokens per decode pass, each worked by hand from
+# the rule the header states: the largest expected unit m is T for a shared
+# expert, else a + 2 sqrt(a) with a = T top_k / E; the width is the smallest of
+# 8, 16, 32 with m <= width; 0 outside the decode path.
+@pytest.mark.parametrize("T,k,E,Is,want", [
+    (1, 2, 8, 0, 8),        # a = 0.25, m = 1.25
+    (16, 2, 8, 0, 8),       # a = 4, m = 4 + 4 = 8 (boundary: covered)
+    (24, 2, 8, 0, 16),      # a = 6, m = 6 + 4.90 = 10.90
+    (32, 2, 8, 0, 16),      # a = 8, m = 8 + 5.66 = 13.66
+    (40, 2, 8, 0, 32),      # a = 10, m = 10 + 6.32 = 16.32
+    (255, 2, 8, 0, 32),     # a = 63.75: several 32-token passes
+    (4, 4, 60, 5632, 8),    # shared expert: m = T = 4
+    (9, 4, 60, 5632, 16),   # m = 9
+    (16, 4, 60, 5632, 16),  # m = 16 (boundary: covered)
+    (17, 4, 60, 5632, 32),  # m = 17
+    (64, 4, 60, 0, 16),     # no shared expert: a = 4.27, m = 4.27 + 4.13 = 8.40
+    (0, 2, 8, 0, 0),
+    (256, 2, 8, 0, 0),      # prefill path
+    (5, 0, 8, 0, 0),        # invalid top_k
+])
+def test_decode_tokens_per_pass(T, k, E, Is, want):
+    assert pw.decode_tokens_per_pass(T, k, E, Is) == want

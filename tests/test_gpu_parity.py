@@ -27,7 +27,7 @@ def _gpu(require_gpu):
 # PagedWeight", Core components 1).  Paths: the decode contraction's 128-row
 # tiles (gate_up whole tiles; q = 3 two-set pair tables, q = 4 single tables,
 # q >= 5 bit transpose) and 64-row tiles (gate_up half tiles, down; q <= 4 pair
-# tables), 64-row tiles of 16-token passes (single tables at q = 4), and the
+# tables), 64-row tiles of 16- and 32-token passes (single tables at q = 4), and the
 # prefill decoder (per-lane rotate form).  Shapes: ragged row
 # tiles, ragged K (a last chunk of 1 or 3 words) and several chunks per K-wave.
 DECODE_SHAPES = {"ragged": (352, 224), "multi_chunk": (1056, 608)}
@@ -125,6 +125,28 @@ def test_ffn_each_width(q):
 def test_ffn_mixed_widths_ragged(T):
     w, a = pw_synth.make_small(H=352, I=224, E=5, top_k=2, T=T, seed=300 + T)
     check_layer(w, a, label="mixed T=%d" % T)
+
+
+# Each tokens-per-pass width of the decode contraction against the oracle, and
+# the multi-pass cases (units holding more tokens than a pass, plane loads kept
+# in the cache): 8 (128-row gate_up tiles, routing in the gate_up launch), 16
+# and 32 (64-row tiles; 32: two waves share one activation slice).
+@pytest.mark.parametrize("T,Is,width", [(9, 0, 8), (20, 0, 16), (33, 0, 32), (100, 0, 32),
+                                        (12, 96, 16), (40, 96, 32), (70, 96, 32)])
+def test_ffn_each_pass_width(T, Is, width):
+    import any_precision_expert_amd as pw
+    assert pw.decode_tokens_per_pass(T, 2, 5, Is) == width
+    w, a = pw_synth.make_small(H=352, I=224, E=5, top_k=2, T=T, I_shared=Is, seed=700 + T)
+    check_layer(w, a, label="T=%d Is=%d pass=%d" % (T, Is, width))
+    ctx = make_ctx(w.shape)
+    try:
+        from any_precision_expert_amd.layer import register_layer
+        register_layer(ctx, 0, w)
+        g1 = run_gpu(ctx, 0, a)
+        g2 = run_gpu(ctx, 0, a, separate=True)
+        assert np.array_equal(g1["y"], g2["y"]), "layer call and separate calls differ"
+    finally:
+        ctx.close()
 
 
 def test_ffn_single_expert_all_tokens():
