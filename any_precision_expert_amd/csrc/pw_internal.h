@@ -172,15 +172,17 @@ hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s);
 hipError_t launch_debug_decode(const BlockDesc* entry, int module, int R, int path, uint8_t* codes_out,
                                uint16_t* w_out, hipStream_t s);
 
-// One host-to-device copy of a width change (device-side addresses; src in
-// pinned host memory, bytes a multiple of 16).
+// One copy of a width change (device-side addresses, bytes a multiple of 16).
 struct CopyDesc {
     const void* src;
     void* dst;
     uint64_t bytes;
 };
-// The copies of list[0..n) (the list itself in pinned host memory), one launch.
+// The copies of list[0..n) (the list itself in pinned host memory), one
+// launch: from pinned host memory by a few workgroups (pull), or device to
+// device as a short burst over many workgroups (scatter).
 hipError_t launch_pull_copy(const CopyDesc* list, int n, hipStream_t s);
+hipError_t launch_scatter_copy(const CopyDesc* list, int n, hipStream_t s);
 // table[ids[i]] = descs[i] for i < n (ids and descs in pinned host memory).
 hipError_t launch_scatter_desc(BlockDesc* table, const int32_t* ids, const BlockDesc* descs, int n, hipStream_t s);
 

@@ -1897,37 +1897,40 @@ __global__ void __launch_bounds__(PATH == 2 ? kPfThreads : kThreads)
 
 // ---------------------------------------------------------------- width changes
 //
-// Page movement of a width change in one launch each (Core components 3:
-// pages move asynchronously, widths are committed at safe boundaries), so a
-// change of hundreds of blocks costs the host a few calls instead of one
+// Page movement of a width change (Core components 3: pages move
+// asynchronously, widths are committed at safe boundaries) in a few launches,
+// so a change of hundreds of blocks costs the host a few calls instead of one
 // copy per plane and per page-table entry.
 
-// Host-to-device copies of the new planes and LUTs: the copy list and the
-// sources are pinned host memory, read by the kernel over the host link
-// (device-side addresses); every size is a multiple of 16 bytes.  The copy is
-// bound by the host link, not by the CUs, so a few workgroups (kPullWgs)
-// take the copies round-robin with 8 x 16 bytes per thread in flight, and the
-// compute kernels running meanwhile keep nearly every CU.
+// The copies of a list (pinned host memory, read through its device-side
+// address); every size is a multiple of 16 bytes.  Two uses: the copies of a
+// blocking width change straight from the pinned host masters (bound by the
+// host link: a few workgroups, one copy each at a time), and the scatter of a
+// staging chunk that one DMA brought to the device into the new plane and LUT
+// slabs (a short burst: each copy split in `parts` byte ranges, one
+// workgroup each).  8 x 16 bytes per thread in flight.
 constexpr int kPullWgs = 16;
-__global__ void __launch_bounds__(256) pull_copy_kernel(const CopyDesc* __restrict__ list, int n)
+__global__ void __launch_bounds__(256) pull_copy_kernel(const CopyDesc* __restrict__ list, int n, int parts)
 {
     constexpr int U = 8;
-    for (int j = blockIdx.x; j < n; j += gridDim.x) {
-        const CopyDesc d = list[j];
+    for (int j = blockIdx.x; j < n * parts; j += gridDim.x) {
+        const int item = j / parts, part = j - item * parts;
+        const CopyDesc d = list[item];
         const u32x4* src = (const u32x4*)d.src;
         u32x4* dst = (u32x4*)d.dst;
         const uint64_t n16 = d.bytes / 16;
-        for (uint64_t i = threadIdx.x; i < n16; i += U * 256) {
+        const uint64_t lo = n16 * part / parts, hi = n16 * (part + 1) / parts;
+        for (uint64_t i = lo + threadIdx.x; i < hi; i += U * 256) {
             u32x4 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint64_t at = i + (uint64_t)u * 256;
-                v[u] = at < n16 ? src[at] : u32x4{0, 0, 0, 0};
+                v[u] = at < hi ? src[at] : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint64_t at = i + (uint64_t)u * 256;
-                if (at < n16) dst[at] = v[u];
+                if (at < hi) dst[at] = v[u];
             }
         }
     }
@@ -2101,7 +2104,16 @@ hipError_t launch_fill_f64(double* p, int64_t n, hipStream_t s)
 hipError_t launch_pull_copy(const CopyDesc* list, int n, hipStream_t s)
 {
     if (n <= 0) return hipSuccess;
-    launch(pull_copy_kernel, dim3((unsigned)std::min(n, kPullWgs)), dim3(256), s, list, n);
+    launch(pull_copy_kernel, dim3((unsigned)std::min(n, kPullWgs)), dim3(256), s, list, n, 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_copy(const CopyDesc* list, int n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    constexpr int kScatterWgs = 512;
+    const int parts = std::max(1, kScatterWgs / n);
+    launch(pull_copy_kernel, dim3((unsigned)std::min(n * parts, kScatterWgs)), dim3(256), s, list, n, parts);
     return hipGetLastError();
 }
 

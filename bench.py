@@ -349,6 +349,7 @@ def mixtral_decode_leg(steps, L=2):
 
 
 STACK_CFG = 4
+STACK_REQUEST_LEAD = 6
 
 
 def stack_leg():
@@ -356,9 +357,12 @@ def stack_leg():
     every 8 steps moving 20% of the routed blocks one bit, lowest routing mass
     first; odd events lower, even events raise), one HIP graph per step of 24
     pw_moe_layer calls.  Three runs from the same initial widths: no events,
-    the asynchronous events (pw_request_widths at the event, pw_commit_ready at
-    every step boundary) and the blocking events (pw_set_committed_bits before
-    the event's step).  Reports per-layer tokens/s of each run, the stall the
+    the asynchronous events (pw_request_widths planned from the routing mass
+    of the event's step and issued STACK_REQUEST_LEAD steps later, so the host
+    stays ahead of the GPU while it gathers the copies; pw_commit_ready at every
+    step boundary) and the blocking events (pw_set_committed_bits before the
+    event's step).  An untimed asynchronous run first allocates the library's
+    copy staging.  Reports per-layer tokens/s of each run, the stall the
     events add over the no-event run, the host-to-device bytes and rate of the
     plane / LUT reloads (copy-stream events around each request), and the
     overlap fraction 1 - stall / copy time of the asynchronous run.  For set-up
@@ -410,10 +414,18 @@ def stack_leg():
                                                                           round(100 * spec.extra["commit_fraction"])),
            "weights": "layer-0 codes and LUTs registered for every layer; per-layer Zipf ranks and widths"}
     times = {}
-    for mode in ("none", "async", "blocking"):
+    for mode in ("warmup", "none", "async", "blocking"):
         reset_widths()
+        lead = STACK_REQUEST_LEAD if mode in ("async", "warmup") else 0
         drv = StackDriver(ctx, q0, logits, x, commit_every=spec.extra["commit_every"],
-                          fraction=spec.extra["commit_fraction"], mode=mode)
+                          fraction=spec.extra["commit_fraction"], mode="async" if mode == "warmup" else mode,
+                          request_lead=lead)
+        if mode == "warmup":
+            drv.run()
+            drv.drain()
+            torch.cuda.synchronize()
+            del drv
+            continue
         drv.capture_graphs()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -431,6 +443,7 @@ def stack_leg():
              "events": [(e[0], "lower" if e[1] else "raise", e[2]) for e in drv.events],
              "device_allocs": ctx.pool_stats()["device_allocs"] - allocs0}
         if mode == "async":
+            r["request_lead_steps"] = lead
             copy_ms = [a.elapsed_time(b) for (_, _, _, a, b) in drv.requests]
             h2d = sum(req[2] for req in drv.requests)
             r["commits"] = drv.commits
