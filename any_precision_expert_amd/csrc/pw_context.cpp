@@ -943,7 +943,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     }
     {
         ProfScope ps(c, "gate_up", s);
-        a.rg = a.tok_pass >= 16 ? 2 : kGateUpRowGroups;
+        a.rg = a.tok_pass == 16 ? 2 : kGateUpRowGroups;
         a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         a.tiles_routed = (d.inter + 16 * a.rg - 1) / (16 * a.rg);
         a.tiles_shared = (d.inter_shared + 16 * a.rg - 1) / (16 * a.rg);

@@ -788,16 +788,18 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     // TP tokens per pass: 8, or 16 / 32 (WIDE) for launches where experts hold
     // more than 8 / 16 tokens, so each weight is decoded once per 16 / 32
     // tokens (the MFMA's B operand has 32 token columns in every case).
-    // SHARE (32-token passes): the two waves of a K range (one per row group)
-    // share one 8 KB activation slice, each loading 16 of the 32 token rows,
-    // with a workgroup barrier before and after each chunk's slice store; this
-    // keeps the registers and the LDS of 16-token passes.
+    // SHARE (32-token passes): the RG waves of a K range (one per row group)
+    // share one 8 KB activation slice, each loading 32 / RG of the 32 token
+    // rows, with a workgroup barrier before and after each chunk's slice
+    // store; this keeps the registers of 8- or 16-token passes.  64-row tiles
+    // keep their four slices in LUT space the tile does not use, 128-row
+    // tiles their two in the slice region after the LUT.
     constexpr bool WIDE = TP >= 16;
     constexpr bool SHARE = TP == 32;
-    static_assert(TP == 8 || ((TP == 16 || TP == 32) && RG == 2 && !FUSED),
-                  "16- and 32-token passes: 64-row tiles, routing outside");
+    static_assert(TP == 8 || (TP == 16 && RG == 2 && !FUSED) || (TP == 32 && !FUSED),
+                  "16-token passes: 64-row tiles; 16- and 32-token passes: routing outside");
     constexpr int D = Q <= 4 ? 2 : 1;      // chunks of plane loads in flight
-    constexpr int NLOAD = SHARE ? 16 : TP;  // token rows this wave loads per chunk
+    constexpr int NLOAD = SHARE ? 32 / RG : TP;  // token rows this wave loads per chunk
     constexpr int NPART = NLOAD / 4;       // activation loads per lane and chunk
     constexpr int SB = TP * 256;           // bytes of a slice (TP token rows x 256 B)
     constexpr int KW = kWaves / RG;        // waves per row group (K split)
@@ -832,13 +834,30 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
     // else rows 128..255 (2^q <= 128 single entries, or 64 rows of the q = 3
     // pair table).
     char* const ldsb = (char*)lds;
+    // Double-buffered shared slices (one barrier per chunk: a chunk's store
+    // goes to the buffer every wave finished reading before the previous
+    // chunk's barrier): 128-row tiles below q = 8 keep both buffers' two
+    // slices in LUT rows 128..255 (a table of <= 128 entries leaves them
+    // free); 64-row tiles up to q = 6 keep buffer 0's four slices in rows
+    // 128..255 and buffer 1's in the slice region after the LUT (slices 0, 1)
+    // and rows 64..127 (slices 2, 3; tables of <= 64 entries).  The others
+    // keep one buffer and a second barrier.
+    constexpr bool DBUF4 = SHARE && RG == 4 && Q < 8;
+    constexpr bool DBUF2 = SHARE && RG == 2 && Q <= 6;
+    constexpr bool DBUF = DBUF4 || DBUF2;
+    int sbuf = 0;  // DBUF: this chunk's buffer
     auto slice_at = [&](int w, int b) -> char* {
-        if constexpr (!WIDE) return ldsb + kLutBytes + w * (kSliceWords * 4) + b;
+        if constexpr (DBUF4) return ldsb + 32768 + (2 * sbuf + w) * SB + b;
+        else if constexpr (DBUF2) {
+            if (sbuf == 0) return ldsb + 32768 + w * SB + b;
+            return w < 2 ? ldsb + kLutBytes + w * SB + b : ldsb + 16384 + (w - 2) * SB + b;
+        } else if constexpr (SHARE && RG == 4) return ldsb + kLutBytes + w * SB + b;
+        else if constexpr (!WIDE) return ldsb + kLutBytes + w * (kSliceWords * 4) + b;
         else if constexpr (Q == 8) return ldsb + (((((SB / 128) * w + (b >> 7)) << 8) | 128) | (b & 127));
         else return ldsb + 32768 + w * SB + b;
     };
     const int sl = SHARE ? kw : wave;  // this wave's activation slice
-    const int tb = SHARE ? 16 * grp : 0;  // first slice row this wave loads
+    const int tb = SHARE ? (32 / RG) * grp : 0;  // first slice row this wave loads
     const uint32_t lane_off = tl.lane_off;
     const char* lutb = (const char*)lds;
     WordDecoder<Q, RG, WIDE> dec;
@@ -940,13 +959,14 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 // this chunk's activations -> the wave's slice (zero past K and
                 // in padding chunks)
                 const bool ok = live && c * kChunkCols + 8 * xg < K;
-                if constexpr (SHARE) __syncthreads();  // the partner wave has read the slice's last chunk
+                if constexpr (DBUF) sbuf = ci & 1;
+                if constexpr (SHARE && !DBUF) __syncthreads();  // the partner waves have read the slice's last chunk
 #pragma unroll
                 for (int pp = 0; pp < NPART; ++pp) {
                     const int j = tb + 4 * pp + xt;
                     *(u32x4*)slice_at(sl, 16 * slice_unit(j, j, xg)) = ok ? xv[pp] : u32x4{0, 0, 0, 0};
                 }
-                if constexpr (SHARE) __syncthreads();  // both halves of this chunk's tokens are in the slice
+                if constexpr (SHARE) __syncthreads();  // every part of this chunk's tokens is in the slice
                 // prefetch: next chunk's activations, then the planes D chunks on
                 u32x2 cur[Q];
 #pragma unroll
@@ -991,13 +1011,32 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
 
         // cross-wave reduction through the slices: wave w's partial of (row r,
         // token n) at byte 4 (r TP + n) of its slice (SHARE: of half w % 2 of
-        // slice w / 2)
+        // slice w / 2).  SHARE with 128-row tiles sums in two phases in the
+        // 16 KB slice region (row group g's sums at 4 KB g): the partials of
+        // K-wave 1, then K-wave 0 adds its own (the same order and rounding as
+        // the one-phase sum 0 + p0 + p1).
+        static_assert(!(SHARE && RG == 4) || KW == 2, "two-phase sum of two K-waves");
+        sbuf = 0;  // the 64-row tiles' reduction uses buffer 0's contiguous 32 KB
+        auto red4 = [&](int g, int r, int n) -> float* { return (float*)(ldsb + kLutBytes + 4096 * g + 4 * (r * 32 + n)); };
         __syncthreads();
         auto red = [&](int w, int r, int n) -> float* {
             if constexpr (SHARE) return (float*)slice_at(w >> 1, 4096 * (w & 1) + 4 * (r * TP + n));
             else return (float*)slice_at(w, 4 * (r * TP + n));
         };
-        if (nvalid) {
+        if constexpr (SHARE && RG == 4) {
+            if (nvalid && kw == 1) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) *red4(grp, 8 * (i >> 2) + 4 * kh + (i & 3), rho) = C[i];
+            }
+            __syncthreads();
+            if (nvalid && kw == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float* p = red4(grp, 8 * (i >> 2) + 4 * kh + (i & 3), rho);
+                    *p = C[i] + *p;
+                }
+            }
+        } else if (nvalid) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = 8 * (i >> 2) + 4 * kh + (i & 3);
@@ -1010,10 +1049,15 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 const int hr = idx / nt, n = idx - hr * nt;
                 const int sub = hr >> 5, r = hr & 31;
                 float g = 0.0f, u = 0.0f;
+                if constexpr (SHARE && RG == 4) {
+                    g = *red4(sub, r, n);
+                    u = *red4(RG / 2 + sub, r, n);
+                } else {
 #pragma unroll
-                for (int w = 0; w < KW; ++w) {
-                    g += *red(sub * KW + w, r, n);
-                    u += *red((RG / 2 + sub) * KW + w, r, n);
+                    for (int w = 0; w < KW; ++w) {
+                        g += *red(sub * KW + w, r, n);
+                        u += *red((RG / 2 + sub) * KW + w, r, n);
+                    }
                 }
                 const int i = tile * HR + hr;
                 if (i < Iblk) {
@@ -1027,8 +1071,12 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 const int rt = idx / nt, n = idx - rt * nt;
                 const int g = rt >> 5, r = rt & 31;
                 float d = 0.0f;
+                if constexpr (SHARE && RG == 4) {
+                    d = *red4(g, r, n);
+                } else {
 #pragma unroll
-                for (int w = 0; w < KW; ++w) d += *red(g * KW + w, r, n);
+                    for (int w = 0; w < KW; ++w) d += *red(g * KW + w, r, n);
+                }
                 const int orow_r = tile * TR + rt;
                 if (orow_r < R) {
                     const int orow = shared ? TK + t0 + n : a.sorted[p0 + t0 + n];
@@ -1284,7 +1332,7 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
         case 8: mfma_block<MODE, 8, RGX, FUSED, KEEP, TP>(ka, bd, shared, p0, ntok, TILE, split, nsplit, lds, tokreg); break; \
         default: break;                                                                                          \
     }
-    if constexpr (RG == 4 && TP == 8) {
+    if constexpr (RG == 4) {
         if (half >= 0) {
             const int t2 = 2 * tile + half;
             PW_GEMV_CASES(2, t2)
@@ -2021,9 +2069,14 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s)
     const int grid = gemv_grid(a);
     if (grid == 0) return hipSuccess;
     if (a.tok_pass == 16 || a.tok_pass == 32) {
-        if (a.rg != 2 || a.logits) return hipErrorInvalidValue;
+        if (a.logits || (a.tok_pass == 16 && a.rg != 2)) return hipErrorInvalidValue;
         if (a.tok_pass == 32) {
-            if (a.keep_planes)
+            if (a.rg == 4) {
+                if (a.keep_planes)
+                    launch((ffn_gemv_kernel<0, 4, false, true, 32>), dim3(grid), dim3(kThreads), s, a);
+                else
+                    launch((ffn_gemv_kernel<0, 4, false, false, 32>), dim3(grid), dim3(kThreads), s, a);
+            } else if (a.keep_planes)
                 launch((ffn_gemv_kernel<0, 2, false, true, 32>), dim3(grid), dim3(kThreads), s, a);
             else
                 launch((ffn_gemv_kernel<0, 2, false, false, 32>), dim3(grid), dim3(kThreads), s, a);
