@@ -28,7 +28,7 @@ LUT_HALVES_PER_ROW = sum(1 << k for k in range(QMIN, QMAX + 1))
 # every function declared in include/pw.h
 EXPORTS = (
     "pw_last_error", "pw_create", "pw_destroy", "pw_pack_bitplanes", "pw_plane_words",
-    "pw_register_block", "pw_workspace_size", "pw_decode_tokens_per_pass", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
+    "pw_register_block", "pw_workspace_size", "pw_decode_tokens_per_pass", "pw_set_tokens_per_pass", "pw_route_topk", "pw_permute_by_expert", "pw_route_permute",
     "pw_moe_ffn_bitplane", "pw_moe_layer", "pw_moe_layer_noalloc", "pw_routing_mass_enable", "pw_routing_mass_reset",
     "pw_routing_mass_read", "pw_plan_widths", "pw_request_widths", "pw_commit_ready", "pw_block_state",
     "pw_set_committed_bits", "pw_get_committed_bits", "pw_block_id", "pw_plane_states", "pw_committed_widths",
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.pw_workspace_size.restype = sz
         L.pw_decode_tokens_per_pass.argtypes = [ctypes.c_int] * 4
         L.pw_decode_tokens_per_pass.restype = i32
+        L.pw_set_tokens_per_pass.argtypes = [vp, ctypes.c_int]
         L.pw_route_topk.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
         L.pw_permute_by_expert.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp]
         L.pw_route_permute.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
@@ -242,6 +243,11 @@ class Context:
     # hot path -----------------------------------------------------------
     def workspace_size(self, T: int) -> int:
         return int(lib().pw_workspace_size(self.h, T))
+
+    def set_tokens_per_pass(self, tokens: int) -> None:
+        """pw_set_tokens_per_pass: 8, 16 or 32 tokens per decode pass for this
+        context's later calls, 0 for the per-call choice."""
+        _check(lib().pw_set_tokens_per_pass(self.h, tokens))
 
     def route_topk(self, logits, T: int, topk_idx, topk_w, stream=None) -> None:
         _check(lib().pw_route_topk(self.h, _ptr(logits), T, _ptr(topk_idx), _ptr(topk_w), _stream(stream)))

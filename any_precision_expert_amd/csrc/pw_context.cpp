@@ -447,6 +447,7 @@ struct pw_ctx {
     uint64_t chunk_uses = 0;
     std::unique_ptr<Gang> gang;      // gather threads, started with the first width change
     int num_cus = 256;  // compute units of the device (decode tile schedule)
+    int tok_pass = 0;   // decode tokens per pass set by pw_set_tokens_per_pass (0: chosen per call)
     void* scratch = nullptr;  // this device's library-held workspace (pw_moe_layer_noalloc)
     std::map<int, WidthChange> pending;  // width requests whose commit has not happened
     double* d_mass = nullptr;  // routing-mass accumulator [L][E] fp64 (pw_routing_mass_enable)
@@ -779,6 +780,15 @@ size_t pw_workspace_size(const pw_ctx* c, int T)
     return ws_layout(T, c->d.top_k, c->d.hidden, c->d.inter, c->d.inter_shared).total;
 }
 
+pw_status pw_set_tokens_per_pass(pw_ctx* c, int tokens)
+{
+    if (!c) return fail(PW_ERR_INVALID, "pw_set_tokens_per_pass: null context");
+    if (tokens != 0 && tokens != 8 && tokens != 16 && tokens != 32)
+        return fail(PW_ERR_INVALID, "pw_set_tokens_per_pass: %d is not 0, 8, 16 or 32", tokens);
+    c->tok_pass = tokens;
+    return ok();
+}
+
 int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared)
 {
     if (T <= 0 || T >= kPrefillMinT || top_k <= 0 || E <= 0) return 0;
@@ -910,7 +920,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     a.E = E;
     a.k = d.top_k;
     a.n_slots = std::min(E, T * d.top_k);
-    a.tok_pass = decode_tok_pass(T, d.top_k, E, d.inter_shared);
+    a.tok_pass = c->tok_pass ? c->tok_pass : decode_tok_pass(T, d.top_k, E, d.inter_shared);
     a.keep_planes = keep_planes(T, d.top_k, E, d.inter_shared, a.tok_pass) ? 1 : 0;
     a.hstride = std::max(d.inter, d.inter_shared);
     a.drows = T * d.top_k + (d.inter_shared ? T : 0);
@@ -1010,7 +1020,7 @@ pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t
                                std::min<long long>(d.num_experts, n) * ((d.inter + gu_rows - 1) / gu_rows);
     double* mass = c->mass_on ? c->d_mass + (size_t)layer * d.num_experts : nullptr;
     if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus ||
-        decode_tok_pass(T, d.top_k, d.num_experts, d.inter_shared) != 8) {
+        (c->tok_pass ? c->tok_pass : decode_tok_pass(T, d.top_k, d.num_experts, d.inter_shared)) != 8) {
         // the separate routing launch, then the FFN (identical results)
         st = pw_route_permute(c, logits, T, idx, w, offsets, sorted, stream);
         if (st != PW_OK || T == 0) return st;

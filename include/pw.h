@@ -139,6 +139,14 @@ size_t pw_workspace_size(const pw_ctx *ctx, int T);
  * the call takes the prefill GEMM path (T >= 256).  Pure function; no GPU. */
 int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared);
 
+/* Fix the decode contraction's tokens per pass of this context's later calls
+ * to 8, 16 or 32 (0: chosen per call as pw_decode_tokens_per_pass states),
+ * for callers that know their batches' spread over the experts better than
+ * that estimate.  Results do not depend on it beyond rounding: 8- and
+ * 32-token passes give bit-identical y, 16-token passes split K over four
+ * waves of 64-row gate_up tiles instead of two.  Errors: INVALID. */
+pw_status pw_set_tokens_per_pass(pw_ctx *ctx, int tokens);
+
 /* Top-k routing (Problem statement: each token activates a subset of the
  * experts).  logits: dev fp32 [T][E]; topk_idx: dev int32 [T][k]; topk_w: dev
  * fp32 [T][k].  Per token the k largest logits are chosen in the order

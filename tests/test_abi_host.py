@@ -118,6 +118,7 @@ def test_null_context_calls_are_invalid():
     assert L.pw_routing_mass_read(None, None, None) == pw.PW_ERR_INVALID
     assert L.pw_plan_widths(1, 1, 32, 32, None, None, None, None, 0, None, None) == pw.PW_ERR_INVALID
     assert L.pw_set_committed_bits(None, 1, None, None, None, None) == pw.PW_ERR_INVALID
+    assert L.pw_set_tokens_per_pass(None, 8) == pw.PW_ERR_INVALID
     assert L.pw_destroy(None) == pw.PW_OK
     assert L.pw_workspace_size(None, 4) == 0
     assert L.pw_block_id(None, 0, 0, 0) == -1

@@ -152,6 +152,31 @@ def test_ffn_each_pass_width(T, Is, width):
         ctx.close()
 
 
+# Forced pass widths (pw_set_tokens_per_pass) on one layer: 8- and 32-token
+# passes run the same K split on the same tiles, so y is bit-identical; every
+# width stays within tolerance of the oracle.
+@pytest.mark.parametrize("T,Is", [(40, 0), (70, 0), (20, 96), (45, 96)])
+def test_forced_pass_widths(T, Is):
+    import oracle
+    from any_precision_expert_amd.layer import register_layer
+    w, a = pw_synth.make_small(H=352, I=224, E=8, top_k=2, T=T, I_shared=Is, seed=800 + T + Is)
+    ref = oracle.moe_layer(w, a)
+    ctx = make_ctx(w.shape)
+    try:
+        register_layer(ctx, 0, w)
+        import any_precision_expert_amd as pw
+        assert pw.lib().pw_set_tokens_per_pass(ctx.h, 12) == pw.PW_ERR_INVALID
+        ys = {}
+        for tp in (8, 16, 32, 0):
+            ctx.set_tokens_per_pass(tp)
+            g = run_gpu(ctx, 0, a)
+            compare(g, ref, label="T=%d Is=%d forced %d" % (T, Is, tp))
+            ys[tp] = g["y"]
+        assert np.array_equal(ys[8], ys[32]), "8- and 32-token passes differ"
+    finally:
+        ctx.close()
+
+
 def test_ffn_single_expert_all_tokens():
     w, a = pw_synth.make_small(H=256, I=128, E=1, top_k=1, T=11, seed=401)
     check_layer(w, a, label="E=1")
