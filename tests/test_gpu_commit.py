@@ -254,3 +254,41 @@ def test_copy_and_update_events_are_recycled():
         assert created <= 8
     finally:
         ctx.close()
+
+
+def test_staged_copies_beyond_the_chunk_ring():
+    """One pw_request_widths raising twelve Mixtral-sized blocks (6 experts x
+    gate_up / down, H = 4096, I = 14336) from q = 3 to 8 moves ~760 MB of
+    planes and LUTs through the library's staging (16 chunks of 32 MB), so
+    chunks are reused within the call after their scatter completes.  After
+    the commit every block decodes to its parent codes bit for bit (code8 >>
+    (8 - q) at q = 8, "Technical summary: PagedWeight", Core components 1)."""
+    import torch
+    import any_precision_expert_amd as pw
+    E, H, I = 6, 4096, 14336
+    ctx = pw.Context(0, 1, E, H, I, 2, 0)
+    try:
+        rng = np.random.default_rng(901)
+        codes = {}
+        for e in range(E):
+            for m in (0, 1):
+                R, K = (2 * I, H) if m == 0 else (H, I)
+                c = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
+                luts = {k: np.zeros((R, 1 << k), np.float16) for k in range(3, 9)}  # unused by the check
+                ctx.register_block(0, e, m, pw.pack_bitplanes(c), pw.concat_luts(luts), 3)
+                codes[(e, m)] = c
+        ids = [ctx.block_id(0, e, m) for e in range(E) for m in (0, 1)]
+        compute, copy_stream = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        ctx.request_widths(ids, [8] * len(ids), copy_stream)
+        copy_stream.synchronize()
+        assert ctx.commit_ready(compute) == len(ids)
+        compute.synchronize()
+        for (e, m), c in codes.items():
+            out = torch.empty(c.shape, dtype=torch.uint8, device="cuda")
+            ctx.debug_decode_codes(ctx.block_id(0, e, m), out)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), c), "expert %d module %d" % (e, m)
+        say("staged raise of %d blocks: resident %.2f GB" % (len(ids), ctx.resident_bytes() / 1e9))
+    finally:
+        ctx.close()
