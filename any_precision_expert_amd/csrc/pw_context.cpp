@@ -51,6 +51,24 @@ pw_status hip_fail(hipError_t e, const char* what)
     return fail(PW_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+
+// Entry points return statuses, never exceptions: a C++ exception (host
+// memory exhausted in a container, a thread that cannot start) becomes OOM or
+// INVALID with a message instead of unwinding into a C caller.
+template <class F>
+pw_status guarded(const char* fn, F&& body)
+{
+    try {
+        return body();
+    } catch (const std::bad_alloc&) {
+        return fail(PW_ERR_OOM, "%s: host memory exhausted", fn);
+    } catch (const std::exception& e) {
+        return fail(PW_ERR_INVALID, "%s: %s", fn, e.what());
+    } catch (...) {
+        return fail(PW_ERR_INVALID, "%s: unexpected exception", fn);
+    }
+}
+
 pw_status ok()
 {
     g_err.clear();
@@ -422,6 +440,10 @@ struct ProfRec {
 namespace pw {
 // error path of the host planner (pw_planner.cpp): the thread-local message
 pw_status plan_fail(const char* msg) { return fail(PW_ERR_INVALID, "%s", msg); }
+pw_status plan_exception(const char* fn, bool oom)
+{
+    return oom ? fail(PW_ERR_OOM, "%s: host memory exhausted", fn) : fail(PW_ERR_INVALID, "%s: unexpected exception", fn);
+}
 }  // namespace pw
 
 struct pw_ctx {
@@ -609,81 +631,87 @@ int64_t pw_plane_words(int64_t R, int64_t K) { return (R > 0 && K > 0) ? plane_w
 
 pw_status pw_pack_bitplanes(const uint8_t* codes, int64_t R, int64_t K, uint32_t* planes)
 {
-    if (!codes || !planes) return fail(PW_ERR_INVALID, "pw_pack_bitplanes: null pointer");
-    if (R <= 0 || K <= 0 || K % 32 != 0 || R > (1 << 24) || K > (1 << 24))
-        return fail(PW_ERR_INVALID, "pw_pack_bitplanes: need R > 0 and K a positive multiple of 32 (R=%lld K=%lld)",
-                    (long long)R, (long long)K);
-    pack_bitplanes(codes, R, K, planes);
-    return ok();
+    return guarded("pw_pack_bitplanes", [&]() -> pw_status {
+        if (!codes || !planes) return fail(PW_ERR_INVALID, "pw_pack_bitplanes: null pointer");
+        if (R <= 0 || K <= 0 || K % 32 != 0 || R > (1 << 24) || K > (1 << 24))
+            return fail(PW_ERR_INVALID, "pw_pack_bitplanes: need R > 0 and K a positive multiple of 32 (R=%lld K=%lld)",
+                        (long long)R, (long long)K);
+        pack_bitplanes(codes, R, K, planes);
+        return ok();
+    });
 }
 
 pw_status pw_create(pw_ctx** out, int hip_device, const pw_model_desc* d)
 {
-    if (!out || !d) return fail(PW_ERR_INVALID, "pw_create: null pointer");
-    *out = nullptr;
-    const bool shape_ok = d->num_layers >= 1 && d->num_layers <= 4096 && d->num_experts >= 1 &&
-                          d->num_experts <= 256 && d->hidden >= 32 && d->hidden <= 32768 &&
-                          d->hidden % 32 == 0 && d->inter >= 32 && d->inter <= 131072 && d->inter % 32 == 0 &&
-                          d->inter_shared >= 0 && d->inter_shared <= 131072 && d->inter_shared % 32 == 0 &&
-                          d->top_k >= 1 && d->top_k <= 8 && d->top_k <= d->num_experts;
-    if (!shape_ok) return fail(PW_ERR_INVALID, "pw_create: model description out of range");
-    int ndev = 0;
-    hipError_t e = hipGetDeviceCount(&ndev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
-    if (hip_device < 0 || hip_device >= ndev) return fail(PW_ERR_INVALID, "pw_create: no HIP device %d", hip_device);
-    e = hipSetDevice(hip_device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    pw_ctx* c = new (std::nothrow) pw_ctx();
-    if (!c) return fail(PW_ERR_OOM, "pw_create: host allocation");
-    c->device = hip_device;
-    c->d = *d;
-    c->nblocks = d->num_layers * (d->num_experts + 1) * 2;
-    c->h_table.assign(c->nblocks, BlockDesc{});
-    c->blocks.assign(c->nblocks, HostBlock{});
-    e = hipMalloc(&c->d_table, sizeof(BlockDesc) * c->nblocks);
-    if (e != hipSuccess) {
-        delete c;
-        return fail(PW_ERR_OOM, "pw_create: page table: %s", hipGetErrorString(e));
-    }
-    e = hipMemset(c->d_table, 0, sizeof(BlockDesc) * c->nblocks);
-    if (e != hipSuccess) {
-        (void)hipFree(c->d_table);
-        delete c;
-        return hip_fail(e, "hipMemset(page table)");
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess && cus > 0)
-        c->num_cus = cus;
-    // device address of the library-held workspace, with this device current
-    e = static_scratch(hip_device, &c->scratch);
-    if (e != hipSuccess) {
-        (void)hipFree(c->d_table);
-        delete c;
-        return hip_fail(e, "pw_create: static scratch address");
-    }
-    *out = c;
-    return ok();
+    return guarded("pw_create", [&]() -> pw_status {
+        if (!out || !d) return fail(PW_ERR_INVALID, "pw_create: null pointer");
+        *out = nullptr;
+        const bool shape_ok = d->num_layers >= 1 && d->num_layers <= 4096 && d->num_experts >= 1 &&
+                              d->num_experts <= 256 && d->hidden >= 32 && d->hidden <= 32768 &&
+                              d->hidden % 32 == 0 && d->inter >= 32 && d->inter <= 131072 && d->inter % 32 == 0 &&
+                              d->inter_shared >= 0 && d->inter_shared <= 131072 && d->inter_shared % 32 == 0 &&
+                              d->top_k >= 1 && d->top_k <= 8 && d->top_k <= d->num_experts;
+        if (!shape_ok) return fail(PW_ERR_INVALID, "pw_create: model description out of range");
+        int ndev = 0;
+        hipError_t e = hipGetDeviceCount(&ndev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+        if (hip_device < 0 || hip_device >= ndev) return fail(PW_ERR_INVALID, "pw_create: no HIP device %d", hip_device);
+        e = hipSetDevice(hip_device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        pw_ctx* c = new (std::nothrow) pw_ctx();
+        if (!c) return fail(PW_ERR_OOM, "pw_create: host allocation");
+        c->device = hip_device;
+        c->d = *d;
+        c->nblocks = d->num_layers * (d->num_experts + 1) * 2;
+        c->h_table.assign(c->nblocks, BlockDesc{});
+        c->blocks.assign(c->nblocks, HostBlock{});
+        e = hipMalloc(&c->d_table, sizeof(BlockDesc) * c->nblocks);
+        if (e != hipSuccess) {
+            delete c;
+            return fail(PW_ERR_OOM, "pw_create: page table: %s", hipGetErrorString(e));
+        }
+        e = hipMemset(c->d_table, 0, sizeof(BlockDesc) * c->nblocks);
+        if (e != hipSuccess) {
+            (void)hipFree(c->d_table);
+            delete c;
+            return hip_fail(e, "hipMemset(page table)");
+        }
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess && cus > 0)
+            c->num_cus = cus;
+        // device address of the library-held workspace, with this device current
+        e = static_scratch(hip_device, &c->scratch);
+        if (e != hipSuccess) {
+            (void)hipFree(c->d_table);
+            delete c;
+            return hip_fail(e, "pw_create: static scratch address");
+        }
+        *out = c;
+        return ok();
+    });
 }
 
 static void free_chunk(StageChunk& ch);
 
 pw_status pw_destroy(pw_ctx* c)
 {
-    if (!c) return ok();
-    (void)hipSetDevice(c->device);
-    (void)hipDeviceSynchronize();
-    prof_release(c);
-    for (auto& b : c->blocks)
-        if (b.registered) free_block_now(c, b);
-    for (auto& s : c->staging) (void)hipHostFree(s.p);
-    c->gang.reset();
-    for (auto& ch : c->chunks) free_chunk(ch);
-    c->pool.clear();
-    c->evs.clear();
-    (void)hipFree(c->d_table);
-    if (c->d_mass) (void)hipFree(c->d_mass);
-    delete c;
-    return ok();
+    return guarded("pw_destroy", [&]() -> pw_status {
+        if (!c) return ok();
+        (void)hipSetDevice(c->device);
+        (void)hipDeviceSynchronize();
+        prof_release(c);
+        for (auto& b : c->blocks)
+            if (b.registered) free_block_now(c, b);
+        for (auto& s : c->staging) (void)hipHostFree(s.p);
+        c->gang.reset();
+        for (auto& ch : c->chunks) free_chunk(ch);
+        c->pool.clear();
+        c->evs.clear();
+        (void)hipFree(c->d_table);
+        if (c->d_mass) (void)hipFree(c->d_mass);
+        delete c;
+        return ok();
+    });
 }
 
 int32_t pw_block_id(const pw_ctx* c, int layer, int expert, int module)
@@ -694,84 +722,86 @@ int32_t pw_block_id(const pw_ctx* c, int layer, int expert, int module)
 pw_status pw_register_block(pw_ctx* c, int layer, int expert, int module, const uint32_t* host_planes,
                             const uint16_t* host_luts, int q_init)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_register_block: null context");
-    const int id = block_id(c, layer, expert, module);
-    if (id < 0) return fail(PW_ERR_INVALID, "pw_register_block: (layer %d, expert %d, module %d) out of range",
-                            layer, expert, module);
-    if (!host_planes || !host_luts) return fail(PW_ERR_INVALID, "pw_register_block: null pointer");
-    if (c->pending.count(id)) return fail(PW_ERR_STATE, "pw_register_block: block has a width request in flight");
-    if (q_init < PW_QMIN || q_init > PW_QMAX) return fail(PW_ERR_INVALID, "pw_register_block: q_init %d not in 3..8", q_init);
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    int R, K;
-    block_shape(c, id, &R, &K);
-    HostBlock nb;
-    nb.R = R;
-    nb.K = K;
-    nb.q = q_init;
-    nb.S = lut_slots(R, module);
-    nb.pw = plane_words(R, K);
-    const size_t plane_b = (size_t)nb.pw * 4;
-    const size_t luts_b = lut_offset_words(nb.S, PW_QMAX + 1) * 4;  // LUT_3..LUT_8, slot layout
-    auto undo = [&]() {
-        for (int p = 0; p < 8; ++p) c->pool.release_now(nb.dplanes[p], plane_b, p);
-        c->pool.release_now(nb.dlut, lut_bytes(nb.S, q_init), SlabPool::kLutTag);
-        if (nb.hplanes) (void)hipHostFree(nb.hplanes);
-        if (nb.hluts) (void)hipHostFree(nb.hluts);
-    };
-    for (int p = 0; p < q_init; ++p) {
-        if ((e = c->pool.alloc(plane_b, p, &nb.dplanes[p])) != hipSuccess) {
-            undo();
-            return fail(PW_ERR_OOM, "pw_register_block: device plane: %s", hipGetErrorString(e));
+    return guarded("pw_register_block", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_register_block: null context");
+        const int id = block_id(c, layer, expert, module);
+        if (id < 0) return fail(PW_ERR_INVALID, "pw_register_block: (layer %d, expert %d, module %d) out of range",
+                                layer, expert, module);
+        if (!host_planes || !host_luts) return fail(PW_ERR_INVALID, "pw_register_block: null pointer");
+        if (c->pending.count(id)) return fail(PW_ERR_STATE, "pw_register_block: block has a width request in flight");
+        if (q_init < PW_QMIN || q_init > PW_QMAX) return fail(PW_ERR_INVALID, "pw_register_block: q_init %d not in 3..8", q_init);
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        int R, K;
+        block_shape(c, id, &R, &K);
+        HostBlock nb;
+        nb.R = R;
+        nb.K = K;
+        nb.q = q_init;
+        nb.S = lut_slots(R, module);
+        nb.pw = plane_words(R, K);
+        const size_t plane_b = (size_t)nb.pw * 4;
+        const size_t luts_b = lut_offset_words(nb.S, PW_QMAX + 1) * 4;  // LUT_3..LUT_8, slot layout
+        auto undo = [&]() {
+            for (int p = 0; p < 8; ++p) c->pool.release_now(nb.dplanes[p], plane_b, p);
+            c->pool.release_now(nb.dlut, lut_bytes(nb.S, q_init), SlabPool::kLutTag);
+            if (nb.hplanes) (void)hipHostFree(nb.hplanes);
+            if (nb.hluts) (void)hipHostFree(nb.hluts);
+        };
+        for (int p = 0; p < q_init; ++p) {
+            if ((e = c->pool.alloc(plane_b, p, &nb.dplanes[p])) != hipSuccess) {
+                undo();
+                return fail(PW_ERR_OOM, "pw_register_block: device plane: %s", hipGetErrorString(e));
+            }
         }
-    }
-    if ((e = c->pool.alloc(lut_bytes(nb.S, q_init), SlabPool::kLutTag, &nb.dlut)) != hipSuccess) {
-        undo();
-        return fail(PW_ERR_OOM, "pw_register_block: device LUT: %s", hipGetErrorString(e));
-    }
-    if (c->d.keep_host_masters) {
-        if (hipHostMalloc((void**)&nb.hplanes, plane_b * 8, hipHostMallocDefault) != hipSuccess ||
-            hipHostMalloc((void**)&nb.hluts, luts_b, hipHostMallocDefault) != hipSuccess) {
+        if ((e = c->pool.alloc(lut_bytes(nb.S, q_init), SlabPool::kLutTag, &nb.dlut)) != hipSuccess) {
+            undo();
+            return fail(PW_ERR_OOM, "pw_register_block: device LUT: %s", hipGetErrorString(e));
+        }
+        if (c->d.keep_host_masters) {
+            if (hipHostMalloc((void**)&nb.hplanes, plane_b * 8, hipHostMallocDefault) != hipSuccess ||
+                hipHostMalloc((void**)&nb.hluts, luts_b, hipHostMallocDefault) != hipSuccess) {
+                (void)hipGetLastError();
+                undo();
+                return fail(PW_ERR_OOM, "pw_register_block: pinned host master");
+            }
+            void *dvp = nullptr, *dvl = nullptr;
+            if (hipHostGetDevicePointer(&dvp, nb.hplanes, 0) == hipSuccess &&
+                hipHostGetDevicePointer(&dvl, nb.hluts, 0) == hipSuccess) {
+                nb.dv_hplanes = (const uint32_t*)dvp;
+                nb.dv_hluts = (const uint32_t*)dvl;
+            }
             (void)hipGetLastError();
+            std::memcpy(nb.hplanes, host_planes, plane_b * 8);
+            for (int q = PW_QMIN; q <= PW_QMAX; ++q)
+                convert_lut(host_luts, R, module, q, nb.hluts + lut_offset_words(nb.S, q));
+        }
+        for (int p = 0; p < q_init && e == hipSuccess; ++p)
+            e = hipMemcpy(nb.dplanes[p], host_planes + (size_t)p * nb.pw, plane_b, hipMemcpyHostToDevice);
+        if (e == hipSuccess) {
+            std::vector<uint32_t> lq(lut_bytes(nb.S, q_init) / 4);
+            convert_lut(host_luts, R, module, q_init, lq.data());
+            e = hipMemcpy(nb.dlut, lq.data(), lut_bytes(nb.S, q_init), hipMemcpyHostToDevice);
+        }
+        if (e != hipSuccess) {
             undo();
-            return fail(PW_ERR_OOM, "pw_register_block: pinned host master");
+            return hip_fail(e, "pw_register_block: copy to device");
         }
-        void *dvp = nullptr, *dvl = nullptr;
-        if (hipHostGetDevicePointer(&dvp, nb.hplanes, 0) == hipSuccess &&
-            hipHostGetDevicePointer(&dvl, nb.hluts, 0) == hipSuccess) {
-            nb.dv_hplanes = (const uint32_t*)dvp;
-            nb.dv_hluts = (const uint32_t*)dvl;
+        nb.registered = true;
+        BlockDesc desc = make_desc(nb);
+        e = hipMemcpy(c->d_table + id, &desc, sizeof desc, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            undo();
+            return hip_fail(e, "pw_register_block: page-table entry");
         }
-        (void)hipGetLastError();
-        std::memcpy(nb.hplanes, host_planes, plane_b * 8);
-        for (int q = PW_QMIN; q <= PW_QMAX; ++q)
-            convert_lut(host_luts, R, module, q, nb.hluts + lut_offset_words(nb.S, q));
-    }
-    for (int p = 0; p < q_init && e == hipSuccess; ++p)
-        e = hipMemcpy(nb.dplanes[p], host_planes + (size_t)p * nb.pw, plane_b, hipMemcpyHostToDevice);
-    if (e == hipSuccess) {
-        std::vector<uint32_t> lq(lut_bytes(nb.S, q_init) / 4);
-        convert_lut(host_luts, R, module, q_init, lq.data());
-        e = hipMemcpy(nb.dlut, lq.data(), lut_bytes(nb.S, q_init), hipMemcpyHostToDevice);
-    }
-    if (e != hipSuccess) {
-        undo();
-        return hip_fail(e, "pw_register_block: copy to device");
-    }
-    nb.registered = true;
-    BlockDesc desc = make_desc(nb);
-    e = hipMemcpy(c->d_table + id, &desc, sizeof desc, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        undo();
-        return hip_fail(e, "pw_register_block: page-table entry");
-    }
-    if (c->blocks[id].registered) {
-        (void)hipDeviceSynchronize();
-        free_block_now(c, c->blocks[id]);
-    }
-    c->blocks[id] = nb;
-    c->h_table[id] = desc;
-    return ok();
+        if (c->blocks[id].registered) {
+            (void)hipDeviceSynchronize();
+            free_block_now(c, c->blocks[id]);
+        }
+        c->blocks[id] = nb;
+        c->h_table[id] = desc;
+        return ok();
+    });
 }
 
 size_t pw_workspace_size(const pw_ctx* c, int T)
@@ -782,11 +812,13 @@ size_t pw_workspace_size(const pw_ctx* c, int T)
 
 pw_status pw_set_tokens_per_pass(pw_ctx* c, int tokens)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_set_tokens_per_pass: null context");
-    if (tokens != 0 && tokens != 8 && tokens != 16 && tokens != 32)
-        return fail(PW_ERR_INVALID, "pw_set_tokens_per_pass: %d is not 0, 8, 16 or 32", tokens);
-    c->tok_pass = tokens;
-    return ok();
+    return guarded("pw_set_tokens_per_pass", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_set_tokens_per_pass: null context");
+        if (tokens != 0 && tokens != 8 && tokens != 16 && tokens != 32)
+            return fail(PW_ERR_INVALID, "pw_set_tokens_per_pass: %d is not 0, 8, 16 or 32", tokens);
+        c->tok_pass = tokens;
+        return ok();
+    });
 }
 
 int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared)
@@ -797,54 +829,60 @@ int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared)
 
 pw_status pw_route_topk(pw_ctx* c, const float* logits, int T, int32_t* idx, float* w, pw_stream stream)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_route_topk: null context");
-    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_route_topk: T=%d out of range", T);
-    if (T == 0) return ok();
-    if (!logits || !idx || !w) return fail(PW_ERR_INVALID, "pw_route_topk: null pointer");
-    if (!aligned4(logits) || !aligned4(idx) || !aligned4(w))
-        return fail(PW_ERR_INVALID, "pw_route_topk: device pointers must be 4-byte aligned");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    ProfScope ps(c, "route", (hipStream_t)stream);
-    e = launch_route_topk(logits, T, c->d.num_experts, c->d.top_k, idx, w, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "route_topk launch");
+    return guarded("pw_route_topk", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_route_topk: null context");
+        if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_route_topk: T=%d out of range", T);
+        if (T == 0) return ok();
+        if (!logits || !idx || !w) return fail(PW_ERR_INVALID, "pw_route_topk: null pointer");
+        if (!aligned4(logits) || !aligned4(idx) || !aligned4(w))
+            return fail(PW_ERR_INVALID, "pw_route_topk: device pointers must be 4-byte aligned");
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        ProfScope ps(c, "route", (hipStream_t)stream);
+        e = launch_route_topk(logits, T, c->d.num_experts, c->d.top_k, idx, w, (hipStream_t)stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "route_topk launch");
+    });
 }
 
 pw_status pw_route_permute(pw_ctx* c, const float* logits, int T, int32_t* idx, float* w, int32_t* offsets,
                            int32_t* sorted, pw_stream stream)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_route_permute: null context");
-    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_route_permute: T=%d out of range", T);
-    if (!offsets) return fail(PW_ERR_INVALID, "pw_route_permute: null offsets");
-    if (T > 0 && (!logits || !idx || !w || !sorted)) return fail(PW_ERR_INVALID, "pw_route_permute: null pointer");
-    if (!aligned4(offsets) || (T > 0 && (!aligned4(logits) || !aligned4(idx) || !aligned4(w) || !aligned4(sorted))))
-        return fail(PW_ERR_INVALID, "pw_route_permute: device pointers must be 4-byte aligned");
-    const int k = c->d.top_k, E = c->d.num_experts;
-    if ((long long)T * k > kFusedMaxAssign) {
-        pw_status st = pw_route_topk(c, logits, T, idx, w, stream);
-        return st != PW_OK ? st : pw_permute_by_expert(c, idx, T, offsets, sorted, stream);
-    }
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    ProfScope ps(c, "route", (hipStream_t)stream);
-    e = launch_route_permute(logits, T, E, k, idx, w, offsets, sorted, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "route_permute launch");
+    return guarded("pw_route_permute", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_route_permute: null context");
+        if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_route_permute: T=%d out of range", T);
+        if (!offsets) return fail(PW_ERR_INVALID, "pw_route_permute: null offsets");
+        if (T > 0 && (!logits || !idx || !w || !sorted)) return fail(PW_ERR_INVALID, "pw_route_permute: null pointer");
+        if (!aligned4(offsets) || (T > 0 && (!aligned4(logits) || !aligned4(idx) || !aligned4(w) || !aligned4(sorted))))
+            return fail(PW_ERR_INVALID, "pw_route_permute: device pointers must be 4-byte aligned");
+        const int k = c->d.top_k, E = c->d.num_experts;
+        if ((long long)T * k > kFusedMaxAssign) {
+            pw_status st = pw_route_topk(c, logits, T, idx, w, stream);
+            return st != PW_OK ? st : pw_permute_by_expert(c, idx, T, offsets, sorted, stream);
+        }
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        ProfScope ps(c, "route", (hipStream_t)stream);
+        e = launch_route_permute(logits, T, E, k, idx, w, offsets, sorted, (hipStream_t)stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "route_permute launch");
+    });
 }
 
 pw_status pw_permute_by_expert(pw_ctx* c, const int32_t* idx, int T, int32_t* offsets, int32_t* sorted,
                                pw_stream stream)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null context");
-    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_permute_by_expert: T=%d out of range", T);
-    if (!offsets) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null offsets");
-    if (T > 0 && (!idx || !sorted)) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null pointer");
-    if (!aligned4(offsets) || (T > 0 && (!aligned4(idx) || !aligned4(sorted))))
-        return fail(PW_ERR_INVALID, "pw_permute_by_expert: device pointers must be 4-byte aligned");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    ProfScope ps(c, "permute", (hipStream_t)stream);
-    e = launch_permute(idx, T, c->d.top_k, c->d.num_experts, offsets, sorted, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
+    return guarded("pw_permute_by_expert", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null context");
+        if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_permute_by_expert: T=%d out of range", T);
+        if (!offsets) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null offsets");
+        if (T > 0 && (!idx || !sorted)) return fail(PW_ERR_INVALID, "pw_permute_by_expert: null pointer");
+        if (!aligned4(offsets) || (T > 0 && (!aligned4(idx) || !aligned4(sorted))))
+            return fail(PW_ERR_INVALID, "pw_permute_by_expert: device pointers must be 4-byte aligned");
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        ProfScope ps(c, "permute", (hipStream_t)stream);
+        e = launch_permute(idx, T, c->d.top_k, c->d.num_experts, offsets, sorted, (hipStream_t)stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
+    });
 }
 
 // Argument checks of the FFN (fn names the entry point in messages).
@@ -992,107 +1030,121 @@ pw_status pw_moe_ffn_bitplane(pw_ctx* c, int layer, const uint16_t* x, int T, co
                               const float* w, const int32_t* offsets, const int32_t* sorted, uint16_t* y,
                               void* workspace, size_t ws_bytes, pw_stream stream)
 {
-    const pw_status st =
-        ffn_check(c, "pw_moe_ffn_bitplane", layer, x, T, idx, w, offsets, sorted, y, workspace, ws_bytes);
-    if (st != PW_OK || T == 0) return st;
-    return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, nullptr);
+    return guarded("pw_moe_ffn_bitplane", [&]() -> pw_status {
+        const pw_status st =
+            ffn_check(c, "pw_moe_ffn_bitplane", layer, x, T, idx, w, offsets, sorted, y, workspace, ws_bytes);
+        if (st != PW_OK || T == 0) return st;
+        return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, nullptr);
+    });
 }
 
 pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t* x, int T, int32_t* idx, float* w,
                        int32_t* offsets, int32_t* sorted, uint16_t* y, void* workspace, size_t ws_bytes,
                        pw_stream stream)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_moe_layer: null context");
-    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_layer: T=%d out of range", T);
-    if (!offsets) return fail(PW_ERR_INVALID, "pw_moe_layer: null offsets");
-    if (!aligned4(offsets) || (T > 0 && (!logits || !aligned4(logits))))
-        return fail(PW_ERR_INVALID, "pw_moe_layer: null or misaligned logits / offsets (4 B)");
-    pw_status st = ffn_check(c, "pw_moe_layer", layer, x, T, idx, w, offsets, sorted, y, workspace, ws_bytes);
-    if (st != PW_OK) return st;
-    // In-launch routing pays off only when every gate_up work unit gets a
-    // workgroup slot at once (two per CU): each routed workgroup routes the
-    // batch itself, so a launch with several rounds of workgroups would repeat
-    // it per round.
-    const pw_model_desc& d = c->d;
-    const long long n = (long long)T * d.top_k;
-    const long long gu_rows = 16LL * kGateUpRowGroups;
-    const long long gu_units = (d.inter_shared + gu_rows - 1) / gu_rows +
-                               std::min<long long>(d.num_experts, n) * ((d.inter + gu_rows - 1) / gu_rows);
-    double* mass = c->mass_on ? c->d_mass + (size_t)layer * d.num_experts : nullptr;
-    if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus ||
-        (c->tok_pass ? c->tok_pass : decode_tok_pass(T, d.top_k, d.num_experts, d.inter_shared)) != 8) {
-        // the separate routing launch, then the FFN (identical results)
-        st = pw_route_permute(c, logits, T, idx, w, offsets, sorted, stream);
-        if (st != PW_OK || T == 0) return st;
-        if (mass) {
-            const hipError_t e = launch_routing_mass(offsets, sorted, w, d.num_experts, mass, (hipStream_t)stream);
-            if (e != hipSuccess) return hip_fail(e, "routing mass launch");
+    return guarded("pw_moe_layer", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_moe_layer: null context");
+        if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_layer: T=%d out of range", T);
+        if (!offsets) return fail(PW_ERR_INVALID, "pw_moe_layer: null offsets");
+        if (!aligned4(offsets) || (T > 0 && (!logits || !aligned4(logits))))
+            return fail(PW_ERR_INVALID, "pw_moe_layer: null or misaligned logits / offsets (4 B)");
+        pw_status st = ffn_check(c, "pw_moe_layer", layer, x, T, idx, w, offsets, sorted, y, workspace, ws_bytes);
+        if (st != PW_OK) return st;
+        // In-launch routing pays off only when every gate_up work unit gets a
+        // workgroup slot at once (two per CU): each routed workgroup routes the
+        // batch itself, so a launch with several rounds of workgroups would repeat
+        // it per round.
+        const pw_model_desc& d = c->d;
+        const long long n = (long long)T * d.top_k;
+        const long long gu_rows = 16LL * kGateUpRowGroups;
+        const long long gu_units = (d.inter_shared + gu_rows - 1) / gu_rows +
+                                   std::min<long long>(d.num_experts, n) * ((d.inter + gu_rows - 1) / gu_rows);
+        double* mass = c->mass_on ? c->d_mass + (size_t)layer * d.num_experts : nullptr;
+        if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus ||
+            (c->tok_pass ? c->tok_pass : decode_tok_pass(T, d.top_k, d.num_experts, d.inter_shared)) != 8) {
+            // the separate routing launch, then the FFN (identical results)
+            st = pw_route_permute(c, logits, T, idx, w, offsets, sorted, stream);
+            if (st != PW_OK || T == 0) return st;
+            if (mass) {
+                const hipError_t e = launch_routing_mass(offsets, sorted, w, d.num_experts, mass, (hipStream_t)stream);
+                if (e != hipSuccess) return hip_fail(e, "routing mass launch");
+            }
+            return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, nullptr);
         }
-        return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, nullptr);
-    }
-    const LayerRoute r{logits, idx, w, offsets, sorted, mass};
-    return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, &r);
+        const LayerRoute r{logits, idx, w, offsets, sorted, mass};
+        return ffn_launch(c, layer, x, T, w, offsets, sorted, y, workspace, stream, &r);
+    });
 }
 
 pw_status pw_moe_layer_noalloc(pw_ctx* c, int layer, const float* logits, const uint16_t* x, int T, int32_t* idx,
                                float* w, int32_t* offsets, int32_t* sorted, uint16_t* y, pw_stream stream)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: null context");
-    if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: T=%d out of range", T);
-    const size_t need = pw_workspace_size(c, T);
-    if (need > kStaticScratchBytes)
-        return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: T=%d needs %zu B of workspace, above the %zu B the library "
-                    "holds; use pw_moe_layer with a caller workspace", T, need, kStaticScratchBytes);
-    return pw_moe_layer(c, layer, logits, x, T, idx, w, offsets, sorted, y, c->scratch, kStaticScratchBytes, stream);
+    return guarded("pw_moe_layer_noalloc", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: null context");
+        if (T < 0 || T > PW_MAX_TOKENS) return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: T=%d out of range", T);
+        const size_t need = pw_workspace_size(c, T);
+        if (need > kStaticScratchBytes)
+            return fail(PW_ERR_INVALID, "pw_moe_layer_noalloc: T=%d needs %zu B of workspace, above the %zu B the library "
+                        "holds; use pw_moe_layer with a caller workspace", T, need, kStaticScratchBytes);
+        return pw_moe_layer(c, layer, logits, x, T, idx, w, offsets, sorted, y, c->scratch, kStaticScratchBytes, stream);
+    });
 }
 
 pw_status pw_routing_mass_enable(pw_ctx* c, int on)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_routing_mass_enable: null context");
-    if (on && !c->d_mass) {
-        hipError_t e = hipSetDevice(c->device);
-        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-        const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
-        double* p = nullptr;
-        if ((e = hipMalloc((void**)&p, bytes)) != hipSuccess) return fail(PW_ERR_OOM, "pw_routing_mass_enable: %s", hipGetErrorString(e));
-        if ((e = hipMemset(p, 0, bytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess) {
-            (void)hipFree(p);
-            return hip_fail(e, "pw_routing_mass_enable: zero");
+    return guarded("pw_routing_mass_enable", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_routing_mass_enable: null context");
+        if (on && !c->d_mass) {
+            hipError_t e = hipSetDevice(c->device);
+            if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+            const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
+            double* p = nullptr;
+            if ((e = hipMalloc((void**)&p, bytes)) != hipSuccess) return fail(PW_ERR_OOM, "pw_routing_mass_enable: %s", hipGetErrorString(e));
+            if ((e = hipMemset(p, 0, bytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess) {
+                (void)hipFree(p);
+                return hip_fail(e, "pw_routing_mass_enable: zero");
+            }
+            c->d_mass = p;
         }
-        c->d_mass = p;
-    }
-    c->mass_on = on != 0;
-    return ok();
+        c->mass_on = on != 0;
+        return ok();
+    });
 }
 
 pw_status pw_routing_mass_reset(pw_ctx* c, pw_stream stream)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_routing_mass_reset: null context");
-    if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_reset: routing mass was never enabled");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    e = launch_fill_f64(c->d_mass, (int64_t)c->d.num_layers * c->d.num_experts, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "routing mass reset launch");
+    return guarded("pw_routing_mass_reset", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_routing_mass_reset: null context");
+        if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_reset: routing mass was never enabled");
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        e = launch_fill_f64(c->d_mass, (int64_t)c->d.num_layers * c->d.num_experts, (hipStream_t)stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "routing mass reset launch");
+    });
 }
 
 pw_status pw_routing_mass_read(pw_ctx* c, double* host_out, pw_stream stream)
 {
-    if (!c || !host_out) return fail(PW_ERR_INVALID, "pw_routing_mass_read: null pointer");
-    if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_read: routing mass was never enabled");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
-    e = hipMemcpyAsync(host_out, c->d_mass, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
-    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "pw_routing_mass_read: copy");
+    return guarded("pw_routing_mass_read", [&]() -> pw_status {
+        if (!c || !host_out) return fail(PW_ERR_INVALID, "pw_routing_mass_read: null pointer");
+        if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_read: routing mass was never enabled");
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
+        e = hipMemcpyAsync(host_out, c->d_mass, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
+        if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "pw_routing_mass_read: copy");
+    });
 }
 
 pw_status pw_get_committed_bits(const pw_ctx* c, int32_t id, int32_t* q_out)
 {
-    if (!c || !q_out) return fail(PW_ERR_INVALID, "pw_get_committed_bits: null pointer");
-    if (id < 0 || id >= c->nblocks) return fail(PW_ERR_INVALID, "pw_get_committed_bits: block id %d out of range", id);
-    *q_out = c->blocks[id].registered ? c->blocks[id].q : 0;
-    return ok();
+    return guarded("pw_get_committed_bits", [&]() -> pw_status {
+        if (!c || !q_out) return fail(PW_ERR_INVALID, "pw_get_committed_bits: null pointer");
+        if (id < 0 || id >= c->nblocks) return fail(PW_ERR_INVALID, "pw_get_committed_bits: block id %d out of range", id);
+        *q_out = c->blocks[id].registered ? c->blocks[id].q : 0;
+        return ok();
+    });
 }
 
 int64_t pw_resident_bytes(const pw_ctx* c) { return c ? c->pool.resident() : 0; }
@@ -1403,204 +1455,226 @@ static pw_status check_changes(pw_ctx* c, const char* fn, int n, const int32_t* 
 pw_status pw_set_committed_bits(pw_ctx* c, int n, const int32_t* ids, const uint8_t* q_new, pw_stream compute,
                                 pw_stream copy)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_set_committed_bits: null context");
-    std::vector<std::pair<int, int>> todo;
-    pw_status st = check_changes(c, "pw_set_committed_bits", n, ids, q_new, todo);
-    if (st != PW_OK || todo.empty()) return st;
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    hipStream_t cs = (hipStream_t)compute, xs = (hipStream_t)copy;
-    std::vector<WidthChange> plans;
-    if ((st = prepare_changes(c, "pw_set_committed_bits", todo, xs, false, plans)) != PW_OK) return st;
-    if ((e = hipStreamWaitEvent(cs, plans[0].copied, 0)) != hipSuccess) {
-        (void)hipStreamSynchronize(xs);
-        release_prepared(c, plans);
-        return hip_fail(e, "pw_set_committed_bits: compute waits for the copies");
-    }
-    if ((st = apply_changes(c, plans, cs)) != PW_OK) {
-        (void)hipStreamSynchronize(xs);
-        release_prepared(c, plans);
+    return guarded("pw_set_committed_bits", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_set_committed_bits: null context");
+        std::vector<std::pair<int, int>> todo;
+        pw_status st = check_changes(c, "pw_set_committed_bits", n, ids, q_new, todo);
+        if (st != PW_OK || todo.empty()) return st;
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        hipStream_t cs = (hipStream_t)compute, xs = (hipStream_t)copy;
+        std::vector<WidthChange> plans;
+        if ((st = prepare_changes(c, "pw_set_committed_bits", todo, xs, false, plans)) != PW_OK) return st;
+        if ((e = hipStreamWaitEvent(cs, plans[0].copied, 0)) != hipSuccess) {
+            (void)hipStreamSynchronize(xs);
+            release_prepared(c, plans);
+            return hip_fail(e, "pw_set_committed_bits: compute waits for the copies");
+        }
+        if ((st = apply_changes(c, plans, cs)) != PW_OK) {
+            (void)hipStreamSynchronize(xs);
+            release_prepared(c, plans);
+            return st;
+        }
+        drop_copy_events(c, plans);
         return st;
-    }
-    drop_copy_events(c, plans);
-    return st;
+    });
 }
 
 pw_status pw_request_widths(pw_ctx* c, int n, const int32_t* ids, const uint8_t* q_desired, pw_stream copy)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_request_widths: null context");
-    std::vector<std::pair<int, int>> todo;
-    pw_status st = check_changes(c, "pw_request_widths", n, ids, q_desired, todo);
-    if (st != PW_OK || todo.empty()) return st;
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    std::vector<WidthChange> plans;
-    if ((st = prepare_changes(c, "pw_request_widths", todo, (hipStream_t)copy, true, plans)) != PW_OK) return st;
-    for (const auto& p : plans) c->pending[p.id] = p;
-    return ok();
+    return guarded("pw_request_widths", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_request_widths: null context");
+        std::vector<std::pair<int, int>> todo;
+        pw_status st = check_changes(c, "pw_request_widths", n, ids, q_desired, todo);
+        if (st != PW_OK || todo.empty()) return st;
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        std::vector<WidthChange> plans;
+        if ((st = prepare_changes(c, "pw_request_widths", todo, (hipStream_t)copy, true, plans)) != PW_OK) return st;
+        for (const auto& p : plans) c->pending[p.id] = p;
+        return ok();
+    });
 }
 
 pw_status pw_commit_ready(pw_ctx* c, pw_stream compute, int* n_committed)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_commit_ready: null context");
-    if (n_committed) *n_committed = 0;
-    if (c->pending.empty()) return ok();
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    std::vector<WidthChange> ready;
-    for (const auto& kv : c->pending) {
-        const hipError_t q = hipEventQuery(kv.second.copied);
-        if (q == hipSuccess) ready.push_back(kv.second);
-        else if (q != hipErrorNotReady) return hip_fail(q, "pw_commit_ready: copy event");
-    }
-    if (ready.empty()) return ok();
-    std::sort(ready.begin(), ready.end(), [](const WidthChange& a, const WidthChange& b) { return a.id < b.id; });
-    const pw_status st = apply_changes(c, ready, (hipStream_t)compute);
-    if (st != PW_OK) return st;
-    drop_copy_events(c, ready);
-    for (const auto& p : ready) c->pending.erase(p.id);
-    if (n_committed) *n_committed = (int)ready.size();
-    return ok();
+    return guarded("pw_commit_ready", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_commit_ready: null context");
+        if (n_committed) *n_committed = 0;
+        if (c->pending.empty()) return ok();
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        std::vector<WidthChange> ready;
+        for (const auto& kv : c->pending) {
+            const hipError_t q = hipEventQuery(kv.second.copied);
+            if (q == hipSuccess) ready.push_back(kv.second);
+            else if (q != hipErrorNotReady) return hip_fail(q, "pw_commit_ready: copy event");
+        }
+        if (ready.empty()) return ok();
+        std::sort(ready.begin(), ready.end(), [](const WidthChange& a, const WidthChange& b) { return a.id < b.id; });
+        const pw_status st = apply_changes(c, ready, (hipStream_t)compute);
+        if (st != PW_OK) return st;
+        drop_copy_events(c, ready);
+        for (const auto& p : ready) c->pending.erase(p.id);
+        if (n_committed) *n_committed = (int)ready.size();
+        return ok();
+    });
 }
 
 pw_status pw_block_state(const pw_ctx* c, int32_t id, int32_t* q_committed, int32_t* q_desired, int32_t* state)
 {
-    if (!c || !q_committed || !q_desired || !state) return fail(PW_ERR_INVALID, "pw_block_state: null pointer");
-    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
-        return fail(PW_ERR_INVALID, "pw_block_state: block id %d not registered", id);
-    *q_committed = c->blocks[id].q;
-    const auto it = c->pending.find(id);
-    if (it == c->pending.end()) {
-        *q_desired = c->blocks[id].q;
-        *state = PW_PAGE_RESIDENT;
+    return guarded("pw_block_state", [&]() -> pw_status {
+        if (!c || !q_committed || !q_desired || !state) return fail(PW_ERR_INVALID, "pw_block_state: null pointer");
+        if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+            return fail(PW_ERR_INVALID, "pw_block_state: block id %d not registered", id);
+        *q_committed = c->blocks[id].q;
+        const auto it = c->pending.find(id);
+        if (it == c->pending.end()) {
+            *q_desired = c->blocks[id].q;
+            *state = PW_PAGE_RESIDENT;
+            return ok();
+        }
+        *q_desired = it->second.qn;
+        const hipError_t q = hipEventQuery(it->second.copied);
+        if (q != hipSuccess && q != hipErrorNotReady) return hip_fail(q, "pw_block_state: copy event");
+        *state = q == hipSuccess ? PW_PAGE_READY : PW_PAGE_IN_TRANSFER;
         return ok();
-    }
-    *q_desired = it->second.qn;
-    const hipError_t q = hipEventQuery(it->second.copied);
-    if (q != hipSuccess && q != hipErrorNotReady) return hip_fail(q, "pw_block_state: copy event");
-    *state = q == hipSuccess ? PW_PAGE_READY : PW_PAGE_IN_TRANSFER;
-    return ok();
+    });
 }
 
 pw_status pw_committed_widths(const pw_ctx* c, uint8_t* q_out)
 {
-    if (!c || !q_out) return fail(PW_ERR_INVALID, "pw_committed_widths: null pointer");
-    for (int id = 0; id < c->nblocks; ++id) q_out[id] = c->blocks[id].registered ? (uint8_t)c->blocks[id].q : 0;
-    return ok();
+    return guarded("pw_committed_widths", [&]() -> pw_status {
+        if (!c || !q_out) return fail(PW_ERR_INVALID, "pw_committed_widths: null pointer");
+        for (int id = 0; id < c->nblocks; ++id) q_out[id] = c->blocks[id].registered ? (uint8_t)c->blocks[id].q : 0;
+        return ok();
+    });
 }
 
 pw_status pw_routing_mass_copy(pw_ctx* c, double* dst, pw_stream stream)
 {
-    if (!c || !dst) return fail(PW_ERR_INVALID, "pw_routing_mass_copy: null pointer");
-    if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_copy: routing mass was never enabled");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
-    e = hipMemcpyAsync(dst, c->d_mass, bytes, hipMemcpyDefault, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "pw_routing_mass_copy");
+    return guarded("pw_routing_mass_copy", [&]() -> pw_status {
+        if (!c || !dst) return fail(PW_ERR_INVALID, "pw_routing_mass_copy: null pointer");
+        if (!c->d_mass) return fail(PW_ERR_STATE, "pw_routing_mass_copy: routing mass was never enabled");
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        const size_t bytes = sizeof(double) * (size_t)c->d.num_layers * c->d.num_experts;
+        e = hipMemcpyAsync(dst, c->d_mass, bytes, hipMemcpyDefault, (hipStream_t)stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "pw_routing_mass_copy");
+    });
 }
 
 pw_status pw_plane_states(const pw_ctx* c, int32_t id, int32_t* states)
 {
-    if (!c || !states) return fail(PW_ERR_INVALID, "pw_plane_states: null pointer");
-    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
-        return fail(PW_ERR_INVALID, "pw_plane_states: block id %d not registered", id);
-    const HostBlock& b = c->blocks[id];
-    const int off_gpu = c->d.keep_host_masters ? PW_PLANE_CPU : PW_PLANE_ABSENT;
-    const auto it = c->pending.find(id);
-    if (it == c->pending.end()) {
-        for (int p = 0; p < 8; ++p) states[p] = p < b.q ? PW_PLANE_GPU : off_gpu;
-        states[8] = PW_PLANE_GPU;
+    return guarded("pw_plane_states", [&]() -> pw_status {
+        if (!c || !states) return fail(PW_ERR_INVALID, "pw_plane_states: null pointer");
+        if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+            return fail(PW_ERR_INVALID, "pw_plane_states: block id %d not registered", id);
+        const HostBlock& b = c->blocks[id];
+        const int off_gpu = c->d.keep_host_masters ? PW_PLANE_CPU : PW_PLANE_ABSENT;
+        const auto it = c->pending.find(id);
+        if (it == c->pending.end()) {
+            for (int p = 0; p < 8; ++p) states[p] = p < b.q ? PW_PLANE_GPU : off_gpu;
+            states[8] = PW_PLANE_GPU;
+            return ok();
+        }
+        const hipError_t q = hipEventQuery(it->second.copied);
+        if (q != hipSuccess && q != hipErrorNotReady) return hip_fail(q, "pw_plane_states: copy event");
+        const int moving = q == hipSuccess ? PW_PLANE_READY : PW_PLANE_IN_TRANSFER;
+        const int qo = it->second.qo, qn = it->second.qn;
+        for (int p = 0; p < 8; ++p) {
+            if (p < qo) states[p] = PW_PLANE_GPU;  // lowering: planes qn..qo-1 stay in use until the commit
+            else if (p < qn) states[p] = moving;
+            else states[p] = off_gpu;
+        }
+        states[8] = moving;  // LUT_{d_i}
         return ok();
-    }
-    const hipError_t q = hipEventQuery(it->second.copied);
-    if (q != hipSuccess && q != hipErrorNotReady) return hip_fail(q, "pw_plane_states: copy event");
-    const int moving = q == hipSuccess ? PW_PLANE_READY : PW_PLANE_IN_TRANSFER;
-    const int qo = it->second.qo, qn = it->second.qn;
-    for (int p = 0; p < 8; ++p) {
-        if (p < qo) states[p] = PW_PLANE_GPU;  // lowering: planes qn..qo-1 stay in use until the commit
-        else if (p < qn) states[p] = moving;
-        else states[p] = off_gpu;
-    }
-    states[8] = moving;  // LUT_{d_i}
-    return ok();
+    });
 }
 
 pw_status pw_trim(pw_ctx* c, int64_t* freed_bytes)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_trim: null context");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    const size_t freed = c->pool.trim();
-    if (freed_bytes) *freed_bytes = (int64_t)freed;
-    return ok();
+    return guarded("pw_trim", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_trim: null context");
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        const size_t freed = c->pool.trim();
+        if (freed_bytes) *freed_bytes = (int64_t)freed;
+        return ok();
+    });
 }
 
 pw_status pw_pool_stats(const pw_ctx* c, int64_t* resident, int64_t* cached, int64_t* waiting, int64_t* held,
                         int64_t* device_allocs, int64_t* events)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_pool_stats: null context");
-    if (resident) *resident = c->pool.resident();
-    if (cached) *cached = c->pool.free_bytes();
-    if (waiting) *waiting = c->pool.waiting_bytes();
-    if (held) *held = c->pool.held();
-    if (device_allocs) *device_allocs = c->pool.device_allocs();
-    if (events) *events = (int64_t)c->evs.created();
-    return ok();
+    return guarded("pw_pool_stats", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_pool_stats: null context");
+        if (resident) *resident = c->pool.resident();
+        if (cached) *cached = c->pool.free_bytes();
+        if (waiting) *waiting = c->pool.waiting_bytes();
+        if (held) *held = c->pool.held();
+        if (device_allocs) *device_allocs = c->pool.device_allocs();
+        if (events) *events = (int64_t)c->evs.created();
+        return ok();
+    });
 }
 
 pw_status pw_retarget(pw_ctx* c, int64_t byte_target, const double* mass, const float* sens,
                       const pw_plan_params* params, pw_stream copy, int* n_requested, int64_t* planned_bytes)
 {
-    if (!c || !mass || !sens || !params) return fail(PW_ERR_INVALID, "pw_retarget: null pointer");
-    if (n_requested) *n_requested = 0;
-    const int L = c->d.num_layers, E = c->d.num_experts;
-    std::vector<uint8_t> q_cur((size_t)L * E * 2), q_plan(q_cur.size());
-    for (int l = 0; l < L; ++l)
-        for (int e = 0; e < E; ++e)
-            for (int m = 0; m < 2; ++m) {
-                const int id = (l * (E + 1) + e) * 2 + m;
-                if (!c->blocks[id].registered)
-                    return fail(PW_ERR_STATE, "pw_retarget: block (layer %d, expert %d, module %d) not registered", l, e, m);
-                const auto it = c->pending.find(id);
-                q_cur[((size_t)l * E + e) * 2 + m] = (uint8_t)(it == c->pending.end() ? c->blocks[id].q : it->second.qn);
-            }
-    int64_t total = 0;
-    pw_status st = pw_plan_widths(L, E, c->d.hidden, c->d.inter, q_cur.data(), mass, sens, params, byte_target,
-                                  q_plan.data(), &total);
-    if (st != PW_OK) return st;
-    std::vector<int32_t> ids;
-    std::vector<uint8_t> qs;
-    for (int l = 0; l < L; ++l)
-        for (int e = 0; e < E; ++e)
-            for (int m = 0; m < 2; ++m) {
-                const size_t b = ((size_t)l * E + e) * 2 + m;
-                const int id = (l * (E + 1) + e) * 2 + m;
-                if (q_plan[b] != q_cur[b] && !c->pending.count(id)) {
-                    ids.push_back(id);
-                    qs.push_back(q_plan[b]);
+    return guarded("pw_retarget", [&]() -> pw_status {
+        if (!c || !mass || !sens || !params) return fail(PW_ERR_INVALID, "pw_retarget: null pointer");
+        if (n_requested) *n_requested = 0;
+        const int L = c->d.num_layers, E = c->d.num_experts;
+        std::vector<uint8_t> q_cur((size_t)L * E * 2), q_plan(q_cur.size());
+        for (int l = 0; l < L; ++l)
+            for (int e = 0; e < E; ++e)
+                for (int m = 0; m < 2; ++m) {
+                    const int id = (l * (E + 1) + e) * 2 + m;
+                    if (!c->blocks[id].registered)
+                        return fail(PW_ERR_STATE, "pw_retarget: block (layer %d, expert %d, module %d) not registered", l, e, m);
+                    const auto it = c->pending.find(id);
+                    q_cur[((size_t)l * E + e) * 2 + m] = (uint8_t)(it == c->pending.end() ? c->blocks[id].q : it->second.qn);
                 }
-            }
-    if (!ids.empty()) {
-        st = pw_request_widths(c, (int)ids.size(), ids.data(), qs.data(), copy);
+        int64_t total = 0;
+        pw_status st = pw_plan_widths(L, E, c->d.hidden, c->d.inter, q_cur.data(), mass, sens, params, byte_target,
+                                      q_plan.data(), &total);
         if (st != PW_OK) return st;
-    }
-    if (n_requested) *n_requested = (int)ids.size();
-    if (planned_bytes) *planned_bytes = total;
-    return ok();
+        std::vector<int32_t> ids;
+        std::vector<uint8_t> qs;
+        for (int l = 0; l < L; ++l)
+            for (int e = 0; e < E; ++e)
+                for (int m = 0; m < 2; ++m) {
+                    const size_t b = ((size_t)l * E + e) * 2 + m;
+                    const int id = (l * (E + 1) + e) * 2 + m;
+                    if (q_plan[b] != q_cur[b] && !c->pending.count(id)) {
+                        ids.push_back(id);
+                        qs.push_back(q_plan[b]);
+                    }
+                }
+        if (!ids.empty()) {
+            st = pw_request_widths(c, (int)ids.size(), ids.data(), qs.data(), copy);
+            if (st != PW_OK) return st;
+        }
+        if (n_requested) *n_requested = (int)ids.size();
+        if (planned_bytes) *planned_bytes = total;
+        return ok();
+    });
 }
 
 pw_status pw_debug_decode(pw_ctx* c, int32_t id, int path, uint8_t* codes_out, uint16_t* w_out, pw_stream stream)
 {
-    if (!c || (!codes_out && !w_out)) return fail(PW_ERR_INVALID, "pw_debug_decode: null pointer");
-    if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
-        return fail(PW_ERR_INVALID, "pw_debug_decode: block id %d not registered", id);
-    if (path < PW_DECODE_PATH_TILE128 || path > PW_DECODE_PATH_TILE64_WIDE)
-        return fail(PW_ERR_INVALID, "pw_debug_decode: path %d not in 0..3", path);
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    e = launch_debug_decode(c->d_table + id, id & 1, c->blocks[id].R, path, codes_out, w_out, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "debug decode launch");
+    return guarded("pw_debug_decode", [&]() -> pw_status {
+        if (!c || (!codes_out && !w_out)) return fail(PW_ERR_INVALID, "pw_debug_decode: null pointer");
+        if (id < 0 || id >= c->nblocks || !c->blocks[id].registered)
+            return fail(PW_ERR_INVALID, "pw_debug_decode: block id %d not registered", id);
+        if (path < PW_DECODE_PATH_TILE128 || path > PW_DECODE_PATH_TILE64_WIDE)
+            return fail(PW_ERR_INVALID, "pw_debug_decode: path %d not in 0..3", path);
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        e = launch_debug_decode(c->d_table + id, id & 1, c->blocks[id].R, path, codes_out, w_out, (hipStream_t)stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "debug decode launch");
+    });
 }
 
 // The decode contraction's tile of each module: gate_up 128-row tiles, down
@@ -1609,53 +1683,61 @@ static int default_decode_path(int32_t id) { return (id & 1) ? PW_DECODE_PATH_TI
 
 pw_status pw_debug_decode_codes(pw_ctx* c, int32_t id, uint8_t* out, pw_stream stream)
 {
-    if (!out) return fail(PW_ERR_INVALID, "pw_debug_decode_codes: null pointer");
-    return pw_debug_decode(c, id, default_decode_path(id), out, nullptr, stream);
+    return guarded("pw_debug_decode_codes", [&]() -> pw_status {
+        if (!out) return fail(PW_ERR_INVALID, "pw_debug_decode_codes: null pointer");
+        return pw_debug_decode(c, id, default_decode_path(id), out, nullptr, stream);
+    });
 }
 
 pw_status pw_debug_dequant(pw_ctx* c, int32_t id, uint16_t* out, pw_stream stream)
 {
-    if (!out) return fail(PW_ERR_INVALID, "pw_debug_dequant: null pointer");
-    return pw_debug_decode(c, id, default_decode_path(id), nullptr, out, stream);
+    return guarded("pw_debug_dequant", [&]() -> pw_status {
+        if (!out) return fail(PW_ERR_INVALID, "pw_debug_dequant: null pointer");
+        return pw_debug_decode(c, id, default_decode_path(id), nullptr, out, stream);
+    });
 }
 
 pw_status pw_profile_enable(pw_ctx* c, int on)
 {
-    if (!c) return fail(PW_ERR_INVALID, "pw_profile_enable: null context");
-    hipError_t e = hipSetDevice(c->device);
-    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-    (void)hipDeviceSynchronize();
-    prof_reset(c);
-    if (on && c->prof_pool.empty()) {
-        c->prof_pool.reserve(kProfEvents);
-        for (size_t i = 0; i < kProfEvents; ++i) {
-            hipEvent_t ev;
-            if ((e = hipEventCreate(&ev)) != hipSuccess) {
-                prof_release(c);
-                return hip_fail(e, "pw_profile_enable: hipEventCreate");
+    return guarded("pw_profile_enable", [&]() -> pw_status {
+        if (!c) return fail(PW_ERR_INVALID, "pw_profile_enable: null context");
+        hipError_t e = hipSetDevice(c->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+        (void)hipDeviceSynchronize();
+        prof_reset(c);
+        if (on && c->prof_pool.empty()) {
+            c->prof_pool.reserve(kProfEvents);
+            for (size_t i = 0; i < kProfEvents; ++i) {
+                hipEvent_t ev;
+                if ((e = hipEventCreate(&ev)) != hipSuccess) {
+                    prof_release(c);
+                    return hip_fail(e, "pw_profile_enable: hipEventCreate");
+                }
+                c->prof_pool.push_back(ev);
             }
-            c->prof_pool.push_back(ev);
         }
-    }
-    c->profiling = on != 0;
-    return ok();
+        c->profiling = on != 0;
+        return ok();
+    });
 }
 
 pw_status pw_profile_read(pw_ctx* c, const char* kernel, double* total_ms, int64_t* launches)
 {
-    if (!c || !kernel || !total_ms || !launches) return fail(PW_ERR_INVALID, "pw_profile_read: null pointer");
-    *total_ms = 0.0;
-    *launches = 0;
-    auto it = c->prof.find(kernel);
-    if (it == c->prof.end()) return ok();
-    for (auto& r : it->second) {
-        float ms = 0.0f;
-        hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
-        if (e != hipSuccess) return hip_fail(e, "pw_profile_read: hipEventElapsedTime (stream not synchronised?)");
-        *total_ms += ms;
-        *launches += 1;
-    }
-    return ok();
+    return guarded("pw_profile_read", [&]() -> pw_status {
+        if (!c || !kernel || !total_ms || !launches) return fail(PW_ERR_INVALID, "pw_profile_read: null pointer");
+        *total_ms = 0.0;
+        *launches = 0;
+        auto it = c->prof.find(kernel);
+        if (it == c->prof.end()) return ok();
+        for (auto& r : it->second) {
+            float ms = 0.0f;
+            hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
+            if (e != hipSuccess) return hip_fail(e, "pw_profile_read: hipEventElapsedTime (stream not synchronised?)");
+            *total_ms += ms;
+            *launches += 1;
+        }
+        return ok();
+    });
 }
 
 }  // extern "C"

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstring>
 #include <set>
+#include <new>
 #include <vector>
 
 #include "../../include/pw.h"
@@ -16,6 +17,9 @@
 
 namespace pw {
 pw_status plan_fail(const char* msg);
+// an exception inside a planner call as a status: OOM for host memory
+// exhausted, else INVALID (the entry points return statuses, never exceptions)
+pw_status plan_exception(const char* fn, bool oom);
 }
 
 namespace {
@@ -36,79 +40,93 @@ double drop_damage(const Block& b, int q) { return b.weight * (3.0 * (double)(1L
 
 }  // namespace
 
+template <class F>
+pw_status plan_guarded(const char* fn, F&& body)
+{
+    try {
+        return body();
+    } catch (const std::bad_alloc&) {
+        return pw::plan_exception(fn, true);
+    } catch (...) {
+        return pw::plan_exception(fn, false);
+    }
+}
+
 extern "C" pw_status pw_plan_widths(int L, int E, int H, int I, const uint8_t* q_cur, const double* mass,
                                     const float* sens, const pw_plan_params* p, int64_t byte_target, uint8_t* q_out,
                                     int64_t* bytes_out)
 {
-    using namespace pw;
-    if (!q_cur || !mass || !sens || !p || !q_out) return plan_fail("pw_plan_widths: null pointer");
-    if (L < 1 || E < 1 || H < 32 || I < 32 || H % 32 || I % 32) return plan_fail("pw_plan_widths: shape out of range");
-    if (p->q_min < PW_QMIN || p->q_max > PW_QMAX || p->q_min > p->q_max || p->hot_floor > p->q_max)
-        return plan_fail("pw_plan_widths: widths out of range");
-    const int n = 2 * L * E;
-    std::vector<Block> bl(n);
-    std::vector<int> q(n);
-    for (int l = 0; l < L; ++l) {
-        double sum = 0.0;
-        for (int e = 0; e < E; ++e) sum += mass[(size_t)l * E + e];
-        for (int e = 0; e < E; ++e) {
-            const double share = sum > 0.0 ? mass[(size_t)l * E + e] / sum : 0.0;
-            const bool hot = p->hot_share > 0.0 && share >= p->hot_share;
-            for (int m = 0; m < 2; ++m) {
-                const int b = (l * E + e) * 2 + m;
-                const int R = m == 0 ? 2 * I : H, K = m == 0 ? H : I;
-                Block& x = bl[b];
-                x.plane_b = (int64_t)R * K / 8;
-                x.R = R;
-                x.weight = (double)sens[b] * (share + p->mass_eps) * (hot ? p->hot_mult : 1.0);
-                x.floor = hot ? std::max(p->q_min, p->hot_floor) : p->q_min;
-                q[b] = std::min(std::max((int)q_cur[b], x.floor), p->q_max);
+    return plan_guarded("pw_plan_widths", [&]() -> pw_status {
+        using namespace pw;
+        if (!q_cur || !mass || !sens || !p || !q_out) return plan_fail("pw_plan_widths: null pointer");
+        if (L < 1 || E < 1 || H < 32 || I < 32 || H % 32 || I % 32) return plan_fail("pw_plan_widths: shape out of range");
+        if (p->q_min < PW_QMIN || p->q_max > PW_QMAX || p->q_min > p->q_max || p->hot_floor > p->q_max)
+            return plan_fail("pw_plan_widths: widths out of range");
+        const int n = 2 * L * E;
+        std::vector<Block> bl(n);
+        std::vector<int> q(n);
+        for (int l = 0; l < L; ++l) {
+            double sum = 0.0;
+            for (int e = 0; e < E; ++e) sum += mass[(size_t)l * E + e];
+            for (int e = 0; e < E; ++e) {
+                const double share = sum > 0.0 ? mass[(size_t)l * E + e] / sum : 0.0;
+                const bool hot = p->hot_share > 0.0 && share >= p->hot_share;
+                for (int m = 0; m < 2; ++m) {
+                    const int b = (l * E + e) * 2 + m;
+                    const int R = m == 0 ? 2 * I : H, K = m == 0 ? H : I;
+                    Block& x = bl[b];
+                    x.plane_b = (int64_t)R * K / 8;
+                    x.R = R;
+                    x.weight = (double)sens[b] * (share + p->mass_eps) * (hot ? p->hot_mult : 1.0);
+                    x.floor = hot ? std::max(p->q_min, p->hot_floor) : p->q_min;
+                    q[b] = std::min(std::max((int)q_cur[b], x.floor), p->q_max);
+                }
             }
         }
-    }
-    int64_t total = 0;
-    for (int b = 0; b < n; ++b) total += block_bytes(bl[b], q[b]);
-    if (total > byte_target) {
-        // lower: smallest damage per byte saved first (ties: lower block index)
-        std::set<std::pair<double, int>> cand;
-        auto key = [&](int b) {
-            return drop_damage(bl[b], q[b]) / (double)(block_bytes(bl[b], q[b]) - block_bytes(bl[b], q[b] - 1));
-        };
-        for (int b = 0; b < n; ++b)
-            if (q[b] > bl[b].floor) cand.insert({key(b), b});
-        while (total > byte_target && !cand.empty()) {
-            const int b = cand.begin()->second;
-            cand.erase(cand.begin());
-            total -= block_bytes(bl[b], q[b]) - block_bytes(bl[b], q[b] - 1);
-            --q[b];
-            if (q[b] > bl[b].floor) cand.insert({key(b), b});
-        }
-    } else {
-        // raise: largest damage removed per byte added first, while the target allows
-        // (ties: lower block index)
-        std::set<std::pair<double, int>> cand;  // (-key, b)
-        auto key = [&](int b) {
-            return drop_damage(bl[b], q[b] + 1) / (double)(block_bytes(bl[b], q[b] + 1) - block_bytes(bl[b], q[b]));
-        };
-        for (int b = 0; b < n; ++b)
-            if (q[b] < p->q_max) cand.insert({-key(b), b});
-        for (;;) {
-            auto it = cand.begin();
-            for (; it != cand.end(); ++it) {
+        int64_t total = 0;
+        for (int b = 0; b < n; ++b) total += block_bytes(bl[b], q[b]);
+        if (total > byte_target) {
+            // lower: smallest damage per byte saved first (ties: lower block index)
+            std::set<std::pair<double, int>> cand;
+            auto key = [&](int b) {
+                return drop_damage(bl[b], q[b]) / (double)(block_bytes(bl[b], q[b]) - block_bytes(bl[b], q[b] - 1));
+            };
+            for (int b = 0; b < n; ++b)
+                if (q[b] > bl[b].floor) cand.insert({key(b), b});
+            while (total > byte_target && !cand.empty()) {
+                const int b = cand.begin()->second;
+                cand.erase(cand.begin());
+                total -= block_bytes(bl[b], q[b]) - block_bytes(bl[b], q[b] - 1);
+                --q[b];
+                if (q[b] > bl[b].floor) cand.insert({key(b), b});
+            }
+        } else {
+            // raise: largest damage removed per byte added first, while the target allows
+            // (ties: lower block index)
+            std::set<std::pair<double, int>> cand;  // (-key, b)
+            auto key = [&](int b) {
+                return drop_damage(bl[b], q[b] + 1) / (double)(block_bytes(bl[b], q[b] + 1) - block_bytes(bl[b], q[b]));
+            };
+            for (int b = 0; b < n; ++b)
+                if (q[b] < p->q_max) cand.insert({-key(b), b});
+            for (;;) {
+                auto it = cand.begin();
+                for (; it != cand.end(); ++it) {
+                    const int b = it->second;
+                    if (total + block_bytes(bl[b], q[b] + 1) - block_bytes(bl[b], q[b]) <= byte_target) break;
+                }
+                if (it == cand.end()) break;
                 const int b = it->second;
-                if (total + block_bytes(bl[b], q[b] + 1) - block_bytes(bl[b], q[b]) <= byte_target) break;
+                cand.erase(it);
+                total += block_bytes(bl[b], q[b] + 1) - block_bytes(bl[b], q[b]);
+                ++q[b];
+                if (q[b] < p->q_max) cand.insert({-key(b), b});
             }
-            if (it == cand.end()) break;
-            const int b = it->second;
-            cand.erase(it);
-            total += block_bytes(bl[b], q[b] + 1) - block_bytes(bl[b], q[b]);
-            ++q[b];
-            if (q[b] < p->q_max) cand.insert({-key(b), b});
         }
-    }
-    for (int b = 0; b < n; ++b) q_out[b] = (uint8_t)q[b];
-    if (bytes_out) *bytes_out = total;
-    return PW_OK;
+        for (int b = 0; b < n; ++b) q_out[b] = (uint8_t)q[b];
+        if (bytes_out) *bytes_out = total;
+        return PW_OK;
+    });
 }
 
 // One commit event of the fixed-fraction schedule: among the routed blocks
@@ -118,33 +136,35 @@ extern "C" pw_status pw_plan_widths(int L, int E, int H, int I, const uint8_t* q
 extern "C" pw_status pw_plan_event(int L, int E, const uint8_t* q_cur, const double* mass, const uint8_t* skip,
                                    int lower, int n_change, int32_t* ids_out, uint8_t* q_out, int* n_out)
 {
-    using namespace pw;
-    if (!q_cur || !mass || !n_out || (n_change > 0 && (!ids_out || !q_out)))
-        return plan_fail("pw_plan_event: null pointer");
-    if (L < 1 || E < 1 || n_change < 0) return plan_fail("pw_plan_event: size out of range");
-    struct Cand {
-        double m;
-        int32_t id;
-        int b;
-    };
-    std::vector<Cand> cand;
-    for (int l = 0; l < L; ++l)
-        for (int e = 0; e < E; ++e)
-            for (int m = 0; m < 2; ++m) {
-                const int b = (l * E + e) * 2 + m;
-                const int q = q_cur[b];
-                if (q < PW_QMIN || q > PW_QMAX) return plan_fail("pw_plan_event: width out of range");
-                if ((skip && skip[b]) || (lower ? q <= PW_QMIN : q >= PW_QMAX)) continue;
-                cand.push_back({mass[(size_t)l * E + e], (l * (E + 1) + e) * 2 + m, b});
-            }
-    std::sort(cand.begin(), cand.end(), [](const Cand& x, const Cand& y) {
-        return x.m < y.m || (x.m == y.m && x.id < y.id);
+    return plan_guarded("pw_plan_event", [&]() -> pw_status {
+        using namespace pw;
+        if (!q_cur || !mass || !n_out || (n_change > 0 && (!ids_out || !q_out)))
+            return plan_fail("pw_plan_event: null pointer");
+        if (L < 1 || E < 1 || n_change < 0) return plan_fail("pw_plan_event: size out of range");
+        struct Cand {
+            double m;
+            int32_t id;
+            int b;
+        };
+        std::vector<Cand> cand;
+        for (int l = 0; l < L; ++l)
+            for (int e = 0; e < E; ++e)
+                for (int m = 0; m < 2; ++m) {
+                    const int b = (l * E + e) * 2 + m;
+                    const int q = q_cur[b];
+                    if (q < PW_QMIN || q > PW_QMAX) return plan_fail("pw_plan_event: width out of range");
+                    if ((skip && skip[b]) || (lower ? q <= PW_QMIN : q >= PW_QMAX)) continue;
+                    cand.push_back({mass[(size_t)l * E + e], (l * (E + 1) + e) * 2 + m, b});
+                }
+        std::sort(cand.begin(), cand.end(), [](const Cand& x, const Cand& y) {
+            return x.m < y.m || (x.m == y.m && x.id < y.id);
+        });
+        const int n = std::min<int>(n_change, (int)cand.size());
+        for (int i = 0; i < n; ++i) {
+            ids_out[i] = cand[i].id;
+            q_out[i] = (uint8_t)(q_cur[cand[i].b] + (lower ? -1 : 1));
+        }
+        *n_out = n;
+        return PW_OK;
     });
-    const int n = std::min<int>(n_change, (int)cand.size());
-    for (int i = 0; i < n; ++i) {
-        ids_out[i] = cand[i].id;
-        q_out[i] = (uint8_t)(q_cur[cand[i].b] + (lower ? -1 : 1));
-    }
-    *n_out = n;
-    return PW_OK;
 }
