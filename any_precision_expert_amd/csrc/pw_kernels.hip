@@ -1010,43 +1010,55 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
         }
 
         // cross-wave reduction through the slices: wave w's partial of (row r,
-        // token n) at byte 4 (r TP + n) of its slice (SHARE: of half w % 2 of
-        // slice w / 2).  SHARE with 128-row tiles sums in two phases in the
-        // 16 KB slice region (row group g's sums at 4 KB g): the partials of
-        // K-wave 1, then K-wave 0 adds its own (the same order and rounding as
-        // the one-phase sum 0 + p0 + p1).
+        // token n) at word rix(r, n) = 32 n + (r ^ n) of its slice (SHARE: of
+        // half w % 2 of slice w / 2), token-major so the epilogue reads and
+        // stores run along rows; the XOR keeps both the partial stores (lanes
+        // = tokens) and the epilogue reads (lanes = rows) free of bank
+        // conflicts.  SHARE with 128-row tiles sums in two phases in the 16 KB
+        // slice region (row group g's sums at 4 KB g): the partials of K-wave
+        // 1, then K-wave 0 adds its own (the same order and rounding as the
+        // one-phase sum 0 + p0 + p1).
         static_assert(!(SHARE && RG == 4) || KW == 2, "two-phase sum of two K-waves");
         sbuf = 0;  // the 64-row tiles' reduction uses buffer 0's contiguous 32 KB
-        auto red4 = [&](int g, int r, int n) -> float* { return (float*)(ldsb + kLutBytes + 4096 * g + 4 * (r * 32 + n)); };
+        auto rix = [](int r, int n) { return 32 * n + (r ^ (n & 31)); };
+        auto red4 = [&](int g, int r, int n) -> float* { return (float*)(ldsb + kLutBytes + 4096 * g + 4 * rix(r, n)); };
         __syncthreads();
         auto red = [&](int w, int r, int n) -> float* {
-            if constexpr (SHARE) return (float*)slice_at(w >> 1, 4096 * (w & 1) + 4 * (r * TP + n));
-            else return (float*)slice_at(w, 4 * (r * TP + n));
+            if constexpr (SHARE) return (float*)slice_at(w >> 1, 4096 * (w & 1) + 4 * rix(r, n));
+            else return (float*)slice_at(w, 4 * rix(r, n));
         };
+        // this lane's partial C[i] (row r_i = 8 (i / 4) + 4 kh + i % 4, token
+        // rho) goes to word 32 rho + (r_i ^ rho) = 32 rho + (c_i ^ mx); mx is
+        // made opaque here so the sixteen addresses are formed per pass and not
+        // hoisted into registers held across the K loop
+        int mx = (kh << 2) ^ rho;
+        asm volatile("" : "+v"(mx));
+        auto wix = [&](int i) { return 32 * rho + ((((i >> 2) << 3) | (i & 3)) ^ mx); };
         if constexpr (SHARE && RG == 4) {
             if (nvalid && kw == 1) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) *red4(grp, 8 * (i >> 2) + 4 * kh + (i & 3), rho) = C[i];
+                for (int i = 0; i < 16; ++i) *(float*)(ldsb + kLutBytes + 4096 * grp + 4 * wix(i)) = C[i];
             }
             __syncthreads();
             if (nvalid && kw == 0) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    float* p = red4(grp, 8 * (i >> 2) + 4 * kh + (i & 3), rho);
+                    float* p = (float*)(ldsb + kLutBytes + 4096 * grp + 4 * wix(i));
                     *p = C[i] + *p;
                 }
             }
         } else if (nvalid) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int r = 8 * (i >> 2) + 4 * kh + (i & 3);
-                *red(wave, r, rho) = C[i];
+                if constexpr (SHARE) *(float*)slice_at(wave >> 1, 4096 * (wave & 1) + 4 * wix(i)) = C[i];
+                else *(float*)slice_at(wave, 4 * wix(i)) = C[i];
             }
         }
         __syncthreads();
         if (MODE == 0) {
+            // rows fastest: a wave stores 64 consecutive h entries of one token
             for (int idx = tid; idx < HR * nt; idx += kThreads) {
-                const int hr = idx / nt, n = idx - hr * nt;
+                const int n = idx / HR, hr = idx % HR;
                 const int sub = hr >> 5, r = hr & 31;
                 float g = 0.0f, u = 0.0f;
                 if constexpr (SHARE && RG == 4) {
@@ -1068,7 +1080,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
             }
         } else {
             for (int idx = tid; idx < TR * nt; idx += kThreads) {
-                const int rt = idx / nt, n = idx - rt * nt;
+                const int n = idx / TR, rt = idx % TR;
                 const int g = rt >> 5, r = rt & 31;
                 float d = 0.0f;
                 if constexpr (SHARE && RG == 4) {

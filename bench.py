@@ -473,7 +473,9 @@ UNIFORM_WIDTHS = (4, 5, 8)
 
 
 def _graph_ms(run_steps, L, steps, stream):
-    """ms per step of `run_steps(L)` captured in one HIP graph and replayed."""
+    """ms per step of `run_steps(L)` captured in one HIP graph and replayed:
+    as many untimed replays as timed ones first, so the clocks and caches are
+    in their steady state (a single cold measurement read up to 8% slower)."""
     import torch
     with torch.cuda.stream(stream):
         run_steps(L)
@@ -485,7 +487,7 @@ def _graph_ms(run_steps, L, steps, stream):
     reps = max(1, steps // L)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        for _ in range(2):
+        for _ in range(max(2, reps)):
             graph.replay()
         ev0.record(stream)
         for _ in range(reps):
