@@ -514,6 +514,77 @@ __device__ __forceinline__ RoutePick route_pick(const float* __restrict__ logits
     return RoutePick{lane < k ? lane : -1, e, wv};
 }
 
+// Top-k of token t's logits by one lane, for E <= EM (8, 16 or 32): the
+// same keys, picks and softmax arithmetic as route_token (so the results are
+// bit-identical), with the E keys in the lane's registers instead of across a
+// wave.  A wave routes 64 tokens at once; a batch of up to 1024 tokens takes
+// one round trip for its logits instead of one per token and wave.
+template <int EM>
+__device__ __forceinline__ void route_lane(const float* __restrict__ logits, int t, int E, int k, int (&eo)[8],
+                                           float (&wo)[8])
+{
+    // the high key words only: an entry's low word is fixed by its index, so
+    // the order (value descending, index ascending) is a scan in index order
+    // that replaces the best on a strictly larger value; picked entries are
+    // masked out by a bit each
+    const float* l = logits + (size_t)t * E;
+    uint32_t hi[EM];
+#pragma unroll
+    for (int e = 0; e < EM; ++e) hi[e] = route_key(l[min(e, E - 1)], e).hi;
+    uint32_t used = 0;
+    float m = 0.0f, s = 0.0f, ex[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ex[j] = 0.0f;
+        eo[j] = -1;
+        if (j < k) {
+            uint32_t bh = 0u;
+            int be = -1;
+#pragma unroll
+            for (int e = 0; e < EM; ++e) {
+                const bool take = e < E && !((used >> e) & 1u) && (be < 0 || hi[e] > bh);
+                bh = take ? hi[e] : bh;
+                be = take ? e : be;
+            }
+            used |= 1u << be;
+            const float bv = route_key_value(bh);
+            if (j == 0) m = bv;
+            ex[j] = expf(bv - m);
+            s += ex[j];
+            eo[j] = be;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wo[j] = j < k ? ex[j] / s : 0.0f;
+}
+
+// Largest expert count routed one token per lane.
+constexpr int kLaneRouteMaxE = 32;
+
+__device__ __forceinline__ void route_lane_any(const float* __restrict__ logits, int t, int E, int k, int (&eo)[8],
+                                               float (&wo)[8])
+{
+    if (E <= 8) route_lane<8>(logits, t, E, k, eo, wo);
+    else if (E <= 16) route_lane<16>(logits, t, E, k, eo, wo);
+    else route_lane<32>(logits, t, E, k, eo, wo);
+}
+
+__global__ void __launch_bounds__(256) route_topk_lane_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                              int32_t* __restrict__ idx, float* __restrict__ w)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    int eo[8];
+    float wo[8];
+    route_lane_any(logits, t, E, k, eo, wo);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k) {
+            idx[(size_t)t * k + j] = eo[j];
+            w[(size_t)t * k + j] = wo[j];
+        }
+}
+
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T, int E,
                                                          int k, int32_t* __restrict__ idx,
                                                          float* __restrict__ w)
@@ -663,10 +734,10 @@ __device__ __forceinline__ void sort_small(const int* sidx, int n, int E, int32_
     if (e < E) sorted[base[e] + rank] = lane;
 }
 
-// Routing and permutation of a decode-sized batch in one workgroup: the 16
-// waves route the tokens (one token per wave at a time), the assignments stay
-// in LDS, and the same workgroup sorts them.  Results equal those of the two
-// separate kernels.
+// Routing and permutation of a decode-sized batch in one workgroup: the
+// threads route the tokens (up to 32 experts one token per lane, else one
+// token per wave at a time), the assignments stay in LDS, and the same
+// workgroup sorts them.  Results equal those of the two separate kernels.
 __global__ void __launch_bounds__(1024) route_permute_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                              int32_t* __restrict__ idx, float* __restrict__ w,
                                                              int32_t* __restrict__ offsets,
@@ -677,12 +748,27 @@ __global__ void __launch_bounds__(1024) route_permute_kernel(const float* __rest
     __shared__ int wcnt[16][256];
     __shared__ int sidx[kFusedMaxAssign];
     const int wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += 16) {
-        const RoutePick p = route_pick(logits, t, E, k);
-        if (p.j >= 0) {
-            idx[(size_t)t * k + p.j] = p.e;
-            w[(size_t)t * k + p.j] = p.w;
-            sidx[t * k + p.j] = p.e;
+    if (E <= kLaneRouteMaxE) {
+        for (int t = threadIdx.x; t < T; t += 1024) {
+            int eo[8];
+            float wo[8];
+            route_lane_any(logits, t, E, k, eo, wo);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < k) {
+                    idx[(size_t)t * k + j] = eo[j];
+                    w[(size_t)t * k + j] = wo[j];
+                    sidx[t * k + j] = eo[j];
+                }
+        }
+    } else {
+        for (int t = wave; t < T; t += 16) {
+            const RoutePick p = route_pick(logits, t, E, k);
+            if (p.j >= 0) {
+                idx[(size_t)t * k + p.j] = p.e;
+                w[(size_t)t * k + p.j] = p.w;
+                sidx[t * k + p.j] = p.e;
+            }
         }
     }
     __syncthreads();
@@ -1199,7 +1285,8 @@ __global__ void __launch_bounds__(256) fill_f64_kernel(double* p, int64_t n)
 }
 
 // Routing of the whole batch inside a gate_up workgroup (n = T * k <= 64):
-// the waves route the tokens, wave 0 sorts the assignments.  LDS layout of rt
+// the threads route the tokens (one per lane up to 32 experts, else one per
+// wave at a time), wave 0 sorts the assignments.  LDS layout of rt
 // (words): idx [64] | w [64] | offsets [257] | sorted [64] | cnt [256] | base [256].
 constexpr int kRtIdx = 0, kRtW = 64, kRtOff = 128, kRtSorted = 385, kRtCnt = 449, kRtBase = 705, kRtWords = 961;
 static_assert(kRtWords <= kWaves * kSliceWords, "routing scratch lives in the slice region");
@@ -1207,11 +1294,26 @@ static_assert(kRtWords <= kWaves * kSliceWords, "routing scratch lives in the sl
 __device__ __forceinline__ void route_in_workgroup(const FfnArgs& a, int* rt)
 {
     const int wave = threadIdx.x >> 6;
-    for (int t = wave; t < a.T; t += kWaves) {
-        const RoutePick p = route_pick(a.logits, t, a.E, a.k);
-        if (p.j >= 0) {
-            rt[kRtIdx + t * a.k + p.j] = p.e;
-            ((float*)rt)[kRtW + t * a.k + p.j] = p.w;
+    if (a.E <= kLaneRouteMaxE) {
+        const int t = threadIdx.x;  // T <= 64 here
+        if (t < a.T) {
+            int eo[8];
+            float wo[8];
+            route_lane_any(a.logits, t, a.E, a.k, eo, wo);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < a.k) {
+                    rt[kRtIdx + t * a.k + j] = eo[j];
+                    ((float*)rt)[kRtW + t * a.k + j] = wo[j];
+                }
+        }
+    } else {
+        for (int t = wave; t < a.T; t += kWaves) {
+            const RoutePick p = route_pick(a.logits, t, a.E, a.k);
+            if (p.j >= 0) {
+                rt[kRtIdx + t * a.k + p.j] = p.e;
+                ((float*)rt)[kRtW + t * a.k + p.j] = p.w;
+            }
         }
     }
     __syncthreads();
@@ -2049,7 +2151,10 @@ static void launch(Kern kernel, dim3 grid, dim3 block, hipStream_t s, Args... ar
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s)
 {
-    launch(route_topk_kernel, dim3((T + 3) / 4), dim3(256), s, logits, T, E, k, idx, w);
+    if (E <= kLaneRouteMaxE)
+        launch(route_topk_lane_kernel, dim3((T + 255) / 256), dim3(256), s, logits, T, E, k, idx, w);
+    else
+        launch(route_topk_kernel, dim3((T + 3) / 4), dim3(256), s, logits, T, E, k, idx, w);
     return hipGetLastError();
 }
 

@@ -77,11 +77,12 @@ def test_ffn_decode_paths_bit_exact(q, shape):
 
 # ------------------------------------------------------------------ routing
 
-# Expert counts around the 64-lane groups of the top-k (E = 16, 17, 33, 63,
-# 64) and exact ties on every fourth token.
+# Expert counts around the 64-lane groups of the wave-per-token top-k (E = 33,
+# 63, 64), the one-token-per-lane top-k up to 32 experts (E = 1..32, k up to
+# 8) and exact ties on every fourth token.
 @pytest.mark.parametrize("T,E,k", [(1, 4, 2), (16, 4, 2), (37, 60, 4), (300, 8, 2), (4096, 8, 2),
                                    (64, 256, 8), (5, 7, 7), (1000, 1, 1), (9, 16, 3), (23, 17, 5),
-                                   (50, 33, 2), (40, 63, 6), (31, 64, 8)])
+                                   (50, 33, 2), (40, 63, 6), (31, 64, 8), (70, 32, 4), (200, 12, 8)])
 def test_route_and_permute_bit_exact(T, E, k):
     import torch
     import oracle
