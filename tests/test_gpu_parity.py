@@ -396,6 +396,51 @@ def test_decode_calls_repeatable(qwen, T):
         compare(gpu, oracle.moe_layer(w, acts[i]), label="repeated T=%d batch %d" % (T, i))
 
 
+@pytest.mark.parametrize("T", [4, 16])
+def test_graph_replays_repeatable(qwen, T):
+    """pw_moe_layer captured in a HIP graph (two batches sharing one
+    workspace, so the fused launch's counters and epoch carry over from call
+    to call) and replayed six times, with eager calls on the same workspace
+    (fused and separate) between the replays: every replay's y equals the
+    eager result bit for bit."""
+    import torch
+    from any_precision_expert_amd.layer import Batch
+    w, ctx = qwen
+    spec = pw_synth.CONFIGS[1]
+    acts = [pw_synth.make_activations(spec.shape, T, pw_synth.config_seed(1), 0, 40 + i, spec.logits, w.rank)
+            for i in range(2)]
+    batches = []
+    for a in acts:
+        b = Batch(ctx, T)
+        b.load(a.logits, a.x)
+        batches.append(b)
+    batches[1].ws = batches[0].ws  # one workspace for both
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for b in batches:
+            b.step(0, stream)
+    torch.cuda.synchronize()
+    want = [b.y.clone() for b in batches]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for b in batches:
+            b.step(0, stream)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        for b in batches:
+            b.y.fill_(-7.0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        for i, b in enumerate(batches):
+            assert torch.equal(b.y.view(torch.int16), want[i].view(torch.int16)), "replay %d batch %d" % (rep, i)
+        with torch.cuda.stream(stream):
+            batches[rep % 2].step(0, stream, separate=(rep % 3 == 2))
+        torch.cuda.synchronize()
+        assert torch.equal(batches[rep % 2].y.view(torch.int16), want[rep % 2].view(torch.int16)), "eager %d" % rep
+
+
 @pytest.mark.parametrize("T", [16, 300])
 def test_layer_call_equals_separate_calls_toy(T):
     from any_precision_expert_amd.layer import register_layer
