@@ -399,10 +399,9 @@ def test_decode_calls_repeatable(qwen, T):
 @pytest.mark.parametrize("T", [4, 16])
 def test_graph_replays_repeatable(qwen, T):
     """pw_moe_layer captured in a HIP graph (two batches sharing one
-    workspace, so the fused launch's counters and epoch carry over from call
-    to call) and replayed six times, with eager calls on the same workspace
-    (fused and separate) between the replays: every replay's y equals the
-    eager result bit for bit."""
+    workspace) and replayed six times, with eager calls on the same workspace
+    (in-launch and separate routing) between the replays: every replay's y
+    equals the eager result bit for bit."""
     import torch
     from any_precision_expert_amd.layer import Batch
     w, ctx = qwen
