@@ -1015,7 +1015,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
         a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         a.tiles_routed = (d.hidden + 32 * a.rg - 1) / (32 * a.rg);
         a.tiles_shared = d.inter_shared ? (d.hidden + 32 * a.rg - 1) / (32 * a.rg) : 0;
-        a.splits_routed = down_splits(d.inter);
+        a.splits_routed = down_splits_routed(d.inter, T, d.top_k, E, a.tiles_routed, c->num_cus);
         a.splits_shared = d.inter_shared ? down_splits(d.inter_shared) : 1;
         if ((e = launch_down(a, s)) != hipSuccess) return hip_fail(e, "down launch");
     }

@@ -129,6 +129,24 @@ inline int down_splits(int K)
     return nchunks <= per ? 1 : (nchunks + per - 1) / per;
 }
 
+// K splits of the routed down tiles of a decode launch: the fewest (powers of
+// two, at most down_splits(K)) that keep ~1.75 workgroups per CU busy, counting
+// the row tiles of the experts a batch is expected to activate (an expert is
+// idle with probability (1 - k/E)^T).  Each split re-stages the tile's LUT and
+// pays the tile's start-up chain, so splits only pay where there are too few
+// active tiles to fill the chip.  Mixtral-shaped down (112 chunks, 64 row
+// tiles), 4 / 2 / 1 splits: batch 1 23.5 / 25.1 / 41.2 us, batch 4 53.8 /
+// 46.8 / 58.1, batch 16 76.2 / 64.4 / 64.2, batch 64 93.1 / 81.7 / 75.8.
+inline int down_splits_routed(int K, int T, int k, int E, int tiles, int cus)
+{
+    const int cap = down_splits(K);
+    const double idle = __builtin_pow(1.0 - (double)k / E, (double)T);
+    const double active_tiles = (double)tiles * E * (1.0 - idle);
+    int s = 1;
+    while (s < cap && active_tiles * s < 1.75 * cus) s *= 2;
+    return s < cap ? s : cap;
+}
+
 // Workspace carve-up for T tokens (byte offsets, 256-aligned): h as fp16
 // [T*k (+T)][max(I, Is)], then the per-split down outputs
 // [splits][T*k (+T)][H] fp32.
