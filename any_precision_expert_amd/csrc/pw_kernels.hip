@@ -1040,6 +1040,15 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
                 // would wait on that slot's loads too)
                 __builtin_amdgcn_sched_barrier(0);
                 const int ci = ci0 + d;
+                // Waves w and w + 4 share a SIMD, and issue arbitration favours
+                // the older one: waves 4-7 (gate_up's up rows) ended their K loop
+                // ~3 us after waves 0-3.  Swapping which wave of the pair has the
+                // higher issue priority every chunk keeps the pair in step
+                // (Qwen-shaped batch 4 step 0.0373 -> 0.0362 ms).
+                if constexpr (!SHARE) {
+                    if ((ci ^ (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
+                    else __builtin_amdgcn_s_setprio(0);
+                }
                 const bool live = ci < nch;  // padding chunk of the ring: B = 0
                 const int c = min(first + ci * KW, lastc);
                 // this chunk's activations -> the wave's slice (zero past K and
@@ -1095,6 +1104,7 @@ __device__ __forceinline__ void mfma_block(const KArgs& a, const BlockDesc* __re
             }
         }
 
+        if constexpr (!SHARE) __builtin_amdgcn_s_setprio(0);
         // cross-wave reduction through the slices: wave w's partial of (row r,
         // token n) at word rix(r, n) = 32 n + (r ^ n) of its slice (SHARE: of
         // half w % 2 of slice w / 2), token-major so the epilogue reads and
