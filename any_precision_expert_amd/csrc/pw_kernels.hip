@@ -446,10 +446,54 @@ __device__ __forceinline__ void route_dpp_step(RouteKey& a)
     route_key_max(a, oh, ol);
 }
 
+// Wave-wide maximum of an unsigned word (the same DPP pattern as the key
+// maximum below; 0 is the identity, so lanes a step leaves out keep theirs).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of token t's logits for E <= 64, lane = expert: each pick is the
+// wave maximum of the 32-bit high key words of the experts still in play,
+// then the lowest lane holding it (the same order as the 64-bit keys: value
+// descending, index ascending), so the results equal route_token's with a
+// quarter of its instructions on the dependent chain.
+__device__ __forceinline__ int route_token64(const float* __restrict__ logits, int t, int E, int k, float& wout)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t hi = route_key(logits[(size_t)t * E + min(lane, E - 1)], lane).hi;
+    bool alive = lane < E;
+    int out = -1;
+    float mine = 0.0f, m = 0.0f, s = 0.0f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+        const uint32_t mx = wave_max_u32(alive ? hi : 0u);
+        const uint64_t win = __ballot(alive && hi == mx);
+        const int w = __ffsll((long long)win) - 1;
+        alive = alive && lane != w;
+        const float bv = route_key_value(mx);
+        if (j == 0) m = bv;
+        const float ex = expf(bv - m);
+        s += ex;
+        const bool me = lane == j;
+        out = me ? w : out;
+        mine = me ? ex : mine;
+    }
+    wout = lane < k ? mine / s : 0.0f;
+    return out;
+}
+
 // Top-k of token t's logits by one wave; lanes j < k hold the j-th expert
 // and its gate weight (returned; other lanes return -1).
 __device__ __forceinline__ int route_token(const float* __restrict__ logits, int t, int E, int k, float& wout)
 {
+    if (E <= 64) return route_token64(logits, t, E, k, wout);
     const int lane = threadIdx.x & 63;
     const float* l = logits + (size_t)t * E;
     RouteKey key[4];
