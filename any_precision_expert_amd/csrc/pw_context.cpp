@@ -348,6 +348,7 @@ public:
     }
     void run(const std::function<void(int, int)>& fn)
     {
+        std::lock_guard<std::mutex> one(run_mu_);  // one run at a time (callers on several threads)
         {
             std::lock_guard<std::mutex> g(mu_);
             fn_ = &fn;
@@ -381,7 +382,7 @@ private:
     }
     int n_ = 1;
     std::vector<std::thread> th_;
-    std::mutex mu_;
+    std::mutex run_mu_, mu_;
     std::condition_variable cv_, done_;
     const std::function<void(int, int)>* fn_ = nullptr;
     uint64_t gen_ = 0;
@@ -407,6 +408,7 @@ struct StageChunk {
     CopyDesc* list = nullptr;       // pinned copy list ...
     const CopyDesc* dlist = nullptr;  // ... and its device-side address
     hipEvent_t ev = nullptr;        // behind the chunk's last scatter
+    hipEvent_t gev = nullptr;       // behind the chunk's gather (gather stream)
     uint64_t used = 0;              // use order
 };
 
@@ -468,6 +470,7 @@ struct pw_ctx {
     std::vector<StageChunk> chunks;  // gather staging of width-change copies (reserved to kStageChunksMax)
     uint64_t chunk_uses = 0;
     std::unique_ptr<Gang> gang;      // gather threads, started with the first width change
+    hipStream_t gather_stream = nullptr;  // runs the gathers of staged copies (host functions)
     int num_cus = 256;  // compute units of the device (decode tile schedule)
     int tok_pass = 0;   // decode tokens per pass set by pw_set_tokens_per_pass (0: chosen per call)
     void* scratch = nullptr;  // this device's library-held workspace (pw_moe_layer_noalloc)
@@ -699,12 +702,14 @@ pw_status pw_destroy(pw_ctx* c)
         if (!c) return ok();
         (void)hipSetDevice(c->device);
         (void)hipDeviceSynchronize();
+        if (c->gather_stream) (void)hipStreamSynchronize(c->gather_stream);  // gathers use the gang and chunks
         prof_release(c);
         for (auto& b : c->blocks)
             if (b.registered) free_block_now(c, b);
         for (auto& s : c->staging) (void)hipHostFree(s.p);
         c->gang.reset();
         for (auto& ch : c->chunks) free_chunk(ch);
+        if (c->gather_stream) (void)hipStreamDestroy(c->gather_stream);
         c->pool.clear();
         c->evs.clear();
         (void)hipFree(c->d_table);
@@ -1171,6 +1176,7 @@ static void free_chunk(StageChunk& ch)
         (void)hipEventSynchronize(ch.ev);
         (void)hipEventDestroy(ch.ev);
     }
+    if (ch.gev) (void)hipEventDestroy(ch.gev);
     if (ch.h) (void)hipHostFree(ch.h);
     if (ch.list) (void)hipHostFree(ch.list);
     if (ch.d) (void)hipFree(ch.d);
@@ -1185,6 +1191,7 @@ static hipError_t alloc_chunk(StageChunk& ch)
     if (e == hipSuccess) e = hipHostGetDevicePointer(&dl, ch.list, 0);
     if (e == hipSuccess) e = hipMalloc((void**)&ch.d, kStageChunkBytes);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ch.ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ch.gev, hipEventDisableTiming);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_chunk(ch);
@@ -1231,15 +1238,53 @@ static hipError_t take_chunk(pw_ctx* c, StageChunk** out)
     return hipSuccess;
 }
 
+// The gather of one staging chunk, run as a host function on the context's
+// gather stream: the gang copies the items' source ranges into the pinned
+// chunk, and the chunk's DMA on the copy stream waits for it (an event).  The
+// caller of a width request is not held for the gathers (~3 ms per 300 MB),
+// and one chunk's gather runs while the previous chunk is in flight.  The
+// function makes no HIP calls.
+struct GatherJob {
+    Gang* gang;
+    char* dst;
+    size_t total;
+    std::vector<std::pair<const char*, size_t>> src;  // source, bytes
+    std::vector<size_t> at;                            // offsets in the chunk
+};
+
+static void gather_in_stream(void* user)
+{
+    GatherJob* j = (GatherJob*)user;
+    try {
+        j->gang->run([j](int m, int M) {
+            const size_t lo = j->total * m / M, hi = j->total * (m + 1) / M;
+            for (size_t k = 0; k < j->src.size(); ++k) {
+                const size_t a = j->at[k], b = a + j->src[k].second;
+                const size_t s0 = std::max(a, lo), s1 = std::min(b, hi);
+                if (s0 < s1) std::memcpy(j->dst + s0, j->src[k].first + (s0 - a), s1 - s0);
+            }
+        });
+    } catch (...) {
+        // a gang that cannot run leaves the whole copy to this thread
+        for (size_t k = 0; k < j->src.size(); ++k) std::memcpy(j->dst + j->at[k], j->src[k].first, j->src[k].second);
+    }
+    delete j;
+}
+
 // Enqueue `items` on stream xs through the staging chunks (see StageChunk):
-// per chunk the gather (host threads), one DMA, one scatter launch.  Items
-// larger than a chunk, and every item when no chunk can be allocated, are one
-// DMA each.  Returns once everything is enqueued.
+// per chunk the gather (host threads, a host function on the gather stream),
+// one DMA after it, one scatter launch.  Items larger than a chunk, and every
+// item when no chunk can be allocated, are one DMA each.  Returns once
+// everything is enqueued.
 static hipError_t stage_copies(pw_ctx* c, const std::vector<CopyItem>& items, hipStream_t xs)
 {
     if (!c->gang) {
         const unsigned hw = std::thread::hardware_concurrency();
         c->gang.reset(new Gang(std::max(1, std::min(kGatherThreads, (int)(hw / 2)))));
+    }
+    if (!c->gather_stream) {
+        const hipError_t e = hipStreamCreateWithFlags(&c->gather_stream, hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
     }
     std::vector<size_t> at;
     size_t i = 0;
@@ -1266,17 +1311,22 @@ static hipError_t stage_copies(pw_ctx* c, const std::vector<CopyItem>& items, hi
             off = (total + 255) & ~(size_t)255;
             ++i;
         }
-        // member m copies bytes [total m / M, total (m + 1) / M) of the packed chunk
+        // the gather (gang member m copies bytes [total m / M, total (m + 1) / M)
+        // of the packed chunk) runs on the stream ahead of the chunk's DMA
         const size_t i1 = i;
-        c->gang->run([&](int m, int M) {
-            const size_t lo = total * m / M, hi = total * (m + 1) / M;
-            for (size_t j = i0; j < i1; ++j) {
-                const size_t a = at[j - i0], b = a + items[j].bytes;
-                const size_t s0 = std::max(a, lo), s1 = std::min(b, hi);
-                if (s0 < s1) std::memcpy(ch->h + s0, items[j].src + (s0 - a), s1 - s0);
-            }
-        });
-        hipError_t e = hipMemcpyAsync(ch->d, ch->h, total, hipMemcpyHostToDevice, xs);
+        std::unique_ptr<GatherJob> job(new GatherJob);
+        job->gang = c->gang.get();
+        job->dst = ch->h;
+        job->total = total;
+        job->at = at;
+        job->src.reserve(i1 - i0);
+        for (size_t j = i0; j < i1; ++j) job->src.emplace_back(items[j].src, items[j].bytes);
+        hipError_t e = hipLaunchHostFunc(c->gather_stream, gather_in_stream, job.get());
+        if (e != hipSuccess) return e;
+        job.release();  // gather_in_stream frees it
+        e = hipEventRecord(ch->gev, c->gather_stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(xs, ch->gev, 0);
+        if (e == hipSuccess) e = hipMemcpyAsync(ch->d, ch->h, total, hipMemcpyHostToDevice, xs);
         if (e == hipSuccess) e = launch_scatter_copy(ch->dlist, (int)(i1 - i0), xs);
         if (e == hipSuccess) e = hipEventRecord(ch->ev, xs);
         if (e != hipSuccess) return e;

@@ -305,10 +305,11 @@ pw_status pw_set_committed_bits(pw_ctx *ctx, int n, const int32_t *block_ids,
  * from the pinned host masters (lowering copies only the smaller LUT).  The
  * copies go through library-held staging (up to 16 chunks of 32 MB pinned
  * host and 32 MB device memory, kept until pw_destroy): host threads of the
- * library gather the source ranges into a pinned chunk before this call
- * returns (about 3 ms per 300 MB on eight threads), one DMA per chunk moves
- * it and one short kernel on `copy` scatters it into the new slabs, so the
- * kernels running meanwhile lose almost nothing to the copies.  The
+ * library gather the source ranges into a pinned chunk (about 3 ms per 300 MB
+ * on eight threads) in a host function on a library-owned stream, so this
+ * call returns once the work is enqueued; one DMA per chunk on `copy` waits
+ * for its gather, and one short kernel on `copy` scatters it into the new
+ * slabs, so the kernels running meanwhile lose little to the copies.  The
  * committed widths do not change.  Errors as pw_set_committed_bits, plus
  * STATE for a block that already has a request in flight (one request per
  * block until it is committed).
