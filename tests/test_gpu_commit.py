@@ -292,3 +292,43 @@ def test_staged_copies_beyond_the_chunk_ring():
         say("staged raise of %d blocks: resident %.2f GB" % (len(ids), ctx.resident_bytes() / 1e9))
     finally:
         ctx.close()
+
+
+def test_close_with_staged_copies_in_flight():
+    """pw_destroy right after pw_request_widths, with the staged gathers, DMAs
+    and scatters of ~500 MB still queued (no synchronisation, no commit): the
+    context waits for them before it frees the staging and its gather
+    threads, and a new context on the same device then runs a layer that
+    matches the oracle."""
+    import torch
+    import any_precision_expert_amd as pw
+    E, H, I = 4, 4096, 14336
+    ctx = pw.Context(0, 1, E, H, I, 2, 0)
+    closed = False
+    try:
+        rng = np.random.default_rng(902)
+        for e in range(E):
+            for m in (0, 1):
+                R, K = (2 * I, H) if m == 0 else (H, I)
+                c = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
+                luts = {k: np.zeros((R, 1 << k), np.float16) for k in range(3, 9)}
+                ctx.register_block(0, e, m, pw.pack_bitplanes(c), pw.concat_luts(luts), 3)
+        ids = [ctx.block_id(0, e, m) for e in range(E) for m in (0, 1)]
+        copy_stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        ctx.request_widths(ids, [8] * len(ids), copy_stream)
+        ctx.close()
+        closed = True
+    finally:
+        if not closed:
+            ctx.close()
+    torch.cuda.synchronize()
+    import oracle
+    from any_precision_expert_amd.layer import register_layer
+    w, a = _layer(seed=903)
+    ctx2 = make_ctx(w.shape)
+    try:
+        register_layer(ctx2, 0, w)
+        compare(_fetch(_run(ctx2, a)), oracle.moe_layer(w, a), label="after closing with copies in flight")
+    finally:
+        ctx2.close()
