@@ -1329,7 +1329,13 @@ static hipError_t stage_copies(pw_ctx* c, const std::vector<CopyItem>& items, hi
         if (e == hipSuccess) e = hipMemcpyAsync(ch->d, ch->h, total, hipMemcpyHostToDevice, xs);
         if (e == hipSuccess) e = launch_scatter_copy(ch->dlist, (int)(i1 - i0), xs);
         if (e == hipSuccess) e = hipEventRecord(ch->ev, xs);
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess) {
+            // the chunk's event is stale: let the queued gather and copies end
+            // before the chunk (or a slab they write) can be reused
+            (void)hipStreamSynchronize(c->gather_stream);
+            (void)hipStreamSynchronize(xs);
+            return e;
+        }
     }
     return hipSuccess;
 }
