@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <condition_variable>
 #include <cstdarg>
 #include <cstdio>
@@ -1006,11 +1007,21 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
         // the halves fit in the second slots; a single token activates exactly
         // k experts, and when those units' halves would overflow the second
         // slots into another round, whole units are faster (Mixtral-shaped
-        // batch 1: 448 units, gate_up 47.6 -> 44.7 us).
+        // batch 1: 448 units, gate_up 47.6 -> 44.7 us).  A launch expected to
+        // hold more than three units per CU (experts active with probability
+        // 1 - (1 - k/E)^T) runs several rounds anyway, and there halves only
+        // add workgroup start-ups: whole units took Mixtral-shaped gate_up
+        // batch 4 111 -> 109 us, batch 16 165 -> 155, batch 64 208 -> 181
+        // (at two to three units per CU, Qwen-shaped batch 6 and 8, halves
+        // stay faster).
         a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         if (a.rg == 4 && T == 1) {
             const long long units = a.tiles_shared + (long long)d.top_k * a.tiles_routed;
             if (2 * (units - c->num_cus) > c->num_cus) a.big_wgs = 0;
+        }
+        if (a.rg == 4) {
+            const double active = E * (1.0 - std::pow(1.0 - (double)d.top_k / E, (double)T));
+            if (a.tiles_shared + active * a.tiles_routed > 3.0 * c->num_cus) a.big_wgs = 0;
         }
         if (route) {
             a.logits = route->logits;
