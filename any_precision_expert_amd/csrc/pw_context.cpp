@@ -997,6 +997,20 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     }
     {
         ProfScope ps(c, "gate_up", s);
+        // Expected 128-row units: the shared tiles plus the tiles of the experts
+        // a batch is expected to activate (each with probability 1 - (1 - k/E)^T).
+        // More than three per CU means several rounds of workgroups whatever the
+        // tile split; such launches take whole 128-row tiles (see big_wgs below),
+        // and 32-token passes where 16 would do: a 128-row tile needs 32-token
+        // passes (the 16-token form is for 64-row tiles only), and halving the
+        // workgroups paid more than the wider passes cost (Qwen-shaped gate_up
+        // batch 16 34.5 -> 29.5 us, batch 12 31.0 -> 29.0, Mixtral-shaped batch
+        // 32 186 -> 176; at batch 9 and 10, below the threshold, 64-row tiles of
+        // 16-token passes stay faster: 29.4 vs 31.1 us).
+        const double active = E * (1.0 - std::pow(1.0 - (double)d.top_k / E, (double)T));
+        const bool rounds = (d.inter_shared + 63) / 64 + active * ((d.inter + 63) / 64) > 3.0 * c->num_cus;
+        const int tok_pass_call = a.tok_pass;
+        if (a.tok_pass == 16 && !c->tok_pass && rounds) a.tok_pass = 32;
         a.rg = a.tok_pass == 16 ? 2 : kGateUpRowGroups;
         a.tiles_routed = (d.inter + 16 * a.rg - 1) / (16 * a.rg);
         a.tiles_shared = (d.inter_shared + 16 * a.rg - 1) / (16 * a.rg);
@@ -1007,22 +1021,17 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
         // the halves fit in the second slots; a single token activates exactly
         // k experts, and when those units' halves would overflow the second
         // slots into another round, whole units are faster (Mixtral-shaped
-        // batch 1: 448 units, gate_up 47.6 -> 44.7 us).  A launch expected to
-        // hold more than three units per CU (experts active with probability
-        // 1 - (1 - k/E)^T) runs several rounds anyway, and there halves only
-        // add workgroup start-ups: whole units took Mixtral-shaped gate_up
-        // batch 4 111 -> 109 us, batch 16 165 -> 155, batch 64 208 -> 181
-        // (at two to three units per CU, Qwen-shaped batch 6 and 8, halves
-        // stay faster).
+        // batch 1: 448 units, gate_up 47.6 -> 44.7 us).  A launch that runs
+        // several rounds anyway (`rounds`) only gains workgroup start-ups from
+        // halves: whole units took Mixtral-shaped gate_up batch 4 111 -> 109 us,
+        // batch 16 165 -> 155, batch 64 208 -> 181 (at two to three units per
+        // CU, Qwen-shaped batch 6 and 8, halves stay faster).
         a.big_wgs = a.rg == 4 ? c->num_cus : 0;
         if (a.rg == 4 && T == 1) {
             const long long units = a.tiles_shared + (long long)d.top_k * a.tiles_routed;
             if (2 * (units - c->num_cus) > c->num_cus) a.big_wgs = 0;
         }
-        if (a.rg == 4) {
-            const double active = E * (1.0 - std::pow(1.0 - (double)d.top_k / E, (double)T));
-            if (a.tiles_shared + active * a.tiles_routed > 3.0 * c->num_cus) a.big_wgs = 0;
-        }
+        if (a.rg == 4 && rounds) a.big_wgs = 0;
         if (route) {
             a.logits = route->logits;
             a.idx_out = route->idx;
@@ -1032,6 +1041,7 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
             a.mass = route->mass;
         }
         if ((e = launch_gate_up(a, s)) != hipSuccess) return hip_fail(e, "gate_up launch");
+        a.tok_pass = tok_pass_call;
         a.logits = nullptr;
         a.mass = nullptr;
     }

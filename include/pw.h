@@ -135,12 +135,17 @@ size_t pw_workspace_size(const pw_ctx *ctx, int T);
  * 32, the smallest that covers the largest token count a work unit is
  * expected to hold (the shared expert's T; routed experts: T top_k / E plus
  * two standard deviations of a Poisson count).  A unit holding more tokens
- * takes several passes, each decoding its weights again.  0 when T <= 0 or
- * the call takes the prefill GEMM path (T >= 256).  Pure function; no GPU. */
+ * takes several passes, each decoding its weights again.  Where this is 16
+ * and the gate_up launch is expected to hold more than three 128-row units
+ * per compute unit (active experts estimated as E (1 - (1 - top_k/E)^T)),
+ * gate_up runs 32-token passes over whole 128-row tiles instead; the down
+ * launch keeps 16.  0 when T <= 0 or the call takes the prefill GEMM path
+ * (T >= 256).  Pure function; no GPU. */
 int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared);
 
 /* Fix the decode contraction's tokens per pass of this context's later calls
- * to 8, 16 or 32 (0: chosen per call as pw_decode_tokens_per_pass states),
+ * to 8, 16 or 32 for both launches (0: chosen per call as
+ * pw_decode_tokens_per_pass states),
  * for callers that know their batches' spread over the experts better than
  * that estimate.  Results do not depend on it beyond rounding: 8- and
  * 32-token passes give bit-identical y, 16-token passes split K over four
