@@ -985,12 +985,13 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
             ProfScope ps(c, "down", s);
             a.tiles_routed = (d.hidden + 127) / 128;
             a.tiles_shared = d.inter_shared ? (d.hidden + 127) / 128 : 0;
+            // K in two halves where the workspace holds two partial planes
+            const int ws_splits = std::max(down_splits(d.inter), d.inter_shared ? down_splits(d.inter_shared) : 1);
+            a.splits_routed = a.splits_shared = std::min(2, ws_splits);
             if ((e = launch_prefill(a, 1, s)) != hipSuccess) return hip_fail(e, "prefill down launch");
         }
         {
             ProfScope ps(c, "combine", s);
-            a.splits_routed = 1;
-            a.splits_shared = 1;
             if ((e = launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
         }
         return ok();

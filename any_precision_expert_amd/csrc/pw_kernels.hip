@@ -1381,33 +1381,37 @@ __device__ __forceinline__ void route_in_workgroup(const FfnArgs& a, int* rt)
 // weighted and summed over the picks in pick order, plus the shared row
 // summed over its SS K splits.  Every load of the first split (and of up to
 // four shared splits) is issued before the first is used (clamped addresses,
-// masked sums): one memory round trip instead of one per term.
+// masked sums): one memory round trip instead of one per term.  KM >= k
+// picks and SU splits per round trip are compile-time bounds, so a launch with
+// few picks or splits issues no clamped duplicate loads (prefill-sized
+// batches: a load instruction per term, not the bytes, set the time).
+template <int KM, int SU>
 __device__ __forceinline__ float combine_value(const FfnArgs& a, int t, int o, int SR, int SS)
 {
     const size_t plane = (size_t)a.drows * a.H;
     const float* dr = a.dout + (size_t)t * a.k * a.H + o;                      // token t's routed rows
     const float* ds = SS ? a.dout + ((size_t)a.T * a.k + t) * a.H + o : dr;  // its shared row
-    float wj[8], dj[8], sv[4];
+    float wj[KM], dj[KM], sv[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wj[j] = a.topk_w[t * a.k + min(j, a.k - 1)];
+    for (int j = 0; j < KM; ++j) wj[j] = a.topk_w[t * a.k + min(j, a.k - 1)];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dj[j] = dr[(size_t)min(j, a.k - 1) * a.H];
+    for (int j = 0; j < KM; ++j) dj[j] = dr[(size_t)min(j, a.k - 1) * a.H];
 #pragma unroll
     for (int u = 0; u < 4; ++u) sv[u] = ds[(size_t)min(u, max(SS - 1, 0)) * plane];
-    for (int sp0 = 1; sp0 < SR; sp0 += 4) {
-        float v[4][8];
+    for (int sp0 = 1; sp0 < SR; sp0 += SU) {
+        float v[SU][KM];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < SU; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[u][j] = dr[(size_t)min(sp0 + u, SR - 1) * plane + (size_t)min(j, a.k - 1) * a.H];
+            for (int j = 0; j < KM; ++j) v[u][j] = dr[(size_t)min(sp0 + u, SR - 1) * plane + (size_t)min(j, a.k - 1) * a.H];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < SU; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dj[j] += sp0 + u < SR ? v[u][j] : 0.0f;
+            for (int j = 0; j < KM; ++j) dj[j] += sp0 + u < SR ? v[u][j] : 0.0f;
     }
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s += j < a.k ? wj[j] * dj[j] : 0.0f;
+    for (int j = 0; j < KM; ++j) s += j < a.k ? wj[j] * dj[j] : 0.0f;
     if (SS) {
         float sh = 0.0f;
 #pragma unroll
@@ -1635,7 +1639,8 @@ __device__ __forceinline__ half8_t pf_decode(const uint32_t (&W)[Q], const PfLan
 
 template <int MODE, int Q, int W>
 __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* __restrict__ bd, bool shared, int p0,
-                                              int ntok, int mtile, int ntile, uint32_t* lds)
+                                              int ntok, int mtile, int ntile, uint32_t* lds, int split = 0,
+                                              int nsplit = 1)
 {
     constexpr bool PAIR = LutLoad<Q, 4>::PAIR;
     constexpr int NTH = 64 * W;
@@ -1650,7 +1655,11 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
     const bool decoder = !SPLIT || wave < 8;
     const int R = bd->R;
     const int kwords = bd->kwords;
-    const int nsteps = kwords;
+    // K split `split` of nsplit (down): steps k0 .. k0 + nsteps - 1, partial
+    // outputs to plane `split` of dout (the combine sums the planes in order)
+    const int cps = (kwords + nsplit - 1) / nsplit;
+    const int k0 = min(split * cps, kwords);
+    const int nsteps = min(kwords - k0, cps);
     const int Iblk = R >> 1;
     const int TK = a.T * a.k;
     // decoder: a wave decodes 16 rows of the tile, four lanes per row (PfLane)
@@ -1702,7 +1711,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
         u32x4 xr[2][DX ? 4 : 1];
         uint32_t pw[2][DW ? Q : 1];
         auto issue = [&](int st, int slot) {
-            const int s = min(st, nsteps - 1);
+            const int s = k0 + min(st, nsteps - 1);
             if constexpr (DX) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) xr[slot][j] = *(gcu32x4p)(xbase + (xoff[j] + (uint32_t)s * (2 * kPfStepCols)));
@@ -1880,7 +1889,7 @@ __device__ __forceinline__ void prefill_block(const KArgs& a, const BlockDesc* _
                 if (n0 + t < ntok && row < R) {
                     const int orow = shared ? TK + n0 + t : a.sorted[p0 + n0 + t];
                     const u32x4 v = *(const u32x4*)&sto[t * 64 + ((4 * g4) ^ ((t & 15) << 2))];
-                    *(u32x4*)(a.dout + (size_t)orow * a.H + row) = v;
+                    *(u32x4*)(a.dout + ((size_t)split * a.drows + orow) * a.H + row) = v;
                 }
             }
         }
@@ -1901,21 +1910,30 @@ __global__ void __launch_bounds__(kPfThreads, kPfWaves / 4) ffn_prefill_kernel(F
     __shared__ __align__(16) uint32_t lds[kPfLdsWords];
     KArgs& ka = kernel_args();
     const int wg = blockIdx.x;
-    const int shared_wgs = a.tiles_shared * a.tok_tiles_shared;
+    // K splits (down): each (token tile, row tile) pair takes nsplit
+    // workgroups, row tiles fastest, then splits
+    const int nsplit = MODE == 1 ? a.splits_routed : 1;
+    const int shared_wgs = a.tiles_shared * a.tok_tiles_shared * nsplit;
     bool shared;
-    int mtile, ntile, p0, ntok, e;
+    int mtile, ntile, p0, ntok, e, split;
     if (wg < shared_wgs) {
         shared = true;
-        ntile = wg / a.tiles_shared;
-        mtile = wg - ntile * a.tiles_shared;
+        const int per = a.tiles_shared * nsplit;
+        ntile = wg / per;
+        const int rem = wg - ntile * per;
+        split = rem / a.tiles_shared;
+        mtile = rem - split * a.tiles_shared;
         p0 = 0;
         ntok = a.T;
         e = a.E;
     } else {
         shared = false;
         const int r = wg - shared_wgs;
-        const int gn = r / a.tiles_routed;
-        mtile = r - gn * a.tiles_routed;
+        const int per = a.tiles_routed * nsplit;
+        const int gn = r / per;
+        const int rem = r - gn * per;
+        split = rem / a.tiles_routed;
+        mtile = rem - split * a.tiles_routed;
         // expert of routed token tile gn: inclusive scan of the tile counts
         const int lane = threadIdx.x & 63;
         int base = 0;
@@ -1948,23 +1966,24 @@ __global__ void __launch_bounds__(kPfThreads, kPfWaves / 4) ffn_prefill_kernel(F
     }
     const BlockDesc* bd = a.table + (e * 2 + MODE);
     switch (bd->q) {
-        case 3: prefill_block<MODE, 3, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 4: prefill_block<MODE, 4, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 5: prefill_block<MODE, 5, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 6: prefill_block<MODE, 6, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 7: prefill_block<MODE, 7, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
-        case 8: prefill_block<MODE, 8, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds); break;
+        case 3: prefill_block<MODE, 3, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds, split, nsplit); break;
+        case 4: prefill_block<MODE, 4, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds, split, nsplit); break;
+        case 5: prefill_block<MODE, 5, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds, split, nsplit); break;
+        case 6: prefill_block<MODE, 6, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds, split, nsplit); break;
+        case 7: prefill_block<MODE, 7, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds, split, nsplit); break;
+        case 8: prefill_block<MODE, 8, kPfWaves>(ka, bd, shared, p0, ntok, mtile, ntile, lds, split, nsplit); break;
         default: break;
     }
 }
 
 // y[t][o] = sum_j w[t][j] * (sum over splits of d_(t,j)[o]) (+ shared d), rounded once to fp16.
+template <int KM, int SU>
 __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a)
 {
     // grid: (token, 256-column group of H)
     const int t = blockIdx.x, o = blockIdx.y * 256 + threadIdx.x;
     if (o >= a.H) return;
-    const float v = combine_value(a, t, o, a.splits_routed, a.tiles_shared ? a.splits_shared : 0);
+    const float v = combine_value<KM, SU>(a, t, o, a.splits_routed, a.tiles_shared ? a.splits_shared : 0);
     a.y[(size_t)t * a.H + o] = __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
@@ -2295,7 +2314,9 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s)
 
 hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s)
 {
-    const int grid = a.tiles_shared * a.tok_tiles_shared + a.tiles_routed * a.tok_tiles_routed;
+    const int nsplit = module == 1 ? a.splits_routed : 1;
+    if (nsplit < 1 || (module == 1 && a.splits_shared != nsplit)) return hipErrorInvalidValue;
+    const int grid = (a.tiles_shared * a.tok_tiles_shared + a.tiles_routed * a.tok_tiles_routed) * nsplit;
     if (grid == 0) return hipSuccess;
     if (module == 0)
         launch(ffn_prefill_kernel<0>, dim3(grid), dim3(kPfThreads), s, a);
@@ -2307,7 +2328,21 @@ hipError_t launch_prefill(const FfnArgs& a, int module, hipStream_t s)
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s)
 {
     if (a.T <= 0 || a.H <= 0) return hipSuccess;
-    launch(combine_kernel, dim3((unsigned)a.T, (unsigned)((a.H + 255) / 256)), dim3(256), s, a);
+    const dim3 grid((unsigned)a.T, (unsigned)((a.H + 255) / 256));
+    // picks bound 2 / 4 / 8; routed splits one (<= 2) or four per round trip
+    if (a.k > 8) return hipErrorInvalidValue;
+    const bool su1 = a.splits_routed <= 2;
+    if (a.k <= 2) {
+        if (su1) launch((combine_kernel<2, 1>), grid, dim3(256), s, a);
+        else launch((combine_kernel<2, 4>), grid, dim3(256), s, a);
+    } else if (a.k <= 4) {
+        if (su1) launch((combine_kernel<4, 1>), grid, dim3(256), s, a);
+        else launch((combine_kernel<4, 4>), grid, dim3(256), s, a);
+    } else if (su1) {
+        launch((combine_kernel<8, 1>), grid, dim3(256), s, a);
+    } else {
+        launch((combine_kernel<8, 4>), grid, dim3(256), s, a);
+    }
     return hipGetLastError();
 }
 
