@@ -474,8 +474,11 @@ UNIFORM_WIDTHS = (4, 5, 8)
 
 def _graph_ms(run_steps, L, steps, stream):
     """ms per step of `run_steps(L)` captured in one HIP graph and replayed:
-    as many untimed replays as timed ones first, so the clocks and caches are
-    in their steady state (a single cold measurement read up to 8% slower)."""
+    untimed replays first (as many as timed ones, and at least ~50 ms of GPU
+    time), so the clocks and caches are in their steady state after the
+    host-side set-up (a cold measurement read up to 8% slower, and a batch-1
+    Mixtral-shaped step measured first in its leg up to 20% slower after only
+    32 warm replays)."""
     import torch
     with torch.cuda.stream(stream):
         run_steps(L)
@@ -488,6 +491,14 @@ def _graph_ms(run_steps, L, steps, stream):
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         for _ in range(max(2, reps)):
+            graph.replay()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    one_ms = max(ev0.elapsed_time(ev1), 1e-3)
+    with torch.cuda.stream(stream):
+        for _ in range(min(10000, int(50.0 / one_ms))):
             graph.replay()
         ev0.record(stream)
         for _ in range(reps):
