@@ -661,7 +661,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=800)
-    ap.add_argument("--warmup", type=int, default=80)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first (~75 ms of graph replays: the clocks settle; 80 read ~1.4%% slower)")
     ap.add_argument("--layers", type=int, default=8, help="distinct weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true")
