@@ -970,11 +970,25 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
     a.drows = T * d.top_k + (d.inter_shared ? T : 0);
     hipStream_t s = (hipStream_t)stream;
     if (T >= kPrefillMinT) {
-        // prefill: GEMM tiles of 128 weight rows x 512 tokens, full K, one
-        // dout plane
+        // prefill: GEMM tiles of 128 weight rows x 512 tokens, full K; an
+        // expert's tail of fewer than kPrefillTail tokens past its last whole
+        // tile goes to the decode kernels instead (32-token passes that stream
+        // the expert's weights once per pass, where a GEMM tile decodes them in
+        // full for a few dozen tokens; the shared expert keeps its tiles)
         const int tt = (T + 511) / 512;
         a.tok_tiles_shared = d.inter_shared ? tt : 0;
         a.tok_tiles_routed = (T * d.top_k + 511) / 512 + std::min(E, T * d.top_k);
+        a.pf_tail = kPrefillTail;
+        // the decode launches on the tails: routed experts only, whole
+        // 128-row gate_up tiles, 32-token passes with planes kept in the MALL
+        // for a tail's later passes
+        FfnArgs tl = a;
+        tl.tiles_shared = 0;
+        tl.splits_shared = 1;
+        tl.n_slots = E;
+        tl.tok_pass = 32;
+        tl.keep_planes = 1;
+        tl.big_wgs = 0;
         {
             ProfScope ps(c, "gate_up", s);
             a.tiles_routed = (d.inter + 63) / 64;
@@ -982,13 +996,29 @@ static pw_status ffn_launch(pw_ctx* c, int layer, const uint16_t* x, int T, cons
             if ((e = launch_prefill(a, 0, s)) != hipSuccess) return hip_fail(e, "prefill gate_up launch");
         }
         {
+            ProfScope ps(c, "gate_up_tail", s);
+            tl.rg = kGateUpRowGroups;
+            tl.tiles_routed = (d.inter + 16 * tl.rg - 1) / (16 * tl.rg);
+            tl.splits_routed = 1;
+            if ((e = launch_gate_up(tl, s)) != hipSuccess) return hip_fail(e, "prefill tail gate_up launch");
+        }
+        // K in two halves where the workspace holds two partial planes (the
+        // combine sums the planes of every row, tails included)
+        const int ws_splits = std::max(down_splits(d.inter), d.inter_shared ? down_splits(d.inter_shared) : 1);
+        const int pf_splits = std::min(2, ws_splits);
+        {
             ProfScope ps(c, "down", s);
             a.tiles_routed = (d.hidden + 127) / 128;
             a.tiles_shared = d.inter_shared ? (d.hidden + 127) / 128 : 0;
-            // K in two halves where the workspace holds two partial planes
-            const int ws_splits = std::max(down_splits(d.inter), d.inter_shared ? down_splits(d.inter_shared) : 1);
-            a.splits_routed = a.splits_shared = std::min(2, ws_splits);
+            a.splits_routed = a.splits_shared = pf_splits;
             if ((e = launch_prefill(a, 1, s)) != hipSuccess) return hip_fail(e, "prefill down launch");
+        }
+        {
+            ProfScope ps(c, "down_tail", s);
+            tl.rg = kDownRowGroups;
+            tl.tiles_routed = (d.hidden + 32 * tl.rg - 1) / (32 * tl.rg);
+            tl.splits_routed = pf_splits;
+            if ((e = launch_down(tl, s)) != hipSuccess) return hip_fail(e, "prefill tail down launch");
         }
         {
             ProfScope ps(c, "combine", s);

@@ -55,6 +55,10 @@ struct FfnArgs {
     // on the routed token tiles (sum over experts of ceil(tokens / 512))
     int32_t tok_tiles_shared;
     int32_t tok_tiles_routed;
+    // prefill tails: an expert's last (n mod 512) tokens, when fewer than
+    // pf_tail, are left out of the GEMM tiles and taken by the decode launches,
+    // which then run on those tails only (0: no tails)
+    int32_t pf_tail;
     // routing inside the decode gate_up launch (logits non-null; T * k <=
     // kLayerRouteMaxAssign): every routed workgroup routes and sorts the batch
     // in LDS, and one of them writes the results that the down and combine
@@ -109,6 +113,16 @@ inline bool keep_planes(int T, int k, int E, int I_shared, int tok_pass)
 
 // Tokens per call from which the prefill GEMM path runs.
 constexpr int kPrefillMinT = 256;
+// Tokens per prefill GEMM tile, and the bound below which an expert's tail
+// (its n mod 512 tokens past the last whole tile) goes to the decode launches
+// instead of a GEMM tile: a GEMM tile decodes the expert's weights once
+// whatever its token count, a decode pass streams them once per 32 tokens.
+// Mixtral-shaped prefill, same box: a tail tile cost ~97 us of gate_up GEMM and
+// ~40 us of down GEMM, a 32-token decode pass ~27 + ~14 us, so up to three
+// passes (96 tokens) the decode launches are cheaper; with the three 24-32
+// token tails of uniform routing the layer step went 4.06-4.08 -> 3.84-3.88 ms.
+constexpr int kPrefillTokTile = 512;
+constexpr int kPrefillTail = 96;
 
 // 32-row groups per workgroup tile (two share one LUT set; four use both
 // halves of the LUT slots): gate_up tiles hold 16 * rg gate rows and their up

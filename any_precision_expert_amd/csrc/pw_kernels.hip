@@ -1268,7 +1268,10 @@ __device__ __forceinline__ void load_widths(const BlockDesc* __restrict__ table,
 // or LDS.  Each expert's rank in that order is counted branch-free, width by
 // width (one ballot each; groups of 64 experts past E are skipped, a
 // wave-uniform test), then one ballot finds the expert of rank `slot`.
-__device__ __forceinline__ SlotExpert find_slot(const int32_t* offsets, const int (&q)[4], int E, int slot)
+// tail > 0 (decode launches on prefill tails): an expert's range is its last
+// n mod kPrefillTokTile assignments when fewer than `tail`, else empty.
+__device__ __forceinline__ SlotExpert find_slot(const int32_t* offsets, const int (&q)[4], int E, int slot,
+                                                int tail = 0)
 {
     const int lane = threadIdx.x & 63;
     int lo[4], hi[4], rank[4];
@@ -1279,6 +1282,10 @@ __device__ __forceinline__ SlotExpert find_slot(const int32_t* offsets, const in
         const int ec = e < E ? e : 0;
         lo[g] = offsets[ec];
         hi[g] = offsets[ec + 1];
+        if (tail > 0) {
+            const int r = (hi[g] - lo[g]) % kPrefillTokTile;
+            lo[g] = r < tail ? hi[g] - r : hi[g];
+        }
         act[g] = e < E && hi[g] > lo[g];
         rank[g] = -1;
     }
@@ -1477,7 +1484,7 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
             tokreg = rt[kRtSorted + min(se.p0 + (int)(threadIdx.x & 63), n - 1)];
             __syncthreads();  // the slice region is reused from here on
         } else {
-            se = find_slot(a.offsets, qw, a.E, slot);
+            se = find_slot(a.offsets, qw, a.E, slot, a.pf_tail);
         }
         if (se.e < 0) return;
         p0 = se.p0;
@@ -1538,7 +1545,7 @@ __global__ void __launch_bounds__(kThreads, 4) ffn_gemv_kernel(FfnArgs a)
 // weights and sums.
 
 constexpr int kPfRows = 128;   // weight rows per tile
-constexpr int kPfTok = 512;    // tokens per tile
+constexpr int kPfTok = kPrefillTokTile;  // tokens per tile
 // 16 waves per prefill workgroup (four per SIMD; 8 is the two-per-SIMD form
 // in which every thread both decodes and gathers: 5% slower on the
 // Mixtral-shaped prefill layer)
@@ -1944,7 +1951,9 @@ __global__ void __launch_bounds__(kPfThreads, kPfWaves / 4) ffn_prefill_kernel(F
         for (int g = 0; g < (a.E + 63) / 64; ++g) {
             const int ee = 64 * g + lane;
             const int lo = ee < a.E ? a.offsets[ee] : 0, hi = ee < a.E ? a.offsets[ee + 1] : 0;
-            const int cnt = (hi - lo + kPfTok - 1) / kPfTok;
+            // token tiles of the expert (a short tail is left to the decode launches)
+            const int n = hi - lo;
+            const int cnt = a.pf_tail > 0 ? n / kPfTok + (n % kPfTok >= a.pf_tail ? 1 : 0) : (n + kPfTok - 1) / kPfTok;
             const int incl = wave_inclusive_sum(cnt);
             const int excl = base + incl - cnt;
             const uint64_t hit = __ballot(cnt > 0 && gn >= excl && gn < excl + cnt);

@@ -269,13 +269,15 @@ def prefill_leg(steps):
             b.step(0, stream)
     torch.cuda.synchronize()
     kern = {}
-    for name in ("route", "gate_up", "down", "combine"):
+    # the GEMM launches and the decode launches on the experts' short tails
+    for name in ("route", "gate_up", "gate_up_tail", "down", "down_tail", "combine"):
         kms, cnt = ctx.profile_read(name)
         kern[name] = kms / max(cnt, 1) * 1e3
     ctx.profile_enable(False)
     assign = int(b.offsets[-1].item())
-    gu_tf = 2.0 * assign * 2 * shape.I * shape.H / (kern["gate_up"] * 1e-6) / 1e12
-    dn_tf = 2.0 * assign * shape.H * shape.I / (kern["down"] * 1e-6) / 1e12
+    # every assignment's flops over the GEMM and tail launches of the module together
+    gu_tf = 2.0 * assign * 2 * shape.I * shape.H / ((kern["gate_up"] + kern["gate_up_tail"]) * 1e-6) / 1e12
+    dn_tf = 2.0 * assign * shape.H * shape.I / ((kern["down"] + kern["down_tail"]) * 1e-6) / 1e12
     all_tf = 2.0 * assign * 3 * shape.I * shape.H / (ms * 1e-3) / 1e12
     ctx.close()
     log("prefill: %.3f ms/step, gate_up %.1f TFLOP/s, down %.1f TFLOP/s" % (ms, gu_tf, dn_tf))
