@@ -205,8 +205,9 @@ def test_prefill_each_width(q):
 
 
 def test_prefill_mixed_widths_hot_expert():
-    """Mixed widths and one expert with every token: 600 tokens -> two token
-    tiles for that expert (the second holds 88), empty experts skipped."""
+    """Mixed widths and one expert with every token: 600 tokens -> one token
+    tile for that expert and a tail of 88 on the decode kernels, empty
+    experts skipped."""
     w, a = pw_synth.make_small(H=256, I=192, E=6, top_k=2, T=600, seed=710)
     a.logits[:, 4] += 100.0
     check_layer(w, a, label="prefill hot expert")
@@ -214,9 +215,9 @@ def test_prefill_mixed_widths_hot_expert():
 
 def test_prefill_ragged_token_tiles():
     """Token counts per expert just past a 512-token tile and at the 64-token
-    boundary of a wave's range: last tiles holding 1, 64 and 65 tokens (the
-    waves past them skip their matrix work), an expert with none, and a
-    shared expert whose third tile holds 130 tokens."""
+    boundary of a wave's range: tails of 1, 64 and 65 tokens past the last
+    whole tile (fewer than 96: taken by the decode kernels on the tails), an
+    expert with none, and a shared expert whose third tile holds 130 tokens."""
     counts = [513, 576, 65, 0]
     T = sum(counts)
     w, a = pw_synth.make_small(H=256, I=192, E=4, top_k=1, T=T, I_shared=96, seed=720)
@@ -224,6 +225,20 @@ def test_prefill_ragged_token_tiles():
     np.random.default_rng(720).shuffle(target)
     a.logits[np.arange(T), target] += 100.0
     check_layer(w, a, label="prefill ragged tiles")
+
+
+def test_prefill_ragged_gemm_tiles():
+    """Tails of 96 tokens or more stay GEMM tiles: last tiles holding 97, 129
+    (two whole 64-token wave ranges and one token) and 511 tokens, whose waves
+    past the last token skip their matrix work, beside an expert with a tail
+    of 95 on the decode kernels."""
+    counts = [512 + 97, 129, 511, 95]
+    T = sum(counts)
+    w, a = pw_synth.make_small(H=256, I=192, E=4, top_k=1, T=T, seed=721)
+    target = np.repeat(np.arange(4), counts)
+    np.random.default_rng(721).shuffle(target)
+    a.logits[np.arange(T), target] += 100.0
+    check_layer(w, a, label="prefill ragged GEMM tiles")
 
 
 def test_zero_tokens_enqueues_nothing():
