@@ -140,7 +140,9 @@ size_t pw_workspace_size(const pw_ctx *ctx, int T);
  * per compute unit (active experts estimated as E (1 - (1 - top_k/E)^T)),
  * gate_up runs 32-token passes over whole 128-row tiles instead; the down
  * launch keeps 16.  0 when T <= 0 or the call takes the prefill GEMM path
- * (T >= 256).  Pure function; no GPU. */
+ * (T >= 256; there an expert's tail of fewer than 96 tokens past its last
+ * 512-token GEMM tile runs on the decode contraction in 32-token passes).
+ * Pure function; no GPU. */
 int32_t pw_decode_tokens_per_pass(int T, int top_k, int E, int I_shared);
 
 /* Fix the decode contraction's tokens per pass of this context's later calls
@@ -180,9 +182,9 @@ pw_status pw_permute_by_expert(pw_ctx *ctx, const int32_t *topk_idx, int T,
 pw_status pw_route_permute(pw_ctx *ctx, const float *logits, int T, int32_t *topk_idx, float *topk_w,
                            int32_t *expert_offsets, int32_t *sorted_assign, pw_stream stream);
 
-/* The fused mixed-precision MoE FFN of one layer (Core components 3: "fused
- * mixed-precision kernel" reading planes and LUTs directly, a different width
- * per linear block inside one operation).  Every block is decoded at the width
+/* The fused mixed-precision MoE FFN of one layer ("Technical summary:
+ * PagedWeight", Core components 3: one operation reads the bit-planes and LUTs
+ * directly, each linear block at its own width).  Every block is decoded at the width
  * committed in the device page table when the work runs.
  * x: dev fp16 [T][H]; topk_idx / topk_w: as written by pw_route_topk;
  * expert_offsets / sorted_assign: as written by pw_permute_by_expert;
