@@ -1,5 +1,5 @@
 // Host bit-plane packer: uint8 parent codes -> 8 bit-planes in the library's
-// chunk-major layout (the Any-Precision "overlaid bit-plane" form of the
+// chunk-major layout (the Any-Precision overlaid bit-plane form of the
 // PagedWeight pages, Core components 1).
 //
 // Plane p holds bit (7 - p) of every code, so reading planes 0..q-1 yields
