@@ -1124,8 +1124,12 @@ pw_status pw_moe_layer(pw_ctx* c, int layer, const float* logits, const uint16_t
         const pw_model_desc& d = c->d;
         const long long n = (long long)T * d.top_k;
         const long long gu_rows = 16LL * kGateUpRowGroups;
+        // units of the shared tiles and of the experts a batch is expected to
+        // activate (the slots past the active ones exit right after routing;
+        // Qwen-shaped batch 5: 0.0445 -> 0.0432 ms with the routing inside)
+        const double act_e = d.num_experts * (1.0 - std::pow(1.0 - (double)d.top_k / d.num_experts, (double)T));
         const long long gu_units = (d.inter_shared + gu_rows - 1) / gu_rows +
-                                   std::min<long long>(d.num_experts, n) * ((d.inter + gu_rows - 1) / gu_rows);
+                                   (long long)(act_e * ((d.inter + gu_rows - 1) / gu_rows));
         double* mass = c->mass_on ? c->d_mass + (size_t)layer * d.num_experts : nullptr;
         if (T == 0 || T >= kPrefillMinT || n > kLayerRouteMaxAssign || gu_units > 2LL * c->num_cus ||
             (c->tok_pass ? c->tok_pass : decode_tok_pass(T, d.top_k, d.num_experts, d.inter_shared)) != 8) {

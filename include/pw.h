@@ -205,7 +205,8 @@ pw_status pw_moe_ffn_bitplane(pw_ctx *ctx, int layer, const uint16_t *x, int T,
  * y, bit for bit).  For decode-sized batches (T * k <= 64, T below the
  * prefill crossover of 256 tokens, and few enough gate_up work units that
  * all of them run at once: at most two per compute unit, counting the
- * shared expert's 64-row tiles and min(E, T*k) routed blocks' 64-row tiles)
+ * shared expert's 64-row tiles and those of the E (1 - (1 - k/E)^T) routed
+ * blocks a batch is expected to activate)
  * the routing runs inside the gate_up launch:
  * every workgroup with routed work routes and sorts the batch in LDS (3-5 us
  * of its start-up, while the shared expert's workgroups already stream)
