@@ -241,6 +241,15 @@ def test_prefill_ragged_gemm_tiles():
     check_layer(w, a, label="prefill ragged GEMM tiles")
 
 
+def test_prefill_tails_many_experts():
+    """A 300-token batch over 70 experts (top-2: a few tokens each, so every
+    expert's tokens are a tail taken by the decode kernels, whose slot search
+    then spans two groups of 64 experts) beside a shared expert on its GEMM
+    tiles."""
+    w, a = pw_synth.make_small(H=256, I=128, E=70, top_k=2, T=300, I_shared=64, seed=730)
+    check_layer(w, a, label="prefill tails, 70 experts")
+
+
 def test_zero_tokens_enqueues_nothing():
     import torch
     w, a = pw_synth.make_small(H=64, I=32, E=2, top_k=1, T=1, seed=404)
